@@ -1,0 +1,196 @@
+"""Textbook FP64 CG and Jacobi-PCG around the perturbed SpMV.
+
+Follows the CG recurrence of the EvoCG paper (Sec. 2.1, Eq. 1, Fig. 1, and
+the solver lines of Algorithm 1): one SpMV, two dot products and three AXPYs
+per iteration,
+
+    alpha = (r.r) / (p.q),  x += alpha p,  r_new = r - alpha q,
+    beta = (r_new.r_new) / (r.r),  p = r_new + beta p,
+
+with q = (A + E(a_k)) p the mixed-precision product (Eq. 5). The stopping
+rule is the recurrence residual ||r_k|| / ||r_0|| <= tol or k = max_iter,
+checked at the top of every iteration (Algorithm 1's loop header; Sec. 4.1
+"Unified solver configuration"). Jacobi-PCG (Sec. 4.6) keeps the precision
+control on q = A p only; z = M^-1 r with M = diag(A), every scalar in FP64,
+and the stop still uses the unpreconditioned residual.
+
+Conventions taken where the paper is silent:
+
+* x0 = 0 unless given; r0 = b - A x0 with the exact FP64 matrix.
+* K counts completed iterations; ``hist`` holds rho_0 .. rho_K with rho_0 = 1.
+* p.q <= 0 or a non-finite alpha/beta stops with status "breakdown".
+* ||r0|| = 0 returns x0 with K = 0 and hist = [0].
+* The map for iteration k is chosen from (k, rho_k) by a schedule.
+
+Test infrastructure only: see the package docstring.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import scipy.sparse as sp
+
+from . import maps as _maps
+from .rounding import to_bf16_value, to_fp32
+from .tilecsc import TileCSC
+
+
+class StaticSchedule:
+    def __init__(self, prec_map):
+        self.map = np.asarray(prec_map, dtype=np.uint8)
+
+    def map_for(self, k, rho, T):
+        return self.map if k == 0 else None
+
+
+class RatchetSchedule:
+    def __init__(self, thresholds, prec):
+        self.r = _maps.Ratchet(thresholds, prec)
+        self.current = None
+
+    def map_for(self, k, rho, T):
+        p = self.r.step(rho)
+        if p != self.current:
+            self.current = p
+            return np.full(T, p, dtype=np.uint8)
+        return None
+
+
+class TileRuleSchedule:
+    def __init__(self, scores, period, hi, lo):
+        self.scores = np.asarray(scores, dtype=np.float64)
+        self.period = int(period)
+        self.hi, self.lo = float(hi), float(lo)
+
+    def map_for(self, k, rho, T):
+        if k % self.period == 0:
+            return _maps.tile_rule(self.scores, rho, self.hi, self.lo)
+        return None
+
+
+@dataclass
+class Result:
+    x: np.ndarray
+    K: int
+    hist: list
+    status: str
+    windows: list = field(default_factory=list)  # (k, counts[3], map) at every map change
+    true_residual: float = float("nan")
+
+
+class PerturbedOperator:
+    """Holds the three value streams in CSR order and forms (A + E(map)) on demand."""
+
+    def __init__(self, L: TileCSC, indptr, indices, data):
+        self.n = L.n
+        self.T = L.T
+        tile_canon = L.tile_of_nnz()
+        self.tile_of_csr = np.empty_like(tile_canon)
+        self.tile_of_csr[L.perm] = tile_canon
+        a = np.asarray(data, dtype=np.float64)
+        self.streams = (a, to_fp32(a).astype(np.float64), to_bf16_value(a))
+        self.M = sp.csr_matrix((a.copy(), np.asarray(indices), np.asarray(indptr)),
+                               shape=(L.n, L.n))
+
+    def set_map(self, prec_map):
+        prec_nnz = np.asarray(prec_map, dtype=np.uint8)[self.tile_of_csr]
+        self.M.data = np.choose(prec_nnz, self.streams)
+
+    def __matmul__(self, p):
+        return self.M @ p
+
+
+def solve(L: TileCSC, indptr, indices, data, b, schedule, tol, maxit, x0=None,
+          jacobi=False, trace=None, keep_maps=True) -> Result:
+    n = L.n
+    A = sp.csr_matrix((np.asarray(data, dtype=np.float64), np.asarray(indices),
+                       np.asarray(indptr)), shape=(n, n))
+    op = PerturbedOperator(L, indptr, indices, data)
+    b = np.asarray(b, dtype=np.float64)
+    x = np.zeros(n) if x0 is None else np.array(x0, dtype=np.float64)
+    r = b - A @ x
+    if jacobi:
+        dinv = 1.0 / A.diagonal()
+        z = dinv * r
+    else:
+        z = r
+    p = z.copy()
+    rr = float(np.dot(r, r))
+    rz = float(np.dot(r, z))
+    norm0 = math.sqrt(rr)
+    windows = []
+    if norm0 == 0.0:
+        res = Result(x=x, K=0, hist=[0.0], status="converged", windows=windows)
+        res.true_residual = _true_residual(A, x, b)
+        return res
+    hist = [1.0]
+    k = 0
+    status = "maxit"
+    while True:
+        rho = hist[-1]
+        if rho <= tol:
+            status = "converged"
+            break
+        if k == maxit:
+            status = "maxit"
+            break
+        new_map = schedule.map_for(k, rho, L.T)
+        if new_map is not None:
+            op.set_map(new_map)
+            counts = np.bincount(new_map, minlength=3)[:3].tolist()
+            windows.append((k, counts, new_map.copy() if keep_maps else None))
+        q = op @ p
+        pq = float(np.dot(p, q))
+        if not (pq > 0.0) or not math.isfinite(pq):
+            status = "breakdown"
+            break
+        alpha = rz / pq
+        if trace is not None:
+            trace(k, x, r, p, q, alpha)
+        x += alpha * p
+        r -= alpha * q
+        rr_new = float(np.dot(r, r))
+        if jacobi:
+            z = dinv * r
+            rz_new = float(np.dot(r, z))
+        else:
+            z = r
+            rz_new = rr_new
+        beta = rz_new / rz
+        if not (math.isfinite(alpha) and math.isfinite(beta)):
+            status = "breakdown"
+            k += 1
+            hist.append(math.sqrt(rr_new) / norm0)
+            break
+        p = z + beta * p
+        rz = rz_new
+        k += 1
+        hist.append(math.sqrt(rr_new) / norm0)
+    res = Result(x=x, K=k, hist=hist, status=status, windows=windows)
+    res.true_residual = _true_residual(A, x, b)
+    return res
+
+
+def _true_residual(A, x, b):
+    nb = float(np.linalg.norm(b))
+    r = b - A @ x
+    return float(np.linalg.norm(r)) / nb if nb > 0 else float(np.linalg.norm(r))
+
+
+def schedule_for(spec: dict, L: TileCSC, scores=None, static=None):
+    """Build the schedule that a workload's map specification describes."""
+    kind = spec["kind"]
+    if kind == "fp64":
+        return StaticSchedule(np.zeros(L.T, dtype=np.uint8))
+    if kind == "static":
+        return StaticSchedule(static)
+    if kind == "magnitude":
+        return StaticSchedule(_maps.magnitude_rule(L, spec["t_bf16"], spec["t_fp32"]))
+    if kind == "ratchet":
+        return RatchetSchedule(spec["thresholds"], spec["prec"])
+    if kind == "tile_rule":
+        return TileRuleSchedule(scores, spec["period"], spec["hi"], spec["lo"])
+    raise ValueError(kind)

@@ -1,0 +1,71 @@
+"""Precision-map rules of the five workloads (codes 0 = FP64, 1 = FP32, 2 = BF16).
+
+The EvoCG paper selects tile precisions with a learned policy (Sec. 3.2),
+which is out of scope here; the workloads use rules instead. The paper fixes
+the action encoding (Eq. 9: a in {0, 1, 2} for {FP64, FP32, BF16}) and the
+idea of re-selecting a map at the start of a reuse window and keeping it for
+the window (Sec. 3.4, "Interval Reuse Scheduling"). Every rule below is a
+reading of a workload description and is applied per tile.
+
+Test infrastructure only: see the package docstring.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .tilecsc import TileCSC
+
+FP64, FP32, BF16 = 0, 1, 2
+
+
+def magnitude_rule(L: TileCSC, t_bf16: float = 1e-4, t_fp32: float = 1e-2) -> np.ndarray:
+    """Map from ratio_t = max_{(i,j) in t} |a_ij| / max_i |a_ii| (global diagonal max).
+
+    BF16 if ratio_t < t_bf16, FP32 if ratio_t < t_fp32, else FP64 (strict
+    comparisons, FP64 division).
+    """
+    tile = L.tile_of_nnz()
+    rb = L.tile_row_block()[tile]
+    rows = rb * L.R + L.row_idx.astype(np.int64)
+    cols = L.tile_col_idx.astype(np.int64)[tile] * L.C + L.local_col()
+    absval = np.abs(L.val)
+    diag = absval[rows == cols]
+    dmax = float(diag.max()) if diag.size else 0.0
+    tmax = np.zeros(L.T, dtype=np.float64)
+    np.maximum.at(tmax, tile, absval)
+    ratio = tmax / dmax
+    out = np.full(L.T, FP64, dtype=np.uint8)
+    out[ratio < t_fp32] = FP32
+    out[ratio < t_bf16] = BF16
+    return out
+
+
+class Ratchet:
+    """One-way residual schedule: the map for iteration k depends on rho_k = ||r_k|| / ||r_0||.
+
+    ``prec[0]`` applies until rho <= thresholds[0] has been seen, ``prec[1]``
+    until rho <= thresholds[1] has been seen, and so on; a stage once reached
+    is never left. The map is uniform over all tiles.
+    """
+
+    def __init__(self, thresholds, prec):
+        self.thresholds = [float(t) for t in thresholds]
+        self.prec = [int(p) for p in prec]
+        if len(self.prec) != len(self.thresholds) + 1:
+            raise ValueError("need one more precision than thresholds")
+        self.stage = 0
+
+    def step(self, rho: float) -> int:
+        while self.stage < len(self.thresholds) and rho <= self.thresholds[self.stage]:
+            self.stage += 1
+        return self.prec[self.stage]
+
+
+def tile_rule(scores: np.ndarray, rho: float, hi: float = 1e-3, lo: float = 1e-6) -> np.ndarray:
+    """Per-tile re-selection: v_t = s_t * rho; BF16 if v_t > hi, FP32 if v_t > lo, else FP64."""
+    v = np.asarray(scores, dtype=np.float64) * float(rho)
+    out = np.full(v.shape, FP64, dtype=np.uint8)
+    out[v > lo] = FP32
+    out[v > hi] = BF16
+    return out

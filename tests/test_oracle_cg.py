@@ -1,0 +1,174 @@
+"""Pins for the oracle's CG and Jacobi-PCG.
+
+Each check rests on something outside the oracle: a dense Cholesky solve,
+the finite-termination property of CG on a matrix with k distinct
+eigenvalues, A-orthogonality of the search directions, orthogonality of the
+residuals, agreement of the recurrence residual with the true residual, and
+the equivalence of Jacobi-PCG with CG on the symmetrically scaled system.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg as sla
+import scipy.sparse as sp
+
+from gen import make_workload
+from oracle import cg, tilecsc as tc
+
+
+def _csr(M):
+    M = sp.csr_matrix(M)
+    M.sort_indices()
+    return M
+
+
+def _solve(M, b, tol, maxit, R=4, C=4, jacobi=False, trace=None, prec_map=None, x0=None):
+    L = tc.build(M.shape[0], M.indptr, M.indices, M.data, R, C)
+    sched = cg.StaticSchedule(np.zeros(L.T, np.uint8) if prec_map is None else prec_map)
+    return cg.solve(L, M.indptr, M.indices, M.data, b, sched, tol, maxit, x0=x0,
+                    jacobi=jacobi, trace=trace)
+
+
+def test_cg_matches_dense_cholesky():
+    rng = np.random.default_rng(0)
+    n = 40
+    B = rng.standard_normal((n, n))
+    Adense = B @ B.T + n * np.eye(n)
+    b = rng.standard_normal(n)
+    res = _solve(_csr(Adense), b, 1e-14, 500)
+    x_chol = sla.cho_solve(sla.cho_factor(Adense), b)
+    assert res.status == "converged"
+    assert np.linalg.norm(res.x - x_chol) <= 1e-10 * np.linalg.norm(x_chol)
+
+
+@pytest.mark.parametrize("k", [1, 3, 7])
+def test_cg_terminates_in_k_steps_on_k_distinct_eigenvalues(k):
+    n = 200
+    eig = np.repeat(np.arange(1, k + 1, dtype=np.float64) * 2.0, -(-n // k))[:n]
+    rng = np.random.default_rng(k)
+    b = rng.uniform(-1, 1, n)
+    res = _solve(_csr(sp.diags(eig)), b, 1e-10, 100)
+    assert res.status == "converged"
+    assert res.K <= k
+
+
+def _collect(w, iters=10, jacobi=False):
+    A = w.A
+    P, X, Rv = [], [], []
+
+    def tr(k, x, r, p, q, alpha):
+        if k < iters:
+            P.append(p.copy())
+            X.append(x.copy())
+            Rv.append(r.copy())
+
+    L = tc.build(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    sched = cg.StaticSchedule(np.zeros(L.T, np.uint8))
+    res = cg.solve(L, A.indptr, A.indices, A.data, w.b, sched, 1e-12, iters, trace=tr,
+                   jacobi=jacobi)
+    return A.to_scipy(), P, X, Rv, res
+
+
+def test_search_directions_are_A_orthogonal():
+    w = make_workload(1, "small")
+    S, P, _, _, _ = _collect(w)
+    ap = [S @ p for p in P]
+    norms = [math.sqrt(float(p @ q)) for p, q in zip(P, ap)]
+    for i in range(len(P)):
+        for j in range(len(P)):
+            if i != j:
+                assert abs(float(P[i] @ ap[j])) / (norms[i] * norms[j]) < 1e-8
+
+
+def test_residuals_are_orthogonal():
+    w = make_workload(2, "small")
+    S, _, _, Rv, _ = _collect(w)
+    for i in range(len(Rv)):
+        for j in range(i):
+            c = abs(float(Rv[i] @ Rv[j])) / (np.linalg.norm(Rv[i]) * np.linalg.norm(Rv[j]))
+            assert c < 1e-8
+
+
+def test_recurrence_residual_tracks_true_residual():
+    w = make_workload(1, "small")
+    A = w.A
+    S = A.to_scipy()
+    gaps = []
+
+    def tr(k, x, r, p, q, alpha):
+        gaps.append(np.linalg.norm((w.b - S @ x) - r) / np.linalg.norm(w.b))
+
+    L = tc.build(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    res = cg.solve(L, A.indptr, A.indices, A.data, w.b, cg.StaticSchedule(np.zeros(L.T, np.uint8)),
+                   w.tol, w.maxit, trace=tr)
+    assert res.status == "converged"
+    assert max(gaps) < 1e-12
+    assert abs(res.true_residual - res.hist[-1] * np.linalg.norm(w.b) / np.linalg.norm(w.b)) < 1e-11
+
+
+def test_jacobi_pcg_equals_cg_on_scaled_system():
+    w = make_workload(3, "small")
+    A = w.A
+    S = A.to_scipy()
+    d = S.diagonal()
+    Dm = sp.diags(1.0 / np.sqrt(d))
+    Sh = _csr(Dm @ S @ Dm)
+    bh = w.b / np.sqrt(d)
+    m = 25
+    r1 = _solve(S.tocsr(), w.b, 0.0, m, R=16, C=16, jacobi=True)
+    r2 = _solve(Sh, bh, 0.0, m, R=16, C=16)
+    x_from_scaled = r2.x / np.sqrt(d)
+    assert r1.K == r2.K == m
+    assert np.linalg.norm(r1.x - x_from_scaled) <= 1e-8 * np.linalg.norm(x_from_scaled)
+
+
+def test_jacobi_pcg_on_diagonal_matrix_is_one_step():
+    d = np.linspace(1.0, 1e4, 300)
+    b = np.random.default_rng(0).uniform(-1, 1, 300)
+    res = _solve(_csr(sp.diags(d)), b, 1e-12, 10, jacobi=True)
+    assert res.K == 1
+    assert np.allclose(res.x, b / d, rtol=1e-14)
+
+
+def test_breakdown_on_indefinite_matrix():
+    res = _solve(_csr(np.diag([1.0, -1.0])), np.array([1.0, 1.0]), 1e-10, 10)
+    assert res.status == "breakdown" and res.K == 0
+
+
+def test_degenerate_inputs():
+    M = _csr(np.diag([2.0, 3.0, 4.0]))
+    z = _solve(M, np.zeros(3), 1e-10, 10)
+    assert z.K == 0 and z.hist == [0.0] and z.status == "converged"
+    m0 = _solve(M, np.ones(3), 1e-10, 0)
+    assert m0.K == 0 and m0.hist == [1.0] and m0.status == "maxit"
+    t1 = _solve(M, np.ones(3), 1.0, 10)
+    assert t1.K == 0 and t1.status == "converged"
+    xs = np.array([1.0, 2.0, 3.0])
+    ex = _solve(M, M @ xs, 1e-10, 10, x0=xs)  # exact initial guess
+    assert ex.K == 0 and np.array_equal(ex.x, xs)
+
+
+def test_integer_stencil_mixed_map_reproduces_fp64_history():
+    w = make_workload(2, "small")
+    A = w.A
+    L = tc.build(A.n, A.indptr, A.indices, A.data, 16, 16)
+    mixed = np.random.default_rng(2).integers(0, 3, L.T).astype(np.uint8)
+    r64 = cg.solve(L, A.indptr, A.indices, A.data, w.b, cg.StaticSchedule(np.zeros(L.T, np.uint8)),
+                   w.tol, w.maxit)
+    rmx = cg.solve(L, A.indptr, A.indices, A.data, w.b, cg.StaticSchedule(mixed), w.tol, w.maxit)
+    assert r64.hist == rmx.hist and np.array_equal(r64.x, rmx.x)
+
+
+def test_low_precision_values_raise_true_residual_floor():
+    """Eq. (3): a perturbed operator leaves a true-residual gap the recurrence does not see."""
+    w = make_workload(3, "small")
+    A = w.A
+    L = tc.build(A.n, A.indptr, A.indices, A.data, 16, 16)
+    r16 = cg.solve(L, A.indptr, A.indices, A.data, w.b,
+                   cg.StaticSchedule(np.full(L.T, 2, np.uint8)), 1e-10, 10_000)
+    r64 = cg.solve(L, A.indptr, A.indices, A.data, w.b,
+                   cg.StaticSchedule(np.zeros(L.T, np.uint8)), 1e-10, 10_000)
+    assert r64.status == "converged" and r64.true_residual < 1e-9
+    assert r16.true_residual > 100 * r16.hist[-1]
