@@ -1,0 +1,228 @@
+/*
+ * mpcg.h -- C ABI of the mixed-precision Tile-CSC Conjugate Gradient library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "EvoCG: Self-Evolving Precision Control for Faster
+ * Conjugate Gradient" (Zhai et al.):
+ *   - Tile-CSC storage: Sec. 3.3 and Fig. 4(a)/(b);
+ *   - three resident value streams (FP64, FP32, BF16) selected per tile:
+ *     Sec. 3.3.2 and Sec. 4.8 "Memory cost";
+ *   - the precision action encoding {0, 1, 2} = {FP64, FP32, BF16}: Eq. (9);
+ *   - the mixed-precision product y = (A + E(a)) p: Eq. (2) and Eq. (5);
+ *   - the CG recurrence: Sec. 2.1, Eq. (1), Fig. 1 and Algorithm 1's solver
+ *     lines; Jacobi-preconditioned CG: Sec. 4.6;
+ *   - the stopping rule ||r_k||/||r_0|| <= tol or k = max_iter: Sec. 4.1.
+ *
+ * Conventions for every entry point:
+ *   - Return value: CG_OK (0) on success, a positive status from cg_solve,
+ *     or a negative error code. No entry point aborts; on error,
+ *     cg_last_error() returns a message naming the bad argument (the message
+ *     is per calling thread and valid until that thread's next call).
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are HIP
+ *     device memory of the GPU the handle was created on (for example the
+ *     data pointer of a torch tensor on that GPU).
+ *   - A stream argument is a hipStream_t passed as void*; NULL means the
+ *     default stream.
+ *   - All device-side indices are 32-bit: a handle accepts at most
+ *     2^31 - 1 nonzeros and 2^31 - 1 non-empty tiles.
+ *   - Handles are not thread-safe: calls on one handle must not overlap.
+ */
+#ifndef MPCG_H
+#define MPCG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    CG_OK = 0,
+    CG_NOT_CONVERGED = 1, /* cg_solve stopped at maxit */
+    CG_BREAKDOWN = 2,     /* cg_solve met p.q <= 0 or a non-finite scalar */
+    CG_EINVAL = -1,       /* invalid argument or input data */
+    CG_ENOMEM = -2,       /* host or device allocation failed */
+    CG_EDEVICE = -3,      /* a HIP runtime call failed */
+    CG_EINTERNAL = -4
+};
+
+/* Precision codes of a tile (Eq. (9)). */
+enum { CG_FP64 = 0, CG_FP32 = 1, CG_BF16 = 2 };
+
+/* Opaque host-side canonical Tile-CSC matrix. */
+typedef struct cg_tilecsc cg_tilecsc;
+/* Opaque solver handle: device-resident matrix, value planes, map, CG state. */
+typedef struct cg_handle cg_handle;
+
+/*
+ * Read-only view of a canonical Tile-CSC matrix (Sec. 3.3, Fig. 4):
+ *   tile (I, J) covers rows [I*R, (I+1)*R) and columns [J*C, (J+1)*C);
+ *   non-empty tiles are listed row block by row block, column blocks
+ *   ascending; tile t owns nonzeros tile_nnz_ptr[t] .. tile_nnz_ptr[t+1]-1,
+ *   stored column by column (CSC) with row offsets ascending in a column.
+ * Pointers are owned by the library object the view came from.
+ */
+typedef struct {
+    int64_t n;                    /* rows (= columns) */
+    int64_t T;                    /* non-empty tiles */
+    int64_t nnz;
+    int32_t R, C;                 /* tile height and width, each in [1, 256] */
+    const int64_t* tile_row_ptr;  /* [ceil(n/R) + 1] */
+    const int32_t* tile_col_idx;  /* [T] column-block index */
+    const int64_t* tile_nnz_ptr;  /* [T + 1] */
+    const uint8_t* row_idx;       /* [nnz] row offset inside the row block */
+    const uint8_t* col_local;     /* [nnz] column offset inside the tile */
+    const double* val;            /* [nnz] FP64 values in canonical order */
+} cg_tilecsc_view;
+
+/*
+ * Build the canonical Tile-CSC form of a square CSR matrix (Sec. 3.3).
+ *   n       : rows and columns, n >= 1.
+ *   rowptr  : host int64[n+1], rowptr[0] = 0, non-decreasing.
+ *   colind  : host int32[nnz], strictly increasing inside each row, in [0, n).
+ *   val     : host double[nnz], finite (explicit zeros are kept as entries).
+ *   R, C    : tile shape, each in [1, 256].
+ *   out     : receives a library-owned object; free with cg_tilecsc_free.
+ * Inputs are read only and may be freed after the call.
+ * Errors: CG_EINVAL (bad sizes, unsorted or duplicate columns, non-finite
+ * values, more than 2^31 - 1 nonzeros), CG_ENOMEM.
+ */
+int cg_tilecsc_from_csr(int64_t n, const int64_t* rowptr, const int32_t* colind,
+                        const double* val, int32_t R, int32_t C, cg_tilecsc** out);
+
+/* Fill *view with pointers into A (valid until cg_tilecsc_free(A)). */
+int cg_tilecsc_get_view(const cg_tilecsc* A, cg_tilecsc_view* view);
+
+/* Intra-tile column pointers (Fig. 4(b) colPtr, unpadded): host int32[T*(C+1)],
+ * entry t*(C+1)+c is the start of local column c relative to the tile's first
+ * nonzero. */
+int cg_tilecsc_col_ptr(const cg_tilecsc* A, int32_t* out);
+
+/* CSR position of every canonical nonzero: host int64[nnz]. */
+int cg_tilecsc_perm(const cg_tilecsc* A, int64_t* out);
+
+void cg_tilecsc_free(cg_tilecsc* A);
+
+/* Options for cg_create. Zero-initialise and set what you need. */
+typedef struct {
+    int32_t jacobi;      /* 1: Jacobi-preconditioned CG (Sec. 4.6), M = diag(A) */
+    int32_t window;      /* iterations enqueued between stop-flag polls; 0 = default (16) */
+    int32_t use_graph;   /* 1: replay each window as a captured HIP graph; 0 = plain launches;
+                            -1 = default (graph) */
+    int32_t reserved[5];
+} cg_options;
+
+/*
+ * Create a solver handle on the current HIP device.
+ *   A             : canonical matrix; copied to library-owned device memory
+ *                   (index arrays, the FP64 values, and the FP32 and BF16 value
+ *                   planes rounded on the device by round-to-nearest-even from
+ *                   FP64). A may be freed right after the call.
+ *   precision_map : host uint8[T] with codes 0/1/2, or NULL for all FP64.
+ *   opt           : NULL for defaults.
+ *   stream        : stream for the set-up copies and kernels.
+ * Errors: CG_EINVAL (map code > 2, bad layout, Jacobi with a zero or
+ * missing diagonal entry), CG_ENOMEM, CG_EDEVICE.
+ */
+int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, const cg_options* opt,
+              void* stream, cg_handle** out);
+
+int cg_destroy(cg_handle* h);
+
+/* Replace the active per-tile map (uint8[T], codes 0..2) without touching the
+ * value planes (Sec. 3.3.2: switching reads another stream, nothing is
+ * re-uploaded). on_device = 0: host pointer; 1: device pointer. Clears any
+ * schedule. Synchronous with respect to the host. */
+int cg_set_precision_map(cg_handle* h, const uint8_t* map, int32_t on_device);
+
+/* Copy the active map to host uint8[T]. Under a uniform residual schedule the
+ * map reported is that stage's precision for every tile. */
+int cg_get_active_map(const cg_handle* h, uint8_t* out);
+
+/* Static magnitude rule, computed on the device: ratio_t = max |a_ij| over the
+ * tile / max |a_ii| over the whole diagonal (FP64 division); BF16 if
+ * ratio_t < t_bf16, FP32 if ratio_t < t_fp32, else FP64. Sets the active map
+ * and clears any schedule. Requires t_bf16 <= t_fp32. */
+int cg_map_from_magnitude(cg_handle* h, double t_bf16, double t_fp32);
+
+/* One-way residual schedule (uniform over tiles): precision prec[0] until
+ * rho_k = ||r_k||/||r_0|| <= thresholds[0] has been seen, then prec[1] until
+ * rho_k <= thresholds[1], ... ; a stage once reached is kept. nstage >= 1 is
+ * the number of precisions; thresholds has nstage-1 entries. Applies to
+ * cg_solve; cg_spmv uses prec[0]. */
+int cg_set_schedule_residual(cg_handle* h, int32_t nstage, const double* thresholds,
+                             const uint8_t* prec);
+
+/* Windowed per-tile rule (Sec. 3.4 "Interval Reuse Scheduling": a map chosen
+ * at a window start is kept for the window). At every k with k % period == 0,
+ * v_t = scores[t] * rho_k and tile t gets BF16 if v_t > hi, FP32 if v_t > lo,
+ * else FP64. scores: host double[T], copied. Requires period >= 1, lo <= hi. */
+int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const double* scores, double hi,
+                              double lo);
+
+/* Apply the tile rule of cg_set_schedule_tile_rule once at the given rho and
+ * make the result the active map (the schedule stays set). */
+int cg_eval_tile_rule(cg_handle* h, double rho);
+
+/* Remove any schedule; the active map stays as it is. */
+int cg_clear_schedule(cg_handle* h);
+
+/*
+ * y = (A + E(map)) x (Eq. (5)): each tile's values are read from the plane
+ * its active map entry selects, widened exactly, and every product and sum is
+ * formed in FP64.
+ *   x, y : device double[n]; y must not overlap x. Asynchronous on stream.
+ * Errors: CG_EINVAL on NULL or overlapping pointers.
+ */
+int cg_spmv(cg_handle* h, const double* x, double* y, void* stream);
+
+/*
+ * Solve A x = b by CG (or Jacobi-PCG when the handle was created with
+ * opt.jacobi) with the mixed-precision SpMV under the active map or schedule.
+ *   b          : device double[n].
+ *   x0         : device double[n] initial guess, or NULL for zero.
+ *                r0 = b - A x0 uses the exact FP64 values.
+ *   tol        : stop when ||r_k||/||r_0|| <= tol (recurrence residual), tol >= 0.
+ *   maxit      : iteration cap, maxit >= 0.
+ *   x          : device double[n] receiving the last iterate; may equal x0.
+ *   iterations : host int32, completed iterations K.
+ *   res_hist   : host double[maxit+1] receiving rho_0 .. rho_K (rho_0 = 1;
+ *                a zero r0 gives K = 0 and rho_0 = 0), or NULL.
+ *   stream     : the solve is ordered after prior work on stream; the call
+ *                returns when the solve has finished.
+ * Returns CG_OK (converged), CG_NOT_CONVERGED (K = maxit), CG_BREAKDOWN
+ * (p.q <= 0 or non-finite alpha/beta; x holds the last iterate), or an error.
+ */
+int cg_solve(cg_handle* h, const double* b, const double* x0, double tol, int32_t maxit,
+             double* x, int32_t* iterations, double* res_hist, void* stream);
+
+/* Map trace of the last cg_solve: one entry per map change (the first at
+ * k = 0). Writes up to cap entries: k_out[i] (iteration the map took effect)
+ * and counts_out[3*i + p] (tiles at precision p). Returns the number of
+ * entries recorded (which may exceed cap), or a negative error. */
+int cg_get_map_trace(const cg_handle* h, int32_t cap, int32_t* k_out, int64_t* counts_out);
+
+/* Copy the device-resident layout back to host arrays in canonical form:
+ * tile_row_ptr int64[ceil(n/R)+1], tile_col_idx int32[T], tile_nnz_ptr
+ * int64[T+1], row_idx uint8[nnz], col_local uint8[nnz], and the three value
+ * planes val64 double[nnz], val32 float[nnz], bf16 uint16[nnz] (bit
+ * patterns). Any output pointer may be NULL to skip it. */
+int cg_export_layout(const cg_handle* h, int64_t* tile_row_ptr, int32_t* tile_col_idx,
+                     int64_t* tile_nnz_ptr, uint8_t* row_idx, uint8_t* col_local,
+                     double* val64, float* val32, uint16_t* bf16);
+
+/* Sizes of a handle: n, T, nnz, R, C (any pointer may be NULL). */
+int cg_get_sizes(const cg_handle* h, int64_t* n, int64_t* T, int64_t* nnz, int32_t* R,
+                 int32_t* C);
+
+/* Device-resident bytes held by the handle (matrix, planes, map, vectors). */
+int64_t cg_device_bytes(const cg_handle* h);
+
+const char* cg_last_error(void);
+int cg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MPCG_H */

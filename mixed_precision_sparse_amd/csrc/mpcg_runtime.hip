@@ -1,0 +1,756 @@
+// HIP runtime behind the C ABI: device-resident Tile-CSC matrix with its
+// three value planes, the precision map and schedules, cg_spmv, and the
+// cg_solve loop (device-resident scalars, window-wise stop polling, optional
+// HIP-graph replay of each window).
+//
+// EvoCG paper: value-stream selection without re-quantisation (Sec. 3.3.2,
+// Sec. 4.8), the per-iteration CG step (Sec. 2.1, Fig. 1), interval reuse of
+// a map over a window (Sec. 3.4), device-side reductions and scalar broadcast
+// plus graph replay of the solver backbone (Sec. 3.4 "Fused Execution and
+// Graph Replay"), Jacobi-PCG (Sec. 4.6), stopping rule (Sec. 4.1).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "mpcg_internal.hpp"
+#include "mpcg_kernels.hpp"
+
+using mpcg::fail;
+namespace dev = mpcg::dev;
+
+namespace {
+
+enum SchedKind { kSchedStatic = 0, kSchedResidual = 1, kSchedTileRule = 2 };
+
+struct DeviceBuffers {
+    std::vector<void*> owned;
+    ~DeviceBuffers() {
+        for (void* p : owned) (void)hipFree(p);
+    }
+};
+
+}  // namespace
+
+struct cg_handle {
+    int device = 0;
+    hipStream_t stream = nullptr;  // internal stream for the solve loop
+    int64_t n = 0, T = 0, nnz = 0, nrb = 0;
+    int32_t R = 0, C = 0, G = 0, rows_per_group = 0, ngroups = 0;
+    bool meta16 = false;
+    bool jacobi = false;
+    int window = 16;
+    bool use_graph = true;
+    int64_t device_bytes = 0;
+
+    // Matrix (device).
+    int32_t* trp = nullptr;
+    int32_t* tcol = nullptr;
+    int32_t* tptr = nullptr;
+    uint8_t* map = nullptr;
+    void* meta = nullptr;
+    double* v64 = nullptr;
+    float* v32 = nullptr;
+    uint16_t* v16 = nullptr;
+    double* dinv = nullptr;
+
+    // CG vectors and reduction scratch (device).
+    double *x = nullptr, *r = nullptr, *p = nullptr, *q = nullptr, *z = nullptr;
+    double* partials = nullptr;
+    int partial_cap = 0;
+    dev::State* st = nullptr;
+    double* hist = nullptr;
+    int64_t hist_cap = 0;
+    int32_t* trace_k = nullptr;
+    int64_t* trace_counts = nullptr;
+    int64_t trace_cap = 0;
+    unsigned long long* scratch_u64 = nullptr;
+
+    // Schedules.
+    int sched = kSchedStatic;
+    std::vector<double> thresholds;
+    std::vector<int32_t> stage_prec;
+    double* scores = nullptr;
+    int32_t period = 0;
+    double hi = 0.0, lo = 0.0;
+
+    // Host staging for polling.
+    int32_t* pinned = nullptr;  // [2 windows][2 ints] (done, k)
+    hipEvent_t ev[2] = {nullptr, nullptr};
+
+    // Captured window graph.
+    hipGraphExec_t graph = nullptr;
+    int graph_window = 0;
+    int graph_sched = -1;
+
+    DeviceBuffers bufs;
+};
+
+namespace {
+
+#define HIP_CHECK(expr)                                                                   \
+    do {                                                                                  \
+        hipError_t e_ = (expr);                                                           \
+        if (e_ != hipSuccess)                                                             \
+            return fail(CG_EDEVICE, std::string(#expr) + ": " + hipGetErrorString(e_));   \
+    } while (0)
+
+template <class Tp>
+int dalloc(cg_handle* h, Tp** ptr, int64_t count) {
+    *ptr = nullptr;
+    if (count <= 0) count = 1;
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, sizeof(Tp) * (size_t)count);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(CG_ENOMEM, "device allocation of " + std::to_string(sizeof(Tp) * count) +
+                                   " bytes failed: " + hipGetErrorString(e));
+    }
+    h->bufs.owned.push_back(p);
+    h->device_bytes += (int64_t)(sizeof(Tp) * count);
+    *ptr = static_cast<Tp*>(p);
+    return CG_OK;
+}
+
+void dfree(cg_handle* h, void* p) {
+    if (!p) return;
+    auto it = std::find(h->bufs.owned.begin(), h->bufs.owned.end(), p);
+    if (it != h->bufs.owned.end()) h->bufs.owned.erase(it);
+    (void)hipFree(p);
+}
+
+int grid_for(int64_t work, int per_thread, int cap) {
+    int64_t g = (work + (int64_t)dev::kBlock * per_thread - 1) / ((int64_t)dev::kBlock * per_thread);
+    return (int)std::max<int64_t>(1, std::min<int64_t>(g, cap));
+}
+
+constexpr int kVecGridCap = 2048;
+
+int vec_grid(const cg_handle* h) { return grid_for(h->n, 4, kVecGridCap); }
+int spmv_grid(const cg_handle* h) {
+    return (int)((h->ngroups + dev::kWavesPerBlock - 1) / dev::kWavesPerBlock);
+}
+
+dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t* uprec) {
+    dev::SpmvArgs a{};
+    a.trp = h->trp;
+    a.tcol = h->tcol;
+    a.tptr = h->tptr;
+    a.map = h->map;
+    a.meta = h->meta;
+    a.v64 = h->v64;
+    a.v32 = h->v32;
+    a.v16 = h->v16;
+    a.x = x;
+    a.y = y;
+    a.b = nullptr;
+    a.uprec = uprec;
+    a.st = h->st;
+    a.partials = h->partials;
+    a.n = (int32_t)h->n;
+    a.nrb = (int32_t)h->nrb;
+    a.R = h->R;
+    a.C = h->C;
+    a.G = h->G;
+    a.rows_per_group = h->rows_per_group;
+    a.ngroups = h->ngroups;
+    return a;
+}
+
+template <int MODE>
+void launch_spmv(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
+    const int grid = spmv_grid(h);
+    if (h->meta16)
+        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE>), dim3(grid), dim3(dev::kBlock), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE>), dim3(grid), dim3(dev::kBlock), 0,
+                           s, a);
+}
+
+dev::VecArgs vec_args(cg_handle* h, const double* b, const double* x0) {
+    dev::VecArgs a{};
+    a.x = h->x;
+    a.r = h->r;
+    a.p = h->p;
+    a.q = h->q;
+    a.z = h->z;
+    a.dinv = h->dinv;
+    a.b = b;
+    a.x0 = x0;
+    a.hist = h->hist;
+    a.st = h->st;
+    a.partials = h->partials;
+    a.trace_k = h->trace_k;
+    a.trace_counts = h->trace_counts;
+    a.T = h->T;
+    a.n = (int32_t)h->n;
+    a.jacobi = h->jacobi ? 1 : 0;
+    a.r_ready = 0;
+    return a;
+}
+
+dev::MapArgs map_args(cg_handle* h, double rho, int solve) {
+    dev::MapArgs a{};
+    a.map = h->map;
+    a.scores = h->scores;
+    a.st = h->st;
+    a.hist = h->hist;
+    a.trace_k = h->trace_k;
+    a.trace_counts = h->trace_counts;
+    a.T = h->T;
+    a.rho = rho;
+    a.solve = solve;
+    return a;
+}
+
+// Writes the host-side schedule description into the device state.
+int upload_schedule(cg_handle* h) {
+    dev::State hs{};
+    HIP_CHECK(hipMemcpy(&hs, h->st, sizeof(hs), hipMemcpyDeviceToHost));
+    hs.nstage = 0;
+    hs.period = 0;
+    hs.spmv_uprec = -1;
+    if (h->sched == kSchedResidual) {
+        hs.nstage = (int32_t)h->stage_prec.size();
+        for (size_t i = 0; i < h->thresholds.size(); ++i) hs.thresholds[i] = h->thresholds[i];
+        for (size_t i = 0; i < h->stage_prec.size(); ++i) hs.stage_prec[i] = h->stage_prec[i];
+        hs.spmv_uprec = h->stage_prec[0];
+    } else if (h->sched == kSchedTileRule) {
+        hs.period = h->period;
+        hs.hi = h->hi;
+        hs.lo = h->lo;
+    }
+    hs.zero_prec = 0;
+    hs.uprec = hs.spmv_uprec;
+    HIP_CHECK(hipMemcpy(h->st, &hs, sizeof(hs), hipMemcpyHostToDevice));
+    return CG_OK;
+}
+
+void drop_graph(cg_handle* h) {
+    if (h->graph) (void)hipGraphExecDestroy(h->graph);
+    h->graph = nullptr;
+    h->graph_window = 0;
+    h->graph_sched = -1;
+}
+
+// One CG iteration: [map window step] -> SpMV with fused p.q and alpha ->
+// x/r update with fused r.r (r.z), beta, rho and stop flag -> new direction.
+void enqueue_iteration(cg_handle* h, hipStream_t s) {
+    if (h->sched == kSchedTileRule) {
+        dev::MapArgs ma = map_args(h, 0.0, 1);
+        hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(grid_for(h->T, 4, 1024)), dim3(dev::kBlock), 0,
+                           s, ma);
+    }
+    dev::SpmvArgs sa = spmv_args(h, h->p, h->q, &h->st->uprec);
+    launch_spmv<dev::kSpmvCg>(h, sa, s);
+    dev::VecArgs va = vec_args(h, nullptr, nullptr);
+    hipLaunchKernelGGL(dev::cg_update_kernel, dim3(vec_grid(h)), dim3(dev::kBlock), 0, s, va);
+    hipLaunchKernelGGL(dev::cg_direction_kernel, dim3(vec_grid(h)), dim3(dev::kBlock), 0, s, va);
+}
+
+int ensure_graph(cg_handle* h) {
+    if (h->graph && h->graph_window == h->window && h->graph_sched == h->sched) return CG_OK;
+    drop_graph(h);
+    hipGraph_t g = nullptr;
+    HIP_CHECK(hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
+    for (int i = 0; i < h->window; ++i) enqueue_iteration(h, h->stream);
+    hipError_t e = hipStreamEndCapture(h->stream, &g);
+    if (e != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        return fail(CG_EDEVICE, std::string("graph capture failed: ") + hipGetErrorString(e));
+    }
+    e = hipGraphInstantiate(&h->graph, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) {
+        h->graph = nullptr;
+        return fail(CG_EDEVICE, std::string("graph instantiation failed: ") + hipGetErrorString(e));
+    }
+    h->graph_window = h->window;
+    h->graph_sched = h->sched;
+    return CG_OK;
+}
+
+bool ranges_overlap(const void* a, const void* b, size_t bytes) {
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + bytes && pb < pa + bytes;
+}
+
+}  // namespace
+
+extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, const cg_options* opt,
+                         void* stream, cg_handle** out) {
+    mpcg::clear_error();
+    if (!out) return fail(CG_EINVAL, "cg_create: out is NULL");
+    *out = nullptr;
+    if (!A) return fail(CG_EINVAL, "cg_create: A is NULL");
+    const int64_t T = A->T(), nnz = A->nnz(), n = A->n;
+    if (n > INT32_MAX || T > INT32_MAX || nnz > INT32_MAX)
+        return fail(CG_EINVAL, "cg_create: n, T and nnz must be below 2^31");
+    if (precision_map) {
+        for (int64_t t = 0; t < T; ++t)
+            if (precision_map[t] > 2)
+                return fail(CG_EINVAL, "cg_create: precision_map[" + std::to_string(t) +
+                                           "] is not 0, 1 or 2");
+    }
+    cg_handle* h = new (std::nothrow) cg_handle();
+    if (!h) return fail(CG_ENOMEM, "cg_create: out of host memory");
+    auto bail = [&](int rc) {
+        if (h->graph) (void)hipGraphExecDestroy(h->graph);
+        for (auto& e : h->ev)
+            if (e) (void)hipEventDestroy(e);
+        if (h->pinned) (void)hipHostFree(h->pinned);
+        if (h->stream) (void)hipStreamDestroy(h->stream);
+        delete h;
+        return rc;
+    };
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipGetDevice(&h->device) != hipSuccess) return bail(fail(CG_EDEVICE, "cg_create: no HIP device"));
+    h->n = n;
+    h->T = T;
+    h->nnz = nnz;
+    h->R = A->R;
+    h->C = A->C;
+    h->nrb = A->nrb;
+    h->meta16 = !(A->R <= 16 && A->C <= 16);
+    h->G = std::max(1, 64 / A->R);
+    h->rows_per_group = h->G * A->R;
+    h->ngroups = (int32_t)((h->nrb + h->G - 1) / h->G);
+    if (opt) {
+        h->jacobi = opt->jacobi != 0;
+        if (opt->window > 0) h->window = std::min(opt->window, 4096);
+        if (opt->use_graph >= 0) h->use_graph = opt->use_graph != 0;
+    }
+
+    // Host-side packing of the device layout: 32-bit offsets and packed (row, col).
+    std::vector<int32_t> trp(h->nrb + 1), tptr(T + 1);
+    for (int64_t i = 0; i <= h->nrb; ++i) trp[i] = (int32_t)A->tile_row_ptr[i];
+    for (int64_t i = 0; i <= T; ++i) tptr[i] = (int32_t)A->tile_nnz_ptr[i];
+    std::vector<uint8_t> meta8;
+    std::vector<uint16_t> meta16;
+    if (h->meta16) {
+        meta16.resize(nnz);
+        mpcg::parallel_for(nnz, [&](int64_t lo, int64_t hi) {
+            for (int64_t k = lo; k < hi; ++k)
+                meta16[k] = (uint16_t)((A->row_idx[k] << 8) | A->col_local[k]);
+        });
+    } else {
+        meta8.resize(nnz);
+        mpcg::parallel_for(nnz, [&](int64_t lo, int64_t hi) {
+            for (int64_t k = lo; k < hi; ++k) meta8[k] = (uint8_t)((A->row_idx[k] << 4) | A->col_local[k]);
+        });
+    }
+    std::vector<double> dinv_h;
+    if (h->jacobi) {
+        dinv_h.assign(n, 0.0);
+        std::vector<uint8_t> seen(n, 0);
+        for (int64_t I = 0; I < h->nrb; ++I)
+            for (int64_t t = A->tile_row_ptr[I]; t < A->tile_row_ptr[I + 1]; ++t)
+                for (int64_t k = A->tile_nnz_ptr[t]; k < A->tile_nnz_ptr[t + 1]; ++k) {
+                    int64_t row = I * A->R + A->row_idx[k];
+                    int64_t col = (int64_t)A->tile_col_idx[t] * A->C + A->col_local[k];
+                    if (row == col) {
+                        dinv_h[row] = 1.0 / A->val[k];
+                        seen[row] = A->val[k] != 0.0;
+                    }
+                }
+        for (int64_t i = 0; i < n; ++i)
+            if (!seen[i])
+                return bail(fail(CG_EINVAL, "cg_create: Jacobi needs a nonzero diagonal; row " +
+                                                std::to_string(i) + " has none"));
+    }
+
+    int rc = CG_OK;
+#define TRY(expr)                       \
+    do {                                \
+        rc = (expr);                    \
+        if (rc != CG_OK) return bail(rc); \
+    } while (0)
+    TRY(dalloc(h, &h->trp, h->nrb + 1));
+    TRY(dalloc(h, &h->tcol, T));
+    TRY(dalloc(h, &h->tptr, T + 1));
+    TRY(dalloc(h, &h->map, T));
+    if (h->meta16) {
+        uint16_t* m = nullptr;
+        TRY(dalloc(h, &m, nnz));
+        h->meta = m;
+    } else {
+        uint8_t* m = nullptr;
+        TRY(dalloc(h, &m, nnz));
+        h->meta = m;
+    }
+    TRY(dalloc(h, &h->v64, nnz));
+    TRY(dalloc(h, &h->v32, nnz));
+    TRY(dalloc(h, &h->v16, nnz));
+    TRY(dalloc(h, &h->x, n));
+    TRY(dalloc(h, &h->r, n));
+    TRY(dalloc(h, &h->p, n));
+    TRY(dalloc(h, &h->q, n));
+    if (h->jacobi) {
+        TRY(dalloc(h, &h->z, n));
+        TRY(dalloc(h, &h->dinv, n));
+    }
+    h->partial_cap = std::max(spmv_grid(h), kVecGridCap) * 2;
+    TRY(dalloc(h, &h->partials, h->partial_cap));
+    TRY(dalloc(h, &h->st, 1));
+    TRY(dalloc(h, &h->scratch_u64, 4));
+    h->trace_cap = 16;
+    TRY(dalloc(h, &h->trace_k, h->trace_cap));
+    TRY(dalloc(h, &h->trace_counts, 3 * h->trace_cap));
+#undef TRY
+
+    auto dev_err = [&](hipError_t e, const char* what) {
+        return bail(fail(CG_EDEVICE, std::string("cg_create: ") + what + ": " + hipGetErrorString(e)));
+    };
+    hipError_t e;
+    if ((e = hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking)) != hipSuccess)
+        return dev_err(e, "stream");
+    for (auto& ev : h->ev)
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess)
+            return dev_err(e, "event");
+    if ((e = hipHostMalloc((void**)&h->pinned, 4 * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess)
+        return dev_err(e, "pinned host memory");
+
+    if ((e = hipMemcpyAsync(h->trp, trp.data(), sizeof(int32_t) * trp.size(), hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->tcol, A->tile_col_idx.data(), sizeof(int32_t) * T, hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->tptr, tptr.data(), sizeof(int32_t) * tptr.size(), hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->meta, h->meta16 ? (const void*)meta16.data() : (const void*)meta8.data(),
+                            (h->meta16 ? 2 : 1) * (size_t)nnz, hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->v64, A->val.data(), sizeof(double) * nnz, hipMemcpyHostToDevice, s)))
+        return dev_err(e, "upload");
+    if (h->jacobi &&
+        (e = hipMemcpyAsync(h->dinv, dinv_h.data(), sizeof(double) * n, hipMemcpyHostToDevice, s)))
+        return dev_err(e, "upload");
+    if (precision_map) {
+        if ((e = hipMemcpyAsync(h->map, precision_map, T, hipMemcpyHostToDevice, s))) return dev_err(e, "upload");
+    } else if ((e = hipMemsetAsync(h->map, 0, T, s))) {
+        return dev_err(e, "map");
+    }
+    hipLaunchKernelGGL(dev::build_planes_kernel, dim3(grid_for(nnz, 4, 8192)), dim3(dev::kBlock), 0, s,
+                       h->v64, h->v32, h->v16, nnz);
+    if ((e = hipGetLastError()) != hipSuccess) return dev_err(e, "plane kernel");
+    dev::State hs{};
+    hs.uprec = -1;
+    hs.spmv_uprec = -1;
+    hs.trace_cap = (int32_t)h->trace_cap;
+    if ((e = hipMemcpyAsync(h->st, &hs, sizeof(hs), hipMemcpyHostToDevice, s))) return dev_err(e, "state");
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return dev_err(e, "set-up");
+    *out = h;
+    return CG_OK;
+}
+
+extern "C" int cg_destroy(cg_handle* h) {
+    mpcg::clear_error();
+    if (!h) return CG_OK;
+    (void)hipDeviceSynchronize();
+    drop_graph(h);
+    for (auto& e : h->ev)
+        if (e) (void)hipEventDestroy(e);
+    if (h->pinned) (void)hipHostFree(h->pinned);
+    if (h->stream) (void)hipStreamDestroy(h->stream);
+    delete h;  // frees device buffers
+    return CG_OK;
+}
+
+extern "C" int cg_get_sizes(const cg_handle* h, int64_t* n, int64_t* T, int64_t* nnz, int32_t* R,
+                            int32_t* C) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_get_sizes: h is NULL");
+    if (n) *n = h->n;
+    if (T) *T = h->T;
+    if (nnz) *nnz = h->nnz;
+    if (R) *R = h->R;
+    if (C) *C = h->C;
+    return CG_OK;
+}
+
+extern "C" int64_t cg_device_bytes(const cg_handle* h) { return h ? h->device_bytes : 0; }
+
+extern "C" int cg_set_precision_map(cg_handle* h, const uint8_t* map, int32_t on_device) {
+    mpcg::clear_error();
+    if (!h || !map) return fail(CG_EINVAL, "cg_set_precision_map: NULL argument");
+    if (!on_device) {
+        for (int64_t t = 0; t < h->T; ++t)
+            if (map[t] > 2)
+                return fail(CG_EINVAL, "cg_set_precision_map: map[" + std::to_string(t) + "] is not 0, 1 or 2");
+        HIP_CHECK(hipMemcpy(h->map, map, h->T, hipMemcpyHostToDevice));
+    } else {
+        HIP_CHECK(hipMemcpy(h->map, map, h->T, hipMemcpyDeviceToDevice));
+    }
+    h->sched = kSchedStatic;
+    return upload_schedule(h);
+}
+
+extern "C" int cg_get_active_map(const cg_handle* h, uint8_t* out) {
+    mpcg::clear_error();
+    if (!h || !out) return fail(CG_EINVAL, "cg_get_active_map: NULL argument");
+    dev::State hs{};
+    HIP_CHECK(hipMemcpy(&hs, h->st, sizeof(hs), hipMemcpyDeviceToHost));
+    if (hs.uprec >= 0) {
+        std::memset(out, hs.uprec, h->T);
+        return CG_OK;
+    }
+    HIP_CHECK(hipMemcpy(out, h->map, h->T, hipMemcpyDeviceToHost));
+    return CG_OK;
+}
+
+extern "C" int cg_map_from_magnitude(cg_handle* h, double t_bf16, double t_fp32) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_map_from_magnitude: h is NULL");
+    if (!(t_bf16 <= t_fp32)) return fail(CG_EINVAL, "cg_map_from_magnitude: need t_bf16 <= t_fp32");
+    HIP_CHECK(hipMemset(h->scratch_u64, 0, sizeof(unsigned long long)));
+    const int g = grid_for(h->T, 1, 8192);
+    hipLaunchKernelGGL(dev::diag_absmax_kernel, dim3(g), dim3(dev::kBlock), 0, h->stream, h->trp, h->tcol,
+                       h->tptr, (const void*)h->meta, h->meta16 ? 1 : 0, h->v64, (int32_t)h->nrb,
+                       (int32_t)h->T, h->R, h->C, h->scratch_u64);
+    hipLaunchKernelGGL(dev::magnitude_map_kernel, dim3(g), dim3(dev::kBlock), 0, h->stream, h->tptr, h->v64,
+                       (int32_t)h->T, (const unsigned long long*)h->scratch_u64, t_bf16, t_fp32, h->map);
+    HIP_CHECK(hipGetLastError());
+    HIP_CHECK(hipStreamSynchronize(h->stream));
+    h->sched = kSchedStatic;
+    return upload_schedule(h);
+}
+
+extern "C" int cg_set_schedule_residual(cg_handle* h, int32_t nstage, const double* thresholds,
+                                        const uint8_t* prec) {
+    mpcg::clear_error();
+    if (!h || !prec) return fail(CG_EINVAL, "cg_set_schedule_residual: NULL argument");
+    if (nstage < 1 || nstage > 8) return fail(CG_EINVAL, "cg_set_schedule_residual: nstage must lie in [1, 8]");
+    if (nstage > 1 && !thresholds) return fail(CG_EINVAL, "cg_set_schedule_residual: thresholds is NULL");
+    h->thresholds.assign(thresholds, thresholds + (nstage - 1));
+    h->stage_prec.clear();
+    for (int i = 0; i < nstage; ++i) {
+        if (prec[i] > 2) return fail(CG_EINVAL, "cg_set_schedule_residual: prec values must be 0, 1 or 2");
+        h->stage_prec.push_back(prec[i]);
+    }
+    for (double t : h->thresholds)
+        if (!std::isfinite(t)) return fail(CG_EINVAL, "cg_set_schedule_residual: thresholds must be finite");
+    h->sched = kSchedResidual;
+    return upload_schedule(h);
+}
+
+extern "C" int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const double* scores, double hi,
+                                         double lo) {
+    mpcg::clear_error();
+    if (!h || !scores) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: NULL argument");
+    if (period < 1) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: period must be >= 1");
+    if (!(lo <= hi)) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: need lo <= hi");
+    if (!h->scores) {
+        int rc = dalloc(h, &h->scores, h->T);
+        if (rc != CG_OK) return rc;
+    }
+    HIP_CHECK(hipMemcpy(h->scores, scores, sizeof(double) * h->T, hipMemcpyHostToDevice));
+    h->period = period;
+    h->hi = hi;
+    h->lo = lo;
+    h->sched = kSchedTileRule;
+    return upload_schedule(h);
+}
+
+extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_eval_tile_rule: h is NULL");
+    if (h->sched != kSchedTileRule) return fail(CG_EINVAL, "cg_eval_tile_rule: no tile rule is set");
+    dev::MapArgs ma = map_args(h, rho, 0);
+    hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(grid_for(h->T, 4, 1024)), dim3(dev::kBlock), 0, h->stream,
+                       ma);
+    HIP_CHECK(hipGetLastError());
+    HIP_CHECK(hipStreamSynchronize(h->stream));
+    return CG_OK;
+}
+
+extern "C" int cg_clear_schedule(cg_handle* h) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_clear_schedule: h is NULL");
+    h->sched = kSchedStatic;
+    return upload_schedule(h);
+}
+
+extern "C" int cg_spmv(cg_handle* h, const double* x, double* y, void* stream) {
+    mpcg::clear_error();
+    if (!h || !x || !y) return fail(CG_EINVAL, "cg_spmv: NULL argument");
+    if (ranges_overlap(x, y, sizeof(double) * h->n)) return fail(CG_EINVAL, "cg_spmv: y overlaps x");
+    dev::SpmvArgs a = spmv_args(h, x, y, &h->st->spmv_uprec);
+    launch_spmv<dev::kSpmvPlain>(h, a, static_cast<hipStream_t>(stream));
+    HIP_CHECK(hipGetLastError());
+    return CG_OK;
+}
+
+extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double tol, int32_t maxit,
+                        double* x, int32_t* iterations, double* res_hist, void* stream) {
+    mpcg::clear_error();
+    if (!h || !b || !x || !iterations) return fail(CG_EINVAL, "cg_solve: NULL argument");
+    if (!(tol >= 0.0)) return fail(CG_EINVAL, "cg_solve: tol must be >= 0");
+    if (maxit < 0) return fail(CG_EINVAL, "cg_solve: maxit must be >= 0");
+    hipStream_t user = static_cast<hipStream_t>(stream);
+    hipStream_t s = h->stream;
+
+    // History and trace capacity.
+    if (h->hist_cap < (int64_t)maxit + 1) {
+        dfree(h, h->hist);
+        h->hist = nullptr;
+        int rc = dalloc(h, &h->hist, (int64_t)maxit + 1);
+        if (rc != CG_OK) return rc;
+        h->hist_cap = (int64_t)maxit + 1;
+        drop_graph(h);
+    }
+    int64_t need_trace = 16;
+    if (h->sched == kSchedTileRule) need_trace = maxit / h->period + 2;
+    if (h->sched == kSchedResidual) need_trace = (int64_t)h->stage_prec.size() + 1;
+    if (need_trace > h->trace_cap) {
+        dfree(h, h->trace_k);
+        dfree(h, h->trace_counts);
+        h->trace_k = nullptr;
+        h->trace_counts = nullptr;
+        int rc = dalloc(h, &h->trace_k, need_trace);
+        if (rc == CG_OK) rc = dalloc(h, &h->trace_counts, 3 * need_trace);
+        if (rc != CG_OK) return rc;
+        h->trace_cap = need_trace;
+        drop_graph(h);
+    }
+
+    // Order after the caller's prior work.
+    HIP_CHECK(hipEventRecord(h->ev[0], user));
+    HIP_CHECK(hipStreamWaitEvent(s, h->ev[0], 0));
+
+    dev::State hs{};
+    HIP_CHECK(hipMemcpyAsync(&hs, h->st, sizeof(hs), hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    hs.tol = tol;
+    hs.maxit = maxit;
+    hs.done = 0;
+    hs.k = 0;
+    hs.trace_cap = (int32_t)h->trace_cap;
+    hs.ntrace = 0;
+    for (auto& t : hs.ticket) t = 0;
+    HIP_CHECK(hipMemcpyAsync(h->st, &hs, sizeof(hs), hipMemcpyHostToDevice, s));
+
+    hipLaunchKernelGGL(dev::fill_i64_kernel, dim3(grid_for(3 * h->trace_cap, 1, 64)), dim3(dev::kBlock), 0, s,
+                       h->trace_counts, (int64_t)0, (int64_t)(3 * h->trace_cap));
+    dev::VecArgs va = vec_args(h, b, x0);
+    if (x0) {
+        // r0 = b - A x0 with the exact FP64 values.
+        dev::SpmvArgs sa = spmv_args(h, x0, h->r, &h->st->zero_prec);
+        sa.b = b;
+        launch_spmv<dev::kSpmvResidual>(h, sa, s);
+        va.r_ready = 1;
+    }
+    hipLaunchKernelGGL(dev::cg_init_kernel, dim3(vec_grid(h)), dim3(dev::kBlock), 0, s, va);
+    HIP_CHECK(hipGetLastError());
+    const bool static_map = h->sched == kSchedStatic;
+    if (static_map) {
+        hipLaunchKernelGGL(dev::map_count_kernel, dim3(grid_for(h->T, 4, 1024)), dim3(dev::kBlock), 0, s,
+                           h->map, h->T, h->trace_counts);
+    }
+
+    // Iterate in windows; poll the device stop flag of the previous window
+    // while the current one runs.
+    int polled = 0;
+    if (h->use_graph) {
+        int rc = ensure_graph(h);
+        if (rc != CG_OK) return rc;
+    }
+    int64_t windows = 0;
+    int32_t done = 0, kdone = 0;
+    const int64_t max_windows = (int64_t)maxit / h->window + 2;
+    while (true) {
+        if (windows < max_windows) {
+            if (h->use_graph) {
+                HIP_CHECK(hipGraphLaunch(h->graph, s));
+            } else {
+                for (int i = 0; i < h->window; ++i) enqueue_iteration(h, s);
+                HIP_CHECK(hipGetLastError());
+            }
+            const int slot = (int)(windows & 1);
+            HIP_CHECK(hipMemcpyAsync(h->pinned + 2 * slot, &h->st->done, sizeof(int32_t) * 2,
+                                     hipMemcpyDeviceToHost, s));
+            HIP_CHECK(hipEventRecord(h->ev[slot], s));
+            ++windows;
+        }
+        if (windows - polled >= 2 || windows >= max_windows) {
+            const int slot = (int)(polled & 1);
+            HIP_CHECK(hipEventSynchronize(h->ev[slot]));
+            done = h->pinned[2 * slot];
+            kdone = h->pinned[2 * slot + 1];
+            ++polled;
+            if (done || polled >= windows) break;
+        }
+    }
+    HIP_CHECK(hipStreamSynchronize(s));
+
+    HIP_CHECK(hipMemcpy(&hs, h->st, sizeof(hs), hipMemcpyDeviceToHost));
+    if (static_map) {
+        // One trace entry: the static map at k = 0.
+        int32_t k0 = 0;
+        HIP_CHECK(hipMemcpy(h->trace_k, &k0, sizeof(k0), hipMemcpyHostToDevice));
+        hs.ntrace = 1;
+        HIP_CHECK(hipMemcpy(&h->st->ntrace, &hs.ntrace, sizeof(int32_t), hipMemcpyHostToDevice));
+    }
+    (void)kdone;
+    *iterations = hs.k;
+    if (res_hist) HIP_CHECK(hipMemcpy(res_hist, h->hist, sizeof(double) * (hs.k + 1), hipMemcpyDeviceToHost));
+    HIP_CHECK(hipMemcpyAsync(x, h->x, sizeof(double) * h->n, hipMemcpyDeviceToDevice, s));
+    HIP_CHECK(hipEventRecord(h->ev[0], s));
+    HIP_CHECK(hipStreamWaitEvent(user, h->ev[0], 0));
+    HIP_CHECK(hipStreamSynchronize(s));
+    if (hs.done == 1) return CG_OK;
+    if (hs.done == 3) return CG_BREAKDOWN;
+    return CG_NOT_CONVERGED;
+}
+
+extern "C" int cg_get_map_trace(const cg_handle* h, int32_t cap, int32_t* k_out, int64_t* counts_out) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_get_map_trace: h is NULL");
+    dev::State hs{};
+    HIP_CHECK(hipMemcpy(&hs, h->st, sizeof(hs), hipMemcpyDeviceToHost));
+    int64_t n = std::min<int64_t>(hs.ntrace, h->trace_cap);
+    int64_t m = std::min<int64_t>(n, cap);
+    if (m > 0 && k_out) HIP_CHECK(hipMemcpy(k_out, h->trace_k, sizeof(int32_t) * m, hipMemcpyDeviceToHost));
+    if (m > 0 && counts_out)
+        HIP_CHECK(hipMemcpy(counts_out, h->trace_counts, sizeof(int64_t) * 3 * m, hipMemcpyDeviceToHost));
+    return hs.ntrace;
+}
+
+extern "C" int cg_export_layout(const cg_handle* h, int64_t* tile_row_ptr, int32_t* tile_col_idx,
+                                int64_t* tile_nnz_ptr, uint8_t* row_idx, uint8_t* col_local, double* val64,
+                                float* val32, uint16_t* bf16) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_export_layout: h is NULL");
+    if (tile_row_ptr) {
+        std::vector<int32_t> t(h->nrb + 1);
+        HIP_CHECK(hipMemcpy(t.data(), h->trp, sizeof(int32_t) * t.size(), hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < t.size(); ++i) tile_row_ptr[i] = t[i];
+    }
+    if (tile_col_idx) HIP_CHECK(hipMemcpy(tile_col_idx, h->tcol, sizeof(int32_t) * h->T, hipMemcpyDeviceToHost));
+    if (tile_nnz_ptr) {
+        std::vector<int32_t> t(h->T + 1);
+        HIP_CHECK(hipMemcpy(t.data(), h->tptr, sizeof(int32_t) * t.size(), hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < t.size(); ++i) tile_nnz_ptr[i] = t[i];
+    }
+    if (row_idx || col_local) {
+        if (h->meta16) {
+            std::vector<uint16_t> m(h->nnz);
+            HIP_CHECK(hipMemcpy(m.data(), h->meta, 2 * (size_t)h->nnz, hipMemcpyDeviceToHost));
+            for (int64_t k = 0; k < h->nnz; ++k) {
+                if (row_idx) row_idx[k] = (uint8_t)(m[k] >> 8);
+                if (col_local) col_local[k] = (uint8_t)(m[k] & 255);
+            }
+        } else {
+            std::vector<uint8_t> m(h->nnz);
+            HIP_CHECK(hipMemcpy(m.data(), h->meta, (size_t)h->nnz, hipMemcpyDeviceToHost));
+            for (int64_t k = 0; k < h->nnz; ++k) {
+                if (row_idx) row_idx[k] = (uint8_t)(m[k] >> 4);
+                if (col_local) col_local[k] = (uint8_t)(m[k] & 15);
+            }
+        }
+    }
+    if (val64) HIP_CHECK(hipMemcpy(val64, h->v64, sizeof(double) * h->nnz, hipMemcpyDeviceToHost));
+    if (val32) HIP_CHECK(hipMemcpy(val32, h->v32, sizeof(float) * h->nnz, hipMemcpyDeviceToHost));
+    if (bf16) HIP_CHECK(hipMemcpy(bf16, h->v16, sizeof(uint16_t) * h->nnz, hipMemcpyDeviceToHost));
+    return CG_OK;
+}

@@ -9,7 +9,7 @@ Definition used here (Fig. 4(a) inter-tile CSR, Fig. 4(b) intra-tile CSC):
   row block I's tiles; ``tile_col_idx[t]`` is tile t's column block.
 * Inside a tile the nonzeros are stored column by column (CSC):
   ``col_ptr[t, c]`` (relative to the tile's first nonzero) starts local
-  column c, ``row_idx`` holds the row offset from the row block's first row,
+  column c (derived on demand from the per-nonzero local column), ``row_idx`` holds the row offset from the row block's first row,
   ascending inside a column. ``tile_nnz_ptr`` is the prefix sum of the tiles'
   nonzero counts, so tile t owns positions
   ``tile_nnz_ptr[t]..tile_nnz_ptr[t+1]`` of every per-nonzero array.
@@ -38,10 +38,21 @@ class TileCSC:
     tile_row_ptr: np.ndarray  # int64[nRB+1]
     tile_col_idx: np.ndarray  # int32[T]
     tile_nnz_ptr: np.ndarray  # int64[T+1]
-    col_ptr: np.ndarray       # int32[T, C+1], relative to the tile start
     row_idx: np.ndarray       # uint8[nnz]   (R <= 256)
+    col_local: np.ndarray     # uint8[nnz]   local column of every nonzero (C <= 256)
     perm: np.ndarray          # int64[nnz]   canonical position -> CSR position
     val: np.ndarray           # float64[nnz] canonical order
+
+    @property
+    def col_ptr(self) -> np.ndarray:
+        """int32[T, C+1]: start of every local column, relative to the tile's first nonzero."""
+        if getattr(self, "_col_ptr", None) is None:
+            key = self.tile_of_nnz() * self.C + self.col_local.astype(np.int64)
+            q = (np.arange(self.T, dtype=np.int64)[:, None] * self.C
+                 + np.arange(self.C + 1, dtype=np.int64)[None, :])
+            pos = np.searchsorted(key, q.ravel(), side="left").reshape(self.T, self.C + 1)
+            self._col_ptr = (pos - self.tile_nnz_ptr[:-1, None]).astype(np.int32)
+        return self._col_ptr
 
     @property
     def T(self) -> int:
@@ -61,14 +72,8 @@ class TileCSC:
         return np.repeat(np.arange(nrb, dtype=np.int64), np.diff(self.tile_row_ptr))
 
     def local_col(self) -> np.ndarray:
-        """Local column of every canonical nonzero (expanded from col_ptr)."""
-        out = np.empty(self.nnz, dtype=np.int64)
-        cols = np.arange(self.C, dtype=np.int64)
-        for t in range(self.T):
-            s = int(self.tile_nnz_ptr[t])
-            cnt = np.diff(self.col_ptr[t])
-            out[s:s + int(self.tile_nnz_ptr[t + 1]) - s] = np.repeat(cols, cnt)
-        return out
+        """Local column of every canonical nonzero."""
+        return self.col_local.astype(np.int64)
 
 
 def build(n: int, indptr: np.ndarray, indices: np.ndarray, data: np.ndarray,
@@ -100,14 +105,9 @@ def build(n: int, indptr: np.ndarray, indices: np.ndarray, data: np.ndarray,
     tiles_per_rb = np.bincount(I_s[starts], minlength=nrb)
     tile_row_ptr = np.zeros(nrb + 1, dtype=np.int64)
     np.cumsum(tiles_per_rb, out=tile_row_ptr[1:])
-    tile_id = np.repeat(np.arange(T, dtype=np.int64), np.diff(tile_nnz_ptr))
-    counts = np.zeros((T, C), dtype=np.int64)
-    np.add.at(counts, (tile_id, c_s), 1)
-    col_ptr = np.zeros((T, C + 1), dtype=np.int32)
-    np.cumsum(counts, axis=1, out=col_ptr[:, 1:])
     return TileCSC(n=n, R=R, C=C, tile_row_ptr=tile_row_ptr, tile_col_idx=tile_col_idx,
-                   tile_nnz_ptr=tile_nnz_ptr, col_ptr=col_ptr,
-                   row_idx=r_s.astype(np.uint8), perm=perm.astype(np.int64),
+                   tile_nnz_ptr=tile_nnz_ptr, row_idx=r_s.astype(np.uint8),
+                   col_local=c_s.astype(np.uint8), perm=perm.astype(np.int64),
                    val=np.asarray(data, dtype=np.float64)[perm])
 
 
