@@ -1,0 +1,227 @@
+"""Benchmark: mixed-precision Tile-CSC CG on one MI355X.
+
+Workload: 3D 7-point Laplacian on a 128^3 grid (n = 2,097,152,
+nnz = 14,581,760), 16x16 tiles, a seeded static per-tile map with 50 % FP64,
+30 % FP32 and 20 % BF16 tiles, b = A x* with x* ~ U[-1, 1], x0 = 0, stopping
+at ||r_k||/||r_0|| <= 1e-8. One step is one complete cg_solve (every
+iteration: SpMV with fused p.q, the x/r update with fused reductions, the
+direction update, the device stop flag), with b already resident on the GPU.
+
+Prints one JSON line: CG iterations/s over the timed solves, time to
+solution, the Tile-CSC SpMV bandwidth against the 8 TB/s HBM roofline, the
+all-FP64-map time to solution for comparison, and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "Tile-CSC SpMV GB/s (% HBM peak); CG iterations/sec; time-to-solution"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spmv_tilecsc_cfg2_traffic.json")
+KERNEL_SOURCES = ["mixed_precision_sparse_amd/csrc/mpcg_kernels.hpp",
+                  "mixed_precision_sparse_amd/csrc/mpcg_runtime.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def spmv_algorithmic_bytes(L, prec_map) -> int:
+    """Bytes one Tile-CSC SpMV must move: values in their stored width, one byte each
+    for the local row and column, 9 B per tile (column block i32, nnz offset i32,
+    map u8), the row-block pointers, x read once and y written once."""
+    nnz_t = np.diff(L.tile_nnz_ptr)
+    width = np.array([8, 4, 2], dtype=np.int64)[prec_map]
+    nrb = -(-L.n // L.R)
+    return int((nnz_t * width).sum() + 2 * L.nnz + 9 * L.T + 4 * (nrb + 1) + 16 * L.n)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--spmv-reps", type=int, default=100)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixed_precision_sparse_amd as mpcg
+    from gen import make_workload, static_map, tile_scores
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    w = make_workload(2, "full")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    pmap = static_map(tile_scores(L.T, 2), w.map_spec["frac_bf16"], w.map_spec["frac_fp32"])
+    S = mpcg.Solver(L, pmap)
+    setup_s = time.time() - t0
+    print(f"# setup {setup_s:.1f}s: n={A.n} nnz={A.nnz} T={L.T} map counts "
+          f"{np.bincount(pmap, minlength=3).tolist()}", file=sys.stderr, flush=True)
+
+    b = torch.from_numpy(w.b).to(dev)
+    x = torch.zeros_like(b)
+
+    def run_solves(solver, steps):
+        its = 0
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            status, K, hist = solver.cg_solve(b, x, w.tol, w.maxit)
+            its += K
+        torch.cuda.synchronize()
+        return time.perf_counter() - t, its, status, K, hist
+
+    run_solves(S, args.warmup)
+    el, its, status, K, hist = run_solves(S, args.steps)
+    tts_ms = 1e3 * el / args.steps
+    iters_per_s = its / el
+    xs = x.cpu().numpy()
+    true_res = float(np.linalg.norm(w.b - A.to_scipy() @ xs) / np.linalg.norm(w.b))
+    print(f"# mixed map: {status} K={K} TTS {tts_ms:.3f} ms, {iters_per_s:.1f} it/s, "
+          f"true residual {true_res:.3e}", file=sys.stderr, flush=True)
+
+    # Tile-CSC SpMV on its own: average launch time from HIP events on the launch stream.
+    y = torch.empty_like(b)
+    xin = torch.from_numpy(np.random.default_rng(7).uniform(-1, 1, A.n)).to(dev)
+    for _ in range(10):
+        S.cg_spmv(xin, y)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.spmv_reps):
+        S.cg_spmv(xin, y)
+    e1.record()
+    torch.cuda.synchronize()
+    spmv_ms = e0.elapsed_time(e1) / args.spmv_reps
+    bytes_spmv = spmv_algorithmic_bytes(L, pmap)
+    spmv_gbs = bytes_spmv / (spmv_ms * 1e-3) / 1e9
+    bytes_spmv64 = spmv_algorithmic_bytes(L, np.zeros(L.T, np.uint8))
+    bytes_vec = 56 * A.n
+    iter_gbs = (bytes_spmv + bytes_vec) * its / el / 1e9
+
+    # The all-FP64 map on the same substrate.
+    S64 = mpcg.Solver(L, np.zeros(L.T, np.uint8))
+    run_solves(S64, max(1, args.warmup))
+    el64, its64, status64, K64, _ = run_solves(S64, args.steps)
+    tts64_ms = 1e3 * el64 / args.steps
+    e0.record()
+    for _ in range(args.spmv_reps):
+        S64.cg_spmv(xin, y)
+    e1.record()
+    torch.cuda.synchronize()
+    spmv64_ms = e0.elapsed_time(e1) / args.spmv_reps
+    print(f"# fp64 map: {status64} K={K64} TTS {tts64_ms:.3f} ms; spmv mixed {spmv_ms * 1e3:.1f} us, "
+          f"fp64 {spmv64_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, pmap, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(iters_per_s, 2),
+        "unit": "CG iterations/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(tts_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic (seeded generator; no dataset)",
+        "config": {
+            "workload": "3D 7-point Laplacian 128^3, 16x16 Tile-CSC, static 50/30/20 FP64/FP32/BF16 "
+                        "tile map, CG to rel. residual 1e-8 from x0 = 0",
+            "n": A.n, "nnz": A.nnz, "tiles": L.T,
+            "map_tiles_fp64_fp32_bf16": np.bincount(pmap, minlength=3).tolist(),
+        },
+        "iterations": K,
+        "status": status,
+        "time_to_solution_ms": round(tts_ms, 4),
+        "true_residual": true_res,
+        "tile_csc_spmv_gbs": round(spmv_gbs, 1),
+        "tile_csc_spmv_frac_hbm": round(spmv_gbs / HBM_PEAK_GBS, 4),
+        "tile_csc_spmv_us": round(spmv_ms * 1e3, 2),
+        "cg_iteration_gbs": round(iter_gbs, 1),
+        "cg_iteration_frac_hbm": round(iter_gbs / HBM_PEAK_GBS, 4),
+        "fp64_map": {"iterations": K64, "time_to_solution_ms": round(tts64_ms, 4),
+                     "spmv_us": round(spmv64_ms * 1e3, 2),
+                     "spmv_gbs": round(bytes_spmv64 / (spmv64_ms * 1e-3) / 1e9, 1)},
+        "mixed_over_fp64_tts_speedup": round(tts64_ms / tts_ms, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "spmv_tilecsc_kernel (cg_spmv)",
+            "achieved": round(spmv_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(spmv_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": bytes_spmv,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, pmap, budget_s):
+    """The CPU oracle on a bounded sample: its CG iterations on the full workload for
+    about ``budget_s`` seconds on one thread. The per-iteration rate is the difference of
+    two runs of different lengths, so the oracle's set-up (layout build, value streams,
+    first residual) is excluded, as it is from the GPU time to solution."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import cg as ocg, tilecsc as otc
+
+    A = w.A
+
+    def timed(iters):
+        t = time.time()
+        r = ocg.solve(Lo, A.indptr, A.indices, A.data, w.b, ocg.StaticSchedule(pmap), 0.0, iters)
+        return time.time() - t, r.K
+
+    with threadpool_limits(limits=1):
+        Lo = otc.build(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+        t_a, k_a = timed(2)
+        t_b, k_b = timed(12)
+        per_iter = max((t_b - t_a) / max(k_b - k_a, 1), 1e-6)
+        iters = max(20, int(budget_s / per_iter))
+        t_c, k_c = timed(iters)
+    rate = (k_c - k_a) / (t_c - t_a)
+    return {"value": round(rate, 3), "unit": "CG iterations/s", "cores": 1, "kind": "oracle",
+            "sample": f"{k_c - k_a} oracle CG iterations (runs of {k_c} and {k_a} differenced) on the "
+                      f"full 128^3 workload with the same map, {t_c - t_a:.1f} s on one thread; "
+                      f"layout build and value streams excluded"}
+
+
+if __name__ == "__main__":
+    main()

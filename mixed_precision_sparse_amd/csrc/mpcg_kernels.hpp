@@ -20,11 +20,14 @@ constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kTileBatch = 64;   // tile descriptors staged in LDS per pass
 constexpr int kMaxRows = 256;    // rows owned by one wavefront (R <= 256)
-constexpr int kMaxGroupRB = 65;  // row blocks per wavefront + 1 (R = 1 gives 64)
+constexpr int kMaxGroupRB = 63;  // row blocks per wavefront at most (boundaries fit one wave)
 
-// Solver scalars, resident on the device for the whole solve.
+// Solver scalars, resident on the device for the whole solve. Each field has
+// one writer per kernel launch (thread 0 of block 0) and no other block of
+// that launch reads it, except `done` (see cg_direction_kernel).
 struct State {
     double rz;        // r.z of the current iterate (r.r for plain CG)
+    double rz_prev;   // r.z before the current update (copied by the update kernel)
     double rr;        // r.r of the current iterate
     double norm0;     // ||r_0||
     double alpha;
@@ -35,6 +38,7 @@ struct State {
     int32_t done;     // 0 running, 1 converged, 2 iteration cap, 3 breakdown
     int32_t k;        // completed iterations (kept next to done: polled together)
     int32_t maxit;
+    int32_t bd;       // breakdown found by the update kernel of this iteration
     int32_t uprec;    // precision used by the solver's SpMV: -1 = per-tile map, else uniform
     int32_t spmv_uprec;  // the same for cg_spmv
     int32_t zero_prec;   // always 0: exact FP64 products (initial residual)
@@ -46,10 +50,17 @@ struct State {
     int32_t period;      // tile-rule window length (0: no tile rule)
     int32_t pad;
     double hi, lo;       // tile-rule thresholds
-    uint32_t ticket[4];  // arrival counters of the single-pass reductions
 };
 
-enum TicketSlot { kTicketSpmv = 0, kTicketUpdate = 1, kTicketInit = 2, kTicketMisc = 3 };
+// Map-trace counts are kept per block of the map kernels: [entry][kTraceBlocks][3].
+constexpr int kTraceBlocks = 256;
+
+__device__ inline int load_done(const State* st) {
+    return __hip_atomic_load(&st->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_done(State* st, int v) {
+    __hip_atomic_store(&st->done, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ---------------------------------------------------------------------------
 // Rounding FP64 -> small binary formats with an 8-bit exponent (bias 127):
@@ -117,33 +128,16 @@ __device__ inline double block_sum(double v, double* s_tmp) {
     return t;
 }
 
-// Publishes this block's partials and returns true in every thread of the
-// block that arrives last. The last block then reads all partials.
+// Fixed-order sum of nparts partials (component j of NV per part); every
+// thread of the block gets the same value, and every block that calls this
+// on the same data gets the same bits.
 template <int NV>
-__device__ inline bool arrive_last(const double (&vals)[NV], double* partials, uint32_t* ticket,
-                                   bool* s_flag) {
-    if (threadIdx.x == 0) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) partials[(size_t)blockIdx.x * NV + j] = vals[j];
-        __threadfence();
-        uint32_t t = atomicAdd(ticket, 1u);
-        *s_flag = (t == gridDim.x - 1);
-    }
-    __syncthreads();
-    bool last = *s_flag;
-    if (last) __threadfence();
-    return last;
-}
-
-// Fixed-order sum of the partials of all blocks (called by the last block).
-template <int NV>
-__device__ inline void reduce_partials(const double* partials, int nblocks, double (&out)[NV],
-                                       double* s_tmp) {
+__device__ inline void sum_partials(const double* partials, int nparts, double (&out)[NV],
+                                    double* s_tmp) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         double a = 0.0;
-        for (int i = threadIdx.x; i < nblocks; i += blockDim.x)
-            a += partials[(size_t)i * NV + j];
+        for (int i = threadIdx.x; i < nparts; i += blockDim.x) a += partials[(size_t)i * NV + j];
         out[j] = block_sum(a, s_tmp);
     }
 }
@@ -166,16 +160,30 @@ __device__ inline void wave_lds_sync() {
 //
 // One wavefront owns a row group: G consecutive row blocks (G*R <= 64 rows,
 // or one row block when R > 64). It walks the group's tiles in batches of up
-// to 64: lane j stages tile j's descriptor (first nonzero, column base,
-// precision, row offset inside the group) in LDS; then the 64 lanes sweep the
-// batch's nonzeros 64 at a time in storage order, so every value plane is
-// read with contiguous, coalesced loads and only from the plane the tile's
-// map entry selects. A lane finds its tile from the tile starts that fall in
-// the current 64-nonzero window (ballot + prefix popcount). The product of
-// the widened stored value and the FP64 vector entry is accumulated in FP64
-// into the group's row accumulators in LDS; the group's rows are written once.
+// to 64: lane j stages tile j's descriptor (column base, precision, row
+// offset inside the group) in LDS; then the 64 lanes sweep the batch's
+// nonzeros in storage order, 64 at a time ("windows"), U windows at once.
+// Every value plane is read with contiguous, coalesced loads and only where
+// the tile's map entry selects it: each lane issues one buffer load per plane
+// and the two planes it does not use get an out-of-range offset, which the
+// hardware answers with zero and no memory access -- no branches, no waits.
+// A lane's tile comes from a per-window record built with the layout (the
+// tile of the window's first nonzero and a bit mask of the tile starts that
+// follow), so the lookup is one prefix popcount. Products of the widened
+// stored value and the FP64 vector entry are accumulated in FP64 into the
+// group's row accumulators in LDS; the group's rows are written once.
+//
+// A block of 4 wavefronts handles a contiguous range of row groups (the
+// grid is capped, and blocks are spread so that each XCD gets a contiguous
+// part of the matrix); in CG mode each block also writes its part of p.q.
 // ---------------------------------------------------------------------------
 enum SpmvMode { kSpmvPlain = 0, kSpmvCg = 1, kSpmvResidual = 2 };
+#ifndef MPCG_SPMV_UNROLL
+#define MPCG_SPMV_UNROLL 8
+#endif
+constexpr int kUnroll = MPCG_SPMV_UNROLL;
+constexpr uint32_t kBufferConfig = 0x00020000u;  // raw buffer, dword3 for the gfx9 family
+constexpr int kOutOfRange = 0x7fffff00;          // offset past every batch: load returns 0
 
 struct SpmvArgs {
     const int32_t* trp;   // tile_row_ptr [nrb+1]
@@ -186,102 +194,170 @@ struct SpmvArgs {
     const double* v64;
     const float* v32;
     const uint16_t* v16;
+    const int32_t* win_base;   // [ngroups+1] first window record of every row group
+    const uint64_t* win_mask;  // per window: bit q = nonzero q+1 of the window starts a tile
+    const int32_t* win_tile;   // per window: batch-relative tile of the window's first nonzero
     const double* x;
     double* y;
     const double* b;       // residual mode: y = b - A x
     const int32_t* uprec;  // -1 per-tile map, else uniform code
-    State* st;
-    double* partials;
-    int32_t n, nrb, R, C, G, rows_per_group, ngroups;
+    const State* st;
+    double* partials;      // CG mode: one p.q partial per block
+    int32_t n, nrb, R, C, G, rows_per_group, ngroups, groups_per_block;
 };
 
 template <typename MetaT>
-__device__ inline void decode_meta(MetaT m, int& r, int& c);
+__device__ inline void decode_meta(uint32_t m, int& r, int& c);
 template <>
-__device__ inline void decode_meta<uint8_t>(uint8_t m, int& r, int& c) {
-    r = m >> 4;
-    c = m & 15;
+__device__ inline void decode_meta<uint8_t>(uint32_t m, int& r, int& c) {
+    r = (int)(m >> 4);
+    c = (int)(m & 15u);
 }
 template <>
-__device__ inline void decode_meta<uint16_t>(uint16_t m, int& r, int& c) {
-    r = m >> 8;
-    c = m & 255;
+__device__ inline void decode_meta<uint16_t>(uint32_t m, int& r, int& c) {
+    r = (int)(m >> 8);
+    c = (int)(m & 255u);
 }
 
-__device__ inline double load_stored_value(const SpmvArgs& a, int prec, int k) {
-    if (prec == 0) return __builtin_nontemporal_load(&a.v64[k]);
-    if (prec == 1) return (double)__builtin_nontemporal_load(&a.v32[k]);
-    uint32_t h = __builtin_nontemporal_load(&a.v16[k]);
-    return (double)__uint_as_float(h << 16);
+__device__ inline __amdgpu_buffer_rsrc_t batch_rsrc(const void* base, int64_t first, int width, int count) {
+    const char* p = static_cast<const char*>(base) + first * width;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, count * width, (int)kBufferConfig);
 }
 
-template <typename MetaT, int MODE>
-__global__ __launch_bounds__(kBlock) void spmv_tilecsc_kernel(SpmvArgs a) {
-    __shared__ double s_acc[kWavesPerBlock][kMaxRows];
-    __shared__ int32_t s_cbase[kWavesPerBlock][kTileBatch];
-    __shared__ int32_t s_pr[kWavesPerBlock][kTileBatch];
-    __shared__ int32_t s_trp[kWavesPerBlock][kMaxGroupRB];
-    __shared__ uint8_t s_flag[kWavesPerBlock][kWave];
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Wave-uniform reads of data no kernel here writes (window records, tile
+// ranges): read through the constant address space so they become scalar loads.
+template <typename T>
+__device__ inline T uniform_load(const T* p, int i) {
+    return ((const __attribute__((address_space(4))) T*)(uintptr_t)p)[i];
+}
+
+// The outputs are separate restrict arguments: the compiler may then treat
+// every other array as read-only for the whole launch and fetch the
+// wave-uniform ones (window records, tile ranges) through the scalar cache.
+template <typename MetaT, int MODE, int MAXROWS>
+__global__ __launch_bounds__(kBlock) void spmv_tilecsc_kernel(SpmvArgs a, double* __restrict__ y,
+                                                              double* __restrict__ partials) {
+    __shared__ double s_acc[kWavesPerBlock][MAXROWS];
+    __shared__ int2 s_desc[kWavesPerBlock][kTileBatch];
     __shared__ double s_tmp[kWavesPerBlock];
-    __shared__ bool s_last;
 
-    if (MODE == kSpmvCg && a.st->done) return;
+    if (MODE == kSpmvCg && load_done(a.st)) return;
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    // The wavefront index is uniform across the wave; saying so keeps every
+    // per-group and per-window quantity in scalar registers and scalar loads.
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
-    const int g = blk * kWavesPerBlock + w;
-    const MetaT* meta = static_cast<const MetaT*>(a.meta);
+    const int g_begin = blk * a.groups_per_block;
+    const int g_end = min(g_begin + a.groups_per_block, a.ngroups);
+    const int uprec = *a.uprec;
     double dot = 0.0;
 
-    if (g < a.ngroups) {
+    for (int g = g_begin + w; g < g_end; g += kWavesPerBlock) {
         const int rb0 = g * a.G;
-        const int rb1 = min(rb0 + a.G, a.nrb);
-        const int nrbg = rb1 - rb0;
+        const int nrbg = min(rb0 + a.G, a.nrb) - rb0;
         const int row0 = rb0 * a.R;
         const int nrows = min(a.rows_per_group, a.n - row0);
         for (int i = lane; i < a.rows_per_group; i += kWave) s_acc[w][i] = 0.0;
-        for (int i = lane; i <= nrbg; i += kWave) s_trp[w][i] = a.trp[rb0 + i];
-        const int uprec = *a.uprec;
-        wave_lds_sync();
-        const int t_begin = s_trp[w][0];
-        const int t_end = s_trp[w][nrbg];
+        // Row-block boundaries of the group, one per lane (nrbg <= 64).
+        const int my_trp = lane <= nrbg ? a.trp[rb0 + lane] : 0x7fffffff;
+        double p_own = 0.0;
+        if (MODE == kSpmvCg && MAXROWS <= kWave && lane < nrows) p_own = a.x[row0 + lane];
+        const int t_begin = __builtin_amdgcn_readlane(my_trp, 0);
+        const int t_end = __builtin_amdgcn_readlane(my_trp, nrbg);
+        int win = uniform_load(a.win_base, g);
         for (int tb = t_begin; tb < t_end; tb += kTileBatch) {
             const int nt = min(kTileBatch, t_end - tb);
-            int my_start = 0x7fffffff;
+            int my_start = 0;
             if (lane < nt) {
                 const int t = tb + lane;
                 my_start = a.tptr[t];
                 int rbi = 0;
-                while (rbi + 1 < nrbg && s_trp[w][rbi + 1] <= t) ++rbi;
+                for (int i = 1; i < nrbg; ++i) rbi += (__builtin_amdgcn_readlane(my_trp, i) <= t) ? 1 : 0;
                 const int prec = uprec >= 0 ? uprec : (int)a.map[t];
-                s_cbase[w][lane] = a.tcol[t] * a.C;
-                s_pr[w][lane] = prec | ((rbi * a.R) << 2);
+                s_desc[w][lane] = make_int2(a.tcol[t] * a.C, prec | ((rbi * a.R) << 2));
             }
-            const int kb = __shfl(my_start, 0, kWave);
-            const int ke = a.tptr[tb + nt];
-            int jprev = -1;
-            for (int k0 = kb; k0 < ke; k0 += kWave) {
-                s_flag[w][lane] = 0;
-                wave_lds_sync();
-                const int pos = my_start - k0;
-                if (pos >= 0 && pos < kWave) s_flag[w][pos] = 1;
-                wave_lds_sync();
-                const int f = s_flag[w][lane];
-                const uint64_t mask = __ballot(f);
-                const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-                const int j = jprev + below + f;
-                jprev += __popcll(mask);
-                const int k = k0 + lane;
-                if (k < ke) {
+            const int kb = __builtin_amdgcn_readlane(my_start, 0);
+            const int len = a.tptr[tb + nt] - kb;
+            const __amdgpu_buffer_rsrc_t r64 = batch_rsrc(a.v64, kb, 8, len);
+            const __amdgpu_buffer_rsrc_t r32 = batch_rsrc(a.v32, kb, 4, len);
+            const __amdgpu_buffer_rsrc_t r16 = batch_rsrc(a.v16, kb, 2, len);
+            const __amdgpu_buffer_rsrc_t rmt = batch_rsrc(a.meta, kb, (int)sizeof(MetaT), len);
+            wave_lds_sync();
+            const int win0 = win;
+            win += (len + kWave - 1) / kWave;  // windows of this batch
+            for (int o0 = 0; o0 < len; o0 += kWave * kUnroll) {
+                int off[kUnroll];
+                int2 d[kUnroll];
+                uint32_t mt[kUnroll];
+                u32x2 b64[kUnroll];
+                uint32_t b32[kUnroll], b16[kUnroll];
+                uint64_t mask[kUnroll];
+                int j0[kUnroll];
+                // Window records first (scalar loads), then the descriptor reads, then
+                // every vector load of the U windows, so their latencies overlap.
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const bool live = o0 + u * kWave < len;  // wave-uniform: the window exists
+                    const int wi = win0 + o0 / kWave + u;
+                    mask[u] = live ? uniform_load(a.win_mask, wi) : 0ull;
+                    j0[u] = live ? uniform_load(a.win_tile, wi) : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    off[u] = o0 + u * kWave + lane;
+                    int j = j0[u] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask[u] >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mask[u], 0u));
+                    d[u] = s_desc[w][min(j, nt - 1)];
+                }
+                // Local (row, column) of every nonzero first, then the vector gathers they
+                // need; the value loads follow and stay in flight alongside the gathers.
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const bool in = off[u] < len;
+                    mt[u] = sizeof(MetaT) == 1
+                                ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rmt, in ? off[u] : kOutOfRange, 0, 0)
+                                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rmt, in ? 2 * off[u] : kOutOfRange, 0, 0);
+                }
+                double xv[kUnroll];
+                int row[kUnroll];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
                     int r, c;
-                    decode_meta<MetaT>(__builtin_nontemporal_load(&meta[k]), r, c);
-                    const int pr = s_pr[w][j];
-                    const int cb = s_cbase[w][j];
-                    const double v = load_stored_value(a, pr & 3, k);
-                    const double xv = a.x[cb + c];
-                    atomicAdd(&s_acc[w][(pr >> 2) + r], v * xv);
+                    decode_meta<MetaT>(mt[u], r, c);
+                    row[u] = (d[u].y >> 2) + r;
+                    xv[u] = a.x[d[u].x + c];
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int prec = d[u].y & 3;
+                    const bool in = off[u] < len;
+                    // A plane no lane of the window uses is not touched at all (wave-uniform
+                    // branch): the address unit then spends no cycles on it.
+                    b64[u] = u32x2{0u, 0u};
+                    b32[u] = 0u;
+                    b16[u] = 0u;
+                    asm volatile("" : "+v"(b64[u]), "+v"(b32[u]), "+v"(b16[u]));
+                    const int o64 = (in && prec == 0) ? 8 * off[u] : kOutOfRange;
+                    const int o32 = (in && prec == 1) ? 4 * off[u] : kOutOfRange;
+                    const int o16 = (in && prec == 2) ? 2 * off[u] : kOutOfRange;
+                    if (__builtin_amdgcn_ballot_w64(o64 != kOutOfRange))
+                        b64[u] = __builtin_amdgcn_raw_buffer_load_b64(r64, o64, 0, 0);
+                    if (__builtin_amdgcn_ballot_w64(o32 != kOutOfRange))
+                        b32[u] = __builtin_amdgcn_raw_buffer_load_b32(r32, o32, 0, 0);
+                    if (__builtin_amdgcn_ballot_w64(o16 != kOutOfRange))
+                        b16[u] = __builtin_amdgcn_raw_buffer_load_b16(r16, o16, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    if (off[u] < len) {
+                        const double v64 = __longlong_as_double(((long long)b64[u].y << 32) | b64[u].x);
+                        const double vlo = (double)__uint_as_float(b32[u] | (b16[u] << 16));
+                        const double v = (d[u].y & 3) == 0 ? v64 : vlo;
+                        atomicAdd(&s_acc[w][row[u]], v * xv[u]);
+                    }
                 }
             }
         }
@@ -289,38 +365,29 @@ __global__ __launch_bounds__(kBlock) void spmv_tilecsc_kernel(SpmvArgs a) {
         for (int i = lane; i < nrows; i += kWave) {
             const double acc = s_acc[w][i];
             if (MODE == kSpmvPlain) {
-                a.y[row0 + i] = acc;
+                y[row0 + i] = acc;
             } else if (MODE == kSpmvCg) {
-                a.y[row0 + i] = acc;
-                dot += a.x[row0 + i] * acc;
+                y[row0 + i] = acc;
+                dot += (MAXROWS <= kWave ? p_own : a.x[row0 + i]) * acc;
             } else {
-                a.y[row0 + i] = a.b[row0 + i] - acc;
+                y[row0 + i] = a.b[row0 + i] - acc;
             }
         }
+        wave_lds_sync();
     }
 
     if (MODE == kSpmvCg) {
-        double part[1] = {block_sum(dot, s_tmp)};
-        if (arrive_last<1>(part, a.partials, &a.st->ticket[kTicketSpmv], &s_last)) {
-            double tot[1];
-            reduce_partials<1>(a.partials, gridDim.x, tot, s_tmp);
-            if (threadIdx.x == 0) {
-                State* st = a.st;
-                const double pq = tot[0];
-                const double alpha = st->rz / pq;
-                st->pq = pq;
-                st->alpha = alpha;
-                if (!(pq > 0.0) || !isfinite(pq) || !isfinite(alpha)) st->done = 3;
-                st->ticket[kTicketSpmv] = 0;
-            }
-        }
+        const double part = block_sum(dot, s_tmp);
+        if (threadIdx.x == 0) partials[blockIdx.x] = part;
     }
 }
 
 // ---------------------------------------------------------------------------
-// CG vector kernels. Grid-stride loops; every block publishes one partial per
-// reduced quantity and the last block to arrive finishes the reduction in a
-// fixed order, computes the scalars and updates the solver state.
+// CG vector kernels. No atomics and no grid-wide fences: every kernel writes
+// one partial per block for each quantity it reduces, and the next kernel
+// sums those partials in a fixed order in every block (kernel boundaries
+// make them visible across XCDs). Scalar state is committed by thread 0 of
+// block 0 into fields the other blocks of the same launch do not read.
 // ---------------------------------------------------------------------------
 struct VecArgs {
     double* x;
@@ -333,27 +400,29 @@ struct VecArgs {
     const double* x0;     // may be null
     double* hist;
     State* st;
-    double* partials;
+    const double* part_in;   // partials written by the previous kernel
+    int32_t nparts_in;
+    double* part_out;        // this kernel's partials
     int32_t* trace_k;
-    int64_t* trace_counts;
+    int32_t* trace_counts;   // [entry][kTraceBlocks][3]
     int64_t T;
     int32_t n;
     int32_t jacobi;
-    int32_t r_ready;      // init: r already holds b - A x0
+    int32_t r_ready;         // init: r already holds b - A x0
 };
 
-__device__ inline void trace_uniform(State* st, int32_t* trace_k, int64_t* trace_counts, int k,
+__device__ inline void trace_uniform(State* st, int32_t* trace_k, int32_t* trace_counts, int k,
                                      int prec, int64_t T) {
     const int i = st->ntrace;
     if (i < st->trace_cap) {
         trace_k[i] = k;
-        for (int p = 0; p < 3; ++p) trace_counts[3 * i + p] = (p == prec) ? T : 0;
+        for (int p = 0; p < 3; ++p) trace_counts[(size_t)i * kTraceBlocks * 3 + p] = (p == prec) ? (int32_t)T : 0;
     }
     st->ntrace = i + 1;
 }
 
 // Advances the one-way residual schedule for the residual rho of iteration k.
-__device__ inline void advance_stage(State* st, int32_t* trace_k, int64_t* trace_counts, int k,
+__device__ inline void advance_stage(State* st, int32_t* trace_k, int32_t* trace_counts, int k,
                                      double rho, int64_t T, bool first) {
     if (st->nstage <= 0) return;
     int s = st->stage;
@@ -365,11 +434,10 @@ __device__ inline void advance_stage(State* st, int32_t* trace_k, int64_t* trace
     }
 }
 
-// Initial state: x = x0 (or 0), r = b - A x0 (computed beforehand when x0 is
-// given), z = dinv .* r, p = z, then ||r0||, r.z and the stop decision at k = 0.
+// Initial vectors: x = x0 (or 0), r = b - A x0 (computed beforehand when x0 is
+// given), z = dinv .* r, p = z; partials of r.r and r.z.
 __global__ __launch_bounds__(kBlock) void cg_init_kernel(VecArgs a) {
     __shared__ double s_tmp[kWavesPerBlock];
-    __shared__ bool s_last;
     double rr = 0.0, rz = 0.0;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += gridDim.x * blockDim.x) {
         const double ri = a.r_ready ? a.r[i] : a.b[i];
@@ -384,88 +452,123 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(VecArgs a) {
         rr += ri * ri;
         rz += ri * zi;
     }
-    double part[2] = {block_sum(rr, s_tmp), block_sum(rz, s_tmp)};
-    if (arrive_last<2>(part, a.partials, &a.st->ticket[kTicketInit], &s_last)) {
-        double tot[2];
-        reduce_partials<2>(a.partials, gridDim.x, tot, s_tmp);
-        if (threadIdx.x == 0) {
-            State* st = a.st;
-            st->rr = tot[0];
-            st->rz = a.jacobi ? tot[1] : tot[0];
-            st->norm0 = sqrt(tot[0]);
-            st->k = 0;
-            st->ntrace = 0;
-            st->stage = 0;
-            st->alpha = 0.0;
-            st->beta = 0.0;
-            const double rho0 = st->norm0 > 0.0 ? 1.0 : 0.0;
-            a.hist[0] = rho0;
-            if (st->nstage > 0) advance_stage(st, a.trace_k, a.trace_counts, 0, rho0, a.T, true);
-            if (st->norm0 == 0.0 || rho0 <= st->tol) st->done = 1;
-            else if (st->maxit <= 0) st->done = 2;
-            else st->done = 0;
-            st->ticket[kTicketInit] = 0;
-        }
+    const double prr = block_sum(rr, s_tmp);
+    const double prz = block_sum(rz, s_tmp);
+    if (threadIdx.x == 0) {
+        a.part_out[2 * blockIdx.x] = prr;
+        a.part_out[2 * blockIdx.x + 1] = prz;
     }
 }
 
-// x += alpha p; r -= alpha q; [z = dinv .* r]; partials of r.r [and r.z];
-// the last block forms beta, rho_{k+1}, the history entry and the stop flag.
+// One block: ||r0||, r.z, rho_0, the stop decision at k = 0, the first stage.
+__global__ __launch_bounds__(kBlock) void cg_init_finish_kernel(VecArgs a) {
+    __shared__ double s_tmp[kWavesPerBlock];
+    double tot[2];
+    sum_partials<2>(a.part_in, a.nparts_in, tot, s_tmp);
+    if (threadIdx.x == 0) {
+        State* st = a.st;
+        st->rr = tot[0];
+        st->rz = a.jacobi ? tot[1] : tot[0];
+        st->rz_prev = st->rz;
+        st->norm0 = sqrt(tot[0]);
+        st->k = 0;
+        st->bd = 0;
+        st->ntrace = 0;
+        st->stage = 0;
+        st->alpha = 0.0;
+        st->beta = 0.0;
+        const double rho0 = st->norm0 > 0.0 ? 1.0 : 0.0;
+        a.hist[0] = rho0;
+        if (st->nstage > 0) advance_stage(st, a.trace_k, a.trace_counts, 0, rho0, a.T, true);
+        int done = 0;
+        if (st->norm0 == 0.0 || rho0 <= st->tol) done = 1;
+        else if (st->maxit <= 0) done = 2;
+        store_done(st, done);
+    }
+}
+
+// alpha = r.z / p.q (p.q summed from the SpMV partials in every block);
+// x += alpha p; r -= alpha q; [z = dinv .* r]; partials of r.r [and r.z].
+// On p.q <= 0 or a non-finite alpha nothing is updated and the breakdown is
+// flagged for the direction kernel.
 __global__ __launch_bounds__(kBlock) void cg_update_kernel(VecArgs a) {
     __shared__ double s_tmp[kWavesPerBlock];
-    __shared__ bool s_last;
     State* st = a.st;
-    if (st->done) return;
-    const double alpha = st->alpha;
+    if (load_done(st)) return;
+    double tot[1];
+    sum_partials<1>(a.part_in, a.nparts_in, tot, s_tmp);
+    const double pq = tot[0];
+    const double alpha = st->rz / pq;
+    const bool bd = !(pq > 0.0) || !isfinite(pq) || !isfinite(alpha);
     double rr = 0.0, rz = 0.0;
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += gridDim.x * blockDim.x) {
-        const double pi = a.p[i];
-        a.x[i] += alpha * pi;
-        const double ri = a.r[i] - alpha * a.q[i];
-        a.r[i] = ri;
-        rr += ri * ri;
-        if (a.jacobi) {
-            const double zi = a.dinv[i] * ri;
-            a.z[i] = zi;
-            rz += ri * zi;
+    if (!bd) {
+        for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += gridDim.x * blockDim.x) {
+            a.x[i] += alpha * a.p[i];
+            const double ri = a.r[i] - alpha * a.q[i];
+            a.r[i] = ri;
+            rr += ri * ri;
+            if (a.jacobi) {
+                const double zi = a.dinv[i] * ri;
+                a.z[i] = zi;
+                rz += ri * zi;
+            }
         }
     }
-    double part[2] = {block_sum(rr, s_tmp), a.jacobi ? block_sum(rz, s_tmp) : 0.0};
-    if (arrive_last<2>(part, a.partials, &st->ticket[kTicketUpdate], &s_last)) {
-        double tot[2];
-        reduce_partials<2>(a.partials, gridDim.x, tot, s_tmp);
-        if (threadIdx.x == 0) {
-            const double rr_new = tot[0];
-            const double rz_new = a.jacobi ? tot[1] : rr_new;
-            const double beta = rz_new / st->rz;
-            const int k = st->k + 1;
-            const double rho = sqrt(rr_new) / st->norm0;
-            a.hist[k] = rho;
-            st->k = k;
-            st->rr = rr_new;
-            st->rz = rz_new;
-            st->beta = beta;
-            if (!isfinite(beta) || !isfinite(rho)) st->done = 3;
-            else if (rho <= st->tol) st->done = 1;
-            else if (k >= st->maxit) st->done = 2;
-            else if (st->nstage > 0) advance_stage(st, a.trace_k, a.trace_counts, k, rho, a.T, false);
-            st->ticket[kTicketUpdate] = 0;
+    const double prr = block_sum(rr, s_tmp);
+    const double prz = a.jacobi ? block_sum(rz, s_tmp) : prr;
+    if (threadIdx.x == 0) {
+        a.part_out[2 * blockIdx.x] = prr;
+        a.part_out[2 * blockIdx.x + 1] = prz;
+        if (blockIdx.x == 0) {
+            st->pq = pq;
+            st->alpha = alpha;
+            st->rz_prev = st->rz;
+            st->bd = bd ? 1 : 0;
         }
     }
 }
 
-// p = z + beta p (z = r for plain CG).
+// beta = (r.z)_new / (r.z)_old from the update partials (in every block);
+// p = z + beta p (z = r for plain CG). Thread 0 of block 0 commits
+// rho_{k+1}, the history entry, the stop flag and the schedule stage.
+// Other blocks may read `done` before or after that commit within the final
+// iteration; either way the direction update they skip or make is unused.
 __global__ __launch_bounds__(kBlock) void cg_direction_kernel(VecArgs a) {
-    const State* st = a.st;
-    if (st->done) return;
-    const double beta = st->beta;
+    __shared__ double s_tmp[kWavesPerBlock];
+    State* st = a.st;
+    if (load_done(st)) return;
+    if (st->bd) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) store_done(st, 3);
+        return;
+    }
+    double tot[2];
+    sum_partials<2>(a.part_in, a.nparts_in, tot, s_tmp);
+    const double rr_new = tot[0];
+    const double rz_new = tot[1];
+    const double beta = rz_new / st->rz_prev;
     const double* z = a.jacobi ? a.z : a.r;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += gridDim.x * blockDim.x)
         a.p[i] = z[i] + beta * a.p[i];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        const int k = st->k + 1;
+        const double rho = sqrt(rr_new) / st->norm0;
+        a.hist[k] = rho;
+        st->k = k;
+        st->rr = rr_new;
+        st->rz = rz_new;
+        st->beta = beta;
+        int done = 0;
+        if (!isfinite(beta) || !isfinite(rho)) done = 3;
+        else if (rho <= st->tol) done = 1;
+        else if (k >= st->maxit) done = 2;
+        else if (st->nstage > 0) advance_stage(st, a.trace_k, a.trace_counts, k, rho, a.T, false);
+        if (done) store_done(st, done);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Map kernels.
+// Map kernels. Launched with exactly kTraceBlocks blocks; per-block precision
+// counts go to the trace (summed on the host), so no atomics are needed.
 // ---------------------------------------------------------------------------
 __device__ inline int tile_rule_code(double s, double rho, double hi, double lo) {
     const double v = s * rho;
@@ -478,29 +581,37 @@ struct MapArgs {
     State* st;
     const double* hist;
     int32_t* trace_k;
-    int64_t* trace_counts;
+    int32_t* trace_counts;
     int64_t T;
     double rho;     // explicit rho (eval mode)
     int32_t solve;  // 1: in-solve window step (reads k and rho_k from the state)
 };
 
+__device__ inline void block_counts_out(unsigned c0, unsigned c1, unsigned c2, int32_t* out) {
+    __shared__ unsigned s_cnt[3];
+    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
+    __syncthreads();
+    atomicAdd(&s_cnt[0], c0);  // LDS atomics
+    atomicAdd(&s_cnt[1], c1);
+    atomicAdd(&s_cnt[2], c2);
+    __syncthreads();
+    if (threadIdx.x < 3) out[threadIdx.x] = (int32_t)s_cnt[threadIdx.x];
+}
+
 // Windowed tile rule: at k % period == 0 every tile's precision is re-selected
 // from its score and rho_k, and the window's precision counts are recorded.
 __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
-    __shared__ unsigned long long s_cnt[3];
     State* st = a.st;
     double rho = a.rho;
     int slot = -1;
     if (a.solve) {
-        if (st->done) return;
+        if (load_done(st)) return;
         const int k = st->k;
         if (k % st->period != 0) return;
         rho = a.hist[k];
         slot = k / st->period;
         if (slot >= st->trace_cap) slot = -1;
     }
-    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
-    __syncthreads();
     unsigned c0 = 0, c1 = 0, c2 = 0;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < a.T;
          t += (int64_t)gridDim.x * blockDim.x) {
@@ -511,12 +622,7 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
         c2 += code == 2;
     }
     if (slot >= 0) {
-        atomicAdd(&s_cnt[0], (unsigned long long)c0);
-        atomicAdd(&s_cnt[1], (unsigned long long)c1);
-        atomicAdd(&s_cnt[2], (unsigned long long)c2);
-        __syncthreads();
-        if (threadIdx.x < 3)
-            atomicAdd((unsigned long long*)&a.trace_counts[3 * slot + threadIdx.x], s_cnt[threadIdx.x]);
+        block_counts_out(c0, c1, c2, a.trace_counts + ((size_t)slot * kTraceBlocks + blockIdx.x) * 3);
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             a.trace_k[slot] = st->k;
             st->ntrace = slot + 1;
@@ -526,21 +632,17 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
 
 // Precision counts of the active map into trace entry 0 (static maps).
 __global__ __launch_bounds__(kBlock) void map_count_kernel(const uint8_t* map, int64_t T,
-                                                           int64_t* counts) {
-    __shared__ unsigned long long s_cnt[3];
-    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
-    __syncthreads();
+                                                           int32_t* trace_k, int32_t* counts) {
     unsigned c[3] = {0, 0, 0};
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T;
          t += (int64_t)gridDim.x * blockDim.x)
         c[map[t] < 3 ? map[t] : 0]++;
-    for (int p = 0; p < 3; ++p) atomicAdd(&s_cnt[p], (unsigned long long)c[p]);
-    __syncthreads();
-    if (threadIdx.x < 3) atomicAdd((unsigned long long*)&counts[threadIdx.x], s_cnt[threadIdx.x]);
+    block_counts_out(c[0], c[1], c[2], counts + (size_t)blockIdx.x * 3);
+    if (blockIdx.x == 0 && threadIdx.x == 0) trace_k[0] = 0;
 }
 
-// Fills n int64 values (device-side clear that is safe inside captured graphs).
-__global__ void fill_i64_kernel(int64_t* p, int64_t v, int64_t n) {
+// Fills n int32 values (a device-side clear that is safe inside captured graphs).
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
         p[i] = v;

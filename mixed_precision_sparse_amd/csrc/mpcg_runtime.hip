@@ -48,6 +48,10 @@ struct cg_handle {
     int64_t device_bytes = 0;
 
     // Matrix (device).
+    int32_t* win_base = nullptr;   // [ngroups+1]
+    uint64_t* win_mask = nullptr;  // [nwin]
+    int32_t* win_tile = nullptr;   // [nwin]
+    int64_t nwin = 0;
     int32_t* trp = nullptr;
     int32_t* tcol = nullptr;
     int32_t* tptr = nullptr;
@@ -60,13 +64,14 @@ struct cg_handle {
 
     // CG vectors and reduction scratch (device).
     double *x = nullptr, *r = nullptr, *p = nullptr, *q = nullptr, *z = nullptr;
-    double* partials = nullptr;
-    int partial_cap = 0;
+    double* part_spmv = nullptr;  // one p.q partial per SpMV block
+    double* part_vec = nullptr;   // two partials per vector-kernel block
+    int spmv_blocks = 0, groups_per_block = 0, vec_blocks = 0;
     dev::State* st = nullptr;
     double* hist = nullptr;
     int64_t hist_cap = 0;
     int32_t* trace_k = nullptr;
-    int64_t* trace_counts = nullptr;
+    int32_t* trace_counts = nullptr;  // [entry][kTraceBlocks][3]
     int64_t trace_cap = 0;
     unsigned long long* scratch_u64 = nullptr;
 
@@ -128,11 +133,20 @@ int grid_for(int64_t work, int per_thread, int cap) {
     return (int)std::max<int64_t>(1, std::min<int64_t>(g, cap));
 }
 
-constexpr int kVecGridCap = 2048;
+constexpr int kVecGridCap = 1024;
+constexpr int kSpmvGridCap = 2048;
 
-int vec_grid(const cg_handle* h) { return grid_for(h->n, 4, kVecGridCap); }
-int spmv_grid(const cg_handle* h) {
-    return (int)((h->ngroups + dev::kWavesPerBlock - 1) / dev::kWavesPerBlock);
+int vec_grid(const cg_handle* h) { return h->vec_blocks; }
+int spmv_grid(const cg_handle* h) { return h->spmv_blocks; }
+
+// SpMV blocks take contiguous ranges of row groups; vector kernels use a capped grid.
+void plan_grids(cg_handle* h) {
+    const int64_t want = (h->ngroups + dev::kWavesPerBlock - 1) / dev::kWavesPerBlock;
+    int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(want, kSpmvGridCap));
+    h->groups_per_block = (int)((h->ngroups + blocks - 1) / blocks);
+    if (h->groups_per_block < 1) h->groups_per_block = 1;
+    h->spmv_blocks = (int)std::max<int64_t>(1, (h->ngroups + h->groups_per_block - 1) / h->groups_per_block);
+    h->vec_blocks = grid_for(h->n, 8, kVecGridCap);
 }
 
 dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t* uprec) {
@@ -145,12 +159,15 @@ dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t*
     a.v64 = h->v64;
     a.v32 = h->v32;
     a.v16 = h->v16;
+    a.win_base = h->win_base;
+    a.win_mask = h->win_mask;
+    a.win_tile = h->win_tile;
     a.x = x;
     a.y = y;
     a.b = nullptr;
     a.uprec = uprec;
     a.st = h->st;
-    a.partials = h->partials;
+    a.partials = h->part_spmv;
     a.n = (int32_t)h->n;
     a.nrb = (int32_t)h->nrb;
     a.R = h->R;
@@ -158,18 +175,25 @@ dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t*
     a.G = h->G;
     a.rows_per_group = h->rows_per_group;
     a.ngroups = h->ngroups;
+    a.groups_per_block = h->groups_per_block;
     return a;
 }
 
 template <int MODE>
 void launch_spmv(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
     const int grid = spmv_grid(h);
-    if (h->meta16)
-        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE>), dim3(grid), dim3(dev::kBlock), 0,
-                           s, a);
-    else
-        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE>), dim3(grid), dim3(dev::kBlock), 0,
-                           s, a);
+    const bool wide = h->rows_per_group > 64;
+    if (h->meta16) {
+        if (wide)
+            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, dev::kMaxRows>), dim3(grid),
+                               dim3(dev::kBlock), 0, s, a, a.y, a.partials);
+        else
+            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, 64>), dim3(grid), dim3(dev::kBlock),
+                               0, s, a, a.y, a.partials);
+    } else {
+        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, 64>), dim3(grid), dim3(dev::kBlock), 0, s,
+                           a, a.y, a.partials);
+    }
 }
 
 dev::VecArgs vec_args(cg_handle* h, const double* b, const double* x0) {
@@ -184,7 +208,9 @@ dev::VecArgs vec_args(cg_handle* h, const double* b, const double* x0) {
     a.x0 = x0;
     a.hist = h->hist;
     a.st = h->st;
-    a.partials = h->partials;
+    a.part_in = h->part_vec;
+    a.nparts_in = vec_grid(h);
+    a.part_out = h->part_vec;
     a.trace_k = h->trace_k;
     a.trace_counts = h->trace_counts;
     a.T = h->T;
@@ -243,13 +269,17 @@ void drop_graph(cg_handle* h) {
 void enqueue_iteration(cg_handle* h, hipStream_t s) {
     if (h->sched == kSchedTileRule) {
         dev::MapArgs ma = map_args(h, 0.0, 1);
-        hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(grid_for(h->T, 4, 1024)), dim3(dev::kBlock), 0,
-                           s, ma);
+        hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, s, ma);
     }
     dev::SpmvArgs sa = spmv_args(h, h->p, h->q, &h->st->uprec);
     launch_spmv<dev::kSpmvCg>(h, sa, s);
     dev::VecArgs va = vec_args(h, nullptr, nullptr);
+    va.part_in = h->part_spmv;
+    va.nparts_in = spmv_grid(h);
+    va.part_out = h->part_vec;
     hipLaunchKernelGGL(dev::cg_update_kernel, dim3(vec_grid(h)), dim3(dev::kBlock), 0, s, va);
+    va.part_in = h->part_vec;
+    va.nparts_in = vec_grid(h);
     hipLaunchKernelGGL(dev::cg_direction_kernel, dim3(vec_grid(h)), dim3(dev::kBlock), 0, s, va);
 }
 
@@ -318,7 +348,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     h->C = A->C;
     h->nrb = A->nrb;
     h->meta16 = !(A->R <= 16 && A->C <= 16);
-    h->G = std::max(1, 64 / A->R);
+    h->G = std::max(1, std::min(dev::kMaxGroupRB, 64 / A->R));
     h->rows_per_group = h->G * A->R;
     h->ngroups = (int32_t)((h->nrb + h->G - 1) / h->G);
     if (opt) {
@@ -345,6 +375,66 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
             for (int64_t k = lo; k < hi; ++k) meta8[k] = (uint8_t)((A->row_idx[k] << 4) | A->col_local[k]);
         });
     }
+    // Window records of the SpMV sweep: row group g's tiles are taken in batches
+    // of kTileBatch; every batch's nonzeros are cut into windows of 64 from the
+    // batch start. A record holds the batch-relative tile of the window's first
+    // nonzero and a mask whose bit q says that nonzero q+1 of the window starts
+    // a tile, so a lane's tile is the first tile plus a prefix popcount.
+    std::vector<int32_t> win_base(h->ngroups + 1, 0);
+    {
+        std::vector<int64_t> cnt(h->ngroups, 0);
+        mpcg::parallel_for(h->ngroups, [&](int64_t lo, int64_t hi) {
+            for (int64_t g = lo; g < hi; ++g) {
+                const int64_t rb0 = g * h->G, rb1 = std::min<int64_t>(rb0 + h->G, h->nrb);
+                const int64_t t0 = A->tile_row_ptr[rb0], t1 = A->tile_row_ptr[rb1];
+                int64_t c = 0;
+                for (int64_t tb = t0; tb < t1; tb += dev::kTileBatch) {
+                    const int64_t nt = std::min<int64_t>(dev::kTileBatch, t1 - tb);
+                    const int64_t len = A->tile_nnz_ptr[tb + nt] - A->tile_nnz_ptr[tb];
+                    c += (len + 63) / 64;
+                }
+                cnt[g] = c;
+            }
+        });
+        int64_t acc = 0;
+        for (int64_t g = 0; g < h->ngroups; ++g) {
+            win_base[g] = (int32_t)acc;
+            acc += cnt[g];
+        }
+        win_base[h->ngroups] = (int32_t)acc;
+        h->nwin = acc;
+        if (acc > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: too many SpMV windows"));
+    }
+    std::vector<uint64_t> win_mask(std::max<int64_t>(h->nwin, 1), 0);
+    std::vector<int32_t> win_tile(std::max<int64_t>(h->nwin, 1), 0);
+    mpcg::parallel_for(h->ngroups, [&](int64_t lo, int64_t hi) {
+        for (int64_t g = lo; g < hi; ++g) {
+            const int64_t rb0 = g * h->G, rb1 = std::min<int64_t>(rb0 + h->G, h->nrb);
+            const int64_t t0 = A->tile_row_ptr[rb0], t1 = A->tile_row_ptr[rb1];
+            int64_t wi = win_base[g];
+            for (int64_t tb = t0; tb < t1; tb += dev::kTileBatch) {
+                const int64_t nt = std::min<int64_t>(dev::kTileBatch, t1 - tb);
+                const int64_t kb = A->tile_nnz_ptr[tb], ke = A->tile_nnz_ptr[tb + nt];
+                int64_t j = 0;  // batch-relative tile of the current position
+                for (int64_t k0 = kb; k0 < ke; k0 += 64, ++wi) {
+                    while (j + 1 < nt && A->tile_nnz_ptr[tb + j + 1] <= k0) ++j;
+                    win_tile[wi] = (int32_t)j;
+                    uint64_t m = 0;
+                    int64_t jn = j + 1;  // next tile start to look for
+                    for (int q = 0; q < 63; ++q) {
+                        const int64_t pos = k0 + q + 1;
+                        if (pos >= ke) break;
+                        if (jn < nt && A->tile_nnz_ptr[tb + jn] == pos) {
+                            m |= 1ull << q;
+                            ++jn;
+                        }
+                    }
+                    win_mask[wi] = m;
+                }
+            }
+        }
+    });
+
     std::vector<double> dinv_h;
     if (h->jacobi) {
         dinv_h.assign(n, 0.0);
@@ -372,6 +462,9 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         if (rc != CG_OK) return bail(rc); \
     } while (0)
     TRY(dalloc(h, &h->trp, h->nrb + 1));
+    TRY(dalloc(h, &h->win_base, h->ngroups + 1));
+    TRY(dalloc(h, &h->win_mask, std::max<int64_t>(h->nwin, 1)));
+    TRY(dalloc(h, &h->win_tile, std::max<int64_t>(h->nwin, 1)));
     TRY(dalloc(h, &h->tcol, T));
     TRY(dalloc(h, &h->tptr, T + 1));
     TRY(dalloc(h, &h->map, T));
@@ -395,13 +488,14 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         TRY(dalloc(h, &h->z, n));
         TRY(dalloc(h, &h->dinv, n));
     }
-    h->partial_cap = std::max(spmv_grid(h), kVecGridCap) * 2;
-    TRY(dalloc(h, &h->partials, h->partial_cap));
+    plan_grids(h);
+    TRY(dalloc(h, &h->part_spmv, spmv_grid(h)));
+    TRY(dalloc(h, &h->part_vec, 2 * vec_grid(h)));
     TRY(dalloc(h, &h->st, 1));
     TRY(dalloc(h, &h->scratch_u64, 4));
     h->trace_cap = 16;
     TRY(dalloc(h, &h->trace_k, h->trace_cap));
-    TRY(dalloc(h, &h->trace_counts, 3 * h->trace_cap));
+    TRY(dalloc(h, &h->trace_counts, 3 * dev::kTraceBlocks * h->trace_cap));
 #undef TRY
 
     auto dev_err = [&](hipError_t e, const char* what) {
@@ -416,7 +510,10 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     if ((e = hipHostMalloc((void**)&h->pinned, 4 * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess)
         return dev_err(e, "pinned host memory");
 
-    if ((e = hipMemcpyAsync(h->trp, trp.data(), sizeof(int32_t) * trp.size(), hipMemcpyHostToDevice, s)) ||
+    if ((e = hipMemcpyAsync(h->win_base, win_base.data(), sizeof(int32_t) * win_base.size(), hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->win_mask, win_mask.data(), sizeof(uint64_t) * win_mask.size(), hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->win_tile, win_tile.data(), sizeof(int32_t) * win_tile.size(), hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->trp, trp.data(), sizeof(int32_t) * trp.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tcol, A->tile_col_idx.data(), sizeof(int32_t) * T, hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tptr, tptr.data(), sizeof(int32_t) * tptr.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->meta, h->meta16 ? (const void*)meta16.data() : (const void*)meta8.data(),
@@ -557,8 +654,7 @@ extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {
     if (!h) return fail(CG_EINVAL, "cg_eval_tile_rule: h is NULL");
     if (h->sched != kSchedTileRule) return fail(CG_EINVAL, "cg_eval_tile_rule: no tile rule is set");
     dev::MapArgs ma = map_args(h, rho, 0);
-    hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(grid_for(h->T, 4, 1024)), dim3(dev::kBlock), 0, h->stream,
-                       ma);
+    hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, h->stream, ma);
     HIP_CHECK(hipGetLastError());
     HIP_CHECK(hipStreamSynchronize(h->stream));
     return CG_OK;
@@ -608,7 +704,7 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
         h->trace_k = nullptr;
         h->trace_counts = nullptr;
         int rc = dalloc(h, &h->trace_k, need_trace);
-        if (rc == CG_OK) rc = dalloc(h, &h->trace_counts, 3 * need_trace);
+        if (rc == CG_OK) rc = dalloc(h, &h->trace_counts, 3 * dev::kTraceBlocks * need_trace);
         if (rc != CG_OK) return rc;
         h->trace_cap = need_trace;
         drop_graph(h);
@@ -627,11 +723,11 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
     hs.k = 0;
     hs.trace_cap = (int32_t)h->trace_cap;
     hs.ntrace = 0;
-    for (auto& t : hs.ticket) t = 0;
     HIP_CHECK(hipMemcpyAsync(h->st, &hs, sizeof(hs), hipMemcpyHostToDevice, s));
 
-    hipLaunchKernelGGL(dev::fill_i64_kernel, dim3(grid_for(3 * h->trace_cap, 1, 64)), dim3(dev::kBlock), 0, s,
-                       h->trace_counts, (int64_t)0, (int64_t)(3 * h->trace_cap));
+    const int64_t ncount = 3 * dev::kTraceBlocks * h->trace_cap;
+    hipLaunchKernelGGL(dev::fill_i32_kernel, dim3(grid_for(ncount, 4, 1024)), dim3(dev::kBlock), 0, s,
+                       h->trace_counts, (int32_t)0, ncount);
     dev::VecArgs va = vec_args(h, b, x0);
     if (x0) {
         // r0 = b - A x0 with the exact FP64 values.
@@ -641,11 +737,12 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
         va.r_ready = 1;
     }
     hipLaunchKernelGGL(dev::cg_init_kernel, dim3(vec_grid(h)), dim3(dev::kBlock), 0, s, va);
+    hipLaunchKernelGGL(dev::cg_init_finish_kernel, dim3(1), dim3(dev::kBlock), 0, s, va);
     HIP_CHECK(hipGetLastError());
     const bool static_map = h->sched == kSchedStatic;
     if (static_map) {
-        hipLaunchKernelGGL(dev::map_count_kernel, dim3(grid_for(h->T, 4, 1024)), dim3(dev::kBlock), 0, s,
-                           h->map, h->T, h->trace_counts);
+        hipLaunchKernelGGL(dev::map_count_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, s, h->map, h->T,
+                           h->trace_k, h->trace_counts);
     }
 
     // Iterate in windows; poll the device stop flag of the previous window
@@ -686,8 +783,6 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
     HIP_CHECK(hipMemcpy(&hs, h->st, sizeof(hs), hipMemcpyDeviceToHost));
     if (static_map) {
         // One trace entry: the static map at k = 0.
-        int32_t k0 = 0;
-        HIP_CHECK(hipMemcpy(h->trace_k, &k0, sizeof(k0), hipMemcpyHostToDevice));
         hs.ntrace = 1;
         HIP_CHECK(hipMemcpy(&h->st->ntrace, &hs.ntrace, sizeof(int32_t), hipMemcpyHostToDevice));
     }
@@ -711,8 +806,17 @@ extern "C" int cg_get_map_trace(const cg_handle* h, int32_t cap, int32_t* k_out,
     int64_t n = std::min<int64_t>(hs.ntrace, h->trace_cap);
     int64_t m = std::min<int64_t>(n, cap);
     if (m > 0 && k_out) HIP_CHECK(hipMemcpy(k_out, h->trace_k, sizeof(int32_t) * m, hipMemcpyDeviceToHost));
-    if (m > 0 && counts_out)
-        HIP_CHECK(hipMemcpy(counts_out, h->trace_counts, sizeof(int64_t) * 3 * m, hipMemcpyDeviceToHost));
+    if (m > 0 && counts_out) {
+        std::vector<int32_t> per_block((size_t)m * dev::kTraceBlocks * 3);
+        HIP_CHECK(hipMemcpy(per_block.data(), h->trace_counts, sizeof(int32_t) * per_block.size(),
+                            hipMemcpyDeviceToHost));
+        for (int64_t i = 0; i < m; ++i)
+            for (int p = 0; p < 3; ++p) {
+                int64_t sum = 0;
+                for (int b = 0; b < dev::kTraceBlocks; ++b) sum += per_block[((size_t)i * dev::kTraceBlocks + b) * 3 + p];
+                counts_out[3 * i + p] = sum;
+            }
+    }
     return hs.ntrace;
 }
 
