@@ -229,15 +229,31 @@ def random_spd_powerlaw(n: int = 4_000_000, seed: int = 1, band: int = 4,
     absrow = np.bincount(lo, weights=np.abs(vals), minlength=n) + \
         np.bincount(hi, weights=np.abs(vals), minlength=n)
     diag = diag_factor * absrow
-    r = np.concatenate([lo, hi, base])
-    c = np.concatenate([hi, lo, base])
-    v = np.concatenate([vals, vals, diag])
-    del lo, hi, vals
-    order = np.lexsort((c, r))
-    r = r[order]
-    c = c[order].astype(np.int32)
-    v = v[order]
-    del order
+    # CSR assembly by counting: row i holds its lower-triangle partners (pairs
+    # with hi = i), then the diagonal, then its upper partners (lo = i). The
+    # keys are sorted by (lo, hi), so the upper partners of a row are already
+    # consecutive and ascending; a stable sort by hi does the same for the lower.
+    m = lo.size
+    n_up = np.bincount(lo, minlength=n)
+    n_lo = np.bincount(hi, minlength=n)
     indptr = np.zeros(n + 1, dtype=np.int64)
-    np.cumsum(np.bincount(r, minlength=n), out=indptr[1:])
-    return CSR(n, indptr, c, v)
+    np.cumsum(n_lo + 1 + n_up, out=indptr[1:])
+    nnz = int(indptr[-1])
+    indices = np.empty(nnz, dtype=np.int32)
+    data = np.empty(nnz, dtype=np.float64)
+    seq = np.arange(m, dtype=np.int64)
+    up_first = np.cumsum(n_up) - n_up
+    pos = indptr[lo] + n_lo[lo] + 1 + (seq - up_first[lo])
+    indices[pos] = hi
+    data[pos] = vals
+    order = np.argsort(hi, kind="stable")
+    hi_s = hi[order]
+    lo_first = np.cumsum(n_lo) - n_lo
+    pos = indptr[hi_s] + (seq - lo_first[hi_s])
+    indices[pos] = lo[order]
+    data[pos] = vals[order]
+    del order, hi_s, pos, seq
+    dpos = indptr[:-1] + n_lo
+    indices[dpos] = base
+    data[dpos] = diag
+    return CSR(n, indptr, indices, data)

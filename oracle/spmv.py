@@ -63,3 +63,21 @@ def abs_bound(indptr, indices, data, x) -> np.ndarray:
     """(|A| |x|)_i, the scale of the accuracy bound |y - y_ref|_i <= tol * (|A||x|)_i."""
     A = sp.csr_matrix((np.abs(np.asarray(data)), np.asarray(indices), np.asarray(indptr)))
     return A @ np.abs(np.asarray(x, dtype=np.float64))
+
+
+def spmv_rows(indptr, indices, data, rows, prec_of_entry, x) -> np.ndarray:
+    """y_i for the listed rows only, one plain loop per row.
+
+    ``prec_of_entry(i, cols)`` returns the precision code of row i's entries.
+    Used to check full-size products on sampled rows.
+    """
+    out = np.empty(len(rows), dtype=np.float64)
+    for m, i in enumerate(rows):
+        s, e = int(indptr[i]), int(indptr[i + 1])
+        cols = np.asarray(indices[s:e], dtype=np.int64)
+        vals = stream_values(np.asarray(data[s:e], dtype=np.float64), prec_of_entry(int(i), cols))
+        acc = 0.0
+        for v, c in zip(vals, cols):
+            acc += float(v) * float(x[c])
+        out[m] = acc
+    return out

@@ -140,3 +140,30 @@ def padded_columns(L: TileCSC, t: int):
         rows.append(col)
         ptr.append(ptr[-1] + len(col))
     return ptr, rows
+
+
+def tile_numbering(n: int, indptr, indices, R: int, C: int):
+    """Canonical tile numbers without building the whole layout.
+
+    Returns ``(keys, tile_row_ptr)``: the sorted distinct tile keys
+    I * ncb + J (their position is the canonical tile number) and the tile
+    row pointers. :func:`tile_of` maps entries to tile numbers with it.
+    """
+    indptr = np.asarray(indptr, dtype=np.int64)
+    ncb = -(-n // C)
+    rows = np.repeat(np.arange(n, dtype=np.int64), np.diff(indptr))
+    keys = np.unique((rows // R) * ncb + np.asarray(indices, dtype=np.int64) // C)
+    nrb = -(-n // R)
+    tile_row_ptr = np.zeros(nrb + 1, dtype=np.int64)
+    np.cumsum(np.bincount(keys // ncb, minlength=nrb), out=tile_row_ptr[1:])
+    return keys, tile_row_ptr
+
+
+def tile_of(keys, n: int, R: int, C: int, rows, cols):
+    """Canonical tile number of entries (rows[i], cols[i]) given :func:`tile_numbering` keys."""
+    ncb = -(-n // C)
+    k = (np.asarray(rows, dtype=np.int64) // R) * ncb + np.asarray(cols, dtype=np.int64) // C
+    t = np.searchsorted(keys, k)
+    if np.any(t >= keys.size) or np.any(keys[np.minimum(t, keys.size - 1)] != k):
+        raise ValueError("entry outside every non-empty tile")
+    return t

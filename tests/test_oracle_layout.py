@@ -159,3 +159,17 @@ def test_fig4b_intra_tile_csc_padded_view():
     for c, expect in g["padded_rowIdx"].items():
         exp = [R - 1 if v == "R-1" else (R if v == "R" else v) for v in expect]
         assert ridx[int(c)] == exp
+
+
+@pytest.mark.parametrize("n,density,seed,R,C,empty", CASES)
+def test_tile_numbering_matches_layout(n, density, seed, R, C, empty):
+    M = random_csr(n, density, seed, empty)
+    L = tc.build(n, M.indptr, M.indices, M.data, R, C)
+    keys, trp = tc.tile_numbering(n, M.indptr, M.indices, R, C)
+    assert np.array_equal(trp, L.tile_row_ptr)
+    coo = M.tocoo()
+    t = tc.tile_of(keys, n, R, C, coo.row, coo.col)
+    # Canonical tile of each CSR entry from the full layout.
+    t_full = np.empty(M.nnz, dtype=np.int64)
+    t_full[L.perm] = L.tile_of_nnz()
+    assert np.array_equal(t, t_full)

@@ -148,3 +148,18 @@ def test_bf16_stream_used_for_bf16_tiles():
         float(np.float32(a)) * 3.0
     assert spmv.spmv(L, M.indptr, M.indices, np.array([2], np.uint8), x)[0] == \
         float(to_bf16_value(np.array([a]))[0]) * 3.0
+
+
+def test_spmv_rows_matches_full_product():
+    M = _fp32_exact_matrix(90, 0.1, 12)
+    M.data = M.data * (1.0 + 2.0 ** -30)
+    R = C = 16
+    L = tc.build(90, M.indptr, M.indices, M.data, R, C)
+    prec = np.random.default_rng(13).integers(0, 3, L.T).astype(np.uint8)
+    x = np.random.default_rng(14).uniform(-1, 1, 90)
+    y = spmv.spmv(L, M.indptr, M.indices, prec, x)
+    keys, _ = tc.tile_numbering(90, M.indptr, M.indices, R, C)
+    rows = [0, 5, 17, 44, 89]
+    yr = spmv.spmv_rows(M.indptr, M.indices, M.data, rows,
+                        lambda i, cols: prec[tc.tile_of(keys, 90, R, C, np.full(cols.size, i), cols)], x)
+    assert np.allclose(yr, y[rows], rtol=1e-15, atol=0)
