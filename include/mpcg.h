@@ -121,8 +121,8 @@ typedef struct {
  *   precision_map : host uint8[T] with codes 0/1/2, or NULL for all FP64.
  *   opt           : NULL for defaults.
  *   stream        : stream for the set-up copies and kernels.
- * Errors: CG_EINVAL (map code > 2, bad layout, Jacobi with a zero or
- * missing diagonal entry), CG_ENOMEM, CG_EDEVICE.
+ * Errors: CG_EINVAL (map code > 2, bad layout, n >= 2^28 or T or nnz >= 2^31,
+ * Jacobi with a zero or missing diagonal entry), CG_ENOMEM, CG_EDEVICE.
  */
 int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, const cg_options* opt,
               void* stream, cg_handle** out);
@@ -131,8 +131,11 @@ int cg_destroy(cg_handle* h);
 
 /* Replace the active per-tile map (uint8[T], codes 0..2) without touching the
  * value planes (Sec. 3.3.2: switching reads another stream, nothing is
- * re-uploaded). on_device = 0: host pointer; 1: device pointer. Clears any
- * schedule. Synchronous with respect to the host. */
+ * re-uploaded); only the SpMV's per-map sweep plan (16 bytes per tile and 12
+ * per window of 64 nonzeros) is rebuilt on the device. on_device = 0: host
+ * pointer; 1: device pointer (copied through the host and validated like a
+ * host map). Clears any schedule. Synchronous with respect to the host.
+ * Errors: CG_EINVAL (NULL argument, a code > 2), CG_EDEVICE. */
 int cg_set_precision_map(cg_handle* h, const uint8_t* map, int32_t on_device);
 
 /* Copy the active map to host uint8[T]. Under a uniform residual schedule the

@@ -115,6 +115,12 @@ __device__ inline double wave_sum(double v) {
     return v;
 }
 
+__device__ inline int wave_sum_int(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
 // Block sum in a fixed order; the result is valid in every thread.
 __device__ inline double block_sum(double v, double* s_tmp) {
     v = wave_sum(v);
@@ -158,45 +164,78 @@ __device__ inline void wave_lds_sync() {
 // ---------------------------------------------------------------------------
 // Mixed-precision Tile-CSC SpMV.
 //
-// One wavefront owns a row group: G consecutive row blocks (G*R <= 64 rows,
-// or one row block when R > 64). It walks the group's tiles in batches of up
-// to 64: lane j stages tile j's descriptor (column base, precision, row
-// offset inside the group) in LDS; then the 64 lanes sweep the batch's
-// nonzeros in storage order, 64 at a time ("windows"), U windows at once.
-// Every value plane is read with contiguous, coalesced loads and only where
-// the tile's map entry selects it: each lane issues one buffer load per plane
-// and the two planes it does not use get an out-of-range offset, which the
-// hardware answers with zero and no memory access -- no branches, no waits.
-// A lane's tile comes from a per-window record built with the layout (the
-// tile of the window's first nonzero and a bit mask of the tile starts that
-// follow), so the lookup is one prefix popcount. Products of the widened
-// stored value and the FP64 vector entry are accumulated in FP64 into the
-// group's row accumulators in LDS; the group's rows are written once.
+// One wavefront owns a row group: G consecutive row blocks (G*R rows, at most
+// kGroupRows, or one row block when R is larger). It walks the group's tiles
+// in batches of up to 64 and the 64 lanes sweep a batch's nonzeros 64 at a
+// time ("windows"), several windows at once. Products of the widened stored
+// value and the FP64 vector entry are accumulated in FP64 into the group's
+// row accumulators in LDS; the group's rows are written once.
 //
-// A block of 4 wavefronts handles a contiguous range of row groups (the
-// grid is capped, and blocks are spread so that each XCD gets a contiguous
-// part of the matrix); in CG mode each block also writes its part of p.q.
+// The sweep follows a plan built on the device whenever the map changes
+// (spmv_plan_kernel). Inside a batch the tiles are taken grouped by
+// precision (FP64 tiles, then FP32, then BF16, each group in storage order)
+// and every group starts on a window boundary, so each window reads exactly
+// one value plane: its precision is a scalar and the plane is read with one
+// load per lane. The plan has one entry per tile (column base in x, row offset
+// in the group's accumulators, the shift from its position in the sweep to
+// its storage position, and its precision) and one record per window (the
+// entry of the window's first nonzero, a bit mask of the entries that start
+// inside the window -- a lane's entry is then a prefix popcount -- the
+// window's precision, and the batch's window count). The lanes past the end
+// of a precision group land on a sentinel entry whose offsets are past the
+// end of every buffer: the hardware answers those loads with zero and no
+// memory access.
+//
+// A block of kSpmvWaves wavefronts handles a contiguous range of row groups
+// (blocks are spread so that each XCD gets a contiguous part of the matrix);
+// in CG mode each block also writes its part of p.q.
 // ---------------------------------------------------------------------------
 enum SpmvMode { kSpmvPlain = 0, kSpmvCg = 1, kSpmvResidual = 2 };
 #ifndef MPCG_SPMV_UNROLL
 #define MPCG_SPMV_UNROLL 8
 #endif
-constexpr int kUnroll = MPCG_SPMV_UNROLL;
+#ifndef MPCG_SPMV_WAVES
+#define MPCG_SPMV_WAVES 4
+#endif
+#ifndef MPCG_GROUP_ROWS
+#define MPCG_GROUP_ROWS 64
+#endif
+constexpr int kUnroll = MPCG_SPMV_UNROLL;      // windows per full sweep (a power of two)
+constexpr int kSpmvWaves = MPCG_SPMV_WAVES;    // wavefronts per SpMV block
+constexpr int kSpmvBlock = kSpmvWaves * kWave;
+constexpr int kGroupRows = MPCG_GROUP_ROWS;    // rows per wavefront when R <= kGroupRows
 constexpr uint32_t kBufferConfig = 0x00020000u;  // raw buffer, dword3 for the gfx9 family
-constexpr int kOutOfRange = 0x7fffff00;          // offset past every batch: load returns 0
+constexpr int kDescSlots = kTileBatch + 3;      // batch tiles + a sentinel after each precision group
+constexpr int kSentinelShift = 1 << 27;         // storage shift: past every batch plane
+constexpr int kSentinelColumn = 0x7fffff00;     // x byte offset: past every x
+
+// Window records a batch executes: whole sweeps of kUnroll windows, then one
+// sweep of the smallest power of two that covers the rest.
+__host__ __device__ inline int sweep_windows(int nw) {
+    const int full = nw / kUnroll * kUnroll;
+    int r = nw - full, t = r > 0 ? 1 : 0;
+    while (t < r) t <<= 1;
+    return full + t;
+}
+// Records reserved for a batch of len nonzeros: at most two windows are added
+// by starting the FP32 and BF16 groups on window boundaries.
+__host__ __device__ inline int batch_records(int len) { return sweep_windows((len + kWave - 1) / kWave + 2); }
+
+// Window record bit fields (int32): entry of the first nonzero, precision, and
+// the batch's window count (the same in every record of the batch).
+constexpr int kRecSlotBits = 8, kRecPrecShift = 8, kRecCountShift = 10;
 
 struct SpmvArgs {
     const int32_t* trp;   // tile_row_ptr [nrb+1]
-    const int32_t* tcol;  // tile_col_idx [T]
     const int32_t* tptr;  // tile_nnz_ptr [T+1]
-    const uint8_t* map;   // [T]
+    const int4* plan;     // [T] per tile, in plan order
     const void* meta;     // per nonzero (row, col) packed: u8 (R, C <= 16) or u16
     const double* v64;
     const float* v32;
     const uint16_t* v16;
     const int32_t* win_base;   // [ngroups+1] first window record of every row group
-    const uint64_t* win_mask;  // per window: bit q = nonzero q+1 of the window starts a tile
-    const int32_t* win_tile;   // per window: batch-relative tile of the window's first nonzero
+    const uint64_t* win_mask;  // per window: bit q = nonzero q+1 of the window starts a new entry
+    const int32_t* win_tile;   // per window: packed record (see kRec*)
     const double* x;
     double* y;
     const double* b;       // residual mode: y = b - A x
@@ -226,22 +265,91 @@ __device__ inline __amdgpu_buffer_rsrc_t batch_rsrc(const void* base, int64_t fi
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Wave-uniform reads of data no kernel here writes (window records, tile
-// ranges): read through the constant address space so they become scalar loads.
+// Wave-uniform reads of data no kernel here writes while the SpMV runs
+// (window records, tile ranges): read through the constant address space so
+// they become scalar loads.
 template <typename T>
 __device__ inline T uniform_load(const T* p, int i) {
     return ((const __attribute__((address_space(4))) T*)(uintptr_t)p)[i];
 }
 
+struct SweepCtx {
+    __amdgpu_buffer_rsrc_t r64, r32, r16, rmt, rx;
+    const uint64_t* win_mask;
+    const int32_t* win_tile;
+    const int4* desc;  // this wave's plan entries in LDS
+    char* acc;         // this wave's row accumulators in LDS
+    int uprec, len, lane;
+};
+
+// U consecutive windows of one batch, starting at record wi and sweep
+// position o0. Loads are issued for all U windows before any is consumed.
+template <typename MetaT, int U>
+__device__ __forceinline__ void spmv_sweep(const SweepCtx& c, int wi, int o0) {
+    uint64_t mask[U];
+    int wp[U], q[U];
+    int4 d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        mask[u] = uniform_load(c.win_mask, wi + u);
+        const int rec = uniform_load(c.win_tile, wi + u);
+        wp[u] = c.uprec >= 0 ? c.uprec : (rec >> kRecPrecShift) & 3;
+        const int j = (rec & ((1 << kRecSlotBits) - 1)) +
+                      (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask[u] >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask[u], 0u));
+        d[u] = c.desc[j];
+        q[u] = o0 + u * kWave + c.lane + d[u].z;  // storage position in the batch
+    }
+    uint32_t mt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        mt[u] = sizeof(MetaT) == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(c.rmt, q[u], 0, 0)
+                                   : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(c.rmt, 2 * q[u], 0, 0);
+    // Stored values, issued before the vector gathers (which wait for the
+    // packed indices); the raw bits are widened after every load is issued.
+    u32x2 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (wp[u] == 0)
+            raw[u] = __builtin_amdgcn_raw_buffer_load_b64(c.r64, 8 * q[u], 0, 0);
+        else if (wp[u] == 1)
+            raw[u].x = __builtin_amdgcn_raw_buffer_load_b32(c.r32, 4 * q[u], 0, 0);
+        else
+            raw[u].x = __builtin_amdgcn_raw_buffer_load_b16(c.r16, 2 * q[u], 0, 0);
+    }
+    double xv[U];
+    int racc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int r, col;
+        decode_meta<MetaT>(mt[u], r, col);
+        racc[u] = d[u].y + 8 * r;
+        const u32x2 xb = __builtin_amdgcn_raw_buffer_load_b64(c.rx, d[u].x + 8 * col, 0, 0);
+        xv[u] = __longlong_as_double(((long long)xb.y << 32) | xb.x);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        double v;
+        if (wp[u] == 0)
+            v = __longlong_as_double(((long long)raw[u].y << 32) | raw[u].x);
+        else if (wp[u] == 1)
+            v = (double)__uint_as_float(raw[u].x);
+        else
+            v = (double)__uint_as_float(raw[u].x << 16);
+        // Sentinel lanes have storage positions past the batch: nothing to add.
+        if (q[u] < c.len) atomicAdd(reinterpret_cast<double*>(c.acc + racc[u]), v * xv[u]);
+    }
+}
+
 // The outputs are separate restrict arguments: the compiler may then treat
-// every other array as read-only for the whole launch and fetch the
-// wave-uniform ones (window records, tile ranges) through the scalar cache.
+// every other array as read-only for the whole launch.
 template <typename MetaT, int MODE, int MAXROWS>
-__global__ __launch_bounds__(kBlock) void spmv_tilecsc_kernel(SpmvArgs a, double* __restrict__ y,
-                                                              double* __restrict__ partials) {
-    __shared__ double s_acc[kWavesPerBlock][MAXROWS];
-    __shared__ int2 s_desc[kWavesPerBlock][kTileBatch];
-    __shared__ double s_tmp[kWavesPerBlock];
+__global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, double* __restrict__ y,
+                                                                  double* __restrict__ partials) {
+    // One spare accumulator per wave: the sentinel entry's row (never added to).
+    __shared__ double s_acc[kSpmvWaves][MAXROWS + 1];
+    __shared__ int4 s_desc[kSpmvWaves][kDescSlots];
+    __shared__ double s_tmp[kSpmvWaves];
 
     if (MODE == kSpmvCg && load_done(a.st)) return;
 
@@ -252,116 +360,61 @@ __global__ __launch_bounds__(kBlock) void spmv_tilecsc_kernel(SpmvArgs a, double
     const int blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
     const int g_begin = blk * a.groups_per_block;
     const int g_end = min(g_begin + a.groups_per_block, a.ngroups);
-    const int uprec = *a.uprec;
+    SweepCtx c;
+    c.uprec = *a.uprec;
+    c.lane = lane;
+    c.win_mask = a.win_mask;
+    c.win_tile = a.win_tile;
+    c.desc = &s_desc[w][0];
+    c.acc = reinterpret_cast<char*>(&s_acc[w][0]);
+    // x through a buffer resource with 32-bit byte offsets (n < 2^28 is
+    // checked when the handle is created).
+    c.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<double*>(a.x), (short)0, a.n * 8, (int)kBufferConfig);
     double dot = 0.0;
 
-    for (int g = g_begin + w; g < g_end; g += kWavesPerBlock) {
+    for (int g = g_begin + w; g < g_end; g += kSpmvWaves) {
         const int rb0 = g * a.G;
         const int nrbg = min(rb0 + a.G, a.nrb) - rb0;
         const int row0 = rb0 * a.R;
         const int nrows = min(a.rows_per_group, a.n - row0);
         for (int i = lane; i < a.rows_per_group; i += kWave) s_acc[w][i] = 0.0;
-        // Row-block boundaries of the group, one per lane (nrbg <= 64).
-        const int my_trp = lane <= nrbg ? a.trp[rb0 + lane] : 0x7fffffff;
+        const int t_begin = uniform_load(a.trp, rb0);
+        const int t_end = uniform_load(a.trp, rb0 + nrbg);
         double p_own = 0.0;
         if (MODE == kSpmvCg && MAXROWS <= kWave && lane < nrows) p_own = a.x[row0 + lane];
-        const int t_begin = __builtin_amdgcn_readlane(my_trp, 0);
-        const int t_end = __builtin_amdgcn_readlane(my_trp, nrbg);
         int win = uniform_load(a.win_base, g);
         for (int tb = t_begin; tb < t_end; tb += kTileBatch) {
             const int nt = min(kTileBatch, t_end - tb);
-            int my_start = 0;
+            const int kb = uniform_load(a.tptr, tb);
+            const int len = uniform_load(a.tptr, tb + nt) - kb;
+            // Every entry starts as the sentinel; tile entries then go to their
+            // slot (plan position + precision: one sentinel after each group).
+            const int4 sentinel = make_int4(kSentinelColumn, MAXROWS * 8, kSentinelShift, 0);
+            s_desc[w][lane] = sentinel;
+            if (lane < kDescSlots - kWave) s_desc[w][kWave + lane] = sentinel;
             if (lane < nt) {
-                const int t = tb + lane;
-                my_start = a.tptr[t];
-                int rbi = 0;
-                for (int i = 1; i < nrbg; ++i) rbi += (__builtin_amdgcn_readlane(my_trp, i) <= t) ? 1 : 0;
-                const int prec = uprec >= 0 ? uprec : (int)a.map[t];
-                s_desc[w][lane] = make_int2(a.tcol[t] * a.C, prec | ((rbi * a.R) << 2));
+                const int4 e = a.plan[tb + lane];
+                s_desc[w][lane + e.w] = e;
             }
-            const int kb = __builtin_amdgcn_readlane(my_start, 0);
-            const int len = a.tptr[tb + nt] - kb;
-            const __amdgpu_buffer_rsrc_t r64 = batch_rsrc(a.v64, kb, 8, len);
-            const __amdgpu_buffer_rsrc_t r32 = batch_rsrc(a.v32, kb, 4, len);
-            const __amdgpu_buffer_rsrc_t r16 = batch_rsrc(a.v16, kb, 2, len);
-            const __amdgpu_buffer_rsrc_t rmt = batch_rsrc(a.meta, kb, (int)sizeof(MetaT), len);
+            c.r64 = batch_rsrc(a.v64, kb, 8, len);
+            c.r32 = batch_rsrc(a.v32, kb, 4, len);
+            c.r16 = batch_rsrc(a.v16, kb, 2, len);
+            c.rmt = batch_rsrc(a.meta, kb, (int)sizeof(MetaT), len);
+            c.len = len;
+            const int w0 = win;
+            win += batch_records(len);
+            int left = sweep_windows(uniform_load(a.win_tile, w0) >> kRecCountShift);
             wave_lds_sync();
-            const int win0 = win;
-            win += (len + kWave - 1) / kWave;  // windows of this batch
-            for (int o0 = 0; o0 < len; o0 += kWave * kUnroll) {
-                int off[kUnroll];
-                int2 d[kUnroll];
-                uint32_t mt[kUnroll];
-                u32x2 b64[kUnroll];
-                uint32_t b32[kUnroll], b16[kUnroll];
-                uint64_t mask[kUnroll];
-                int j0[kUnroll];
-                // Window records first (scalar loads), then the descriptor reads, then
-                // every vector load of the U windows, so their latencies overlap.
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const bool live = o0 + u * kWave < len;  // wave-uniform: the window exists
-                    const int wi = win0 + o0 / kWave + u;
-                    mask[u] = live ? uniform_load(a.win_mask, wi) : 0ull;
-                    j0[u] = live ? uniform_load(a.win_tile, wi) : 0;
-                }
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    off[u] = o0 + u * kWave + lane;
-                    int j = j0[u] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask[u] >> 32),
-                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mask[u], 0u));
-                    d[u] = s_desc[w][min(j, nt - 1)];
-                }
-                // Local (row, column) of every nonzero first, then the vector gathers they
-                // need; the value loads follow and stay in flight alongside the gathers.
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const bool in = off[u] < len;
-                    mt[u] = sizeof(MetaT) == 1
-                                ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rmt, in ? off[u] : kOutOfRange, 0, 0)
-                                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rmt, in ? 2 * off[u] : kOutOfRange, 0, 0);
-                }
-                double xv[kUnroll];
-                int row[kUnroll];
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    int r, c;
-                    decode_meta<MetaT>(mt[u], r, c);
-                    row[u] = (d[u].y >> 2) + r;
-                    xv[u] = a.x[d[u].x + c];
-                }
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int prec = d[u].y & 3;
-                    const bool in = off[u] < len;
-                    // A plane no lane of the window uses is not touched at all (wave-uniform
-                    // branch): the address unit then spends no cycles on it.
-                    b64[u] = u32x2{0u, 0u};
-                    b32[u] = 0u;
-                    b16[u] = 0u;
-                    asm volatile("" : "+v"(b64[u]), "+v"(b32[u]), "+v"(b16[u]));
-                    const int o64 = (in && prec == 0) ? 8 * off[u] : kOutOfRange;
-                    const int o32 = (in && prec == 1) ? 4 * off[u] : kOutOfRange;
-                    const int o16 = (in && prec == 2) ? 2 * off[u] : kOutOfRange;
-                    if (__builtin_amdgcn_ballot_w64(o64 != kOutOfRange))
-                        b64[u] = __builtin_amdgcn_raw_buffer_load_b64(r64, o64, 0, 0);
-                    if (__builtin_amdgcn_ballot_w64(o32 != kOutOfRange))
-                        b32[u] = __builtin_amdgcn_raw_buffer_load_b32(r32, o32, 0, 0);
-                    if (__builtin_amdgcn_ballot_w64(o16 != kOutOfRange))
-                        b16[u] = __builtin_amdgcn_raw_buffer_load_b16(r16, o16, 0, 0);
-                }
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    if (off[u] < len) {
-                        const double v64 = __longlong_as_double(((long long)b64[u].y << 32) | b64[u].x);
-                        const double vlo = (double)__uint_as_float(b32[u] | (b16[u] << 16));
-                        const double v = (d[u].y & 3) == 0 ? v64 : vlo;
-                        atomicAdd(&s_acc[w][row[u]], v * xv[u]);
-                    }
-                }
-            }
+            int wi = w0, o0 = 0;
+            for (; left >= kUnroll; left -= kUnroll, wi += kUnroll, o0 += kUnroll * kWave)
+                spmv_sweep<MetaT, kUnroll>(c, wi, o0);
+            // The rest is 0 or one power of two below kUnroll.
+            if (kUnroll > 8 && left == 8) spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1)>(c, wi, o0);
+            if (kUnroll > 4 && left == 4) spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1)>(c, wi, o0);
+            if (kUnroll > 2 && left == 2) spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1)>(c, wi, o0);
+            if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1>(c, wi, o0);
+            wave_lds_sync();
         }
-        wave_lds_sync();
         for (int i = lane; i < nrows; i += kWave) {
             const double acc = s_acc[w][i];
             if (MODE == kSpmvPlain) {
@@ -377,8 +430,134 @@ __global__ __launch_bounds__(kBlock) void spmv_tilecsc_kernel(SpmvArgs a, double
     }
 
     if (MODE == kSpmvCg) {
-        const double part = block_sum(dot, s_tmp);
-        if (threadIdx.x == 0) partials[blockIdx.x] = part;
+        dot = wave_sum(dot);
+        __syncthreads();
+        if (lane == 0) s_tmp[w] = dot;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double t = 0.0;
+            for (int i = 0; i < kSpmvWaves; ++i) t += s_tmp[i];
+            partials[blockIdx.x] = t;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// SpMV plan for the active map (one wavefront per row group, same batches as
+// the SpMV). Lane l holds tile tb+l. A tile's plan position is its rank in
+// (precision, storage order), found with one ballot per precision; prefix
+// sums of the tile lengths in plan order, with each precision group rounded
+// up to whole windows, give every entry's first sweep position. Lane v then
+// writes the records of windows v, v+64, ...; records past the batch's
+// windows (the rest of the last sweep) point at a sentinel.
+// uniform = 1 plans every tile as FP64 (storage order, no gaps): used while a
+// uniform precision overrides the map.
+// ---------------------------------------------------------------------------
+struct PlanArgs {
+    const int32_t* trp;
+    const int32_t* tptr;
+    const int32_t* tcol;
+    const uint8_t* trow;  // [T] row block of every tile inside its row group
+    const uint8_t* map;
+    const int32_t* win_base;
+    int4* plan;
+    uint64_t* win_mask;
+    int32_t* win_tile;
+    const State* st;
+    int32_t solve;    // 1: run only at the start of a tile-rule window of a running solve
+    int32_t uniform;  // 1: ignore the map
+    int32_t nrb, R, C, G, ngroups;
+};
+
+__device__ inline int wave_prefix_incl(int v, int lane) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(v, off, kWave);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kBlock) void spmv_plan_kernel(PlanArgs a) {
+    __shared__ int s_len[kWavesPerBlock][kTileBatch];
+    __shared__ int s_tile[kWavesPerBlock][kTileBatch];
+    __shared__ int s_start[kWavesPerBlock][kTileBatch];
+    if (a.solve) {
+        if (load_done(a.st)) return;
+        if (a.st->k % a.st->period != 0) return;
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    auto rank_in = [&](uint64_t m) {
+        return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    };
+    for (int g = blockIdx.x * kWavesPerBlock + w; g < a.ngroups; g += gridDim.x * kWavesPerBlock) {
+        const int rb0 = g * a.G;
+        const int t_begin = a.trp[rb0];
+        const int t_end = a.trp[min(rb0 + a.G, a.nrb)];
+        int wb = a.win_base[g];
+        for (int tb = t_begin; tb < t_end; tb += kTileBatch) {
+            const int nt = min(kTileBatch, t_end - tb);
+            const int kb = a.tptr[tb];
+            const int len = a.tptr[tb + nt] - kb;
+            const bool valid = lane < nt;
+            // Every map writer stores 0..2; the clamp only keeps the plan a permutation.
+            const int p = !valid ? -1 : a.uniform ? 0 : min((int)a.map[tb + lane], 2);
+            const int tlen = valid ? a.tptr[tb + lane + 1] - a.tptr[tb + lane] : 0;
+            const uint64_t b0 = __ballot(p == 0), b1 = __ballot(p == 1), b2 = __ballot(p == 2);
+            const int n0 = __popcll(b0), n1 = __popcll(b1), n2 = __popcll(b2);
+            // Nonzeros of each precision group and the sweep position where it starts.
+            const int l0 = wave_sum_int(p == 0 ? tlen : 0), l1 = wave_sum_int(p == 1 ? tlen : 0);
+            const int l2 = len - l0 - l1;
+            const int P1 = (l0 + kWave - 1) / kWave * kWave;
+            const int P2 = P1 + (l1 + kWave - 1) / kWave * kWave;
+            const int nw = (P2 + l2 + kWave - 1) / kWave;
+            if (valid) {
+                const int slot = p == 0 ? rank_in(b0) : p == 1 ? n0 + rank_in(b1) : n0 + n1 + rank_in(b2);
+                s_len[w][slot] = tlen;
+                s_tile[w][slot] = lane;
+            }
+            wave_lds_sync();
+            // Entry q (plan order) of precision c = (q >= n0) + (q >= n0 + n1).
+            const int ql = valid ? s_len[w][lane] : 0;
+            const int qc = (lane >= n0) + (lane >= n0 + n1);
+            const int incl = wave_prefix_incl(ql, lane);
+            const int before = qc == 0 ? 0 : qc == 1 ? l0 : l0 + l1;  // nonzeros of earlier groups
+            const int gstart = qc == 0 ? 0 : qc == 1 ? P1 : P2;       // sweep position of the group
+            const int first = gstart + (incl - ql - before);
+            if (valid) {
+                const int t = tb + s_tile[w][lane];
+                a.plan[tb + lane] = make_int4(a.tcol[t] * a.C * 8, (int)a.trow[t] * a.R * 8,
+                                              (a.tptr[t] - kb) - first, qc);
+                s_start[w][lane] = first;
+            }
+            wave_lds_sync();
+            const int E = sweep_windows(nw);
+            for (int v = lane; v < E; v += kWave) {
+                uint64_t m = 0;
+                int rec = nt + 2;  // padding record: the sentinel after the last group, FP64
+                if (v < nw) {
+                    const int w0 = v * kWave;
+                    const int c = w0 >= P2 ? 2 : (w0 >= P1 ? 1 : 0);
+                    const int lo_q = c == 0 ? 0 : c == 1 ? n0 : n0 + n1;  // entries of group c
+                    const int hi_q = lo_q + (c == 0 ? n0 : c == 1 ? n1 : n2) - 1;
+                    const int gend = (c == 0 ? 0 : c == 1 ? P1 : P2) + (c == 0 ? l0 : c == 1 ? l1 : l2);
+                    int lo_s = lo_q, hi_s = hi_q;  // last entry of the group starting at or before w0
+                    while (lo_s < hi_s) {
+                        const int mid = (lo_s + hi_s + 1) >> 1;
+                        if (s_start[w][mid] <= w0) lo_s = mid; else hi_s = mid - 1;
+                    }
+                    for (int jj = lo_s + 1; jj <= hi_q && s_start[w][jj] < w0 + kWave; ++jj)
+                        m |= 1ull << (s_start[w][jj] - w0 - 1);
+                    if (gend < w0 + kWave) m |= 1ull << (gend - w0 - 1);  // the group's sentinel
+                    rec = (lo_s + c) | (c << kRecPrecShift);
+                }
+                a.win_mask[wb + v] = m;
+                a.win_tile[wb + v] = rec | (nw << kRecCountShift);
+            }
+            wb += batch_records(len);
+            wave_lds_sync();
+        }
     }
 }
 

@@ -52,8 +52,10 @@ struct cg_handle {
     uint64_t* win_mask = nullptr;  // [nwin]
     int32_t* win_tile = nullptr;   // [nwin]
     int64_t nwin = 0;
+    int4* plan = nullptr;          // [T] SpMV plan entries of the active map
     int32_t* trp = nullptr;
     int32_t* tcol = nullptr;
+    uint8_t* trow = nullptr;  // [T] row block of every tile inside its row group
     int32_t* tptr = nullptr;
     uint8_t* map = nullptr;
     void* meta = nullptr;
@@ -90,6 +92,7 @@ struct cg_handle {
     // Captured window graph.
     hipGraphExec_t graph = nullptr;
     int graph_window = 0;
+    int graph_period = 0;
     int graph_sched = -1;
 
     DeviceBuffers bufs;
@@ -134,14 +137,17 @@ int grid_for(int64_t work, int per_thread, int cap) {
 }
 
 constexpr int kVecGridCap = 1024;
-constexpr int kSpmvGridCap = 2048;
+#ifndef MPCG_SPMV_GRID_CAP
+#define MPCG_SPMV_GRID_CAP 2048
+#endif
+constexpr int kSpmvGridCap = MPCG_SPMV_GRID_CAP;
 
 int vec_grid(const cg_handle* h) { return h->vec_blocks; }
 int spmv_grid(const cg_handle* h) { return h->spmv_blocks; }
 
 // SpMV blocks take contiguous ranges of row groups; vector kernels use a capped grid.
 void plan_grids(cg_handle* h) {
-    const int64_t want = (h->ngroups + dev::kWavesPerBlock - 1) / dev::kWavesPerBlock;
+    const int64_t want = (h->ngroups + dev::kSpmvWaves - 1) / dev::kSpmvWaves;
     int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(want, kSpmvGridCap));
     h->groups_per_block = (int)((h->ngroups + blocks - 1) / blocks);
     if (h->groups_per_block < 1) h->groups_per_block = 1;
@@ -152,9 +158,8 @@ void plan_grids(cg_handle* h) {
 dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t* uprec) {
     dev::SpmvArgs a{};
     a.trp = h->trp;
-    a.tcol = h->tcol;
     a.tptr = h->tptr;
-    a.map = h->map;
+    a.plan = h->plan;
     a.meta = h->meta;
     a.v64 = h->v64;
     a.v32 = h->v32;
@@ -186,14 +191,53 @@ void launch_spmv(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
     if (h->meta16) {
         if (wide)
             hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, dev::kMaxRows>), dim3(grid),
-                               dim3(dev::kBlock), 0, s, a, a.y, a.partials);
+                               dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
         else
-            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, 64>), dim3(grid), dim3(dev::kBlock),
-                               0, s, a, a.y, a.partials);
+            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, 64>), dim3(grid),
+                               dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
+    } else if (wide) {
+        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, dev::kMaxRows>), dim3(grid),
+                           dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
     } else {
-        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, 64>), dim3(grid), dim3(dev::kBlock), 0, s,
-                           a, a.y, a.partials);
+        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, 64>), dim3(grid), dim3(dev::kSpmvBlock), 0,
+                           s, a, a.y, a.partials);
     }
+}
+
+// Rebuilds the SpMV plan from the map on the device. solve = 1: only at the
+// start of a tile-rule window of a running solve (the kernel checks).
+void launch_plan(cg_handle* h, int solve, hipStream_t s) {
+    // While a uniform precision overrides the map (residual schedule), plan the
+    // tiles in storage order: no window then carries precision-group gaps.
+    dev::PlanArgs a{};
+    a.trp = h->trp;
+    a.tptr = h->tptr;
+    a.tcol = h->tcol;
+    a.trow = h->trow;
+    a.map = h->map;
+    a.win_base = h->win_base;
+    a.plan = h->plan;
+    a.win_mask = h->win_mask;
+    a.win_tile = h->win_tile;
+    a.st = h->st;
+    a.solve = solve;
+    a.uniform = h->sched == kSchedResidual ? 1 : 0;
+    a.nrb = (int32_t)h->nrb;
+    a.R = h->R;
+    a.C = h->C;
+    a.G = h->G;
+    a.ngroups = h->ngroups;
+    const int64_t blocks = (h->ngroups + dev::kWavesPerBlock - 1) / dev::kWavesPerBlock;
+    hipLaunchKernelGGL(dev::spmv_plan_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 8192))),
+                       dim3(dev::kBlock), 0, s, a);
+}
+
+// Plan for a map just written on the handle's stream; synchronous.
+hipError_t replan(cg_handle* h) {
+    launch_plan(h, 0, h->stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return hipStreamSynchronize(h->stream);
 }
 
 dev::VecArgs vec_args(cg_handle* h, const double* b, const double* x0) {
@@ -264,12 +308,22 @@ void drop_graph(cg_handle* h) {
     h->graph_sched = -1;
 }
 
+// Iterations per enqueued window. Under a tile rule it is a multiple of the
+// rule's period, so the map steps fall on the same iterations of every window.
+int solve_window(const cg_handle* h) {
+    if (h->sched != kSchedTileRule) return h->window;
+    return std::max(1, h->window / h->period) * h->period;
+}
+
 // One CG iteration: [map window step] -> SpMV with fused p.q and alpha ->
 // x/r update with fused r.r (r.z), beta, rho and stop flag -> new direction.
-void enqueue_iteration(cg_handle* h, hipStream_t s) {
-    if (h->sched == kSchedTileRule) {
+// i is the iteration's index in its window (the solve's k modulo the window
+// length while the solve runs).
+void enqueue_iteration(cg_handle* h, int i, hipStream_t s) {
+    if (h->sched == kSchedTileRule && i % h->period == 0) {
         dev::MapArgs ma = map_args(h, 0.0, 1);
         hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, s, ma);
+        launch_plan(h, 1, s);
     }
     dev::SpmvArgs sa = spmv_args(h, h->p, h->q, &h->st->uprec);
     launch_spmv<dev::kSpmvCg>(h, sa, s);
@@ -284,11 +338,13 @@ void enqueue_iteration(cg_handle* h, hipStream_t s) {
 }
 
 int ensure_graph(cg_handle* h) {
-    if (h->graph && h->graph_window == h->window && h->graph_sched == h->sched) return CG_OK;
+    const int W = solve_window(h);
+    if (h->graph && h->graph_window == W && h->graph_sched == h->sched && h->graph_period == h->period)
+        return CG_OK;
     drop_graph(h);
     hipGraph_t g = nullptr;
     HIP_CHECK(hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
-    for (int i = 0; i < h->window; ++i) enqueue_iteration(h, h->stream);
+    for (int i = 0; i < W; ++i) enqueue_iteration(h, i, h->stream);
     hipError_t e = hipStreamEndCapture(h->stream, &g);
     if (e != hipSuccess) {
         if (g) (void)hipGraphDestroy(g);
@@ -300,7 +356,8 @@ int ensure_graph(cg_handle* h) {
         h->graph = nullptr;
         return fail(CG_EDEVICE, std::string("graph instantiation failed: ") + hipGetErrorString(e));
     }
-    h->graph_window = h->window;
+    h->graph_window = W;
+    h->graph_period = h->period;
     h->graph_sched = h->sched;
     return CG_OK;
 }
@@ -322,6 +379,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     const int64_t T = A->T(), nnz = A->nnz(), n = A->n;
     if (n > INT32_MAX || T > INT32_MAX || nnz > INT32_MAX)
         return fail(CG_EINVAL, "cg_create: n, T and nnz must be below 2^31");
+    if (n >= (int64_t(1) << 28))
+        return fail(CG_EINVAL, "cg_create: n must be below 2^28 (x is addressed with 32-bit byte offsets)");
     if (precision_map) {
         for (int64_t t = 0; t < T; ++t)
             if (precision_map[t] > 2)
@@ -348,7 +407,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     h->C = A->C;
     h->nrb = A->nrb;
     h->meta16 = !(A->R <= 16 && A->C <= 16);
-    h->G = std::max(1, std::min(dev::kMaxGroupRB, 64 / A->R));
+    h->G = std::max(1, std::min(dev::kMaxGroupRB, dev::kGroupRows / A->R));
     h->rows_per_group = h->G * A->R;
     h->ngroups = (int32_t)((h->nrb + h->G - 1) / h->G);
     if (opt) {
@@ -376,10 +435,10 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         });
     }
     // Window records of the SpMV sweep: row group g's tiles are taken in batches
-    // of kTileBatch; every batch's nonzeros are cut into windows of 64 from the
-    // batch start. A record holds the batch-relative tile of the window's first
-    // nonzero and a mask whose bit q says that nonzero q+1 of the window starts
-    // a tile, so a lane's tile is the first tile plus a prefix popcount.
+    // of kTileBatch and every batch owns batch_windows(len) records (its windows
+    // of 64 nonzeros, padded to whole sweeps). The records themselves depend on
+    // the map and are written on the device by the plan kernel; here only their
+    // offsets are fixed.
     std::vector<int32_t> win_base(h->ngroups + 1, 0);
     {
         std::vector<int64_t> cnt(h->ngroups, 0);
@@ -390,8 +449,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
                 int64_t c = 0;
                 for (int64_t tb = t0; tb < t1; tb += dev::kTileBatch) {
                     const int64_t nt = std::min<int64_t>(dev::kTileBatch, t1 - tb);
-                    const int64_t len = A->tile_nnz_ptr[tb + nt] - A->tile_nnz_ptr[tb];
-                    c += (len + 63) / 64;
+                    c += dev::batch_records((int)(A->tile_nnz_ptr[tb + nt] - A->tile_nnz_ptr[tb]));
                 }
                 cnt[g] = c;
             }
@@ -400,39 +458,15 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         for (int64_t g = 0; g < h->ngroups; ++g) {
             win_base[g] = (int32_t)acc;
             acc += cnt[g];
+            if (acc > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: too many SpMV windows"));
         }
         win_base[h->ngroups] = (int32_t)acc;
         h->nwin = acc;
-        if (acc > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: too many SpMV windows"));
     }
-    std::vector<uint64_t> win_mask(std::max<int64_t>(h->nwin, 1), 0);
-    std::vector<int32_t> win_tile(std::max<int64_t>(h->nwin, 1), 0);
-    mpcg::parallel_for(h->ngroups, [&](int64_t lo, int64_t hi) {
-        for (int64_t g = lo; g < hi; ++g) {
-            const int64_t rb0 = g * h->G, rb1 = std::min<int64_t>(rb0 + h->G, h->nrb);
-            const int64_t t0 = A->tile_row_ptr[rb0], t1 = A->tile_row_ptr[rb1];
-            int64_t wi = win_base[g];
-            for (int64_t tb = t0; tb < t1; tb += dev::kTileBatch) {
-                const int64_t nt = std::min<int64_t>(dev::kTileBatch, t1 - tb);
-                const int64_t kb = A->tile_nnz_ptr[tb], ke = A->tile_nnz_ptr[tb + nt];
-                int64_t j = 0;  // batch-relative tile of the current position
-                for (int64_t k0 = kb; k0 < ke; k0 += 64, ++wi) {
-                    while (j + 1 < nt && A->tile_nnz_ptr[tb + j + 1] <= k0) ++j;
-                    win_tile[wi] = (int32_t)j;
-                    uint64_t m = 0;
-                    int64_t jn = j + 1;  // next tile start to look for
-                    for (int q = 0; q < 63; ++q) {
-                        const int64_t pos = k0 + q + 1;
-                        if (pos >= ke) break;
-                        if (jn < nt && A->tile_nnz_ptr[tb + jn] == pos) {
-                            m |= 1ull << q;
-                            ++jn;
-                        }
-                    }
-                    win_mask[wi] = m;
-                }
-            }
-        }
+    std::vector<uint8_t> trow(std::max<int64_t>(T, 1), 0);
+    mpcg::parallel_for(h->nrb, [&](int64_t lo, int64_t hi) {
+        for (int64_t I = lo; I < hi; ++I)
+            for (int64_t t = A->tile_row_ptr[I]; t < A->tile_row_ptr[I + 1]; ++t) trow[t] = (uint8_t)(I % h->G);
     });
 
     std::vector<double> dinv_h;
@@ -463,8 +497,10 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     } while (0)
     TRY(dalloc(h, &h->trp, h->nrb + 1));
     TRY(dalloc(h, &h->win_base, h->ngroups + 1));
-    TRY(dalloc(h, &h->win_mask, std::max<int64_t>(h->nwin, 1)));
-    TRY(dalloc(h, &h->win_tile, std::max<int64_t>(h->nwin, 1)));
+    TRY(dalloc(h, &h->win_mask, h->nwin));
+    TRY(dalloc(h, &h->win_tile, h->nwin));
+    TRY(dalloc(h, &h->plan, T));
+    TRY(dalloc(h, &h->trow, std::max<int64_t>(T, 1)));
     TRY(dalloc(h, &h->tcol, T));
     TRY(dalloc(h, &h->tptr, T + 1));
     TRY(dalloc(h, &h->map, T));
@@ -511,10 +547,9 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         return dev_err(e, "pinned host memory");
 
     if ((e = hipMemcpyAsync(h->win_base, win_base.data(), sizeof(int32_t) * win_base.size(), hipMemcpyHostToDevice, s)) ||
-        (e = hipMemcpyAsync(h->win_mask, win_mask.data(), sizeof(uint64_t) * win_mask.size(), hipMemcpyHostToDevice, s)) ||
-        (e = hipMemcpyAsync(h->win_tile, win_tile.data(), sizeof(int32_t) * win_tile.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->trp, trp.data(), sizeof(int32_t) * trp.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tcol, A->tile_col_idx.data(), sizeof(int32_t) * T, hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->trow, trow.data(), trow.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tptr, tptr.data(), sizeof(int32_t) * tptr.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->meta, h->meta16 ? (const void*)meta16.data() : (const void*)meta8.data(),
                             (h->meta16 ? 2 : 1) * (size_t)nnz, hipMemcpyHostToDevice, s)) ||
@@ -536,6 +571,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     hs.spmv_uprec = -1;
     hs.trace_cap = (int32_t)h->trace_cap;
     if ((e = hipMemcpyAsync(h->st, &hs, sizeof(hs), hipMemcpyHostToDevice, s))) return dev_err(e, "state");
+    launch_plan(h, 0, s);
+    if ((e = hipGetLastError()) != hipSuccess) return dev_err(e, "plan kernel");
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return dev_err(e, "set-up");
     *out = h;
     return CG_OK;
@@ -571,15 +608,19 @@ extern "C" int64_t cg_device_bytes(const cg_handle* h) { return h ? h->device_by
 extern "C" int cg_set_precision_map(cg_handle* h, const uint8_t* map, int32_t on_device) {
     mpcg::clear_error();
     if (!h || !map) return fail(CG_EINVAL, "cg_set_precision_map: NULL argument");
-    if (!on_device) {
-        for (int64_t t = 0; t < h->T; ++t)
-            if (map[t] > 2)
-                return fail(CG_EINVAL, "cg_set_precision_map: map[" + std::to_string(t) + "] is not 0, 1 or 2");
-        HIP_CHECK(hipMemcpy(h->map, map, h->T, hipMemcpyHostToDevice));
-    } else {
-        HIP_CHECK(hipMemcpy(h->map, map, h->T, hipMemcpyDeviceToDevice));
+    // A device map is staged through the host so that it is validated like a host map.
+    std::vector<uint8_t> staged;
+    if (on_device) {
+        staged.resize(h->T);
+        HIP_CHECK(hipMemcpy(staged.data(), map, h->T, hipMemcpyDeviceToHost));
+        map = staged.data();
     }
+    for (int64_t t = 0; t < h->T; ++t)
+        if (map[t] > 2)
+            return fail(CG_EINVAL, "cg_set_precision_map: map[" + std::to_string(t) + "] is not 0, 1 or 2");
+    HIP_CHECK(hipMemcpy(h->map, map, h->T, hipMemcpyHostToDevice));
     h->sched = kSchedStatic;
+    HIP_CHECK(replan(h));
     return upload_schedule(h);
 }
 
@@ -608,8 +649,8 @@ extern "C" int cg_map_from_magnitude(cg_handle* h, double t_bf16, double t_fp32)
     hipLaunchKernelGGL(dev::magnitude_map_kernel, dim3(g), dim3(dev::kBlock), 0, h->stream, h->tptr, h->v64,
                        (int32_t)h->T, (const unsigned long long*)h->scratch_u64, t_bf16, t_fp32, h->map);
     HIP_CHECK(hipGetLastError());
-    HIP_CHECK(hipStreamSynchronize(h->stream));
     h->sched = kSchedStatic;
+    HIP_CHECK(replan(h));
     return upload_schedule(h);
 }
 
@@ -628,6 +669,7 @@ extern "C" int cg_set_schedule_residual(cg_handle* h, int32_t nstage, const doub
     for (double t : h->thresholds)
         if (!std::isfinite(t)) return fail(CG_EINVAL, "cg_set_schedule_residual: thresholds must be finite");
     h->sched = kSchedResidual;
+    HIP_CHECK(replan(h));
     return upload_schedule(h);
 }
 
@@ -646,6 +688,7 @@ extern "C" int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const dou
     h->hi = hi;
     h->lo = lo;
     h->sched = kSchedTileRule;
+    HIP_CHECK(replan(h));
     return upload_schedule(h);
 }
 
@@ -656,7 +699,7 @@ extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {
     dev::MapArgs ma = map_args(h, rho, 0);
     hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, h->stream, ma);
     HIP_CHECK(hipGetLastError());
-    HIP_CHECK(hipStreamSynchronize(h->stream));
+    HIP_CHECK(replan(h));
     return CG_OK;
 }
 
@@ -664,6 +707,7 @@ extern "C" int cg_clear_schedule(cg_handle* h) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_clear_schedule: h is NULL");
     h->sched = kSchedStatic;
+    HIP_CHECK(replan(h));
     return upload_schedule(h);
 }
 
@@ -754,13 +798,14 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
     }
     int64_t windows = 0;
     int32_t done = 0, kdone = 0;
-    const int64_t max_windows = (int64_t)maxit / h->window + 2;
+    const int W = solve_window(h);
+    const int64_t max_windows = (int64_t)maxit / W + 2;
     while (true) {
         if (windows < max_windows) {
             if (h->use_graph) {
                 HIP_CHECK(hipGraphLaunch(h->graph, s));
             } else {
-                for (int i = 0; i < h->window; ++i) enqueue_iteration(h, s);
+                for (int i = 0; i < W; ++i) enqueue_iteration(h, i, s);
                 HIP_CHECK(hipGetLastError());
             }
             const int slot = (int)(windows & 1);
