@@ -96,26 +96,10 @@ __host__ __device__ inline uint32_t round_f64_to_e8(uint64_t u) {
     return sign | (uint32_t)bits;
 }
 
-__global__ void build_planes_kernel(const double* __restrict__ v64, float* __restrict__ v32,
-                                    uint16_t* __restrict__ v16, int64_t nnz) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nnz;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        uint64_t u = (uint64_t)__double_as_longlong(v64[i]);
-        v32[i] = __uint_as_float(round_f64_to_e8<23>(u));
-        v16[i] = (uint16_t)round_f64_to_e8<7>(u);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Reduction helpers.
 // ---------------------------------------------------------------------------
 __device__ inline double wave_sum(double v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-}
-
-__device__ inline int wave_sum_int(int v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
     return v;
@@ -164,49 +148,50 @@ __device__ inline void wave_lds_sync() {
 // ---------------------------------------------------------------------------
 // Mixed-precision Tile-CSC SpMV.
 //
-// One wavefront owns a row group: G consecutive row blocks (G*R rows, at most
-// kGroupRows, or one row block when R is larger). It walks the group's tiles
-// in batches of up to 64 and the 64 lanes sweep a batch's nonzeros 64 at a
-// time ("windows"), several windows at once. Products of the widened stored
-// value and the FP64 vector entry are accumulated in FP64 into the group's
-// row accumulators in LDS; the group's rows are written once.
+// One wavefront owns a run of row groups; a row group is G consecutive row
+// blocks (G*R rows: the largest of 32, 64, 128 or 256 rows whose groups hold
+// one batch of tiles on average, and at least one row block).
+// Its tiles are taken in batches of up to 64 in storage order, and the 64
+// lanes sweep a batch's nonzeros 64 at a time ("windows"), several windows
+// at once. Products of the widened stored value and the FP64 vector entry are
+// accumulated in FP64 into the group's row accumulators in LDS; the group's
+// rows are written once.
 //
-// The sweep follows a plan built on the device whenever the map changes
-// (spmv_plan_kernel). Inside a batch the tiles are taken grouped by
-// precision (FP64 tiles, then FP32, then BF16, each group in storage order)
-// and every group starts on a window boundary, so each window reads exactly
-// one value plane: its precision is a scalar and the plane is read with one
-// load per lane. The plan has one entry per tile (column base in x, row offset
-// in the group's accumulators, the shift from its position in the sweep to
-// its storage position, and its precision) and one record per window (the
-// entry of the window's first nonzero, a bit mask of the entries that start
-// inside the window -- a lane's entry is then a prefix popcount -- the
-// window's precision, and the batch's window count). The lanes past the end
-// of a precision group land on a sentinel entry whose offsets are past the
-// end of every buffer: the hardware answers those loads with zero and no
-// memory access.
+// Lane t of a batch stages tile t's entry in LDS: column base in x, row
+// offset in the group's accumulators, and where its precision's values start
+// in the batch's value segment together with their width, both taken from
+// the active map when the batch is staged. A lane finds its tile from a
+// record per window built with the layout (the tile of the window's first
+// nonzero and a bit mask of the tiles that start inside the window, so the
+// lookup is a prefix popcount). Each lane then reads its value with one
+// 8-byte load from its tile's plane: no branch, and a map change costs
+// nothing but the map itself. Lanes past a batch's end land on a sentinel
+// entry whose offsets are past the end of every buffer; the hardware answers
+// those loads with zero and no memory access.
 //
-// A block of kSpmvWaves wavefronts handles a contiguous range of row groups
-// (blocks are spread so that each XCD gets a contiguous part of the matrix);
-// in CG mode each block also writes its part of p.q.
+// A wavefront loads the next batch's header, tile entries and window records
+// while it sweeps the current one. A block of kSpmvWaves wavefronts handles a
+// contiguous range of row groups (blocks are spread so that each XCD gets a
+// contiguous part of the matrix); in CG mode each block also writes its part
+// of p.q.
 // ---------------------------------------------------------------------------
 enum SpmvMode { kSpmvPlain = 0, kSpmvCg = 1, kSpmvResidual = 2 };
 #ifndef MPCG_SPMV_UNROLL
-#define MPCG_SPMV_UNROLL 8
+#define MPCG_SPMV_UNROLL 4
 #endif
 #ifndef MPCG_SPMV_WAVES
 #define MPCG_SPMV_WAVES 4
 #endif
 #ifndef MPCG_GROUP_ROWS
-#define MPCG_GROUP_ROWS 64
+#define MPCG_GROUP_ROWS 0  // 0: chosen per matrix
 #endif
 constexpr int kUnroll = MPCG_SPMV_UNROLL;      // windows per full sweep (a power of two)
 constexpr int kSpmvWaves = MPCG_SPMV_WAVES;    // wavefronts per SpMV block
 constexpr int kSpmvBlock = kSpmvWaves * kWave;
-constexpr int kGroupRows = MPCG_GROUP_ROWS;    // rows per wavefront when R <= kGroupRows
+constexpr int kGroupRows = MPCG_GROUP_ROWS;    // fixed rows per wavefront, or 0
 constexpr uint32_t kBufferConfig = 0x00020000u;  // raw buffer, dword3 for the gfx9 family
-constexpr int kDescSlots = kTileBatch + 3;      // batch tiles + a sentinel after each precision group
-constexpr int kSentinelShift = 1 << 27;         // storage shift: past every batch plane
+constexpr int kDescSlots = kTileBatch + 1;      // batch tiles + the sentinel
+constexpr int kSentinelPlane = 1 << 28;         // plane start: past every value segment
 constexpr int kSentinelColumn = 0x7fffff00;     // x byte offset: past every x
 
 // Window records a batch executes: whole sweeps of kUnroll windows, then one
@@ -217,32 +202,61 @@ __host__ __device__ inline int sweep_windows(int nw) {
     while (t < r) t <<= 1;
     return full + t;
 }
-// Records reserved for a batch of len nonzeros: at most two windows are added
-// by starting the FP32 and BF16 groups on window boundaries.
-__host__ __device__ inline int batch_records(int len) { return sweep_windows((len + kWave - 1) / kWave + 2); }
+// Window records of a batch of len nonzeros.
+__host__ __device__ inline int batch_records(int len) { return sweep_windows((len + kWave - 1) / kWave); }
 
-// Window record bit fields (int32): entry of the first nonzero, precision, and
-// the batch's window count (the same in every record of the batch).
-constexpr int kRecSlotBits = 8, kRecPrecShift = 8, kRecCountShift = 10;
+// Batch table entry (8 int32, one scalar load): the wave's work is a run of
+// consecutive batches covering whole row groups. A row group without tiles
+// has one entry with no tiles, so its rows are still written.
+enum BatchField { kBtTile = 0, kBtTiles, kBtFirstNnz, kBtLen, kBtRecords, kBtGroup, kBtFlags, kBtSegment, kBtFields };
+constexpr int kBatchFirstOfGroup = 1, kBatchLastOfGroup = 2;
+
+// Value planes, stored per batch: one 16-byte aligned segment holds the
+// batch's FP64 values (8*len bytes), then its FP32 values (4*len), then its
+// BF16 values (2*len), all in storage order, and 16 spare bytes. Plane code p
+// starts at byte p*(10-2p)*len of the segment.
+__host__ __device__ inline int64_t segment_bytes(int64_t len) { return (14 * len + 16 + 15) / 16 * 16; }
+
+// Builds every batch's segment from the FP64 values, rounding to nearest even
+// (one wavefront per batch).
+__global__ __launch_bounds__(kBlock) void build_segments_kernel(const int32_t* __restrict__ btab, int64_t nbatch,
+                                                               const double* __restrict__ v64,
+                                                               char* __restrict__ planes) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    for (int64_t b = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave; b < nbatch; b += waves) {
+        const int32_t* e = btab + b * kBtFields;
+        const int first = e[kBtFirstNnz], len = e[kBtLen];
+        char* seg = planes + (int64_t)e[kBtSegment] * 16;
+        double* s64 = reinterpret_cast<double*>(seg);
+        uint32_t* s32 = reinterpret_cast<uint32_t*>(seg + 8 * (int64_t)len);
+        uint16_t* s16 = reinterpret_cast<uint16_t*>(seg + 12 * (int64_t)len);
+        for (int i = lane; i < len; i += kWave) {
+            const double v = v64[first + i];
+            const uint64_t u = (uint64_t)__double_as_longlong(v);
+            s64[i] = v;
+            s32[i] = round_f64_to_e8<23>(u);
+            s16[i] = (uint16_t)round_f64_to_e8<7>(u);
+        }
+    }
+}
 
 struct SpmvArgs {
-    const int32_t* trp;   // tile_row_ptr [nrb+1]
-    const int32_t* tptr;  // tile_nnz_ptr [T+1]
-    const int4* plan;     // [T] per tile, in plan order
-    const void* meta;     // per nonzero (row, col) packed: u8 (R, C <= 16) or u16
-    const double* v64;
-    const float* v32;
-    const uint16_t* v16;
-    const int32_t* win_base;   // [ngroups+1] first window record of every row group
-    const uint64_t* win_mask;  // per window: bit q = nonzero q+1 of the window starts a new entry
-    const int32_t* win_tile;   // per window: packed record (see kRec*)
+    const int32_t* btab;    // [nbatch][8] batch table
+    const int32_t* gbatch;  // [ngroups+1] first batch of every row group
+    const int2* tent;       // [T] per tile: x byte offset of its column block, accumulator byte offset of its rows
+    const uint8_t* map;     // [T] active precision map
+    const void* meta;       // per nonzero (row, col) packed: u8 (R, C <= 16) or u16
+    const char* planes;     // value segments, one per batch
+    const uint64_t* win_mask;  // per window: bit q = nonzero q+1 of the window starts a tile
+    const int32_t* win_tile;   // per window: batch tile of the window's first nonzero
     const double* x;
     double* y;
     const double* b;       // residual mode: y = b - A x
     const int32_t* uprec;  // -1 per-tile map, else uniform code
     const State* st;
     double* partials;      // CG mode: one p.q partial per block
-    int32_t n, nrb, R, C, G, rows_per_group, ngroups, groups_per_block;
+    int32_t n, rows_per_group, ngroups, groups_per_wave, nwin;
 };
 
 template <typename MetaT>
@@ -265,40 +279,89 @@ __device__ inline __amdgpu_buffer_rsrc_t batch_rsrc(const void* base, int64_t fi
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Wave-uniform reads of data no kernel here writes while the SpMV runs
-// (window records, tile ranges): read through the constant address space so
-// they become scalar loads.
+// Wave-uniform reads of data no kernel here writes while the SpMV runs: read
+// through the constant address space so they become scalar loads.
 template <typename T>
 __device__ inline T uniform_load(const T* p, int i) {
     return ((const __attribute__((address_space(4))) T*)(uintptr_t)p)[i];
 }
 
-struct SweepCtx {
-    __amdgpu_buffer_rsrc_t r64, r32, r16, rmt, rx;
-    const uint64_t* win_mask;
-    const int32_t* win_tile;
-    const int4* desc;  // this wave's plan entries in LDS
-    char* acc;         // this wave's row accumulators in LDS
-    int uprec, len, lane;
+// One batch's header in scalar registers.
+struct BatchHdr {
+    int tile, tiles, first, len, records, group, flags, segment;
+};
+__device__ __forceinline__ BatchHdr load_hdr(const int32_t* btab, int b) {
+    const int32_t* e = btab + (size_t)b * kBtFields;
+    BatchHdr h;
+    h.tile = uniform_load(e, kBtTile);
+    h.tiles = uniform_load(e, kBtTiles);
+    h.first = uniform_load(e, kBtFirstNnz);
+    h.len = uniform_load(e, kBtLen);
+    h.records = uniform_load(e, kBtRecords);
+    h.group = uniform_load(e, kBtGroup);
+    h.flags = uniform_load(e, kBtFlags);
+    h.segment = uniform_load(e, kBtSegment);
+    return h;
+}
+
+// A batch's per-lane data: tile `lane`'s entry and precision code (lane <
+// tiles) and window record `lane` of a chunk of 64 windows.
+struct BatchRegs {
+    int2 entry;
+    int prec;
+    uint32_t mlo, mhi;
+    int rec;
 };
 
-// U consecutive windows of one batch, starting at record wi and sweep
-// position o0. Loads are issued for all U windows before any is consumed.
+struct SweepCtx {
+    __amdgpu_buffer_rsrc_t rv, rmt, rx, rmask, rrec;  // rv: this batch's value segment
+    const int4* desc;  // this wave's plan entries in LDS
+    char* acc;         // this wave's row accumulators in LDS
+    const int2* tent;
+    const uint8_t* map;
+    int len, lane;
+    int spare;  // byte offset of this lane's spare accumulator
+};
+
+// Issues the loads of a batch's tile entries and of its window records
+// [chunk, chunk+64) (out-of-range record reads return zero).
+__device__ __forceinline__ void load_batch_regs(const SweepCtx& c, const BatchHdr& h, int chunk, bool with_entry,
+                                                BatchRegs& r) {
+    if (with_entry) {
+        const int t = h.tile + min(c.lane, max(h.tiles - 1, 0));
+        r.entry = c.tent[t];
+        r.prec = c.map[t];
+    }
+    const int wi = h.records + chunk + c.lane;
+    const u32x2 m = __builtin_amdgcn_raw_buffer_load_b64(c.rmask, 8 * wi, 0, 0);
+    r.mlo = m.x;
+    r.mhi = m.y;
+    r.rec = (int)__builtin_amdgcn_raw_buffer_load_b32(c.rrec, 4 * wi, 0, 0);
+}
+
+// U consecutive windows of one batch, starting at batch window wi (records in
+// lanes of R) and batch position o0. Loads are issued for all U windows
+// before any is consumed. With next = true the next batch's tile entries and
+// first records (header Hn) are loaded into Rn once the value loads are issued.
+//
+// A lane's value is one 8-byte load at its plane's start plus its position
+// times the value width, rounded down to 4 bytes (a BF16 lane then takes the
+// half its position selects); the widening is a bitwise blend. Lanes past the
+// batch add their zero product to a private spare accumulator.
 template <typename MetaT, int U>
-__device__ __forceinline__ void spmv_sweep(const SweepCtx& c, int wi, int o0) {
-    uint64_t mask[U];
-    int wp[U], q[U];
+__device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R, int wi, int o0, bool next,
+                                           const BatchHdr& Hn, BatchRegs& Rn) {
+    int q[U];
     int4 d[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        mask[u] = uniform_load(c.win_mask, wi + u);
-        const int rec = uniform_load(c.win_tile, wi + u);
-        wp[u] = c.uprec >= 0 ? c.uprec : (rec >> kRecPrecShift) & 3;
-        const int j = (rec & ((1 << kRecSlotBits) - 1)) +
-                      (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask[u] >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask[u], 0u));
+        const int l = (wi + u) & (kWave - 1);
+        const uint32_t mlo = __builtin_amdgcn_readlane(R.mlo, l);
+        const uint32_t mhi = __builtin_amdgcn_readlane(R.mhi, l);
+        const int j = __builtin_amdgcn_readlane(R.rec, l) +
+                      (int)__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
         d[u] = c.desc[j];
-        q[u] = o0 + u * kWave + c.lane + d[u].z;  // storage position in the batch
+        q[u] = o0 + u * kWave + c.lane;  // position in the batch
     }
     uint32_t mt[U];
 #pragma unroll
@@ -306,39 +369,36 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, int wi, int o0) {
         mt[u] = sizeof(MetaT) == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(c.rmt, q[u], 0, 0)
                                    : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(c.rmt, 2 * q[u], 0, 0);
     // Stored values, issued before the vector gathers (which wait for the
-    // packed indices); the raw bits are widened after every load is issued.
+    // packed indices).
     u32x2 raw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        if (wp[u] == 0)
-            raw[u] = __builtin_amdgcn_raw_buffer_load_b64(c.r64, 8 * q[u], 0, 0);
-        else if (wp[u] == 1)
-            raw[u].x = __builtin_amdgcn_raw_buffer_load_b32(c.r32, 4 * q[u], 0, 0);
-        else
-            raw[u].x = __builtin_amdgcn_raw_buffer_load_b16(c.r16, 2 * q[u], 0, 0);
-    }
+    for (int u = 0; u < U; ++u)
+        raw[u] = __builtin_amdgcn_raw_buffer_load_b64(c.rv, d[u].z + ((q[u] << d[u].w) & ~3), 0, 0);
+    if (next) load_batch_regs(c, Hn, 0, true, Rn);
     double xv[U];
     int racc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int r, col;
         decode_meta<MetaT>(mt[u], r, col);
-        racc[u] = d[u].y + 8 * r;
+        racc[u] = q[u] < c.len ? d[u].y + 8 * r : c.spare;
         const u32x2 xb = __builtin_amdgcn_raw_buffer_load_b64(c.rx, d[u].x + 8 * col, 0, 0);
         xv[u] = __longlong_as_double(((long long)xb.y << 32) | xb.x);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        double v;
-        if (wp[u] == 0)
-            v = __longlong_as_double(((long long)raw[u].y << 32) | raw[u].x);
-        else if (wp[u] == 1)
-            v = (double)__uint_as_float(raw[u].x);
-        else
-            v = (double)__uint_as_float(raw[u].x << 16);
-        // Sentinel lanes have storage positions past the batch: nothing to add.
-        if (q[u] < c.len) atomicAdd(reinterpret_cast<double*>(c.acc + racc[u]), v * xv[u]);
+        // FP32: the low word. BF16 (width shift 1): the half holding element q
+        // (little endian: the high half for odd q), moved to the high half of an
+        // FP32 word. FP64: width shift 3.
+        const uint32_t h = (raw[u].x >> ((q[u] & 1) << 4)) << 16;
+        const uint32_t f = d[u].w == 1 ? h : raw[u].x;
+        const double v32 = (double)__uint_as_float(f);
+        const double v = d[u].w == 3 ? __longlong_as_double(((long long)raw[u].y << 32) | raw[u].x) : v32;
+        atomicAdd(reinterpret_cast<double*>(c.acc + racc[u]), v * xv[u]);
     }
+    // Every load of the sweep has been consumed; saying so keeps the compiler
+    // from guarding the next sweep's loads against this one's.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
 // The outputs are separate restrict arguments: the compiler may then treat
@@ -346,8 +406,8 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, int wi, int o0) {
 template <typename MetaT, int MODE, int MAXROWS>
 __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, double* __restrict__ y,
                                                                   double* __restrict__ partials) {
-    // One spare accumulator per wave: the sentinel entry's row (never added to).
-    __shared__ double s_acc[kSpmvWaves][MAXROWS + 1];
+    // Row accumulators, then one spare per lane for lanes on a sentinel entry.
+    __shared__ double s_acc[kSpmvWaves][MAXROWS + kWave];
     __shared__ int4 s_desc[kSpmvWaves][kDescSlots];
     __shared__ double s_tmp[kSpmvWaves];
 
@@ -355,78 +415,97 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
 
     const int lane = threadIdx.x & (kWave - 1);
     // The wavefront index is uniform across the wave; saying so keeps every
-    // per-group and per-window quantity in scalar registers and scalar loads.
+    // per-batch and per-window quantity in scalar registers.
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
-    const int g_begin = blk * a.groups_per_block;
-    const int g_end = min(g_begin + a.groups_per_block, a.ngroups);
+    const int gw = xcd_contiguous_block(blockIdx.x, gridDim.x) * kSpmvWaves + w;
+    const int g0 = min(gw * a.groups_per_wave, a.ngroups);
+    const int g1 = min(g0 + a.groups_per_wave, a.ngroups);
     SweepCtx c;
-    c.uprec = *a.uprec;
+    const int uprec = *a.uprec;
     c.lane = lane;
-    c.win_mask = a.win_mask;
-    c.win_tile = a.win_tile;
+    c.tent = a.tent;
+    c.map = a.map;
     c.desc = &s_desc[w][0];
     c.acc = reinterpret_cast<char*>(&s_acc[w][0]);
-    // x through a buffer resource with 32-bit byte offsets (n < 2^28 is
-    // checked when the handle is created).
+    c.spare = (MAXROWS + lane) * 8;
+    // Byte offsets are 32-bit: n < 2^28 and the record count < 2^28 are
+    // checked when the handle is created.
     c.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<double*>(a.x), (short)0, a.n * 8, (int)kBufferConfig);
-    double dot = 0.0;
+    c.rmask = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(a.win_mask), (short)0, a.nwin * 8,
+                                                (int)kBufferConfig);
+    c.rrec = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.win_tile), (short)0, a.nwin * 4,
+                                               (int)kBufferConfig);
+    double dot = 0.0, p_own = 0.0;
 
-    for (int g = g_begin + w; g < g_end; g += kSpmvWaves) {
-        const int rb0 = g * a.G;
-        const int nrbg = min(rb0 + a.G, a.nrb) - rb0;
-        const int row0 = rb0 * a.R;
+    int b = uniform_load(a.gbatch, g0);
+    const int b_end = uniform_load(a.gbatch, g1);
+    BatchHdr H{};
+    BatchRegs R{};
+    if (b < b_end) {
+        H = load_hdr(a.btab, b);
+        load_batch_regs(c, H, 0, true, R);
+    }
+    for (; b < b_end; ++b) {
+        const bool more = b + 1 < b_end;
+        BatchHdr Hn{};
+        if (more) Hn = load_hdr(a.btab, b + 1);
+        const int row0 = H.group * a.rows_per_group;
         const int nrows = min(a.rows_per_group, a.n - row0);
-        for (int i = lane; i < a.rows_per_group; i += kWave) s_acc[w][i] = 0.0;
-        const int t_begin = uniform_load(a.trp, rb0);
-        const int t_end = uniform_load(a.trp, rb0 + nrbg);
-        double p_own = 0.0;
-        if (MODE == kSpmvCg && MAXROWS <= kWave && lane < nrows) p_own = a.x[row0 + lane];
-        int win = uniform_load(a.win_base, g);
-        for (int tb = t_begin; tb < t_end; tb += kTileBatch) {
-            const int nt = min(kTileBatch, t_end - tb);
-            const int kb = uniform_load(a.tptr, tb);
-            const int len = uniform_load(a.tptr, tb + nt) - kb;
-            // Every entry starts as the sentinel; tile entries then go to their
-            // slot (plan position + precision: one sentinel after each group).
-            const int4 sentinel = make_int4(kSentinelColumn, MAXROWS * 8, kSentinelShift, 0);
-            s_desc[w][lane] = sentinel;
-            if (lane < kDescSlots - kWave) s_desc[w][kWave + lane] = sentinel;
-            if (lane < nt) {
-                const int4 e = a.plan[tb + lane];
-                s_desc[w][lane + e.w] = e;
-            }
-            c.r64 = batch_rsrc(a.v64, kb, 8, len);
-            c.r32 = batch_rsrc(a.v32, kb, 4, len);
-            c.r16 = batch_rsrc(a.v16, kb, 2, len);
-            c.rmt = batch_rsrc(a.meta, kb, (int)sizeof(MetaT), len);
-            c.len = len;
-            const int w0 = win;
-            win += batch_records(len);
-            int left = sweep_windows(uniform_load(a.win_tile, w0) >> kRecCountShift);
-            wave_lds_sync();
-            int wi = w0, o0 = 0;
-            for (; left >= kUnroll; left -= kUnroll, wi += kUnroll, o0 += kUnroll * kWave)
-                spmv_sweep<MetaT, kUnroll>(c, wi, o0);
-            // The rest is 0 or one power of two below kUnroll.
-            if (kUnroll > 8 && left == 8) spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1)>(c, wi, o0);
-            if (kUnroll > 4 && left == 4) spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1)>(c, wi, o0);
-            if (kUnroll > 2 && left == 2) spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1)>(c, wi, o0);
-            if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1>(c, wi, o0);
-            wave_lds_sync();
+        if (H.flags & kBatchFirstOfGroup) {
+            for (int i = lane; i < a.rows_per_group; i += kWave) s_acc[w][i] = 0.0;
+            if (MODE == kSpmvCg && MAXROWS <= kWave && lane < nrows) p_own = a.x[row0 + lane];
         }
-        for (int i = lane; i < nrows; i += kWave) {
-            const double acc = s_acc[w][i];
-            if (MODE == kSpmvPlain) {
-                y[row0 + i] = acc;
-            } else if (MODE == kSpmvCg) {
-                y[row0 + i] = acc;
-                dot += (MAXROWS <= kWave ? p_own : a.x[row0 + i]) * acc;
-            } else {
-                y[row0 + i] = a.b[row0 + i] - acc;
-            }
+        // Tile entries (precision from the map, or the uniform override), the
+        // sentinel past the batch's tiles.
+        {
+            const int p = uprec >= 0 ? uprec : R.prec;
+            const bool tile = lane < H.tiles;
+            int4 e;
+            e.x = tile ? R.entry.x : kSentinelColumn;
+            e.y = R.entry.y;
+            e.z = tile ? p * (10 - 2 * p) * H.len : kSentinelPlane;
+            e.w = tile ? 3 - p : 3;
+            s_desc[w][lane] = e;
+            if (lane == 0) s_desc[w][kTileBatch] = make_int4(kSentinelColumn, 0, kSentinelPlane, 3);
         }
+        c.rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.planes + (int64_t)H.segment * 16), (short)0,
+                                                 (int)segment_bytes(H.len), (int)kBufferConfig);
+        c.rmt = batch_rsrc(a.meta, H.first, (int)sizeof(MetaT), H.len);
+        c.len = H.len;
+        const int E = batch_records(H.len);
         wave_lds_sync();
+        // The first sweep of the batch also starts the next batch's loads.
+        BatchRegs Rn{};
+        int left = E, wi = 0, o0 = 0;
+        for (; left >= kUnroll; left -= kUnroll, wi += kUnroll, o0 += kUnroll * kWave) {
+            if (wi > 0 && (wi & (kWave - 1)) == 0) load_batch_regs(c, H, wi, false, R);  // next 64 records
+            spmv_sweep<MetaT, kUnroll>(c, R, wi, o0, more && wi == 0, Hn, Rn);
+        }
+        // The rest is 0 or one power of two below kUnroll (never crossing a record chunk).
+        if (wi > 0 && (wi & (kWave - 1)) == 0 && left > 0) load_batch_regs(c, H, wi, false, R);
+        const bool first = more && wi == 0;
+        if (kUnroll > 8 && left == 8) spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1)>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 4 && left == 4) spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1)>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 2 && left == 2) spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1)>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1>(c, R, wi, o0, first, Hn, Rn);
+        if (more && E == 0) load_batch_regs(c, Hn, 0, true, Rn);  // a batch without windows
+        wave_lds_sync();
+        if (H.flags & kBatchLastOfGroup) {
+            for (int i = lane; i < nrows; i += kWave) {
+                const double acc = s_acc[w][i];
+                if (MODE == kSpmvPlain) {
+                    y[row0 + i] = acc;
+                } else if (MODE == kSpmvCg) {
+                    y[row0 + i] = acc;
+                    dot += (MAXROWS <= kWave ? p_own : a.x[row0 + i]) * acc;
+                } else {
+                    y[row0 + i] = a.b[row0 + i] - acc;
+                }
+            }
+            wave_lds_sync();
+        }
+        H = Hn;
+        R = Rn;
     }
 
     if (MODE == kSpmvCg) {
@@ -438,125 +517,6 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
             double t = 0.0;
             for (int i = 0; i < kSpmvWaves; ++i) t += s_tmp[i];
             partials[blockIdx.x] = t;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// SpMV plan for the active map (one wavefront per row group, same batches as
-// the SpMV). Lane l holds tile tb+l. A tile's plan position is its rank in
-// (precision, storage order), found with one ballot per precision; prefix
-// sums of the tile lengths in plan order, with each precision group rounded
-// up to whole windows, give every entry's first sweep position. Lane v then
-// writes the records of windows v, v+64, ...; records past the batch's
-// windows (the rest of the last sweep) point at a sentinel.
-// uniform = 1 plans every tile as FP64 (storage order, no gaps): used while a
-// uniform precision overrides the map.
-// ---------------------------------------------------------------------------
-struct PlanArgs {
-    const int32_t* trp;
-    const int32_t* tptr;
-    const int32_t* tcol;
-    const uint8_t* trow;  // [T] row block of every tile inside its row group
-    const uint8_t* map;
-    const int32_t* win_base;
-    int4* plan;
-    uint64_t* win_mask;
-    int32_t* win_tile;
-    const State* st;
-    int32_t solve;    // 1: run only at the start of a tile-rule window of a running solve
-    int32_t uniform;  // 1: ignore the map
-    int32_t nrb, R, C, G, ngroups;
-};
-
-__device__ inline int wave_prefix_incl(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int t = __shfl_up(v, off, kWave);
-        if (lane >= off) v += t;
-    }
-    return v;
-}
-
-__global__ __launch_bounds__(kBlock) void spmv_plan_kernel(PlanArgs a) {
-    __shared__ int s_len[kWavesPerBlock][kTileBatch];
-    __shared__ int s_tile[kWavesPerBlock][kTileBatch];
-    __shared__ int s_start[kWavesPerBlock][kTileBatch];
-    if (a.solve) {
-        if (load_done(a.st)) return;
-        if (a.st->k % a.st->period != 0) return;
-    }
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    auto rank_in = [&](uint64_t m) {
-        return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    };
-    for (int g = blockIdx.x * kWavesPerBlock + w; g < a.ngroups; g += gridDim.x * kWavesPerBlock) {
-        const int rb0 = g * a.G;
-        const int t_begin = a.trp[rb0];
-        const int t_end = a.trp[min(rb0 + a.G, a.nrb)];
-        int wb = a.win_base[g];
-        for (int tb = t_begin; tb < t_end; tb += kTileBatch) {
-            const int nt = min(kTileBatch, t_end - tb);
-            const int kb = a.tptr[tb];
-            const int len = a.tptr[tb + nt] - kb;
-            const bool valid = lane < nt;
-            // Every map writer stores 0..2; the clamp only keeps the plan a permutation.
-            const int p = !valid ? -1 : a.uniform ? 0 : min((int)a.map[tb + lane], 2);
-            const int tlen = valid ? a.tptr[tb + lane + 1] - a.tptr[tb + lane] : 0;
-            const uint64_t b0 = __ballot(p == 0), b1 = __ballot(p == 1), b2 = __ballot(p == 2);
-            const int n0 = __popcll(b0), n1 = __popcll(b1), n2 = __popcll(b2);
-            // Nonzeros of each precision group and the sweep position where it starts.
-            const int l0 = wave_sum_int(p == 0 ? tlen : 0), l1 = wave_sum_int(p == 1 ? tlen : 0);
-            const int l2 = len - l0 - l1;
-            const int P1 = (l0 + kWave - 1) / kWave * kWave;
-            const int P2 = P1 + (l1 + kWave - 1) / kWave * kWave;
-            const int nw = (P2 + l2 + kWave - 1) / kWave;
-            if (valid) {
-                const int slot = p == 0 ? rank_in(b0) : p == 1 ? n0 + rank_in(b1) : n0 + n1 + rank_in(b2);
-                s_len[w][slot] = tlen;
-                s_tile[w][slot] = lane;
-            }
-            wave_lds_sync();
-            // Entry q (plan order) of precision c = (q >= n0) + (q >= n0 + n1).
-            const int ql = valid ? s_len[w][lane] : 0;
-            const int qc = (lane >= n0) + (lane >= n0 + n1);
-            const int incl = wave_prefix_incl(ql, lane);
-            const int before = qc == 0 ? 0 : qc == 1 ? l0 : l0 + l1;  // nonzeros of earlier groups
-            const int gstart = qc == 0 ? 0 : qc == 1 ? P1 : P2;       // sweep position of the group
-            const int first = gstart + (incl - ql - before);
-            if (valid) {
-                const int t = tb + s_tile[w][lane];
-                a.plan[tb + lane] = make_int4(a.tcol[t] * a.C * 8, (int)a.trow[t] * a.R * 8,
-                                              (a.tptr[t] - kb) - first, qc);
-                s_start[w][lane] = first;
-            }
-            wave_lds_sync();
-            const int E = sweep_windows(nw);
-            for (int v = lane; v < E; v += kWave) {
-                uint64_t m = 0;
-                int rec = nt + 2;  // padding record: the sentinel after the last group, FP64
-                if (v < nw) {
-                    const int w0 = v * kWave;
-                    const int c = w0 >= P2 ? 2 : (w0 >= P1 ? 1 : 0);
-                    const int lo_q = c == 0 ? 0 : c == 1 ? n0 : n0 + n1;  // entries of group c
-                    const int hi_q = lo_q + (c == 0 ? n0 : c == 1 ? n1 : n2) - 1;
-                    const int gend = (c == 0 ? 0 : c == 1 ? P1 : P2) + (c == 0 ? l0 : c == 1 ? l1 : l2);
-                    int lo_s = lo_q, hi_s = hi_q;  // last entry of the group starting at or before w0
-                    while (lo_s < hi_s) {
-                        const int mid = (lo_s + hi_s + 1) >> 1;
-                        if (s_start[w][mid] <= w0) lo_s = mid; else hi_s = mid - 1;
-                    }
-                    for (int jj = lo_s + 1; jj <= hi_q && s_start[w][jj] < w0 + kWave; ++jj)
-                        m |= 1ull << (s_start[w][jj] - w0 - 1);
-                    if (gend < w0 + kWave) m |= 1ull << (gend - w0 - 1);  // the group's sentinel
-                    rec = (lo_s + c) | (c << kRecPrecShift);
-                }
-                a.win_mask[wb + v] = m;
-                a.win_tile[wb + v] = rec | (nw << kRecCountShift);
-            }
-            wb += batch_records(len);
-            wave_lds_sync();
         }
     }
 }

@@ -48,27 +48,29 @@ struct cg_handle {
     int64_t device_bytes = 0;
 
     // Matrix (device).
-    int32_t* win_base = nullptr;   // [ngroups+1]
     uint64_t* win_mask = nullptr;  // [nwin]
     int32_t* win_tile = nullptr;   // [nwin]
     int64_t nwin = 0;
-    int4* plan = nullptr;          // [T] SpMV plan entries of the active map
+    int2* tent = nullptr;          // [T] SpMV tile entries: x byte offset, accumulator byte offset
+    int32_t* btab = nullptr;       // [nbatch][8] SpMV batch table
+    int32_t* gbatch = nullptr;     // [ngroups+1] first batch of every row group
+    int64_t nbatch = 0;
     int32_t* trp = nullptr;
     int32_t* tcol = nullptr;
-    uint8_t* trow = nullptr;  // [T] row block of every tile inside its row group
     int32_t* tptr = nullptr;
     uint8_t* map = nullptr;
     void* meta = nullptr;
-    double* v64 = nullptr;
-    float* v32 = nullptr;
-    uint16_t* v16 = nullptr;
+    double* v64 = nullptr;         // [nnz] FP64 values in storage order
+    char* planes = nullptr;        // per-batch value segments (FP64, FP32, BF16)
+    int64_t planes_bytes = 0;
+    std::vector<int32_t> btab_host;  // host copy of the batch table
     double* dinv = nullptr;
 
     // CG vectors and reduction scratch (device).
     double *x = nullptr, *r = nullptr, *p = nullptr, *q = nullptr, *z = nullptr;
     double* part_spmv = nullptr;  // one p.q partial per SpMV block
     double* part_vec = nullptr;   // two partials per vector-kernel block
-    int spmv_blocks = 0, groups_per_block = 0, vec_blocks = 0;
+    int spmv_blocks = 0, groups_per_wave = 0, vec_blocks = 0;
     dev::State* st = nullptr;
     double* hist = nullptr;
     int64_t hist_cap = 0;
@@ -138,33 +140,31 @@ int grid_for(int64_t work, int per_thread, int cap) {
 
 constexpr int kVecGridCap = 1024;
 #ifndef MPCG_SPMV_GRID_CAP
-#define MPCG_SPMV_GRID_CAP 2048
+#define MPCG_SPMV_GRID_CAP 4096
 #endif
 constexpr int kSpmvGridCap = MPCG_SPMV_GRID_CAP;
 
 int vec_grid(const cg_handle* h) { return h->vec_blocks; }
 int spmv_grid(const cg_handle* h) { return h->spmv_blocks; }
 
-// SpMV blocks take contiguous ranges of row groups; vector kernels use a capped grid.
+// Every SpMV wavefront takes a contiguous range of row groups (a capped grid:
+// a wavefront pipelines its batches); vector kernels use a capped grid.
 void plan_grids(cg_handle* h) {
-    const int64_t want = (h->ngroups + dev::kSpmvWaves - 1) / dev::kSpmvWaves;
-    int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(want, kSpmvGridCap));
-    h->groups_per_block = (int)((h->ngroups + blocks - 1) / blocks);
-    if (h->groups_per_block < 1) h->groups_per_block = 1;
-    h->spmv_blocks = (int)std::max<int64_t>(1, (h->ngroups + h->groups_per_block - 1) / h->groups_per_block);
+    const int64_t waves = std::max<int64_t>(1, std::min<int64_t>(h->ngroups, (int64_t)kSpmvGridCap * dev::kSpmvWaves));
+    h->groups_per_wave = (int)std::max<int64_t>(1, (h->ngroups + waves - 1) / waves);
+    const int64_t used = (h->ngroups + h->groups_per_wave - 1) / h->groups_per_wave;
+    h->spmv_blocks = (int)std::max<int64_t>(1, (used + dev::kSpmvWaves - 1) / dev::kSpmvWaves);
     h->vec_blocks = grid_for(h->n, 8, kVecGridCap);
 }
 
 dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t* uprec) {
     dev::SpmvArgs a{};
-    a.trp = h->trp;
-    a.tptr = h->tptr;
-    a.plan = h->plan;
+    a.btab = h->btab;
+    a.gbatch = h->gbatch;
+    a.tent = h->tent;
+    a.map = h->map;
     a.meta = h->meta;
-    a.v64 = h->v64;
-    a.v32 = h->v32;
-    a.v16 = h->v16;
-    a.win_base = h->win_base;
+    a.planes = h->planes;
     a.win_mask = h->win_mask;
     a.win_tile = h->win_tile;
     a.x = x;
@@ -174,13 +174,10 @@ dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t*
     a.st = h->st;
     a.partials = h->part_spmv;
     a.n = (int32_t)h->n;
-    a.nrb = (int32_t)h->nrb;
-    a.R = h->R;
-    a.C = h->C;
-    a.G = h->G;
     a.rows_per_group = h->rows_per_group;
     a.ngroups = h->ngroups;
-    a.groups_per_block = h->groups_per_block;
+    a.groups_per_wave = h->groups_per_wave;
+    a.nwin = (int32_t)h->nwin;
     return a;
 }
 
@@ -202,42 +199,6 @@ void launch_spmv(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, 64>), dim3(grid), dim3(dev::kSpmvBlock), 0,
                            s, a, a.y, a.partials);
     }
-}
-
-// Rebuilds the SpMV plan from the map on the device. solve = 1: only at the
-// start of a tile-rule window of a running solve (the kernel checks).
-void launch_plan(cg_handle* h, int solve, hipStream_t s) {
-    // While a uniform precision overrides the map (residual schedule), plan the
-    // tiles in storage order: no window then carries precision-group gaps.
-    dev::PlanArgs a{};
-    a.trp = h->trp;
-    a.tptr = h->tptr;
-    a.tcol = h->tcol;
-    a.trow = h->trow;
-    a.map = h->map;
-    a.win_base = h->win_base;
-    a.plan = h->plan;
-    a.win_mask = h->win_mask;
-    a.win_tile = h->win_tile;
-    a.st = h->st;
-    a.solve = solve;
-    a.uniform = h->sched == kSchedResidual ? 1 : 0;
-    a.nrb = (int32_t)h->nrb;
-    a.R = h->R;
-    a.C = h->C;
-    a.G = h->G;
-    a.ngroups = h->ngroups;
-    const int64_t blocks = (h->ngroups + dev::kWavesPerBlock - 1) / dev::kWavesPerBlock;
-    hipLaunchKernelGGL(dev::spmv_plan_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 8192))),
-                       dim3(dev::kBlock), 0, s, a);
-}
-
-// Plan for a map just written on the handle's stream; synchronous.
-hipError_t replan(cg_handle* h) {
-    launch_plan(h, 0, h->stream);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return hipStreamSynchronize(h->stream);
 }
 
 dev::VecArgs vec_args(cg_handle* h, const double* b, const double* x0) {
@@ -323,7 +284,6 @@ void enqueue_iteration(cg_handle* h, int i, hipStream_t s) {
     if (h->sched == kSchedTileRule && i % h->period == 0) {
         dev::MapArgs ma = map_args(h, 0.0, 1);
         hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, s, ma);
-        launch_plan(h, 1, s);
     }
     dev::SpmvArgs sa = spmv_args(h, h->p, h->q, &h->st->uprec);
     launch_spmv<dev::kSpmvCg>(h, sa, s);
@@ -407,7 +367,19 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     h->C = A->C;
     h->nrb = A->nrb;
     h->meta16 = !(A->R <= 16 && A->C <= 16);
-    h->G = std::max(1, std::min(dev::kMaxGroupRB, dev::kGroupRows / A->R));
+    // Row blocks per wavefront: the largest of 32, 64, 128, 256 rows whose row
+    // groups hold at most one batch of tiles on average (at least one row block).
+    auto group_rb = [&](int rows) { return std::max(1, std::min(dev::kMaxGroupRB, rows / A->R)); };
+    if (dev::kGroupRows > 0) {
+        h->G = group_rb(dev::kGroupRows);
+    } else {
+        h->G = group_rb(32);
+        for (int rows : {64, 128, 256}) {
+            const int G = group_rb(rows);
+            const int64_t groups = (h->nrb + G - 1) / G;
+            if (groups > 0 && T <= (int64_t)dev::kTileBatch * groups) h->G = G;
+        }
+    }
     h->rows_per_group = h->G * A->R;
     h->ngroups = (int32_t)((h->nrb + h->G - 1) / h->G);
     if (opt) {
@@ -435,10 +407,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         });
     }
     // Window records of the SpMV sweep: row group g's tiles are taken in batches
-    // of kTileBatch and every batch owns batch_windows(len) records (its windows
-    // of 64 nonzeros, padded to whole sweeps). The records themselves depend on
-    // the map and are written on the device by the plan kernel; here only their
-    // offsets are fixed.
+    // of kTileBatch and every batch owns batch_records(len) records: its windows
+    // of 64 nonzeros, then padding up to the sweep sizes the kernel runs.
     std::vector<int32_t> win_base(h->ngroups + 1, 0);
     {
         std::vector<int64_t> cnt(h->ngroups, 0);
@@ -463,12 +433,94 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         win_base[h->ngroups] = (int32_t)acc;
         h->nwin = acc;
     }
-    std::vector<uint8_t> trow(std::max<int64_t>(T, 1), 0);
+    if (h->nwin >= (int64_t(1) << 28)) return bail(fail(CG_EINVAL, "cg_create: too many SpMV windows"));
+    // Batch table: every row group's batches in order; a group without tiles
+    // gets one entry without tiles so that its rows are written.
+    std::vector<int32_t> gbatch(h->ngroups + 1, 0);
+    std::vector<int32_t> btab;
+    {
+        int64_t nb = 0;
+        for (int64_t g = 0; g < h->ngroups; ++g) {
+            gbatch[g] = (int32_t)nb;
+            const int64_t rb0 = g * h->G, rb1 = std::min<int64_t>(rb0 + h->G, h->nrb);
+            const int64_t ntile = A->tile_row_ptr[rb1] - A->tile_row_ptr[rb0];
+            nb += std::max<int64_t>(1, (ntile + dev::kTileBatch - 1) / dev::kTileBatch);
+            if (nb > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: too many SpMV batches"));
+        }
+        gbatch[h->ngroups] = (int32_t)nb;
+        h->nbatch = nb;
+        btab.assign((size_t)nb * dev::kBtFields, 0);
+        mpcg::parallel_for(h->ngroups, [&](int64_t lo, int64_t hi) {
+            for (int64_t g = lo; g < hi; ++g) {
+                const int64_t rb0 = g * h->G, rb1 = std::min<int64_t>(rb0 + h->G, h->nrb);
+                const int64_t t0 = A->tile_row_ptr[rb0], t1 = A->tile_row_ptr[rb1];
+                int64_t b = gbatch[g], rec = win_base[g];
+                const int64_t b_last = gbatch[g + 1] - 1;
+                for (int64_t tb = t0; b <= b_last; tb += dev::kTileBatch, ++b) {
+                    int32_t* e = &btab[(size_t)b * dev::kBtFields];
+                    const int64_t nt = std::max<int64_t>(0, std::min<int64_t>(dev::kTileBatch, t1 - tb));
+                    const int64_t len = nt ? A->tile_nnz_ptr[tb + nt] - A->tile_nnz_ptr[tb] : 0;
+                    e[dev::kBtTile] = nt ? (int32_t)tb : 0;
+                    e[dev::kBtTiles] = (int32_t)nt;
+                    e[dev::kBtFirstNnz] = nt ? (int32_t)A->tile_nnz_ptr[tb] : 0;
+                    e[dev::kBtLen] = (int32_t)len;
+                    e[dev::kBtRecords] = (int32_t)rec;
+                    e[dev::kBtGroup] = (int32_t)g;
+                    e[dev::kBtFlags] = (b == gbatch[g] ? dev::kBatchFirstOfGroup : 0) |
+                                       (b == b_last ? dev::kBatchLastOfGroup : 0);
+                    if (nt) rec += dev::batch_records((int)len);
+                }
+            }
+        });
+        // Value segments in batch order (16-byte units).
+        int64_t off = 0;
+        for (int64_t b = 0; b < nb; ++b) {
+            int32_t* e = &btab[(size_t)b * dev::kBtFields];
+            e[dev::kBtSegment] = (int32_t)(off / 16);
+            off += e[dev::kBtLen] ? dev::segment_bytes(e[dev::kBtLen]) : 0;
+            if (off / 16 > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: value planes above 32 GiB"));
+        }
+        h->planes_bytes = std::max<int64_t>(off, 16);
+    }
+    // Tile entries and window records. A record holds the batch tile of the
+    // window's first nonzero and a mask whose bit q says that nonzero q+1 of the
+    // window starts a tile; the batch's end counts as the start of the sentinel
+    // (tile index nt), which is also where padding records point.
+    std::vector<int2> tent(std::max<int64_t>(T, 1), make_int2(0, 0));
+    std::vector<uint64_t> win_mask(std::max<int64_t>(h->nwin, 1), 0);
+    std::vector<int32_t> win_tile(std::max<int64_t>(h->nwin, 1), 0);
     mpcg::parallel_for(h->nrb, [&](int64_t lo, int64_t hi) {
         for (int64_t I = lo; I < hi; ++I)
-            for (int64_t t = A->tile_row_ptr[I]; t < A->tile_row_ptr[I + 1]; ++t) trow[t] = (uint8_t)(I % h->G);
+            for (int64_t t = A->tile_row_ptr[I]; t < A->tile_row_ptr[I + 1]; ++t)
+                tent[t] = make_int2((int)(A->tile_col_idx[t] * A->C * 8), (int)((I % h->G) * A->R * 8));
     });
-
+    mpcg::parallel_for(h->nbatch, [&](int64_t lo, int64_t hi) {
+        for (int64_t b = lo; b < hi; ++b) {
+            const int32_t* e = &btab[(size_t)b * dev::kBtFields];
+            const int64_t tb = e[dev::kBtTile], nt = e[dev::kBtTiles], len = e[dev::kBtLen];
+            if (!nt) continue;
+            const int64_t kb = A->tile_nnz_ptr[tb], nw = (len + 63) / 64, E = dev::batch_records((int)len);
+            int64_t j = 0;
+            for (int64_t v = 0; v < E; ++v) {
+                const int64_t wi = e[dev::kBtRecords] + v;
+                if (v >= nw) {
+                    win_tile[wi] = (int32_t)nt;
+                    continue;
+                }
+                const int64_t w0 = v * 64;
+                while (j + 1 < nt && A->tile_nnz_ptr[tb + j + 1] - kb <= w0) ++j;
+                win_tile[wi] = (int32_t)j;
+                uint64_t m = 0;
+                for (int64_t jn = j + 1; jn <= nt; ++jn) {
+                    const int64_t start = (jn < nt ? A->tile_nnz_ptr[tb + jn] - kb : len);
+                    if (start >= w0 + 64) break;
+                    m |= 1ull << (start - w0 - 1);
+                }
+                win_mask[wi] = m;
+            }
+        }
+    });
+    h->btab_host = btab;
     std::vector<double> dinv_h;
     if (h->jacobi) {
         dinv_h.assign(n, 0.0);
@@ -496,11 +548,11 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         if (rc != CG_OK) return bail(rc); \
     } while (0)
     TRY(dalloc(h, &h->trp, h->nrb + 1));
-    TRY(dalloc(h, &h->win_base, h->ngroups + 1));
     TRY(dalloc(h, &h->win_mask, h->nwin));
     TRY(dalloc(h, &h->win_tile, h->nwin));
-    TRY(dalloc(h, &h->plan, T));
-    TRY(dalloc(h, &h->trow, std::max<int64_t>(T, 1)));
+    TRY(dalloc(h, &h->tent, std::max<int64_t>(T, 1)));
+    TRY(dalloc(h, &h->btab, (int64_t)btab.size()));
+    TRY(dalloc(h, &h->gbatch, h->ngroups + 1));
     TRY(dalloc(h, &h->tcol, T));
     TRY(dalloc(h, &h->tptr, T + 1));
     TRY(dalloc(h, &h->map, T));
@@ -514,8 +566,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         h->meta = m;
     }
     TRY(dalloc(h, &h->v64, nnz));
-    TRY(dalloc(h, &h->v32, nnz));
-    TRY(dalloc(h, &h->v16, nnz));
+    TRY(dalloc(h, &h->planes, h->planes_bytes));
     TRY(dalloc(h, &h->x, n));
     TRY(dalloc(h, &h->r, n));
     TRY(dalloc(h, &h->p, n));
@@ -546,10 +597,13 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     if ((e = hipHostMalloc((void**)&h->pinned, 4 * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess)
         return dev_err(e, "pinned host memory");
 
-    if ((e = hipMemcpyAsync(h->win_base, win_base.data(), sizeof(int32_t) * win_base.size(), hipMemcpyHostToDevice, s)) ||
+    if ((e = hipMemcpyAsync(h->win_mask, win_mask.data(), sizeof(uint64_t) * win_mask.size(), hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->win_tile, win_tile.data(), sizeof(int32_t) * win_tile.size(), hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->tent, tent.data(), sizeof(int2) * tent.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->trp, trp.data(), sizeof(int32_t) * trp.size(), hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->btab, btab.data(), sizeof(int32_t) * btab.size(), hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->gbatch, gbatch.data(), sizeof(int32_t) * gbatch.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tcol, A->tile_col_idx.data(), sizeof(int32_t) * T, hipMemcpyHostToDevice, s)) ||
-        (e = hipMemcpyAsync(h->trow, trow.data(), trow.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tptr, tptr.data(), sizeof(int32_t) * tptr.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->meta, h->meta16 ? (const void*)meta16.data() : (const void*)meta8.data(),
                             (h->meta16 ? 2 : 1) * (size_t)nnz, hipMemcpyHostToDevice, s)) ||
@@ -563,16 +617,17 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     } else if ((e = hipMemsetAsync(h->map, 0, T, s))) {
         return dev_err(e, "map");
     }
-    hipLaunchKernelGGL(dev::build_planes_kernel, dim3(grid_for(nnz, 4, 8192)), dim3(dev::kBlock), 0, s,
-                       h->v64, h->v32, h->v16, nnz);
+    if ((e = hipMemsetAsync(h->planes, 0, h->planes_bytes, s))) return dev_err(e, "planes");
+    hipLaunchKernelGGL(dev::build_segments_kernel,
+                       dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>((h->nbatch + 3) / 4, 8192))),
+                       dim3(dev::kBlock), 0, s, h->btab, h->nbatch, h->v64, h->planes);
     if ((e = hipGetLastError()) != hipSuccess) return dev_err(e, "plane kernel");
     dev::State hs{};
     hs.uprec = -1;
     hs.spmv_uprec = -1;
     hs.trace_cap = (int32_t)h->trace_cap;
     if ((e = hipMemcpyAsync(h->st, &hs, sizeof(hs), hipMemcpyHostToDevice, s))) return dev_err(e, "state");
-    launch_plan(h, 0, s);
-    if ((e = hipGetLastError()) != hipSuccess) return dev_err(e, "plan kernel");
+    if ((e = hipGetLastError()) != hipSuccess) return dev_err(e, "plane kernel");
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return dev_err(e, "set-up");
     *out = h;
     return CG_OK;
@@ -620,7 +675,6 @@ extern "C" int cg_set_precision_map(cg_handle* h, const uint8_t* map, int32_t on
             return fail(CG_EINVAL, "cg_set_precision_map: map[" + std::to_string(t) + "] is not 0, 1 or 2");
     HIP_CHECK(hipMemcpy(h->map, map, h->T, hipMemcpyHostToDevice));
     h->sched = kSchedStatic;
-    HIP_CHECK(replan(h));
     return upload_schedule(h);
 }
 
@@ -649,8 +703,8 @@ extern "C" int cg_map_from_magnitude(cg_handle* h, double t_bf16, double t_fp32)
     hipLaunchKernelGGL(dev::magnitude_map_kernel, dim3(g), dim3(dev::kBlock), 0, h->stream, h->tptr, h->v64,
                        (int32_t)h->T, (const unsigned long long*)h->scratch_u64, t_bf16, t_fp32, h->map);
     HIP_CHECK(hipGetLastError());
+    HIP_CHECK(hipStreamSynchronize(h->stream));
     h->sched = kSchedStatic;
-    HIP_CHECK(replan(h));
     return upload_schedule(h);
 }
 
@@ -669,7 +723,6 @@ extern "C" int cg_set_schedule_residual(cg_handle* h, int32_t nstage, const doub
     for (double t : h->thresholds)
         if (!std::isfinite(t)) return fail(CG_EINVAL, "cg_set_schedule_residual: thresholds must be finite");
     h->sched = kSchedResidual;
-    HIP_CHECK(replan(h));
     return upload_schedule(h);
 }
 
@@ -688,7 +741,6 @@ extern "C" int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const dou
     h->hi = hi;
     h->lo = lo;
     h->sched = kSchedTileRule;
-    HIP_CHECK(replan(h));
     return upload_schedule(h);
 }
 
@@ -699,7 +751,7 @@ extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {
     dev::MapArgs ma = map_args(h, rho, 0);
     hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, h->stream, ma);
     HIP_CHECK(hipGetLastError());
-    HIP_CHECK(replan(h));
+    HIP_CHECK(hipStreamSynchronize(h->stream));
     return CG_OK;
 }
 
@@ -707,7 +759,6 @@ extern "C" int cg_clear_schedule(cg_handle* h) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_clear_schedule: h is NULL");
     h->sched = kSchedStatic;
-    HIP_CHECK(replan(h));
     return upload_schedule(h);
 }
 
@@ -899,7 +950,17 @@ extern "C" int cg_export_layout(const cg_handle* h, int64_t* tile_row_ptr, int32
         }
     }
     if (val64) HIP_CHECK(hipMemcpy(val64, h->v64, sizeof(double) * h->nnz, hipMemcpyDeviceToHost));
-    if (val32) HIP_CHECK(hipMemcpy(val32, h->v32, sizeof(float) * h->nnz, hipMemcpyDeviceToHost));
-    if (bf16) HIP_CHECK(hipMemcpy(bf16, h->v16, sizeof(uint16_t) * h->nnz, hipMemcpyDeviceToHost));
+    if (val32 || bf16) {
+        // The reduced planes live in the per-batch segments.
+        std::vector<char> seg(h->planes_bytes);
+        HIP_CHECK(hipMemcpy(seg.data(), h->planes, seg.size(), hipMemcpyDeviceToHost));
+        for (int64_t b = 0; b < h->nbatch; ++b) {
+            const int32_t* e = &h->btab_host[(size_t)b * dev::kBtFields];
+            const int64_t first = e[dev::kBtFirstNnz], len = e[dev::kBtLen];
+            const char* base = seg.data() + (int64_t)e[dev::kBtSegment] * 16;
+            if (val32) std::memcpy(val32 + first, base + 8 * len, 4 * len);
+            if (bf16) std::memcpy(bf16 + first, base + 12 * len, 2 * len);
+        }
+    }
     return CG_OK;
 }
