@@ -105,7 +105,9 @@ __device__ inline double wave_sum(double v) {
     return v;
 }
 
-// Block sum in a fixed order; the result is valid in every thread.
+// Block sum in a fixed order over NW wavefronts; the result is valid in
+// every thread.
+template <int NW = kWavesPerBlock>
 __device__ inline double block_sum(double v, double* s_tmp) {
     v = wave_sum(v);
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -114,22 +116,25 @@ __device__ inline double block_sum(double v, double* s_tmp) {
     __syncthreads();
     double t = 0.0;
 #pragma unroll
-    for (int i = 0; i < kWavesPerBlock; ++i) t += s_tmp[i];
+    for (int i = 0; i < NW; ++i) t += s_tmp[i];
     return t;
 }
 
 // Fixed-order sum of nparts partials (component j of NV per part); every
 // thread of the block gets the same value, and every block that calls this
 // on the same data gets the same bits.
-template <int NV>
+template <int NV, int NW = kWavesPerBlock>
 __device__ inline void sum_partials(const double* partials, int nparts, double (&out)[NV],
                                     double* s_tmp) {
+    double acc[NV];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        double a = 0.0;
-        for (int i = threadIdx.x; i < nparts; i += blockDim.x) a += partials[(size_t)i * NV + j];
-        out[j] = block_sum(a, s_tmp);
+    for (int j = 0; j < NV; ++j) acc[j] = 0.0;
+    for (int i = threadIdx.x; i < nparts; i += blockDim.x) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) acc[j] += partials[(size_t)i * NV + j];
     }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) out[j] = block_sum<NW>(acc[j], s_tmp);
 }
 
 // Logical block index that gives every XCD a contiguous range of the work:
@@ -241,13 +246,98 @@ __global__ __launch_bounds__(kBlock) void build_segments_kernel(const int32_t* _
     }
 }
 
+// Packed values of a per-tile map: inside every batch's packed segment, tile
+// after tile in storage order, each tile's values at its precision, every
+// tile starting on an 8-byte boundary; toff[t] = start of tile t's values
+// minus (its position in the batch << log2 of its value width). One
+// wavefront per batch: lane l sizes tile l and a wave prefix sum places it,
+// then the lanes copy the batch's values 64 at a time, each finding its tile
+// from the window records. Rerun at every map change; in a solve (solve = 1)
+// only at the start of a tile-rule window.
+struct RepackArgs {
+    const int32_t* btab;
+    const int32_t* tptr;
+    const uint8_t* map;
+    const char* planes;
+    char* packed;
+    int32_t* toff;
+    const uint64_t* win_mask;
+    const int32_t* win_tile;
+    const State* st;
+    int64_t nbatch;
+    int32_t solve;
+};
+
+__global__ __launch_bounds__(kBlock) void repack_kernel(RepackArgs a) {
+    __shared__ int s_toff[kWavesPerBlock][kTileBatch];
+    __shared__ int s_prec[kWavesPerBlock][kTileBatch];
+    if (a.solve) {
+        if (load_done(a.st)) return;
+        if (a.st->k % a.st->period != 0) return;
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int64_t waves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + w; b < a.nbatch; b += waves) {
+        const int32_t* e = a.btab + b * kBtFields;
+        const int tb = e[kBtTile], nt = e[kBtTiles], first = e[kBtFirstNnz], len = e[kBtLen];
+        if (nt == 0) continue;
+        const bool valid = lane < nt;
+        const int p = valid ? min((int)a.map[tb + lane], 2) : 0;
+        const int sh = 3 - p;
+        const int start = valid ? a.tptr[tb + lane] - first : 0;
+        const int bytes = valid ? ((a.tptr[tb + lane + 1] - a.tptr[tb + lane]) << sh) : 0;
+        int incl = (bytes + 7) & ~7;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int t = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += t;
+        }
+        const int base = incl - ((bytes + 7) & ~7);
+        if (valid) {
+            const int to = base - (start << sh);
+            a.toff[tb + lane] = to;
+            s_toff[w][lane] = to;
+            s_prec[w][lane] = p;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const char* src = a.planes + (int64_t)e[kBtSegment] * 16;
+        char* dst = a.packed + (int64_t)e[kBtSegment] * 16;
+        for (int o = 0, v = e[kBtRecords]; o < len; o += kWave, ++v) {
+            const uint64_t m = a.win_mask[v];
+            const int j = a.win_tile[v] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            const int i = o + lane;
+            if (i < len) {
+                const int pj = s_prec[w][j];
+                const int shj = 3 - pj;
+                const int64_t from = (int64_t)pj * (10 - 2 * pj) * len + ((int64_t)i << shj);
+                const int64_t to = (int64_t)s_toff[w][j] + ((int64_t)i << shj);
+                if (pj == 0)
+                    *reinterpret_cast<uint64_t*>(dst + to) = *reinterpret_cast<const uint64_t*>(src + from);
+                else if (pj == 1)
+                    *reinterpret_cast<uint32_t*>(dst + to) = *reinterpret_cast<const uint32_t*>(src + from);
+                else
+                    *reinterpret_cast<uint16_t*>(dst + to) = *reinterpret_cast<const uint16_t*>(src + from);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
 struct SpmvArgs {
     const int32_t* btab;    // [nbatch][8] batch table
     const int32_t* gbatch;  // [ngroups+1] first batch of every row group
     const int2* tent;       // [T] per tile: x byte offset of its column block, accumulator byte offset of its rows
     const uint8_t* map;     // [T] active precision map
+    const int32_t* toff;    // [T] per tile: its values' start in the packed segment minus position << width shift
     const void* meta;       // per nonzero (row, col) packed: u8 (R, C <= 16) or u16
     const char* planes;     // value segments, one per batch
+    const char* packed;     // packed value segments of the active map, same offsets
     const uint64_t* win_mask;  // per window: bit q = nonzero q+1 of the window starts a tile
     const int32_t* win_tile;   // per window: batch tile of the window's first nonzero
     const double* x;
@@ -308,7 +398,7 @@ __device__ __forceinline__ BatchHdr load_hdr(const int32_t* btab, int b) {
 // tiles) and window record `lane` of a chunk of 64 windows.
 struct BatchRegs {
     int2 entry;
-    int prec;
+    int prec, toff;
     uint32_t mlo, mhi;
     int rec;
 };
@@ -319,6 +409,7 @@ struct SweepCtx {
     char* acc;         // this wave's row accumulators in LDS
     const int2* tent;
     const uint8_t* map;
+    const int32_t* toff;
     int len, lane;
     int spare;  // byte offset of this lane's spare accumulator
 };
@@ -331,6 +422,7 @@ __device__ __forceinline__ void load_batch_regs(const SweepCtx& c, const BatchHd
         const int t = h.tile + min(c.lane, max(h.tiles - 1, 0));
         r.entry = c.tent[t];
         r.prec = c.map[t];
+        r.toff = c.toff[t];
     }
     const int wi = h.records + chunk + c.lane;
     const u32x2 m = __builtin_amdgcn_raw_buffer_load_b64(c.rmask, 8 * wi, 0, 0);
@@ -344,10 +436,10 @@ __device__ __forceinline__ void load_batch_regs(const SweepCtx& c, const BatchHd
 // before any is consumed. With next = true the next batch's tile entries and
 // first records (header Hn) are loaded into Rn once the value loads are issued.
 //
-// A lane's value is one 8-byte load at its plane's start plus its position
-// times the value width, rounded down to 4 bytes (a BF16 lane then takes the
-// half its position selects); the widening is a bitwise blend. Lanes past the
-// batch add their zero product to a private spare accumulator.
+// A lane's value is one 8-byte load at its tile's entry shift plus its
+// position times the value width, rounded down to 4 bytes (a BF16 lane then
+// takes the half its byte offset selects); the widening is a bitwise blend.
+// Lanes past the batch add their zero product to a private spare accumulator.
 template <typename MetaT, int U>
 __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R, int wi, int o0, bool next,
                                            const BatchHdr& Hn, BatchRegs& Rn) {
@@ -371,9 +463,13 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
     // Stored values, issued before the vector gathers (which wait for the
     // packed indices).
     u32x2 raw[U];
+    int hs[U];  // BF16: 16 when the value is the high half of its 4-byte word
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-        raw[u] = __builtin_amdgcn_raw_buffer_load_b64(c.rv, d[u].z + ((q[u] << d[u].w) & ~3), 0, 0);
+    for (int u = 0; u < U; ++u) {
+        const int off = d[u].z + (q[u] << d[u].w);
+        hs[u] = (off & 2) << 3;
+        raw[u] = __builtin_amdgcn_raw_buffer_load_b64(c.rv, off & ~3, 0, 0);
+    }
     if (next) load_batch_regs(c, Hn, 0, true, Rn);
     double xv[U];
     int racc[U];
@@ -387,10 +483,10 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        // FP32: the low word. BF16 (width shift 1): the half holding element q
-        // (little endian: the high half for odd q), moved to the high half of an
-        // FP32 word. FP64: width shift 3.
-        const uint32_t h = (raw[u].x >> ((q[u] & 1) << 4)) << 16;
+        // FP32: the low word. BF16 (width shift 1): the half holding the value
+        // (little endian), moved to the high half of an FP32 word. FP64: width
+        // shift 3.
+        const uint32_t h = (raw[u].x >> hs[u]) << 16;
         const uint32_t f = d[u].w == 1 ? h : raw[u].x;
         const double v32 = (double)__uint_as_float(f);
         const double v = d[u].w == 3 ? __longlong_as_double(((long long)raw[u].y << 32) | raw[u].x) : v32;
@@ -425,6 +521,7 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
     c.lane = lane;
     c.tent = a.tent;
     c.map = a.map;
+    c.toff = a.toff;
     c.desc = &s_desc[w][0];
     c.acc = reinterpret_cast<char*>(&s_acc[w][0]);
     c.spare = (MAXROWS + lane) * 8;
@@ -455,21 +552,23 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
             for (int i = lane; i < a.rows_per_group; i += kWave) s_acc[w][i] = 0.0;
             if (MODE == kSpmvCg && MAXROWS <= kWave && lane < nrows) p_own = a.x[row0 + lane];
         }
-        // Tile entries (precision from the map, or the uniform override), the
-        // sentinel past the batch's tiles.
+        // Tile entries, the sentinel past the batch's tiles. Under a per-tile map
+        // the values come from the map's packed segment; under a uniform
+        // precision, from that precision's plane of the batch's segment.
         {
             const int p = uprec >= 0 ? uprec : R.prec;
             const bool tile = lane < H.tiles;
             int4 e;
             e.x = tile ? R.entry.x : kSentinelColumn;
             e.y = R.entry.y;
-            e.z = tile ? p * (10 - 2 * p) * H.len : kSentinelPlane;
+            e.z = !tile ? kSentinelPlane : uprec >= 0 ? p * (10 - 2 * p) * H.len : R.toff;
             e.w = tile ? 3 - p : 3;
             s_desc[w][lane] = e;
             if (lane == 0) s_desc[w][kTileBatch] = make_int4(kSentinelColumn, 0, kSentinelPlane, 3);
         }
-        c.rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.planes + (int64_t)H.segment * 16), (short)0,
-                                                 (int)segment_bytes(H.len), (int)kBufferConfig);
+        c.rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>((uprec >= 0 ? a.planes : a.packed) + (int64_t)H.segment * 16), (short)0,
+            (int)segment_bytes(H.len), (int)kBufferConfig);
         c.rmt = batch_rsrc(a.meta, H.first, (int)sizeof(MetaT), H.len);
         c.len = H.len;
         const int E = batch_records(H.len);
@@ -626,35 +725,82 @@ __global__ __launch_bounds__(kBlock) void cg_init_finish_kernel(VecArgs a) {
     }
 }
 
+// Update and direction kernels: blocks of kVecBlock threads; thread t of a
+// grid of S threads handles the 16-byte pairs t, t+S, ... (kVecPairs of them
+// per chunk). The handle's vectors are padded with zeros to an even length,
+// so pairs need no tail handling. Each kernel issues its first chunk's loads
+// before it sums the previous kernel's partials, which hides that sum.
+constexpr int kVecBlock = 1024;
+constexpr int kVecWaves = kVecBlock / kWave;
+constexpr int kVecPairs = 4;
+
 // alpha = r.z / p.q (p.q summed from the SpMV partials in every block);
 // x += alpha p; r -= alpha q; [z = dinv .* r]; partials of r.r [and r.z].
 // On p.q <= 0 or a non-finite alpha nothing is updated and the breakdown is
 // flagged for the direction kernel.
-__global__ __launch_bounds__(kBlock) void cg_update_kernel(VecArgs a) {
-    __shared__ double s_tmp[kWavesPerBlock];
+template <bool JAC>
+__global__ __launch_bounds__(kVecBlock) void cg_update_kernel(VecArgs a) {
+    __shared__ double s_tmp[kVecWaves];
     State* st = a.st;
     if (load_done(st)) return;
+    const int64_t npairs = ((int64_t)a.n + 1) / 2;
+    const int64_t stride = (int64_t)gridDim.x * kVecBlock;
+    const int64_t tid = (int64_t)blockIdx.x * kVecBlock + threadIdx.x;
+    double2* __restrict__ x2 = reinterpret_cast<double2*>(a.x);
+    double2* __restrict__ r2 = reinterpret_cast<double2*>(a.r);
+    double2* __restrict__ z2 = reinterpret_cast<double2*>(a.z);
+    const double2* __restrict__ p2 = reinterpret_cast<const double2*>(a.p);
+    const double2* __restrict__ q2 = reinterpret_cast<const double2*>(a.q);
+    const double2* __restrict__ d2 = reinterpret_cast<const double2*>(a.dinv);
+    double2 xv[kVecPairs], rv[kVecPairs], pv[kVecPairs], qv[kVecPairs], dv[kVecPairs];
+    auto load = [&](int64_t base) {
+#pragma unroll
+        for (int j = 0; j < kVecPairs; ++j) {
+            const int64_t i = base + j * stride + tid;
+            if (i < npairs) {
+                xv[j] = x2[i];
+                rv[j] = r2[i];
+                pv[j] = p2[i];
+                qv[j] = q2[i];
+                if (JAC) dv[j] = d2[i];
+            }
+        }
+    };
+    load(0);
     double tot[1];
-    sum_partials<1>(a.part_in, a.nparts_in, tot, s_tmp);
+    sum_partials<1, kVecWaves>(a.part_in, a.nparts_in, tot, s_tmp);
     const double pq = tot[0];
     const double alpha = st->rz / pq;
     const bool bd = !(pq > 0.0) || !isfinite(pq) || !isfinite(alpha);
     double rr = 0.0, rz = 0.0;
     if (!bd) {
-        for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += gridDim.x * blockDim.x) {
-            a.x[i] += alpha * a.p[i];
-            const double ri = a.r[i] - alpha * a.q[i];
-            a.r[i] = ri;
-            rr += ri * ri;
-            if (a.jacobi) {
-                const double zi = a.dinv[i] * ri;
-                a.z[i] = zi;
-                rz += ri * zi;
+        for (int64_t base = 0; base < npairs; base += stride * kVecPairs) {
+            if (base > 0) load(base);
+#pragma unroll
+            for (int j = 0; j < kVecPairs; ++j) {
+                const int64_t i = base + j * stride + tid;
+                if (i < npairs) {
+                    double2 xn, rn;
+                    xn.x = xv[j].x + alpha * pv[j].x;
+                    xn.y = xv[j].y + alpha * pv[j].y;
+                    rn.x = rv[j].x - alpha * qv[j].x;
+                    rn.y = rv[j].y - alpha * qv[j].y;
+                    x2[i] = xn;
+                    r2[i] = rn;
+                    rr += rn.x * rn.x + rn.y * rn.y;
+                    if (JAC) {
+                        double2 zn;
+                        zn.x = dv[j].x * rn.x;
+                        zn.y = dv[j].y * rn.y;
+                        z2[i] = zn;
+                        rz += rn.x * zn.x + rn.y * zn.y;
+                    }
+                }
             }
         }
     }
-    const double prr = block_sum(rr, s_tmp);
-    const double prz = a.jacobi ? block_sum(rz, s_tmp) : prr;
+    const double prr = block_sum<kVecWaves>(rr, s_tmp);
+    const double prz = JAC ? block_sum<kVecWaves>(rz, s_tmp) : prr;
     if (threadIdx.x == 0) {
         a.part_out[2 * blockIdx.x] = prr;
         a.part_out[2 * blockIdx.x + 1] = prz;
@@ -672,22 +818,50 @@ __global__ __launch_bounds__(kBlock) void cg_update_kernel(VecArgs a) {
 // rho_{k+1}, the history entry, the stop flag and the schedule stage.
 // Other blocks may read `done` before or after that commit within the final
 // iteration; either way the direction update they skip or make is unused.
-__global__ __launch_bounds__(kBlock) void cg_direction_kernel(VecArgs a) {
-    __shared__ double s_tmp[kWavesPerBlock];
+template <bool JAC>
+__global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
+    __shared__ double s_tmp[kVecWaves];
     State* st = a.st;
     if (load_done(st)) return;
     if (st->bd) {
         if (blockIdx.x == 0 && threadIdx.x == 0) store_done(st, 3);
         return;
     }
+    const int64_t npairs = ((int64_t)a.n + 1) / 2;
+    const int64_t stride = (int64_t)gridDim.x * kVecBlock;
+    const int64_t tid = (int64_t)blockIdx.x * kVecBlock + threadIdx.x;
+    double2* __restrict__ p2 = reinterpret_cast<double2*>(a.p);
+    const double2* __restrict__ z2 = reinterpret_cast<const double2*>(JAC ? a.z : a.r);
+    double2 pv[kVecPairs], zv[kVecPairs];
+    auto load = [&](int64_t base) {
+#pragma unroll
+        for (int j = 0; j < kVecPairs; ++j) {
+            const int64_t i = base + j * stride + tid;
+            if (i < npairs) {
+                pv[j] = p2[i];
+                zv[j] = z2[i];
+            }
+        }
+    };
+    load(0);
     double tot[2];
-    sum_partials<2>(a.part_in, a.nparts_in, tot, s_tmp);
+    sum_partials<2, kVecWaves>(a.part_in, a.nparts_in, tot, s_tmp);
     const double rr_new = tot[0];
     const double rz_new = tot[1];
     const double beta = rz_new / st->rz_prev;
-    const double* z = a.jacobi ? a.z : a.r;
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += gridDim.x * blockDim.x)
-        a.p[i] = z[i] + beta * a.p[i];
+    for (int64_t base = 0; base < npairs; base += stride * kVecPairs) {
+        if (base > 0) load(base);
+#pragma unroll
+        for (int j = 0; j < kVecPairs; ++j) {
+            const int64_t i = base + j * stride + tid;
+            if (i < npairs) {
+                double2 pn;
+                pn.x = zv[j].x + beta * pv[j].x;
+                pn.y = zv[j].y + beta * pv[j].y;
+                p2[i] = pn;
+            }
+        }
+    }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         const int k = st->k + 1;
         const double rho = sqrt(rr_new) / st->norm0;

@@ -62,6 +62,8 @@ struct cg_handle {
     void* meta = nullptr;
     double* v64 = nullptr;         // [nnz] FP64 values in storage order
     char* planes = nullptr;        // per-batch value segments (FP64, FP32, BF16)
+    char* packed = nullptr;        // per-batch packed values of the active map (same offsets)
+    int32_t* toff = nullptr;       // [T] packed start of every tile (see repack_kernel)
     int64_t planes_bytes = 0;
     std::vector<int32_t> btab_host;  // host copy of the batch table
     double* dinv = nullptr;
@@ -70,7 +72,7 @@ struct cg_handle {
     double *x = nullptr, *r = nullptr, *p = nullptr, *q = nullptr, *z = nullptr;
     double* part_spmv = nullptr;  // one p.q partial per SpMV block
     double* part_vec = nullptr;   // two partials per vector-kernel block
-    int spmv_blocks = 0, groups_per_wave = 0, vec_blocks = 0;
+    int spmv_blocks = 0, groups_per_wave = 0, vec_blocks = 0, upd_blocks = 0;
     dev::State* st = nullptr;
     double* hist = nullptr;
     int64_t hist_cap = 0;
@@ -155,6 +157,9 @@ void plan_grids(cg_handle* h) {
     const int64_t used = (h->ngroups + h->groups_per_wave - 1) / h->groups_per_wave;
     h->spmv_blocks = (int)std::max<int64_t>(1, (used + dev::kSpmvWaves - 1) / dev::kSpmvWaves);
     h->vec_blocks = grid_for(h->n, 8, kVecGridCap);
+    const int64_t npairs = (h->n + 1) / 2;
+    const int64_t per_block = (int64_t)dev::kVecBlock * dev::kVecPairs;
+    h->upd_blocks = (int)std::max<int64_t>(1, std::min<int64_t>((npairs + per_block - 1) / per_block, 512));
 }
 
 dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t* uprec) {
@@ -165,6 +170,8 @@ dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t*
     a.map = h->map;
     a.meta = h->meta;
     a.planes = h->planes;
+    a.packed = h->packed;
+    a.toff = h->toff;
     a.win_mask = h->win_mask;
     a.win_tile = h->win_tile;
     a.x = x;
@@ -199,6 +206,34 @@ void launch_spmv(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, 64>), dim3(grid), dim3(dev::kSpmvBlock), 0,
                            s, a, a.y, a.partials);
     }
+}
+
+// Packs the active map's values (every map change). solve = 1: only at the
+// start of a tile-rule window of a running solve (the kernel checks).
+void launch_repack(cg_handle* h, int solve, hipStream_t s) {
+    dev::RepackArgs a{};
+    a.btab = h->btab;
+    a.tptr = h->tptr;
+    a.map = h->map;
+    a.planes = h->planes;
+    a.packed = h->packed;
+    a.toff = h->toff;
+    a.win_mask = h->win_mask;
+    a.win_tile = h->win_tile;
+    a.st = h->st;
+    a.nbatch = h->nbatch;
+    a.solve = solve;
+    const int64_t blocks = (h->nbatch + dev::kWavesPerBlock - 1) / dev::kWavesPerBlock;
+    hipLaunchKernelGGL(dev::repack_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 16384))),
+                       dim3(dev::kBlock), 0, s, a);
+}
+
+// Repacks after a map written on the handle's stream; synchronous.
+hipError_t repack(cg_handle* h) {
+    launch_repack(h, 0, h->stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return hipStreamSynchronize(h->stream);
 }
 
 dev::VecArgs vec_args(cg_handle* h, const double* b, const double* x0) {
@@ -284,6 +319,7 @@ void enqueue_iteration(cg_handle* h, int i, hipStream_t s) {
     if (h->sched == kSchedTileRule && i % h->period == 0) {
         dev::MapArgs ma = map_args(h, 0.0, 1);
         hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, s, ma);
+        launch_repack(h, 1, s);
     }
     dev::SpmvArgs sa = spmv_args(h, h->p, h->q, &h->st->uprec);
     launch_spmv<dev::kSpmvCg>(h, sa, s);
@@ -291,10 +327,16 @@ void enqueue_iteration(cg_handle* h, int i, hipStream_t s) {
     va.part_in = h->part_spmv;
     va.nparts_in = spmv_grid(h);
     va.part_out = h->part_vec;
-    hipLaunchKernelGGL(dev::cg_update_kernel, dim3(vec_grid(h)), dim3(dev::kBlock), 0, s, va);
+    if (h->jacobi)
+        hipLaunchKernelGGL(dev::cg_update_kernel<true>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
+    else
+        hipLaunchKernelGGL(dev::cg_update_kernel<false>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
     va.part_in = h->part_vec;
-    va.nparts_in = vec_grid(h);
-    hipLaunchKernelGGL(dev::cg_direction_kernel, dim3(vec_grid(h)), dim3(dev::kBlock), 0, s, va);
+    va.nparts_in = h->upd_blocks;
+    if (h->jacobi)
+        hipLaunchKernelGGL(dev::cg_direction_kernel<true>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
+    else
+        hipLaunchKernelGGL(dev::cg_direction_kernel<false>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
 }
 
 int ensure_graph(cg_handle* h) {
@@ -567,17 +609,22 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     }
     TRY(dalloc(h, &h->v64, nnz));
     TRY(dalloc(h, &h->planes, h->planes_bytes));
-    TRY(dalloc(h, &h->x, n));
-    TRY(dalloc(h, &h->r, n));
-    TRY(dalloc(h, &h->p, n));
-    TRY(dalloc(h, &h->q, n));
+    TRY(dalloc(h, &h->packed, h->planes_bytes));
+    TRY(dalloc(h, &h->toff, std::max<int64_t>(T, 1)));
+    // CG vectors padded with zeros to an even length (the vector kernels work
+    // in 16-byte pairs); nothing writes the padding.
+    const int64_t n_pad = n + (n & 1);
+    TRY(dalloc(h, &h->x, n_pad));
+    TRY(dalloc(h, &h->r, n_pad));
+    TRY(dalloc(h, &h->p, n_pad));
+    TRY(dalloc(h, &h->q, n_pad));
     if (h->jacobi) {
-        TRY(dalloc(h, &h->z, n));
-        TRY(dalloc(h, &h->dinv, n));
+        TRY(dalloc(h, &h->z, n_pad));
+        TRY(dalloc(h, &h->dinv, n_pad));
     }
     plan_grids(h);
     TRY(dalloc(h, &h->part_spmv, spmv_grid(h)));
-    TRY(dalloc(h, &h->part_vec, 2 * vec_grid(h)));
+    TRY(dalloc(h, &h->part_vec, 2 * std::max(vec_grid(h), h->upd_blocks)));
     TRY(dalloc(h, &h->st, 1));
     TRY(dalloc(h, &h->scratch_u64, 4));
     h->trace_cap = 16;
@@ -597,6 +644,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     if ((e = hipHostMalloc((void**)&h->pinned, 4 * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess)
         return dev_err(e, "pinned host memory");
 
+    for (double* v : {h->x, h->r, h->p, h->q, h->z, h->dinv})
+        if (v && (e = hipMemsetAsync(v, 0, sizeof(double) * (size_t)n_pad, s))) return dev_err(e, "vectors");
     if ((e = hipMemcpyAsync(h->win_mask, win_mask.data(), sizeof(uint64_t) * win_mask.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->win_tile, win_tile.data(), sizeof(int32_t) * win_tile.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tent, tent.data(), sizeof(int2) * tent.size(), hipMemcpyHostToDevice, s)) ||
@@ -617,7 +666,9 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     } else if ((e = hipMemsetAsync(h->map, 0, T, s))) {
         return dev_err(e, "map");
     }
-    if ((e = hipMemsetAsync(h->planes, 0, h->planes_bytes, s))) return dev_err(e, "planes");
+    if ((e = hipMemsetAsync(h->planes, 0, h->planes_bytes, s)) ||
+        (e = hipMemsetAsync(h->packed, 0, h->planes_bytes, s)))
+        return dev_err(e, "planes");
     hipLaunchKernelGGL(dev::build_segments_kernel,
                        dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>((h->nbatch + 3) / 4, 8192))),
                        dim3(dev::kBlock), 0, s, h->btab, h->nbatch, h->v64, h->planes);
@@ -627,7 +678,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     hs.spmv_uprec = -1;
     hs.trace_cap = (int32_t)h->trace_cap;
     if ((e = hipMemcpyAsync(h->st, &hs, sizeof(hs), hipMemcpyHostToDevice, s))) return dev_err(e, "state");
-    if ((e = hipGetLastError()) != hipSuccess) return dev_err(e, "plane kernel");
+    launch_repack(h, 0, s);
+    if ((e = hipGetLastError()) != hipSuccess) return dev_err(e, "repack kernel");
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return dev_err(e, "set-up");
     *out = h;
     return CG_OK;
@@ -674,6 +726,7 @@ extern "C" int cg_set_precision_map(cg_handle* h, const uint8_t* map, int32_t on
         if (map[t] > 2)
             return fail(CG_EINVAL, "cg_set_precision_map: map[" + std::to_string(t) + "] is not 0, 1 or 2");
     HIP_CHECK(hipMemcpy(h->map, map, h->T, hipMemcpyHostToDevice));
+    HIP_CHECK(repack(h));
     h->sched = kSchedStatic;
     return upload_schedule(h);
 }
@@ -703,7 +756,7 @@ extern "C" int cg_map_from_magnitude(cg_handle* h, double t_bf16, double t_fp32)
     hipLaunchKernelGGL(dev::magnitude_map_kernel, dim3(g), dim3(dev::kBlock), 0, h->stream, h->tptr, h->v64,
                        (int32_t)h->T, (const unsigned long long*)h->scratch_u64, t_bf16, t_fp32, h->map);
     HIP_CHECK(hipGetLastError());
-    HIP_CHECK(hipStreamSynchronize(h->stream));
+    HIP_CHECK(repack(h));
     h->sched = kSchedStatic;
     return upload_schedule(h);
 }
@@ -751,7 +804,7 @@ extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {
     dev::MapArgs ma = map_args(h, rho, 0);
     hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, h->stream, ma);
     HIP_CHECK(hipGetLastError());
-    HIP_CHECK(hipStreamSynchronize(h->stream));
+    HIP_CHECK(repack(h));
     return CG_OK;
 }
 
