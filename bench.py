@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 256 << 20
 METRIC = "Tile-CSC SpMV GB/s (% HBM peak); CG iterations/sec; time-to-solution"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spmv_tilecsc_cfg2_traffic.json")
 KERNEL_SOURCES = ["mixed_precision_sparse_amd/csrc/mpcg_kernels.hpp",
@@ -58,6 +59,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="counter run: a 256 MiB copy (the scale reference), then 5 cg_spmv "
+                         "launches per map (all FP64, the bench's mixed map, all BF16); no timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -83,6 +87,10 @@ def main():
 
     b = torch.from_numpy(w.b).to(dev)
     x = torch.zeros_like(b)
+
+    if args.pmc_probe:
+        pmc_probe(torch, dev, S, L, A, pmap)
+        return
 
     def run_solves(solver, steps):
         its = 0
@@ -121,6 +129,19 @@ def main():
     bytes_spmv64 = spmv_algorithmic_bytes(L, np.zeros(L.T, np.uint8))
     bytes_vec = 56 * A.n
     iter_gbs = (bytes_spmv + bytes_vec) * its / el / 1e9
+
+    # Measured bandwidth ceiling: a device-to-device copy of 256 MiB.
+    c_src = torch.empty(COPY_BYTES // 8, dtype=torch.float64, device=dev).uniform_()
+    c_dst = torch.empty_like(c_src)
+    for _ in range(3):
+        c_dst.copy_(c_src)
+    e0.record()
+    for _ in range(20):
+        c_dst.copy_(c_src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_BYTES / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e9
+    del c_src, c_dst
 
     # The all-FP64 map on the same substrate.
     S64 = mpcg.Solver(L, np.zeros(L.T, np.uint8))
@@ -178,6 +199,7 @@ def main():
                      "spmv_us": round(spmv64_ms * 1e3, 2),
                      "spmv_gbs": round(bytes_spmv64 / (spmv64_ms * 1e-3) / 1e9, 1)},
         "mixed_over_fp64_tts_speedup": round(tts64_ms / tts_ms, 4),
+        "copy_ceiling_gbs": round(copy_gbs, 1),
         "roofline": {
             "bound": "hbm",
             "kernel": "spmv_tilecsc_kernel (cg_spmv)",
@@ -191,6 +213,25 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def pmc_probe(torch, dev, S, L, A, pmap):
+    """Launch sequence for the HBM counter runs: the copy of known size first, then the
+    SpMV under each map. Counters are read per dispatch by rocprofv3."""
+    src = torch.empty(COPY_BYTES // 8, dtype=torch.float64, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    xin = torch.from_numpy(np.random.default_rng(7).uniform(-1, 1, A.n)).to(dev)
+    y = torch.empty_like(xin)
+    for name, m in (("fp64", np.zeros(L.T, np.uint8)), ("mixed", pmap), ("bf16", np.full(L.T, 2, np.uint8))):
+        S.cg_set_precision_map(m)
+        for _ in range(5):
+            S.cg_spmv(xin, y)
+        torch.cuda.synchronize()
+        print(f"# pmc probe: 5 cg_spmv launches, {name} map, algorithmic bytes "
+              f"{spmv_algorithmic_bytes(L, m)}", file=sys.stderr, flush=True)
 
 
 def cpu_baseline(w, pmap, budget_s):
