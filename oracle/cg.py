@@ -20,7 +20,8 @@ Conventions taken where the paper is silent:
 * K counts completed iterations; ``hist`` holds rho_0 .. rho_K with rho_0 = 1.
 * p.q <= 0 or a non-finite alpha/beta stops with status "breakdown".
 * ||r0|| = 0 returns x0 with K = 0 and hist = [0].
-* The map for iteration k is chosen from (k, rho_k) by a schedule.
+* The map for iteration k is chosen from (k, rho_k) -- or, for the per-segment
+  max|p| rule, from the direction p_k -- by a schedule.
 
 Test infrastructure only: see the package docstring.
 """
@@ -42,7 +43,7 @@ class StaticSchedule:
     def __init__(self, prec_map):
         self.map = np.asarray(prec_map, dtype=np.uint8)
 
-    def map_for(self, k, rho, T):
+    def map_for(self, k, rho, T, p=None):
         return self.map if k == 0 else None
 
 
@@ -51,11 +52,11 @@ class RatchetSchedule:
         self.r = _maps.Ratchet(thresholds, prec)
         self.current = None
 
-    def map_for(self, k, rho, T):
-        p = self.r.step(rho)
-        if p != self.current:
-            self.current = p
-            return np.full(T, p, dtype=np.uint8)
+    def map_for(self, k, rho, T, p=None):
+        code = self.r.step(rho)
+        if code != self.current:
+            self.current = code
+            return np.full(T, code, dtype=np.uint8)
         return None
 
 
@@ -65,10 +66,23 @@ class TileRuleSchedule:
         self.period = int(period)
         self.hi, self.lo = float(hi), float(lo)
 
-    def map_for(self, k, rho, T):
+    def map_for(self, k, rho, T, p=None):
         if k % self.period == 0:
             return _maps.tile_rule(self.scores, rho, self.hi, self.lo)
         return None
+
+
+class PMagSchedule:
+    """The per-segment max|p| rule (Sec. 4.7), re-applied at every iteration to the
+    direction p_k that the iteration's SpMV multiplies."""
+
+    def __init__(self, C, tile_col_idx, lo, hi):
+        self.C = int(C)
+        self.tcol = np.asarray(tile_col_idx)
+        self.lo, self.hi = float(lo), float(hi)
+
+    def map_for(self, k, rho, T, p=None):
+        return _maps.pmag_rule(p, self.C, self.tcol, self.lo, self.hi)
 
 
 @dataclass
@@ -137,7 +151,7 @@ def solve(L: TileCSC, indptr, indices, data, b, schedule, tol, maxit, x0=None,
         if k == maxit:
             status = "maxit"
             break
-        new_map = schedule.map_for(k, rho, L.T)
+        new_map = schedule.map_for(k, rho, L.T, p)
         if new_map is not None:
             op.set_map(new_map)
             counts = np.bincount(new_map, minlength=3)[:3].tolist()
@@ -193,4 +207,6 @@ def schedule_for(spec: dict, L: TileCSC, scores=None, static=None):
         return RatchetSchedule(spec["thresholds"], spec["prec"])
     if kind == "tile_rule":
         return TileRuleSchedule(scores, spec["period"], spec["hi"], spec["lo"])
+    if kind == "pmag":
+        return PMagSchedule(L.C, L.tile_col_idx, spec["lo"], spec["hi"])
     raise ValueError(kind)

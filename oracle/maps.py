@@ -62,6 +62,28 @@ class Ratchet:
         return self.prec[self.stage]
 
 
+def pmag_rule(p: np.ndarray, C: int, tile_col_idx: np.ndarray, lo: float, hi: float) -> np.ndarray:
+    """Residual-threshold rule on the direction vector (Sec. 4.7 "Why Learned Precision Control?").
+
+    Tile t reads its column block J = tile_col_idx[t], i.e. the segment
+    p[J*C : (J+1)*C] of the vector it multiplies (the last segment may be
+    shorter). With m_J = max |p_j| over that segment: BF16 if m_J < lo, FP32 if
+    lo <= m_J < hi, FP64 otherwise. The paper's setting is lo = eps/10, hi = eps
+    for the solver tolerance eps.
+    """
+    p = np.abs(np.asarray(p, dtype=np.float64))
+    n = p.size
+    ncb = -(-n // C)
+    pad = np.zeros(ncb * C)
+    pad[:n] = p
+    m = pad.reshape(ncb, C).max(axis=1)
+    mt = m[np.asarray(tile_col_idx, dtype=np.int64)]
+    out = np.full(mt.shape, FP64, dtype=np.uint8)
+    out[mt < hi] = FP32
+    out[mt < lo] = BF16
+    return out
+
+
 def tile_rule(scores: np.ndarray, rho: float, hi: float = 1e-3, lo: float = 1e-6) -> np.ndarray:
     """Per-tile re-selection: v_t = s_t * rho; BF16 if v_t > hi, FP32 if v_t > lo, else FP64."""
     v = np.asarray(scores, dtype=np.float64) * float(rho)
