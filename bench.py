@@ -157,6 +157,20 @@ def main():
     print(f"# fp64 map: {status64} K={K64} TTS {tts64_ms:.3f} ms; spmv mixed {spmv_ms * 1e3:.1f} us, "
           f"fp64 {spmv64_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # The per-segment max|p| rule (paper Sec. 4.7) at its paper setting,
+    # lo = tol/10, hi = tol, on the same substrate.
+    Spm = mpcg.Solver(L)
+    Spm.cg_set_schedule_pmag(w.tol / 10, w.tol)
+    run_solves(Spm, max(1, args.warmup))
+    elpm, itspm, statuspm, Kpm, _ = run_solves(Spm, args.steps)
+    ttspm_ms = 1e3 * elpm / args.steps
+    ks, cnt = Spm.cg_get_map_trace(cap=w.maxit + 2)
+    pm_frac = (cnt.sum(axis=0) / max(cnt.sum(), 1)).round(4).tolist()
+    truepm = float(np.linalg.norm(w.b - A.to_scipy() @ x.cpu().numpy()) / np.linalg.norm(w.b))
+    print(f"# max|p| rule: {statuspm} K={Kpm} TTS {ttspm_ms:.3f} ms; tile-iterations FP64/FP32/BF16 "
+          f"{pm_frac}", file=sys.stderr, flush=True)
+    Spm.close()
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
@@ -200,6 +214,11 @@ def main():
                      "spmv_gbs": round(bytes_spmv64 / (spmv64_ms * 1e-3) / 1e9, 1)},
         "mixed_over_fp64_tts_speedup": round(tts64_ms / tts_ms, 4),
         "copy_ceiling_gbs": round(copy_gbs, 1),
+        "pmag_rule": {"lo": w.tol / 10, "hi": w.tol, "status": statuspm, "iterations": Kpm,
+                      "time_to_solution_ms": round(ttspm_ms, 4),
+                      "iterations_per_s": round(itspm / elpm, 2),
+                      "true_residual": truepm,
+                      "tile_iterations_fp64_fp32_bf16": pm_frac},
         "roofline": {
             "bound": "hbm",
             "kernel": "spmv_tilecsc_kernel (cg_spmv)",

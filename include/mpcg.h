@@ -156,6 +156,17 @@ int cg_map_from_magnitude(cg_handle* h, double t_bf16, double t_fp32);
 int cg_set_schedule_residual(cg_handle* h, int32_t nstage, const double* thresholds,
                              const uint8_t* prec);
 
+/* Per-segment max|p| rule (Sec. 4.7, the residual-threshold rule the paper
+ * compares against; its setting is lo = eps/10, hi = eps for the tolerance
+ * eps): before every SpMV each tile is given BF16 if the largest |p_j| of its
+ * column block's segment of the multiplied vector is < lo, FP32 if it is <
+ * hi, else FP64. In cg_solve the vector is the iteration's direction p_k and
+ * the map trace gets one entry per iteration; cg_spmv applies the rule to its
+ * input x. The value planes are read directly (no repacking per iteration).
+ * Requires lo <= hi, no NaN (infinities allowed). Errors: CG_EINVAL,
+ * CG_ENOMEM, CG_EDEVICE. */
+int cg_set_schedule_pmag(cg_handle* h, double lo, double hi);
+
 /* Windowed per-tile rule (Sec. 3.4 "Interval Reuse Scheduling": a map chosen
  * at a window start is kept for the window). At every k with k % period == 0,
  * v_t = scores[t] * rho_k and tile t gets BF16 if v_t > hi, FP32 if v_t > lo,

@@ -176,6 +176,10 @@ class Solver:
         check(_lib.load().cg_set_schedule_tile_rule(self._h, int(period), _ptr(sc), float(hi),
                                                     float(lo)))
 
+    def cg_set_schedule_pmag(self, lo, hi):
+        """Per-segment max|p| rule before every SpMV (see include/mpcg.h)."""
+        check(_lib.load().cg_set_schedule_pmag(self._h, float(lo), float(hi)))
+
     def cg_eval_tile_rule(self, rho):
         check(_lib.load().cg_eval_tile_rule(self._h, float(rho)))
 

@@ -48,6 +48,7 @@ SIGNATURES = {
     "cg_set_schedule_residual": (ct.c_int, [vp, i32, vp, vp]),
     "cg_set_schedule_tile_rule": (ct.c_int, [vp, i32, vp, f64, f64]),
     "cg_eval_tile_rule": (ct.c_int, [vp, f64]),
+    "cg_set_schedule_pmag": (ct.c_int, [vp, f64, f64]),
     "cg_clear_schedule": (ct.c_int, [vp]),
     "cg_spmv": (ct.c_int, [vp, vp, vp, vp]),
     "cg_solve": (ct.c_int, [vp, vp, vp, f64, i32, vp, ct.POINTER(i32), vp, vp]),

@@ -335,6 +335,8 @@ struct SpmvArgs {
     const int2* tent;       // [T] per tile: x byte offset of its column block, accumulator byte offset of its rows
     const uint8_t* map;     // [T] active precision map
     const int32_t* toff;    // [T] per tile: its values' start in the packed segment minus position << width shift
+    const int32_t* tcol;    // [T] column block of every tile
+    const uint8_t* cbcode;  // per column block precision (max|p| rule kernels only)
     const void* meta;       // per nonzero (row, col) packed: u8 (R, C <= 16) or u16
     const char* planes;     // value segments, one per batch
     const char* packed;     // packed value segments of the active map, same offsets
@@ -410,19 +412,28 @@ struct SweepCtx {
     const int2* tent;
     const uint8_t* map;
     const int32_t* toff;
+    const int32_t* tcol;
+    const uint8_t* cbcode;
     int len, lane;
     int spare;  // byte offset of this lane's spare accumulator
 };
 
 // Issues the loads of a batch's tile entries and of its window records
-// [chunk, chunk+64) (out-of-range record reads return zero).
+// [chunk, chunk+64) (out-of-range record reads return zero). CB: the tile's
+// precision is its column block's code (max|p| rule), else the map's.
+template <bool CB>
 __device__ __forceinline__ void load_batch_regs(const SweepCtx& c, const BatchHdr& h, int chunk, bool with_entry,
                                                 BatchRegs& r) {
     if (with_entry) {
         const int t = h.tile + min(c.lane, max(h.tiles - 1, 0));
         r.entry = c.tent[t];
-        r.prec = c.map[t];
-        r.toff = c.toff[t];
+        if (CB) {
+            r.prec = c.cbcode[c.tcol[t]];
+            r.toff = 0;
+        } else {
+            r.prec = c.map[t];
+            r.toff = c.toff[t];
+        }
     }
     const int wi = h.records + chunk + c.lane;
     const u32x2 m = __builtin_amdgcn_raw_buffer_load_b64(c.rmask, 8 * wi, 0, 0);
@@ -440,7 +451,7 @@ __device__ __forceinline__ void load_batch_regs(const SweepCtx& c, const BatchHd
 // position times the value width, rounded down to 4 bytes (a BF16 lane then
 // takes the half its byte offset selects); the widening is a bitwise blend.
 // Lanes past the batch add their zero product to a private spare accumulator.
-template <typename MetaT, int U>
+template <typename MetaT, int U, bool CB>
 __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R, int wi, int o0, bool next,
                                            const BatchHdr& Hn, BatchRegs& Rn) {
     int q[U];
@@ -470,7 +481,7 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
         hs[u] = (off & 2) << 3;
         raw[u] = __builtin_amdgcn_raw_buffer_load_b64(c.rv, off & ~3, 0, 0);
     }
-    if (next) load_batch_regs(c, Hn, 0, true, Rn);
+    if (next) load_batch_regs<CB>(c, Hn, 0, true, Rn);
     double xv[U];
     int racc[U];
 #pragma unroll
@@ -499,7 +510,10 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
 
 // The outputs are separate restrict arguments: the compiler may then treat
 // every other array as read-only for the whole launch.
-template <typename MetaT, int MODE, int MAXROWS>
+//
+// CB = true: the max|p| rule's kernels, where a tile's precision is its column
+// block's code for this product (values from the precision planes).
+template <typename MetaT, int MODE, int MAXROWS, bool CB = false>
 __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, double* __restrict__ y,
                                                                   double* __restrict__ partials) {
     // Row accumulators, then one spare per lane for lanes on a sentinel entry.
@@ -522,6 +536,12 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
     c.tent = a.tent;
     c.map = a.map;
     c.toff = a.toff;
+    c.tcol = a.tcol;
+    c.cbcode = a.cbcode;
+    // Values come from the precision planes under a uniform precision or the
+    // max|p| rule (which changes the map every iteration), else from the map's
+    // packed segment.
+    const bool from_planes = CB || uprec >= 0;
     c.desc = &s_desc[w][0];
     c.acc = reinterpret_cast<char*>(&s_acc[w][0]);
     c.spare = (MAXROWS + lane) * 8;
@@ -540,7 +560,7 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
     BatchRegs R{};
     if (b < b_end) {
         H = load_hdr(a.btab, b);
-        load_batch_regs(c, H, 0, true, R);
+        load_batch_regs<CB>(c, H, 0, true, R);
     }
     for (; b < b_end; ++b) {
         const bool more = b + 1 < b_end;
@@ -552,22 +572,20 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
             for (int i = lane; i < a.rows_per_group; i += kWave) s_acc[w][i] = 0.0;
             if (MODE == kSpmvCg && MAXROWS <= kWave && lane < nrows) p_own = a.x[row0 + lane];
         }
-        // Tile entries, the sentinel past the batch's tiles. Under a per-tile map
-        // the values come from the map's packed segment; under a uniform
-        // precision, from that precision's plane of the batch's segment.
+        // Tile entries, the sentinel past the batch's tiles.
         {
             const int p = uprec >= 0 ? uprec : R.prec;
             const bool tile = lane < H.tiles;
             int4 e;
             e.x = tile ? R.entry.x : kSentinelColumn;
             e.y = R.entry.y;
-            e.z = !tile ? kSentinelPlane : uprec >= 0 ? p * (10 - 2 * p) * H.len : R.toff;
+            e.z = !tile ? kSentinelPlane : from_planes ? p * (10 - 2 * p) * H.len : R.toff;
             e.w = tile ? 3 - p : 3;
             s_desc[w][lane] = e;
             if (lane == 0) s_desc[w][kTileBatch] = make_int4(kSentinelColumn, 0, kSentinelPlane, 3);
         }
         c.rv = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char*>((uprec >= 0 ? a.planes : a.packed) + (int64_t)H.segment * 16), (short)0,
+            const_cast<char*>((from_planes ? a.planes : a.packed) + (int64_t)H.segment * 16), (short)0,
             (int)segment_bytes(H.len), (int)kBufferConfig);
         c.rmt = batch_rsrc(a.meta, H.first, (int)sizeof(MetaT), H.len);
         c.len = H.len;
@@ -577,17 +595,17 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
         BatchRegs Rn{};
         int left = E, wi = 0, o0 = 0;
         for (; left >= kUnroll; left -= kUnroll, wi += kUnroll, o0 += kUnroll * kWave) {
-            if (wi > 0 && (wi & (kWave - 1)) == 0) load_batch_regs(c, H, wi, false, R);  // next 64 records
-            spmv_sweep<MetaT, kUnroll>(c, R, wi, o0, more && wi == 0, Hn, Rn);
+            if (wi > 0 && (wi & (kWave - 1)) == 0) load_batch_regs<CB>(c, H, wi, false, R);  // next 64 records
+            spmv_sweep<MetaT, kUnroll, CB>(c, R, wi, o0, more && wi == 0, Hn, Rn);
         }
         // The rest is 0 or one power of two below kUnroll (never crossing a record chunk).
-        if (wi > 0 && (wi & (kWave - 1)) == 0 && left > 0) load_batch_regs(c, H, wi, false, R);
+        if (wi > 0 && (wi & (kWave - 1)) == 0 && left > 0) load_batch_regs<CB>(c, H, wi, false, R);
         const bool first = more && wi == 0;
-        if (kUnroll > 8 && left == 8) spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1)>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 4 && left == 4) spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1)>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 2 && left == 2) spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1)>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1>(c, R, wi, o0, first, Hn, Rn);
-        if (more && E == 0) load_batch_regs(c, Hn, 0, true, Rn);  // a batch without windows
+        if (kUnroll > 8 && left == 8) spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1), CB>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 4 && left == 4) spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1), CB>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 2 && left == 2) spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1), CB>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1, CB>(c, R, wi, o0, first, Hn, Rn);
+        if (more && E == 0) load_batch_regs<CB>(c, Hn, 0, true, Rn);  // a batch without windows
         wave_lds_sync();
         if (H.flags & kBatchLastOfGroup) {
             for (int i = lane; i < nrows; i += kWave) {
@@ -939,6 +957,76 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             a.trace_k[slot] = st->k;
             st->ntrace = slot + 1;
+        }
+    }
+}
+
+// Per-segment max|p| rule (Sec. 4.7): the code of every column block from the
+// largest |p_j| in its segment (BF16 below lo, FP32 below hi, else FP64), and
+// counts of tiles per code into trace entry k. One thread per column block; a
+// whole block of even width is read with 16-byte loads (unrolled, so they are
+// all in flight together) when the vector is 16-byte aligned. Block b adds its
+// counts to the entry's slot b % kTraceBlocks (atomics on addresses shared by
+// a few blocks only). In a solve (solve = 1) the entry is the iteration that
+// multiplies p, and the kernel does nothing once the solve has stopped.
+struct PMagArgs {
+    const double* p;
+    uint8_t* cbcode;
+    const int32_t* tpcb;  // tiles in every column block
+    State* st;
+    int32_t* trace_k;
+    int32_t* trace_counts;
+    int64_t n;
+    int32_t C, ncb, solve, trace_cap;
+    double lo, hi;
+};
+
+__device__ inline double nan_max(double a, double b) { return (a > b || a != a) ? a : b; }
+__device__ inline int pmag_code(double m, double lo, double hi) { return m < lo ? 2 : (m < hi ? 1 : 0); }
+
+__global__ __launch_bounds__(kBlock) void pmag_kernel(PMagArgs a) {
+    __shared__ unsigned s_cnt[3];
+    int slot = -1;
+    if (a.solve) {
+        if (load_done(a.st)) return;
+        slot = a.st->k;
+        if (slot >= a.trace_cap) slot = -1;
+    }
+    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0u;
+    __syncthreads();
+    unsigned cnt[3] = {0u, 0u, 0u};
+    const bool pairs = (a.C & 1) == 0 && ((uintptr_t)a.p & 15) == 0;
+    for (int64_t J = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; J < a.ncb;
+         J += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j0 = J * a.C, j1 = min(j0 + a.C, a.n);
+        const unsigned tiles = (unsigned)a.tpcb[J];  // issued with the vector loads
+        double m = 0.0;
+        if (pairs && j1 - j0 == a.C) {
+            const double2* q = reinterpret_cast<const double2*>(a.p + j0);
+#pragma unroll 8
+            for (int e = 0; e < a.C / 2; ++e) {
+                const double2 v = q[e];
+                m = nan_max(m, nan_max(fabs(v.x), fabs(v.y)));
+            }
+        } else {
+            for (int64_t j = j0; j < j1; ++j) m = nan_max(m, fabs(a.p[j]));
+        }
+        const int code = pmag_code(m, a.lo, a.hi);
+        a.cbcode[J] = (uint8_t)code;
+        cnt[code] += tiles;
+    }
+    if (slot >= 0) {
+        atomicAdd(&s_cnt[0], cnt[0]);  // LDS atomics
+        atomicAdd(&s_cnt[1], cnt[1]);
+        atomicAdd(&s_cnt[2], cnt[2]);
+        __syncthreads();
+        if (threadIdx.x < 3) {
+            int32_t* out = a.trace_counts + ((size_t)slot * kTraceBlocks + blockIdx.x % kTraceBlocks) * 3;
+            atomicAdd(&out[threadIdx.x], (int32_t)s_cnt[threadIdx.x]);
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            a.trace_k[slot] = slot;
+            a.st->ntrace = slot + 1;
         }
     }
 }

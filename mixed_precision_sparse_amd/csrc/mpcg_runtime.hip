@@ -25,7 +25,7 @@ namespace dev = mpcg::dev;
 
 namespace {
 
-enum SchedKind { kSchedStatic = 0, kSchedResidual = 1, kSchedTileRule = 2 };
+enum SchedKind { kSchedStatic = 0, kSchedResidual = 1, kSchedTileRule = 2, kSchedPMag = 3 };
 
 struct DeviceBuffers {
     std::vector<void*> owned;
@@ -88,6 +88,10 @@ struct cg_handle {
     double* scores = nullptr;
     int32_t period = 0;
     double hi = 0.0, lo = 0.0;
+    uint8_t* cbcode = nullptr;  // [ncb] max|p| rule: code per column block
+    int32_t* tpcb = nullptr;    // [ncb] tiles per column block
+    int64_t ncb = 0;
+    double pm_lo = 0.0, pm_hi = 0.0;
 
     // Host staging for polling.
     int32_t* pinned = nullptr;  // [2 windows][2 ints] (done, k)
@@ -172,6 +176,8 @@ dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t*
     a.planes = h->planes;
     a.packed = h->packed;
     a.toff = h->toff;
+    a.tcol = h->tcol;
+    a.cbcode = h->sched == kSchedPMag ? h->cbcode : nullptr;
     a.win_mask = h->win_mask;
     a.win_tile = h->win_tile;
     a.x = x;
@@ -188,24 +194,56 @@ dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t*
     return a;
 }
 
-template <int MODE>
-void launch_spmv(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
+template <int MODE, bool CB>
+void launch_spmv_cb(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
     const int grid = spmv_grid(h);
     const bool wide = h->rows_per_group > 64;
     if (h->meta16) {
         if (wide)
-            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, dev::kMaxRows>), dim3(grid),
+            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, dev::kMaxRows, CB>), dim3(grid),
                                dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
         else
-            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, 64>), dim3(grid),
+            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, 64, CB>), dim3(grid),
                                dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
     } else if (wide) {
-        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, dev::kMaxRows>), dim3(grid),
+        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, dev::kMaxRows, CB>), dim3(grid),
                            dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
     } else {
-        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, 64>), dim3(grid), dim3(dev::kSpmvBlock), 0,
-                           s, a, a.y, a.partials);
+        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, 64, CB>), dim3(grid), dim3(dev::kSpmvBlock),
+                           0, s, a, a.y, a.partials);
     }
+}
+
+// The max|p| rule's kernels take the tile precisions from the column-block
+// codes; every other schedule uses the map (or a uniform precision).
+template <int MODE>
+void launch_spmv(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
+    if (a.cbcode)
+        launch_spmv_cb<MODE, true>(h, a, s);
+    else
+        launch_spmv_cb<MODE, false>(h, a, s);
+}
+
+// Column-block codes of the max|p| rule from vector v (solve = 1: in-solve,
+// trace entry k).
+void launch_pmag(cg_handle* h, const double* v, int solve, hipStream_t s) {
+    dev::PMagArgs a{};
+    a.p = v;
+    a.cbcode = h->cbcode;
+    a.tpcb = h->tpcb;
+    a.st = h->st;
+    a.trace_k = h->trace_k;
+    a.trace_counts = h->trace_counts;
+    a.n = h->n;
+    a.C = h->C;
+    a.ncb = (int32_t)h->ncb;
+    a.solve = solve;
+    a.trace_cap = (int32_t)h->trace_cap;
+    a.lo = h->pm_lo;
+    a.hi = h->pm_hi;
+    // One thread per column block, one pass.
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((h->ncb + dev::kBlock - 1) / dev::kBlock, 16384));
+    hipLaunchKernelGGL(dev::pmag_kernel, dim3((unsigned)blocks), dim3(dev::kBlock), 0, s, a);
 }
 
 // Packs the active map's values (every map change). solve = 1: only at the
@@ -337,6 +375,7 @@ void enqueue_iteration(cg_handle* h, int i, hipStream_t s) {
         hipLaunchKernelGGL(dev::cg_direction_kernel<true>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
     else
         hipLaunchKernelGGL(dev::cg_direction_kernel<false>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
+    if (h->sched == kSchedPMag) launch_pmag(h, h->p, 1, s);  // the map of the next iteration
 }
 
 int ensure_graph(cg_handle* h) {
@@ -740,6 +779,14 @@ extern "C" int cg_get_active_map(const cg_handle* h, uint8_t* out) {
         std::memset(out, hs.uprec, h->T);
         return CG_OK;
     }
+    if (h->sched == kSchedPMag) {  // the column-block codes last computed, per tile
+        std::vector<uint8_t> code(std::max<int64_t>(h->ncb, 1));
+        std::vector<int32_t> tcol(std::max<int64_t>(h->T, 1));
+        HIP_CHECK(hipMemcpy(code.data(), h->cbcode, h->ncb, hipMemcpyDeviceToHost));
+        if (h->T) HIP_CHECK(hipMemcpy(tcol.data(), h->tcol, sizeof(int32_t) * h->T, hipMemcpyDeviceToHost));
+        for (int64_t t = 0; t < h->T; ++t) out[t] = code[tcol[t]];
+        return CG_OK;
+    }
     HIP_CHECK(hipMemcpy(out, h->map, h->T, hipMemcpyDeviceToHost));
     return CG_OK;
 }
@@ -797,6 +844,30 @@ extern "C" int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const dou
     return upload_schedule(h);
 }
 
+extern "C" int cg_set_schedule_pmag(cg_handle* h, double lo, double hi) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_set_schedule_pmag: h is NULL");
+    if (std::isnan(lo) || std::isnan(hi) || !(lo <= hi))
+        return fail(CG_EINVAL, "cg_set_schedule_pmag: need lo <= hi (no NaN)");
+    if (!h->cbcode) {
+        h->ncb = (h->n + h->C - 1) / h->C;
+        std::vector<int32_t> tcol(std::max<int64_t>(h->T, 1));
+        if (h->T) HIP_CHECK(hipMemcpy(tcol.data(), h->tcol, sizeof(int32_t) * h->T, hipMemcpyDeviceToHost));
+        std::vector<int32_t> tpcb(h->ncb, 0);
+        for (int64_t t = 0; t < h->T; ++t) ++tpcb[tcol[t]];
+        int rc = dalloc(h, &h->cbcode, h->ncb);
+        if (rc == CG_OK) rc = dalloc(h, &h->tpcb, h->ncb);
+        if (rc != CG_OK) return rc;
+        HIP_CHECK(hipMemcpy(h->tpcb, tpcb.data(), sizeof(int32_t) * h->ncb, hipMemcpyHostToDevice));
+        HIP_CHECK(hipMemset(h->cbcode, 0, h->ncb));
+    }
+    h->pm_lo = lo;
+    h->pm_hi = hi;
+    h->sched = kSchedPMag;
+    drop_graph(h);  // the thresholds are baked into the captured launches
+    return upload_schedule(h);
+}
+
 extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_eval_tile_rule: h is NULL");
@@ -819,6 +890,7 @@ extern "C" int cg_spmv(cg_handle* h, const double* x, double* y, void* stream) {
     mpcg::clear_error();
     if (!h || !x || !y) return fail(CG_EINVAL, "cg_spmv: NULL argument");
     if (ranges_overlap(x, y, sizeof(double) * h->n)) return fail(CG_EINVAL, "cg_spmv: y overlaps x");
+    if (h->sched == kSchedPMag) launch_pmag(h, x, 0, static_cast<hipStream_t>(stream));  // map from x
     dev::SpmvArgs a = spmv_args(h, x, y, &h->st->spmv_uprec);
     launch_spmv<dev::kSpmvPlain>(h, a, static_cast<hipStream_t>(stream));
     HIP_CHECK(hipGetLastError());
@@ -846,6 +918,7 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
     int64_t need_trace = 16;
     if (h->sched == kSchedTileRule) need_trace = maxit / h->period + 2;
     if (h->sched == kSchedResidual) need_trace = (int64_t)h->stage_prec.size() + 1;
+    if (h->sched == kSchedPMag) need_trace = (int64_t)maxit + 2;
     if (need_trace > h->trace_cap) {
         dfree(h, h->trace_k);
         dfree(h, h->trace_counts);
@@ -886,6 +959,7 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
     }
     hipLaunchKernelGGL(dev::cg_init_kernel, dim3(vec_grid(h)), dim3(dev::kBlock), 0, s, va);
     hipLaunchKernelGGL(dev::cg_init_finish_kernel, dim3(1), dim3(dev::kBlock), 0, s, va);
+    if (h->sched == kSchedPMag) launch_pmag(h, h->p, 1, s);  // the map of iteration 0 from p_0
     HIP_CHECK(hipGetLastError());
     const bool static_map = h->sched == kSchedStatic;
     if (static_map) {

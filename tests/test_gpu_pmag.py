@@ -1,0 +1,155 @@
+"""GPU parity of the per-segment max|p| rule (EvoCG paper, Sec. 4.7) against the oracle.
+
+The rule's decisions are exact on both sides (a maximum of absolute values,
+compared in FP64), so for a given vector the map must match bit for bit; the
+SpMV then meets the usual 1e-13 * (|A||x|)_i bound. Inside CG the direction
+vectors of the two sides differ by rounding, so a column block whose maximum
+sits on a threshold may be classified differently once the trajectories have
+drifted: per-iteration precision counts are compared while the residual
+histories agree, as for the windowed tile rule.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import scipy.sparse as sp
+
+from gen import make_workload
+from oracle import cg as ocg, maps as omaps, spmv as ospmv, tilecsc as otc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mpcg = pytest.importorskip("mixed_precision_sparse_amd")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    return torch.device("cuda:0")
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _random_spd(n, density, seed, R, C):
+    rng = np.random.default_rng(seed)
+    M = sp.random(n, n, density=density, random_state=np.random.RandomState(seed), format="csr")
+    M = (M + M.T).tocsr()
+    M = (M + sp.diags(np.abs(M).sum(axis=1).A1 + 1.0)).tocsr()
+    M.sort_indices()
+    return M
+
+
+CASES = [("cfg2", None), ("cfg3", None), ("cfg5", None), ("C12", (300, 0.02, 8, 12)), ("C128", (700, 0.01, 64, 128))]
+
+
+def _case(name, spec):
+    if spec is None:
+        w = make_workload(int(name[3:]), "small")
+        return w.A.n, w.A.indptr, w.A.indices, w.A.data, w.R, w.C
+    n, dens, R, C = spec
+    M = _random_spd(n, dens, 5, R, C)
+    return n, M.indptr.astype(np.int64), M.indices.astype(np.int32), M.data, R, C
+
+
+@pytest.mark.parametrize("name,spec", CASES)
+def test_pmag_spmv_and_map_match_oracle(name, spec, dev):
+    n, ip, ind, val, R, C = _case(name, spec)
+    log(f"pmag spmv {name} n={n} R={R} C={C}")
+    L = mpcg.cg_tilecsc_from_csr(n, ip, ind, val, R, C)
+    Lo = otc.build(n, ip, ind, val, R, C)
+    S = mpcg.Solver(L)
+    rng = np.random.default_rng(11)
+    lo, hi = 1e-4, 1e-2
+    S.cg_set_schedule_pmag(lo, hi)
+    ncb = -(-n // C)
+    for trial in range(3):
+        # Every column block gets its own scale (FP64, FP32 and BF16 classes in
+        # turn); one block's maximum is planted exactly on lo (FP32 by the rule)
+        # and one exactly on hi (FP64).
+        scale = np.array([1.0, 1e-3, 1e-5])[(np.arange(ncb) + trial) % 3]
+        x = rng.uniform(-1, 1, n) * np.repeat(scale, C)[:n]
+        J_lo = int(np.nonzero(scale == 1e-5)[0][0])
+        J_hi = int(np.nonzero(scale == 1e-3)[0][0])
+        x[J_lo * C] = lo
+        x[J_hi * C] = -hi
+        ref_map = omaps.pmag_rule(x, C, Lo.tile_col_idx, lo, hi)
+        xd = torch.from_numpy(x).to(dev)
+        yd = torch.full_like(xd, float("nan"))
+        S.cg_spmv(xd, yd)
+        torch.cuda.synchronize()
+        assert np.array_equal(S.cg_get_active_map(), ref_map)
+        y_ref = ospmv.spmv(Lo, ip, ind, ref_map, x)
+        bound = 1e-13 * ospmv.abs_bound(ip, ind, val, x)
+        assert np.all(np.abs(yd.cpu().numpy() - y_ref) <= bound)
+        if trial == 0:
+            assert set(np.unique(ref_map)) == {0, 1, 2}
+    S.close()
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_pmag_reduces_to_static_maps_bit_for_bit(cfg, dev):
+    """lo = hi = 0 is the FP64 map and lo = hi = inf the BF16 map, on the GPU as well."""
+    w = make_workload(cfg, "small")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    bd = torch.from_numpy(w.b).to(dev)
+    for lo, code in ((0.0, 0), (math.inf, 2)):
+        S1 = mpcg.Solver(L)
+        S1.cg_set_schedule_pmag(lo, lo)
+        x1 = torch.zeros_like(bd)
+        st1, K1, h1 = S1.cg_solve(bd, x1, w.tol, 400)
+        S2 = mpcg.Solver(L, np.full(L.T, code, np.uint8))
+        x2 = torch.zeros_like(bd)
+        st2, K2, h2 = S2.cg_solve(bd, x2, w.tol, 400)
+        log(f"cfg{cfg} pmag lo=hi={lo}: {st1} K={K1}; static code {code}: {st2} K={K2}")
+        assert (st1, K1) == (st2, K2)
+        assert np.array_equal(h1, h2)
+        assert torch.equal(x1, x2)
+        ks, counts = S1.cg_get_map_trace()
+        assert ks.tolist() == list(range(K1))  # one entry per iteration run
+        assert all(c[code] == L.T for c in counts)
+        S1.close()
+        S2.close()
+
+
+@pytest.mark.parametrize("cfg,lo,hi", [(2, 1e-4, 1e-2), (3, 1e-3, 1e-1)])
+def test_pmag_cg_matches_oracle(cfg, lo, hi, dev):
+    w = make_workload(cfg, "small")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    Lo = otc.build(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    maxit = 10000
+    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, w.b, ocg.PMagSchedule(Lo.C, Lo.tile_col_idx, lo, hi),
+                    w.tol, maxit, keep_maps=False)
+    S = mpcg.Solver(L)
+    S.cg_set_schedule_pmag(lo, hi)
+    bd = torch.from_numpy(w.b).to(dev)
+    xd = torch.zeros_like(bd)
+    status, K, hist = S.cg_solve(bd, xd, w.tol, maxit)
+    x = xd.cpu().numpy()
+    tr = float(np.linalg.norm(w.b - A.to_scipy() @ x) / np.linalg.norm(w.b))
+    log(f"cfg{cfg} pmag: GPU {status} K={K} true={tr:.3e}; oracle {ref.status} K={ref.K} "
+        f"true={ref.true_residual:.3e}")
+    assert status == ref.status
+    assert abs(K - ref.K) <= max(1, math.floor(0.02 * ref.K))
+    a, b = max(tr, w.tol), max(ref.true_residual, w.tol)
+    assert abs(a - b) <= 1e-2 * b
+    ks, counts = S.cg_get_map_trace()
+    agree = 0
+    for k in range(min(K, ref.K)):
+        if abs(hist[k] - ref.hist[k]) > 1e-9 * ref.hist[k]:
+            break
+        assert ks[k] == k and counts[k].tolist() == ref.windows[k][1], k
+        agree += 1
+    log(f"cfg{cfg} pmag: {agree} of {ref.K} iterations' maps compared while trajectories agree")
+    assert agree >= 5
+    assert sum(c[1] + c[2] for _, c, _ in ref.windows) > 0  # the rule did lower some tiles
+    S.close()
