@@ -73,15 +73,24 @@ class TileRuleSchedule:
 
 
 class PMagSchedule:
-    """The per-segment max|p| rule (Sec. 4.7), re-applied at every iteration to the
-    direction p_k that the iteration's SpMV multiplies."""
+    """The per-segment max|p| rule (Sec. 4.7), applied to the direction p_k that the
+    iteration's SpMV multiplies, at every iteration whose index is a multiple of
+    ``period`` and reused in between (Sec. 3.4 "Interval Reuse Scheduling").
+    ``column_codes``, when a list, receives every evaluation's per-column-block
+    codes."""
 
-    def __init__(self, C, tile_col_idx, lo, hi):
+    def __init__(self, C, tile_col_idx, lo, hi, period=1, column_codes=None):
         self.C = int(C)
         self.tcol = np.asarray(tile_col_idx)
         self.lo, self.hi = float(lo), float(hi)
+        self.period = int(period)
+        self.column_codes = column_codes
 
     def map_for(self, k, rho, T, p=None):
+        if k % self.period != 0:
+            return None
+        if self.column_codes is not None:
+            self.column_codes.append(_maps.pmag_column_codes(p, self.C, self.lo, self.hi))
         return _maps.pmag_rule(p, self.C, self.tcol, self.lo, self.hi)
 
 
@@ -208,5 +217,5 @@ def schedule_for(spec: dict, L: TileCSC, scores=None, static=None):
     if kind == "tile_rule":
         return TileRuleSchedule(scores, spec["period"], spec["hi"], spec["lo"])
     if kind == "pmag":
-        return PMagSchedule(L.C, L.tile_col_idx, spec["lo"], spec["hi"])
+        return PMagSchedule(L.C, L.tile_col_idx, spec["lo"], spec["hi"], spec.get("period", 1))
     raise ValueError(kind)

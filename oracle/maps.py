@@ -84,6 +84,60 @@ def pmag_rule(p: np.ndarray, C: int, tile_col_idx: np.ndarray, lo: float, hi: fl
     return out
 
 
+def pmag_column_codes(p: np.ndarray, C: int, lo: float, hi: float) -> np.ndarray:
+    """The max|p| rule's code of every column block (uint8[ceil(n/C)]); see pmag_rule."""
+    p = np.abs(np.asarray(p, dtype=np.float64))
+    ncb = -(-p.size // C)
+    pad = np.zeros(ncb * C)
+    pad[:p.size] = p
+    m = pad.reshape(ncb, C).max(axis=1)
+    out = np.full(ncb, FP64, dtype=np.uint8)
+    out[m < hi] = FP32
+    out[m < lo] = BF16
+    return out
+
+
+def delayed_upward_fraction(codes: np.ndarray, interval: int) -> float:
+    """Interval reuse (Sec. 3.4 "Interval Reuse Scheduling") applied to a per-iteration record.
+
+    ``codes[k, J]`` is column block J's code at iteration k of a per-iteration
+    run (0 = FP64 > 1 = FP32 > 2 = BF16 in precision). An upward transition is
+    a (k, J) with k >= 1 and codes[k, J] < codes[k-1, J]. Reusing decisions over
+    windows of ``interval`` iterations gives iteration k the decision of its
+    window start s = (k // interval) * interval; the transition is delayed when
+    that decision is of lower precision than the one at k (codes[s, J] >
+    codes[k, J]). Returns delayed / upward, or 0 when there is no upward
+    transition.
+    """
+    codes = np.asarray(codes)
+    K = codes.shape[0]
+    if K < 2:
+        return 0.0
+    up = codes[1:] < codes[:-1]
+    ks = np.arange(1, K)
+    start = codes[(ks // int(interval)) * int(interval)]
+    delayed = up & (start > codes[1:])
+    n_up = int(up.sum())
+    return float(delayed.sum()) / n_up if n_up else 0.0
+
+
+def select_reuse_interval(codes: np.ndarray, max_fraction: float = 0.1) -> tuple:
+    """K* (Sec. 3.4): the largest candidate interval 1, 2, 4, ... (below the number
+    of recorded iterations) whose delayed-upward fraction is below ``max_fraction``.
+
+    Returns (K*, [(interval, fraction), ...]) over the candidates tried.
+    """
+    K = np.asarray(codes).shape[0]
+    best, table, interval = 1, [], 1
+    while interval < max(K, 2):
+        f = delayed_upward_fraction(codes, interval)
+        table.append((interval, f))
+        if f < max_fraction:
+            best = interval
+        interval *= 2
+    return best, table
+
+
 def tile_rule(scores: np.ndarray, rho: float, hi: float = 1e-3, lo: float = 1e-6) -> np.ndarray:
     """Per-tile re-selection: v_t = s_t * rho; BF16 if v_t > hi, FP32 if v_t > lo, else FP64."""
     v = np.asarray(scores, dtype=np.float64) * float(rho)

@@ -10,6 +10,8 @@ confirms, iteration by iteration, that the map in force is the rule applied
 to the direction that iteration multiplies.
 """
 
+import math
+
 import numpy as np
 import pytest
 import scipy.sparse as sp
@@ -93,3 +95,81 @@ def test_pmag_spec_builds_the_schedule():
     s = cg.schedule_for({"kind": "pmag", "lo": 1e-9, "hi": 1e-8}, L)
     p = np.linspace(-1, 1, A.n)
     assert np.array_equal(s.map_for(0, 1.0, L.T, p), maps.pmag_rule(p, L.C, L.tile_col_idx, 1e-9, 1e-8))
+
+
+# ---------------------------------------------------------------------------
+# Interval reuse and the offline K* selection (Sec. 3.4).
+# ---------------------------------------------------------------------------
+def _delayed_fraction_loops(codes, interval):
+    up = delayed = 0
+    for k in range(1, len(codes)):
+        s = (k // interval) * interval
+        for J in range(len(codes[0])):
+            if codes[k][J] < codes[k - 1][J]:
+                up += 1
+                if codes[s][J] > codes[k][J]:
+                    delayed += 1
+    return delayed / up if up else 0.0
+
+
+def test_delayed_fraction_hand_cases():
+    # One block climbing BF16 -> FP32 at k = 3 and FP32 -> FP64 at k = 6.
+    c = np.array([[2], [2], [2], [1], [1], [1], [0], [0], [0], [0], [0], [0], [0], [0], [0], [0]], np.uint8)
+    assert maps.delayed_upward_fraction(c, 1) == 0.0
+    assert maps.delayed_upward_fraction(c, 2) == 0.5   # k = 3 waits for k = 4; k = 6 is a window start
+    assert maps.delayed_upward_fraction(c, 4) == 1.0   # both wait
+    assert maps.select_reuse_interval(c)[0] == 1
+    # Transitions only at multiples of 8: reuse up to 8 delays nothing.
+    c = np.full((24, 3), 2, np.uint8)
+    c[8:, 0] = 1
+    c[16:, 1] = 0
+    # At 16 the rise at k = 8 waits for k = 16, the one at k = 16 starts a window.
+    assert [f for _, f in maps.select_reuse_interval(c)[1]] == [0.0, 0.0, 0.0, 0.0, 0.5]
+    assert maps.select_reuse_interval(c)[0] == 8
+    # Only downward moves: nothing to delay, the largest candidate wins.
+    c = np.array([[0, 0], [0, 1], [1, 1], [2, 2], [2, 2]], np.uint8)
+    best, table = maps.select_reuse_interval(c)
+    assert best == 4 and [i for i, _ in table] == [1, 2, 4]
+
+
+def test_delayed_fraction_matches_loops():
+    rng = np.random.default_rng(9)
+    for trial in range(5):
+        c = np.cumsum(rng.integers(-1, 2, (40, 7)), axis=0) % 3
+        c = c.astype(np.uint8)
+        for interval in (1, 2, 3, 4, 8, 16):
+            assert math.isclose(maps.delayed_upward_fraction(c, interval),
+                                _delayed_fraction_loops(c.tolist(), interval), rel_tol=0, abs_tol=0)
+
+
+def test_select_threshold_is_strict():
+    # Exactly 1 of 10 upward transitions delayed at interval 2: 0.1 is not below 0.1.
+    c = np.full((21, 10), 2, np.uint8)
+    for J in range(10):
+        k = 2 * (J + 1) if J else 1  # block 0 rises at k = 1 (delayed at interval 2), the rest at even k
+        c[k:, J] = 1
+    assert maps.delayed_upward_fraction(c, 2) == 0.1
+    assert maps.select_reuse_interval(c, 0.1)[0] == 1
+    assert maps.select_reuse_interval(c, 0.11)[0] >= 2
+
+
+def test_pmag_schedule_with_period_reuses_the_window_start_map():
+    w, A, L = _cfg_small(2)
+    lo, hi, period = 1e-4, 1e-2, 4
+    recorded = []
+    starts = {}
+
+    def hook(k, x, r, p, q, alpha):
+        if k % period == 0:
+            starts[k] = p.copy()
+        m = maps.pmag_rule(starts[(k // period) * period], L.C, L.tile_col_idx, lo, hi)
+        assert np.array_equal(q, spmv.spmv(L, A.indptr, A.indices, m, p))
+
+    res = cg.solve(L, A.indptr, A.indices, A.data, w.b,
+                   cg.PMagSchedule(L.C, L.tile_col_idx, lo, hi, period, recorded), w.tol, 400, trace=hook,
+                   keep_maps=False)
+    assert res.status == "converged"
+    assert [k for k, _, _ in res.windows] == list(range(0, res.K, period))
+    assert len(recorded) == len(res.windows)
+    for (k, _, _), codes in zip(res.windows, recorded):
+        assert np.array_equal(codes, maps.pmag_column_codes(starts[k], L.C, lo, hi))
