@@ -158,14 +158,38 @@ int cg_set_schedule_residual(cg_handle* h, int32_t nstage, const double* thresho
 
 /* Per-segment max|p| rule (Sec. 4.7, the residual-threshold rule the paper
  * compares against; its setting is lo = eps/10, hi = eps for the tolerance
- * eps): before every SpMV each tile is given BF16 if the largest |p_j| of its
- * column block's segment of the multiplied vector is < lo, FP32 if it is <
- * hi, else FP64. In cg_solve the vector is the iteration's direction p_k and
- * the map trace gets one entry per iteration; cg_spmv applies the rule to its
- * input x. The value planes are read directly (no repacking per iteration).
- * Requires lo <= hi, no NaN (infinities allowed). Errors: CG_EINVAL,
- * CG_ENOMEM, CG_EDEVICE. */
-int cg_set_schedule_pmag(cg_handle* h, double lo, double hi);
+ * eps): each tile is given BF16 if the largest |p_j| of its column block's
+ * segment of the multiplied vector is < lo, FP32 if it is < hi, else FP64.
+ * In cg_solve the rule is evaluated on the direction p_k at every iteration k
+ * that is a multiple of `period` and the map is reused in between (Sec. 3.4
+ * "Interval Reuse Scheduling"); the map trace gets one entry per evaluation.
+ * cg_spmv applies the rule to its input x. The value planes are read directly
+ * (no repacking per evaluation). Requires lo <= hi, no NaN (infinities
+ * allowed), period >= 1. Errors: CG_EINVAL, CG_ENOMEM, CG_EDEVICE. */
+int cg_set_schedule_pmag(cg_handle* h, double lo, double hi, int32_t period);
+
+/* With enable != 0, the next cg_solve under the max|p| rule keeps every
+ * evaluation's column-block codes (uint8[ceil(n/C)] each, 0/1/2) in device
+ * memory for cg_get_column_codes. */
+int cg_record_column_codes(cg_handle* h, int32_t enable);
+
+/* Copies up to `cap` recorded evaluations (row e = the codes used from
+ * iteration e * period) into host out[cap][ceil(n/C)]; returns the number
+ * recorded by the last solve (0 when nothing was recorded). */
+int cg_get_column_codes(const cg_handle* h, int32_t cap, uint8_t* out);
+
+/* Offline reuse interval K* (Sec. 3.4 "Interval Reuse Scheduling"), host only.
+ * codes: host uint8[nrec][ncb], the column-block codes of a per-iteration run
+ * (0 = FP64, 1 = FP32, 2 = BF16). An upward transition is a (k >= 1, J) with
+ * codes[k][J] < codes[k-1][J]; reusing the window-start decision over windows
+ * of K iterations delays it when codes[(k/K)*K][J] > codes[k][J]. For
+ * K = 1, 2, 4, ... below max(nrec, 2) the delayed fraction (0 without upward
+ * transitions) is written to intervals[c], fractions[c] for c < cap (either
+ * may be NULL); *kstar = the largest K whose fraction is < max_fraction (the
+ * paper uses 0.1). Returns the number of candidates. Errors: CG_EINVAL (NULL
+ * codes or kstar, negative sizes, a code > 2). */
+int cg_select_reuse_interval(const uint8_t* codes, int32_t nrec, int64_t ncb, double max_fraction,
+                             int32_t* kstar, int32_t cap, int32_t* intervals, double* fractions);
 
 /* Windowed per-tile rule (Sec. 3.4 "Interval Reuse Scheduling": a map chosen
  * at a window start is kept for the window). At every k with k % period == 0,

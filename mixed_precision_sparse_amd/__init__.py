@@ -176,9 +176,20 @@ class Solver:
         check(_lib.load().cg_set_schedule_tile_rule(self._h, int(period), _ptr(sc), float(hi),
                                                     float(lo)))
 
-    def cg_set_schedule_pmag(self, lo, hi):
-        """Per-segment max|p| rule before every SpMV (see include/mpcg.h)."""
-        check(_lib.load().cg_set_schedule_pmag(self._h, float(lo), float(hi)))
+    def cg_set_schedule_pmag(self, lo, hi, period=1):
+        """Per-segment max|p| rule, evaluated every `period` iterations (see include/mpcg.h)."""
+        check(_lib.load().cg_set_schedule_pmag(self._h, float(lo), float(hi), int(period)))
+
+    def cg_record_column_codes(self, enable=True):
+        check(_lib.load().cg_record_column_codes(self._h, 1 if enable else 0))
+
+    def cg_get_column_codes(self, cap=100000):
+        """Recorded column-block codes of the last solve, uint8[evaluations][ceil(n/C)]."""
+        ncb = -(-self.n // self.C)
+        n = check(_lib.load().cg_get_column_codes(self._h, 0, None))
+        out = np.empty((min(n, cap), ncb), dtype=np.uint8)
+        check(_lib.load().cg_get_column_codes(self._h, int(out.shape[0]), _ptr(out)))
+        return out
 
     def cg_eval_tile_rule(self, rho):
         check(_lib.load().cg_eval_tile_rule(self._h, float(rho)))
@@ -240,6 +251,21 @@ def cg_create(A: TileCSC, precision_map=None, **kw) -> Solver:
 
 def cg_spmv(h: Solver, x, y, stream=None):
     h.cg_spmv(x, y, stream)
+
+
+def cg_select_reuse_interval(codes, max_fraction=0.1):
+    """K* from a per-iteration record of column-block codes; returns (K*, [(K, fraction), ...])."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    if c.ndim != 2:
+        raise ValueError("codes must be [records][column blocks]")
+    kstar = ct.c_int32()
+    cap = 40
+    iv = np.empty(cap, dtype=np.int32)
+    fr = np.empty(cap, dtype=np.float64)
+    n = check(_lib.load().cg_select_reuse_interval(_ptr(c), int(c.shape[0]), int(c.shape[1]),
+                                                   float(max_fraction), ct.byref(kstar), cap,
+                                                   _ptr(iv), _ptr(fr)))
+    return int(kstar.value), [(int(iv[i]), float(fr[i])) for i in range(min(n, cap))]
 
 
 def cg_solve(h: Solver, b, x0, tol, maxit, x, stream=None):

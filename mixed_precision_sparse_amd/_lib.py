@@ -48,7 +48,10 @@ SIGNATURES = {
     "cg_set_schedule_residual": (ct.c_int, [vp, i32, vp, vp]),
     "cg_set_schedule_tile_rule": (ct.c_int, [vp, i32, vp, f64, f64]),
     "cg_eval_tile_rule": (ct.c_int, [vp, f64]),
-    "cg_set_schedule_pmag": (ct.c_int, [vp, f64, f64]),
+    "cg_set_schedule_pmag": (ct.c_int, [vp, f64, f64, i32]),
+    "cg_record_column_codes": (ct.c_int, [vp, i32]),
+    "cg_get_column_codes": (ct.c_int, [vp, i32, vp]),
+    "cg_select_reuse_interval": (ct.c_int, [vp, i32, ct.c_int64, f64, vp, i32, vp, vp]),
     "cg_clear_schedule": (ct.c_int, [vp]),
     "cg_spmv": (ct.c_int, [vp, vp, vp, vp]),
     "cg_solve": (ct.c_int, [vp, vp, vp, f64, i32, vp, ct.POINTER(i32), vp, vp]),

@@ -963,12 +963,14 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
 
 // Per-segment max|p| rule (Sec. 4.7): the code of every column block from the
 // largest |p_j| in its segment (BF16 below lo, FP32 below hi, else FP64), and
-// counts of tiles per code into trace entry k. One thread per column block; a
+// counts of tiles per code into the trace. One thread per column block; a
 // whole block of even width is read with 16-byte loads (unrolled, so they are
 // all in flight together) when the vector is 16-byte aligned. Block b adds its
 // counts to the entry's slot b % kTraceBlocks (atomics on addresses shared by
-// a few blocks only). In a solve (solve = 1) the entry is the iteration that
-// multiplies p, and the kernel does nothing once the solve has stopped.
+// a few blocks only). In a solve (solve = 1) the rule is evaluated at the
+// iterations k that are multiples of the period, for the direction p_k, into
+// trace entry k / period (with the codes themselves kept in `history` when it
+// is set); it does nothing once the solve has stopped.
 struct PMagArgs {
     const double* p;
     uint8_t* cbcode;
@@ -976,8 +978,9 @@ struct PMagArgs {
     State* st;
     int32_t* trace_k;
     int32_t* trace_counts;
+    uint8_t* history;  // [trace_cap][ncb] or null
     int64_t n;
-    int32_t C, ncb, solve, trace_cap;
+    int32_t C, ncb, solve, trace_cap, period;
     double lo, hi;
 };
 
@@ -987,11 +990,15 @@ __device__ inline int pmag_code(double m, double lo, double hi) { return m < lo 
 __global__ __launch_bounds__(kBlock) void pmag_kernel(PMagArgs a) {
     __shared__ unsigned s_cnt[3];
     int slot = -1;
+    int k = 0;
     if (a.solve) {
         if (load_done(a.st)) return;
-        slot = a.st->k;
+        k = a.st->k;
+        if (k % a.period != 0) return;
+        slot = k / a.period;
         if (slot >= a.trace_cap) slot = -1;
     }
+    uint8_t* hist = slot >= 0 && a.history ? a.history + (size_t)slot * a.ncb : nullptr;
     if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0u;
     __syncthreads();
     unsigned cnt[3] = {0u, 0u, 0u};
@@ -1013,6 +1020,7 @@ __global__ __launch_bounds__(kBlock) void pmag_kernel(PMagArgs a) {
         }
         const int code = pmag_code(m, a.lo, a.hi);
         a.cbcode[J] = (uint8_t)code;
+        if (hist) hist[J] = (uint8_t)code;
         cnt[code] += tiles;
     }
     if (slot >= 0) {
@@ -1025,7 +1033,7 @@ __global__ __launch_bounds__(kBlock) void pmag_kernel(PMagArgs a) {
             atomicAdd(&out[threadIdx.x], (int32_t)s_cnt[threadIdx.x]);
         }
         if (blockIdx.x == 0 && threadIdx.x == 0) {
-            a.trace_k[slot] = slot;
+            a.trace_k[slot] = k;
             a.st->ntrace = slot + 1;
         }
     }

@@ -92,6 +92,10 @@ struct cg_handle {
     int32_t* tpcb = nullptr;    // [ncb] tiles per column block
     int64_t ncb = 0;
     double pm_lo = 0.0, pm_hi = 0.0;
+    int32_t pm_period = 1;
+    bool rec_cb = false;            // keep every evaluation's column-block codes
+    uint8_t* cbhist = nullptr;      // [cbhist_rows][ncb]
+    int64_t cbhist_rows = 0;
 
     // Host staging for polling.
     int32_t* pinned = nullptr;  // [2 windows][2 ints] (done, k)
@@ -99,6 +103,7 @@ struct cg_handle {
 
     // Captured window graph.
     hipGraphExec_t graph = nullptr;
+    hipGraphExec_t graph_rule = nullptr;  // the window that ends with a max|p| evaluation (long periods)
     int graph_window = 0;
     int graph_period = 0;
     int graph_sched = -1;
@@ -239,6 +244,8 @@ void launch_pmag(cg_handle* h, const double* v, int solve, hipStream_t s) {
     a.ncb = (int32_t)h->ncb;
     a.solve = solve;
     a.trace_cap = (int32_t)h->trace_cap;
+    a.period = h->pm_period;
+    a.history = solve && h->rec_cb ? h->cbhist : nullptr;
     a.lo = h->pm_lo;
     a.hi = h->pm_hi;
     // One thread per column block, one pass.
@@ -337,23 +344,35 @@ int upload_schedule(cg_handle* h) {
 
 void drop_graph(cg_handle* h) {
     if (h->graph) (void)hipGraphExecDestroy(h->graph);
+    if (h->graph_rule) (void)hipGraphExecDestroy(h->graph_rule);
     h->graph = nullptr;
+    h->graph_rule = nullptr;
     h->graph_window = 0;
     h->graph_sched = -1;
 }
 
 // Iterations per enqueued window. Under a tile rule it is a multiple of the
 // rule's period, so the map steps fall on the same iterations of every window.
+// A max|p| rule whose period is a multiple of the window: windows stay short
+// and only the windows that end just before a multiple of the period run the
+// rule (a second captured graph), so a long period does not lengthen the
+// windows and with them the no-op iterations after convergence.
+bool pmag_split(const cg_handle* h) {
+    return h->sched == kSchedPMag && h->pm_period > h->window && h->pm_period % h->window == 0;
+}
+
 int solve_window(const cg_handle* h) {
-    if (h->sched != kSchedTileRule) return h->window;
-    return std::max(1, h->window / h->period) * h->period;
+    if (pmag_split(h)) return h->window;
+    const int period = h->sched == kSchedTileRule ? h->period : h->sched == kSchedPMag ? h->pm_period : 1;
+    return std::max(1, h->window / period) * period;
 }
 
 // One CG iteration: [map window step] -> SpMV with fused p.q and alpha ->
 // x/r update with fused r.r (r.z), beta, rho and stop flag -> new direction.
 // i is the iteration's index in its window (the solve's k modulo the window
-// length while the solve runs).
-void enqueue_iteration(cg_handle* h, int i, hipStream_t s) {
+// length while the solve runs). rule_at_end: under a split max|p| rule, this
+// window's last iteration is followed by the rule's evaluation.
+void enqueue_iteration(cg_handle* h, int i, hipStream_t s, bool rule_at_end = false) {
     if (h->sched == kSchedTileRule && i % h->period == 0) {
         dev::MapArgs ma = map_args(h, 0.0, 1);
         hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, s, ma);
@@ -375,30 +394,39 @@ void enqueue_iteration(cg_handle* h, int i, hipStream_t s) {
         hipLaunchKernelGGL(dev::cg_direction_kernel<true>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
     else
         hipLaunchKernelGGL(dev::cg_direction_kernel<false>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
-    if (h->sched == kSchedPMag) launch_pmag(h, h->p, 1, s);  // the map of the next iteration
+    if (h->sched == kSchedPMag) {  // the map of the next window (iteration i + 1 starts it)
+        if (pmag_split(h) ? (rule_at_end && i == h->window - 1) : (i + 1) % h->pm_period == 0)
+            launch_pmag(h, h->p, 1, s);
+    }
 }
 
 int ensure_graph(cg_handle* h) {
     const int W = solve_window(h);
-    if (h->graph && h->graph_window == W && h->graph_sched == h->sched && h->graph_period == h->period)
+    const int period = h->sched == kSchedPMag ? h->pm_period : h->period;
+    if (h->graph && h->graph_window == W && h->graph_sched == h->sched && h->graph_period == period)
         return CG_OK;
     drop_graph(h);
-    hipGraph_t g = nullptr;
-    HIP_CHECK(hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
-    for (int i = 0; i < W; ++i) enqueue_iteration(h, i, h->stream);
-    hipError_t e = hipStreamEndCapture(h->stream, &g);
-    if (e != hipSuccess) {
-        if (g) (void)hipGraphDestroy(g);
-        return fail(CG_EDEVICE, std::string("graph capture failed: ") + hipGetErrorString(e));
-    }
-    e = hipGraphInstantiate(&h->graph, g, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(g);
-    if (e != hipSuccess) {
-        h->graph = nullptr;
-        return fail(CG_EDEVICE, std::string("graph instantiation failed: ") + hipGetErrorString(e));
+    for (int variant = 0; variant < (pmag_split(h) ? 2 : 1); ++variant) {
+        hipGraph_t g = nullptr;
+        HIP_CHECK(hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
+        for (int i = 0; i < W; ++i) enqueue_iteration(h, i, h->stream, variant == 1);
+        hipError_t e = hipStreamEndCapture(h->stream, &g);
+        if (e != hipSuccess) {
+            if (g) (void)hipGraphDestroy(g);
+            drop_graph(h);
+            return fail(CG_EDEVICE, std::string("graph capture failed: ") + hipGetErrorString(e));
+        }
+        hipGraphExec_t* dst = variant == 1 ? &h->graph_rule : &h->graph;
+        e = hipGraphInstantiate(dst, g, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(g);
+        if (e != hipSuccess) {
+            *dst = nullptr;
+            drop_graph(h);
+            return fail(CG_EDEVICE, std::string("graph instantiation failed: ") + hipGetErrorString(e));
+        }
     }
     h->graph_window = W;
-    h->graph_period = h->period;
+    h->graph_period = period;
     h->graph_sched = h->sched;
     return CG_OK;
 }
@@ -844,11 +872,12 @@ extern "C" int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const dou
     return upload_schedule(h);
 }
 
-extern "C" int cg_set_schedule_pmag(cg_handle* h, double lo, double hi) {
+extern "C" int cg_set_schedule_pmag(cg_handle* h, double lo, double hi, int32_t period) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_set_schedule_pmag: h is NULL");
     if (std::isnan(lo) || std::isnan(hi) || !(lo <= hi))
         return fail(CG_EINVAL, "cg_set_schedule_pmag: need lo <= hi (no NaN)");
+    if (period < 1) return fail(CG_EINVAL, "cg_set_schedule_pmag: period must be >= 1");
     if (!h->cbcode) {
         h->ncb = (h->n + h->C - 1) / h->C;
         std::vector<int32_t> tcol(std::max<int64_t>(h->T, 1));
@@ -863,9 +892,29 @@ extern "C" int cg_set_schedule_pmag(cg_handle* h, double lo, double hi) {
     }
     h->pm_lo = lo;
     h->pm_hi = hi;
+    h->pm_period = period;
     h->sched = kSchedPMag;
     drop_graph(h);  // the thresholds are baked into the captured launches
     return upload_schedule(h);
+}
+
+extern "C" int cg_record_column_codes(cg_handle* h, int32_t enable) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_record_column_codes: h is NULL");
+    h->rec_cb = enable != 0;
+    drop_graph(h);
+    return CG_OK;
+}
+
+extern "C" int cg_get_column_codes(const cg_handle* h, int32_t cap, uint8_t* out) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_get_column_codes: h is NULL");
+    if (h->sched != kSchedPMag || !h->cbhist) return 0;
+    dev::State hs{};
+    HIP_CHECK(hipMemcpy(&hs, h->st, sizeof(hs), hipMemcpyDeviceToHost));
+    const int64_t n = std::min<int64_t>(std::min<int64_t>(hs.ntrace, h->cbhist_rows), std::max(cap, 0));
+    if (n > 0 && out) HIP_CHECK(hipMemcpy(out, h->cbhist, (size_t)(n * h->ncb), hipMemcpyDeviceToHost));
+    return (int)std::min<int64_t>(hs.ntrace, h->cbhist_rows);
 }
 
 extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {
@@ -918,7 +967,7 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
     int64_t need_trace = 16;
     if (h->sched == kSchedTileRule) need_trace = maxit / h->period + 2;
     if (h->sched == kSchedResidual) need_trace = (int64_t)h->stage_prec.size() + 1;
-    if (h->sched == kSchedPMag) need_trace = (int64_t)maxit + 2;
+    if (h->sched == kSchedPMag) need_trace = (int64_t)maxit / h->pm_period + 2;
     if (need_trace > h->trace_cap) {
         dfree(h, h->trace_k);
         dfree(h, h->trace_counts);
@@ -928,6 +977,15 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
         if (rc == CG_OK) rc = dalloc(h, &h->trace_counts, 3 * dev::kTraceBlocks * need_trace);
         if (rc != CG_OK) return rc;
         h->trace_cap = need_trace;
+        drop_graph(h);
+    }
+    if (h->sched == kSchedPMag && h->rec_cb && h->cbhist_rows < h->trace_cap) {
+        dfree(h, h->cbhist);
+        h->cbhist = nullptr;
+        h->cbhist_rows = 0;
+        int rc = dalloc(h, &h->cbhist, h->trace_cap * h->ncb);
+        if (rc != CG_OK) return rc;
+        h->cbhist_rows = h->trace_cap;
         drop_graph(h);
     }
 
@@ -980,10 +1038,13 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
     const int64_t max_windows = (int64_t)maxit / W + 2;
     while (true) {
         if (windows < max_windows) {
+            // Split max|p| rule: window w ends at k = (w + 1) W; evaluate when that is a
+            // multiple of the period.
+            const bool rule_at_end = pmag_split(h) && ((windows + 1) * W) % h->pm_period == 0;
             if (h->use_graph) {
-                HIP_CHECK(hipGraphLaunch(h->graph, s));
+                HIP_CHECK(hipGraphLaunch(rule_at_end ? h->graph_rule : h->graph, s));
             } else {
-                for (int i = 0; i < W; ++i) enqueue_iteration(h, i, s);
+                for (int i = 0; i < W; ++i) enqueue_iteration(h, i, s, rule_at_end);
                 HIP_CHECK(hipGetLastError());
             }
             const int slot = (int)(windows & 1);

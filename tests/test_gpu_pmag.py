@@ -153,3 +153,68 @@ def test_pmag_cg_matches_oracle(cfg, lo, hi, dev):
     assert agree >= 5
     assert sum(c[1] + c[2] for _, c, _ in ref.windows) > 0  # the rule did lower some tiles
     S.close()
+
+
+def test_recorded_column_codes_and_kstar_match_oracle(dev):
+    """A per-iteration run's recorded column-block codes equal the oracle's while the
+    trajectories agree; K* from the recorded codes matches the oracle's selection."""
+    w = make_workload(2, "small")
+    A = w.A
+    lo, hi = 1e-4, 1e-2
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    Lo = otc.build(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    rec = []
+    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, w.b,
+                    ocg.PMagSchedule(Lo.C, Lo.tile_col_idx, lo, hi, 1, rec), w.tol, 1000, keep_maps=False)
+    S = mpcg.Solver(L)
+    S.cg_set_schedule_pmag(lo, hi, 1)
+    S.cg_record_column_codes(True)
+    bd = torch.from_numpy(w.b).to(dev)
+    xd = torch.zeros_like(bd)
+    status, K, hist = S.cg_solve(bd, xd, w.tol, 1000)
+    codes = S.cg_get_column_codes()
+    log(f"pmag record: GPU K={K} records={codes.shape}; oracle K={ref.K} records={len(rec)}")
+    assert codes.shape == (K, -(-A.n // w.C))
+    agree = 0
+    for k in range(min(K, ref.K)):
+        if abs(hist[k] - ref.hist[k]) > 1e-9 * ref.hist[k]:
+            break
+        assert np.array_equal(codes[k], rec[k]), k
+        agree += 1
+    assert agree >= 5
+    kstar, table = mpcg.cg_select_reuse_interval(codes)
+    k_ref, table_ref = omaps.select_reuse_interval(codes)
+    assert (kstar, [i for i, _ in table]) == (k_ref, [i for i, _ in table_ref])
+    if agree == K == ref.K:
+        assert kstar == omaps.select_reuse_interval(np.array(rec))[0]
+    log(f"pmag record: K*={kstar}, table {table}")
+    S.close()
+
+
+@pytest.mark.parametrize("period,use_graph", [(2, -1), (5, -1), (32, -1), (32, 0), (48, -1)])
+def test_pmag_with_period_matches_oracle(period, use_graph, dev):
+    """Periods below the 16-iteration window, a multiple of it (short windows, the rule
+    only in the windows that end before a multiple of the period; captured and eager
+    launches) and a longer non-multiple."""
+    w = make_workload(2, "small")
+    A = w.A
+    lo, hi = 1e-4, 1e-2
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    Lo = otc.build(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, w.b,
+                    ocg.PMagSchedule(Lo.C, Lo.tile_col_idx, lo, hi, period), w.tol, 1000, keep_maps=False)
+    S = mpcg.Solver(L, use_graph=use_graph)
+    S.cg_set_schedule_pmag(lo, hi, period)
+    bd = torch.from_numpy(w.b).to(dev)
+    xd = torch.zeros_like(bd)
+    status, K, hist = S.cg_solve(bd, xd, w.tol, 1000)
+    log(f"pmag period {period} graph {use_graph}: GPU K={K}, oracle K={ref.K}")
+    assert status == ref.status
+    assert abs(K - ref.K) <= max(1, math.floor(0.02 * ref.K))
+    ks, counts = S.cg_get_map_trace()
+    assert ks.tolist() == list(range(0, K, period))
+    for i, (k0, c, _) in enumerate(ref.windows):
+        if k0 > min(K, ref.K) or abs(hist[k0] - ref.hist[k0]) > 1e-9 * ref.hist[k0]:
+            break
+        assert ks[i] == k0 and counts[i].tolist() == c, (i, k0)
+    S.close()

@@ -119,3 +119,23 @@ def test_null_arguments_return_einval_without_gpu():
     assert lib.cg_solve(None, None, None, 1e-8, 10, None, None, None, None) == mpcg.CG_EINVAL
     assert b"NULL" in lib.cg_last_error()
     assert lib.cg_destroy(None) == mpcg.CG_OK
+
+
+def test_select_reuse_interval_matches_oracle():
+    """The library's K* selection (host code) against the oracle on random records."""
+    from oracle import maps as omaps
+
+    rng = np.random.default_rng(3)
+    for nrec, ncb in ((1, 5), (2, 3), (37, 11), (130, 64)):
+        codes = (np.cumsum(rng.integers(-1, 2, (nrec, ncb)), axis=0) % 3).astype(np.uint8)
+        for thr in (0.1, 0.3):
+            k_ref, table_ref = omaps.select_reuse_interval(codes, thr)
+            k, table = mpcg.cg_select_reuse_interval(codes, thr)
+            assert k == k_ref
+            assert [i for i, _ in table] == [i for i, _ in table_ref]
+            assert np.allclose([f for _, f in table], [f for _, f in table_ref], rtol=0, atol=1e-15)
+
+
+def test_select_reuse_interval_rejects_bad_codes():
+    with pytest.raises(mpcg.CGError):
+        mpcg.cg_select_reuse_interval(np.full((4, 2), 3, np.uint8))
