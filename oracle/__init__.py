@@ -11,7 +11,9 @@ Self-Evolving Precision Control for Faster Conjugate Gradient") computes:
 * ``rounding``  -- the three value streams FP64 / FP32 / BF16 (Sec. 3.3.2).
 * ``spmv``      -- the perturbed operator (A + E(a)) p of Eq. (2)/(5), with
   every tile's values rounded to its mapped precision and every product and
-  sum in FP64.
+  sum in FP64; and the paper's own variant ("P1"), which also rounds the
+  vector entry to the tile's precision (Eq. 9/10) and scales reduced-precision
+  values per column (Sec. 3.3.2).
 * ``maps``      -- the precision-map rules used by the workloads.
 * ``cg``        -- textbook CG (Fig. 1, Algorithm 1's solver lines) and
   Jacobi-PCG (Sec. 4.6), with the stopping rule of Sec. 4.1.

@@ -18,7 +18,8 @@ Definition used here (Fig. 4(a) inter-tile CSR, Fig. 4(b) intra-tile CSC):
 
 The paper pads columns to an even count with sentinel rows (Sec. 3.3.2);
 that is storage detail and not part of the canonical layout here. The padded
-view of Fig. 4(b) is available as :func:`padded_columns` for reference.
+view of Fig. 4(b) is available per tile as :func:`padded_columns` and for the
+whole matrix as :func:`padded_layout`.
 
 Test infrastructure only: see the package docstring.
 """
@@ -167,3 +168,30 @@ def tile_of(keys, n: int, R: int, C: int, rows, cols):
     if np.any(t >= keys.size) or np.any(keys[np.minimum(t, keys.size - 1)] != k):
         raise ValueError("entry outside every non-empty tile")
     return t
+
+
+def padded_layout(L: TileCSC):
+    """The canonical layout with every odd-length local column padded (Fig. 4(b)).
+
+    One sentinel entry is appended to each column holding an odd number of
+    nonzeros: row index R, value +0.0. Returns (tile_nnz_ptr int64[T+1],
+    row_idx uint16[nnz'], col_local uint8[nnz'], val float64[nnz']), in the
+    canonical order with the sentinel last in its column.
+    """
+    ptr = [0]
+    rows, cols, vals = [], [], []
+    for t in range(L.T):
+        s = int(L.tile_nnz_ptr[t])
+        for c in range(L.C):
+            a, b = int(L.col_ptr[t, c]), int(L.col_ptr[t, c + 1])
+            for k in range(s + a, s + b):
+                rows.append(int(L.row_idx[k]))
+                cols.append(c)
+                vals.append(float(L.val[k]))
+            if (b - a) % 2:
+                rows.append(L.R)
+                cols.append(c)
+                vals.append(0.0)
+        ptr.append(len(rows))
+    return (np.asarray(ptr, dtype=np.int64), np.asarray(rows, dtype=np.uint16),
+            np.asarray(cols, dtype=np.uint8), np.asarray(vals, dtype=np.float64))
