@@ -181,6 +181,34 @@ def main():
           f"{pm_frac}; K*={kstar}: {statusks} K={Kks} TTS {ttsks_ms:.3f} ms", file=sys.stderr, flush=True)
     Spm.close()
 
+    # The paper's own SpMV numerics on the bench's map: the vector entry rounded
+    # with its tile (Eq. 9/10); with the per-column scale and the sentinel
+    # padding of Sec. 3.3.2 / Fig. 4(b) on top.
+    p1 = {}
+    for name, flags in (("round_vector", mpcg.CG_P1_ROUND_VECTOR),
+                        ("round_scale_pad", mpcg.CG_P1_ROUND_VECTOR | mpcg.CG_P1_COLUMN_SCALE
+                         | mpcg.CG_P1_PAD_COLUMNS)):
+        Sp = mpcg.Solver(L, pmap, p1=flags)
+        for _ in range(10):
+            Sp.cg_spmv(xin, y)
+        e0.record()
+        for _ in range(args.spmv_reps):
+            Sp.cg_spmv(xin, y)
+        e1.record()
+        torch.cuda.synchronize()
+        sp_ms = e0.elapsed_time(e1) / args.spmv_reps
+        run_solves(Sp, max(1, args.warmup))
+        elp, itsp, statusp, Kp, _ = run_solves(Sp, args.steps)
+        truep = float(np.linalg.norm(w.b - A.to_scipy() @ x.cpu().numpy()) / np.linalg.norm(w.b))
+        extra = 2 * A.n if flags & mpcg.CG_P1_COLUMN_SCALE else 0  # the scale exponents
+        p1[name] = {"flags": flags, "spmv_us": round(sp_ms * 1e3, 2),
+                    "spmv_gbs": round((bytes_spmv + extra) / (sp_ms * 1e-3) / 1e9, 1),
+                    "stored_nonzeros": Sp.nnz, "status": statusp, "iterations": Kp,
+                    "time_to_solution_ms": round(1e3 * elp / args.steps, 4), "true_residual": truep}
+        print(f"# P1 {name}: spmv {sp_ms * 1e3:.1f} us; {statusp} K={Kp} TTS {1e3 * elp / args.steps:.3f} ms, "
+              f"true residual {truep:.3e}", file=sys.stderr, flush=True)
+        Sp.close()
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
@@ -233,6 +261,7 @@ def main():
                       "kstar_delayed_upward_fractions": ktable,
                       "reused": {"status": statusks, "iterations": Kks,
                                  "time_to_solution_ms": round(ttsks_ms, 4)}},
+        "p1_numerics": p1,
         "roofline": {
             "bound": "hbm",
             "kernel": "spmv_tilecsc_kernel (cg_spmv)",

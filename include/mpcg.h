@@ -103,13 +103,38 @@ int cg_tilecsc_perm(const cg_tilecsc* A, int64_t* out);
 
 void cg_tilecsc_free(cg_tilecsc* A);
 
+/*
+ * The paper's own SpMV numerics, as options of cg_create (bits of
+ * cg_options.p1; 0 = the default product, which rounds only the matrix):
+ *   CG_P1_ROUND_VECTOR : the vector entry p_j is rounded to its tile's
+ *       precision before the product, as the action sets the precision of the
+ *       vector tile together with its column block (Eq. (9), Eq. (10)).
+ *       FP32 and BF16 are each one round-to-nearest-even step from FP64.
+ *       Products and sums stay FP64. The true-residual product of cg_solve
+ *       (r0 = b - A x0) never rounds.
+ *   CG_P1_COLUMN_SCALE : the FP32 and BF16 values of column j are stored as
+ *       fl(a_ij / s_j) and multiplied back by s_j in FP64, one factor per
+ *       column (Sec. 3.3.2, "Intra-Tile CSC Execution"). The factor is not
+ *       given by the paper; here s_j = 2^e_j with e_j the binary exponent of
+ *       the column's largest |a_ij| (max = m 2^e_j, 0.5 <= m < 1; e_j = 0 for
+ *       a column without a nonzero value), so the stored values stay inside
+ *       the reduced formats' range and scaling is exact. The FP64 values are
+ *       not scaled. Costs 2 bytes per row of extra SpMV traffic.
+ *   CG_P1_PAD_COLUMNS  : every local column with an odd number of nonzeros
+ *       gets one sentinel entry (row offset R, value +0.0) after its last
+ *       nonzero, as in Fig. 4(b); the SpMV skips sentinels. Requires R <= 255.
+ *       cg_get_sizes and cg_export_layout then report the padded layout.
+ */
+enum { CG_P1_ROUND_VECTOR = 1, CG_P1_COLUMN_SCALE = 2, CG_P1_PAD_COLUMNS = 4 };
+
 /* Options for cg_create. Zero-initialise and set what you need. */
 typedef struct {
     int32_t jacobi;      /* 1: Jacobi-preconditioned CG (Sec. 4.6), M = diag(A) */
     int32_t window;      /* iterations enqueued between stop-flag polls; 0 = default (16) */
     int32_t use_graph;   /* 1: replay each window as a captured HIP graph; 0 = plain launches;
                             -1 = default (graph) */
-    int32_t reserved[5];
+    int32_t p1;          /* CG_P1_* bits: the paper's own SpMV numerics (above); 0 = off */
+    int32_t reserved[4];
 } cg_options;
 
 /*
@@ -122,7 +147,8 @@ typedef struct {
  *   opt           : NULL for defaults.
  *   stream        : stream for the set-up copies and kernels.
  * Errors: CG_EINVAL (map code > 2, bad layout, n >= 2^28 or T or nnz >= 2^31,
- * Jacobi with a zero or missing diagonal entry), CG_ENOMEM, CG_EDEVICE.
+ * Jacobi with a zero or missing diagonal entry, unknown p1 bits, padding with
+ * R = 256), CG_ENOMEM, CG_EDEVICE.
  */
 int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, const cg_options* opt,
               void* stream, cg_handle** out);
@@ -244,10 +270,16 @@ int cg_get_map_trace(const cg_handle* h, int32_t cap, int32_t* k_out, int64_t* c
  * tile_row_ptr int64[ceil(n/R)+1], tile_col_idx int32[T], tile_nnz_ptr
  * int64[T+1], row_idx uint8[nnz], col_local uint8[nnz], and the three value
  * planes val64 double[nnz], val32 float[nnz], bf16 uint16[nnz] (bit
- * patterns). Any output pointer may be NULL to skip it. */
+ * patterns). Any output pointer may be NULL to skip it. With
+ * CG_P1_PAD_COLUMNS, nnz counts the sentinels (row offset R); with
+ * CG_P1_COLUMN_SCALE, val32 and bf16 hold the scaled values fl(a / s_j). */
 int cg_export_layout(const cg_handle* h, int64_t* tile_row_ptr, int32_t* tile_col_idx,
                      int64_t* tile_nnz_ptr, uint8_t* row_idx, uint8_t* col_local,
                      double* val64, float* val32, uint16_t* bf16);
+
+/* Exponents e_j of the per-column scale s_j = 2^e_j (CG_P1_COLUMN_SCALE,
+ * Sec. 3.3.2): host int32[n]. Without the option every e_j is 0. */
+int cg_export_column_scale(const cg_handle* h, int32_t* out);
 
 /* Sizes of a handle: n, T, nnz, R, C (any pointer may be NULL). */
 int cg_get_sizes(const cg_handle* h, int64_t* n, int64_t* T, int64_t* nnz, int32_t* R,

@@ -16,7 +16,8 @@ import numpy as np
 
 from . import _lib
 from ._lib import (CG_BF16, CG_BREAKDOWN, CG_EDEVICE, CG_EINVAL, CG_ENOMEM, CG_FP32, CG_FP64,  # noqa: F401
-                   CG_NOT_CONVERGED, CG_OK, CGError, check)
+                   CG_NOT_CONVERGED, CG_OK, CG_P1_COLUMN_SCALE, CG_P1_PAD_COLUMNS, CG_P1_ROUND_VECTOR,
+                   CGError, check)
 
 __all__ = [
     "TileCSC", "Solver", "cg_tilecsc_from_csr", "cg_create", "cg_spmv", "cg_solve",
@@ -131,12 +132,13 @@ class Solver:
     """Device-resident solver handle (owns a ``cg_handle``)."""
 
     def __init__(self, A: TileCSC, precision_map=None, jacobi=False, window=0, use_graph=-1,
-                 stream=None):
+                 p1=0, stream=None):
         lib = _lib.load()
         opt = _lib.cg_options()
         opt.jacobi = 1 if jacobi else 0
         opt.window = int(window)
         opt.use_graph = int(use_graph)
+        opt.p1 = int(p1)
         pm = None
         if precision_map is not None:
             pm = np.ascontiguousarray(precision_map, dtype=np.uint8)
@@ -146,8 +148,12 @@ class Solver:
         check(lib.cg_create(A._h, _ptr(pm) if pm is not None else None, ct.byref(opt),
                             ct.c_void_p(_stream(stream)), ct.byref(out)))
         self._h = out
-        self.n, self.T, self.nnz, self.R, self.C = A.n, A.T, A.nnz, A.R, A.C
+        n, T, nnz = ct.c_int64(), ct.c_int64(), ct.c_int64()
+        check(lib.cg_get_sizes(self._h, ct.byref(n), ct.byref(T), ct.byref(nnz), None, None))
+        # nnz counts the padding sentinels when CG_P1_PAD_COLUMNS is set
+        self.n, self.T, self.nnz, self.R, self.C = n.value, T.value, nnz.value, A.R, A.C
         self.jacobi = bool(jacobi)
+        self.p1 = int(p1)
 
     # -- maps and schedules ------------------------------------------------
     def cg_set_precision_map(self, prec_map):
@@ -228,6 +234,11 @@ class Solver:
         check(_lib.load().cg_export_layout(self._h, *[_ptr(out[k]) for k in (
             "tile_row_ptr", "tile_col_idx", "tile_nnz_ptr", "row_idx", "col_local", "val64", "val32",
             "bf16")]))
+        return out
+
+    def cg_export_column_scale(self) -> np.ndarray:
+        out = np.empty(self.n, dtype=np.int32)
+        check(_lib.load().cg_export_column_scale(self._h, _ptr(out)))
         return out
 
     def device_bytes(self) -> int:

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libmpcg.so")
 CG_OK, CG_NOT_CONVERGED, CG_BREAKDOWN = 0, 1, 2
 CG_EINVAL, CG_ENOMEM, CG_EDEVICE, CG_EINTERNAL = -1, -2, -3, -4
 CG_FP64, CG_FP32, CG_BF16 = 0, 1, 2
+CG_P1_ROUND_VECTOR, CG_P1_COLUMN_SCALE, CG_P1_PAD_COLUMNS = 1, 2, 4
 
 i32, i64, f64, u8p = ct.c_int32, ct.c_int64, ct.c_double, ct.POINTER(ct.c_uint8)
 vp = ct.c_void_p
@@ -30,7 +31,7 @@ class cg_tilecsc_view(ct.Structure):
 
 
 class cg_options(ct.Structure):
-    _fields_ = [("jacobi", i32), ("window", i32), ("use_graph", i32), ("reserved", i32 * 5)]
+    _fields_ = [("jacobi", i32), ("window", i32), ("use_graph", i32), ("p1", i32), ("reserved", i32 * 4)]
 
 
 # name -> (restype, argtypes)
@@ -57,6 +58,7 @@ SIGNATURES = {
     "cg_solve": (ct.c_int, [vp, vp, vp, f64, i32, vp, ct.POINTER(i32), vp, vp]),
     "cg_get_map_trace": (ct.c_int, [vp, i32, vp, vp]),
     "cg_export_layout": (ct.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+    "cg_export_column_scale": (ct.c_int, [vp, vp]),
     "cg_get_sizes": (ct.c_int, [vp, ct.POINTER(i64), ct.POINTER(i64), ct.POINTER(i64),
                                 ct.POINTER(i32), ct.POINTER(i32)]),
     "cg_device_bytes": (i64, [vp]),

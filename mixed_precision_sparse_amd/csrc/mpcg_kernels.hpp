@@ -223,9 +223,11 @@ constexpr int kBatchFirstOfGroup = 1, kBatchLastOfGroup = 2;
 __host__ __device__ inline int64_t segment_bytes(int64_t len) { return (14 * len + 16 + 15) / 16 * 16; }
 
 // Builds every batch's segment from the FP64 values, rounding to nearest even
-// (one wavefront per batch).
+// (one wavefront per batch). The FP32 and BF16 planes are rounded from vlow:
+// the FP64 values themselves, or the per-column scaled values a / s_j.
 __global__ __launch_bounds__(kBlock) void build_segments_kernel(const int32_t* __restrict__ btab, int64_t nbatch,
                                                                const double* __restrict__ v64,
+                                                               const double* __restrict__ vlow,
                                                                char* __restrict__ planes) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
@@ -237,9 +239,8 @@ __global__ __launch_bounds__(kBlock) void build_segments_kernel(const int32_t* _
         uint32_t* s32 = reinterpret_cast<uint32_t*>(seg + 8 * (int64_t)len);
         uint16_t* s16 = reinterpret_cast<uint16_t*>(seg + 12 * (int64_t)len);
         for (int i = lane; i < len; i += kWave) {
-            const double v = v64[first + i];
-            const uint64_t u = (uint64_t)__double_as_longlong(v);
-            s64[i] = v;
+            const uint64_t u = (uint64_t)__double_as_longlong(vlow[first + i]);
+            s64[i] = v64[first + i];
             s32[i] = round_f64_to_e8<23>(u);
             s16[i] = (uint16_t)round_f64_to_e8<7>(u);
         }
@@ -348,7 +349,10 @@ struct SpmvArgs {
     const int32_t* uprec;  // -1 per-tile map, else uniform code
     const State* st;
     double* partials;      // CG mode: one p.q partial per block
+    const int16_t* colexp;  // P1 kernels: per column e_j of the scale 2^e_j (NULL: no scale)
     int32_t n, rows_per_group, ngroups, groups_per_wave, nwin;
+    int32_t p1_round;      // P1 kernels: round the vector entry to the tile's precision
+    int32_t sentinel_row;  // P1 kernels: row offset of padding entries (R), or -1
 };
 
 template <typename MetaT>
@@ -407,6 +411,7 @@ struct BatchRegs {
 
 struct SweepCtx {
     __amdgpu_buffer_rsrc_t rv, rmt, rx, rmask, rrec;  // rv: this batch's value segment
+    __amdgpu_buffer_rsrc_t rexp;                       // P1: per-column scale exponents
     const int4* desc;  // this wave's plan entries in LDS
     char* acc;         // this wave's row accumulators in LDS
     const int2* tent;
@@ -416,7 +421,25 @@ struct SweepCtx {
     const uint8_t* cbcode;
     int len, lane;
     int spare;  // byte offset of this lane's spare accumulator
+    int round_p, scale, sentinel_row;  // P1 options (wave-uniform)
 };
+
+// A vector entry rounded to FP32 and, in one step from FP64, to BF16 (both
+// round-to-nearest-even, returned widened). FP32: the conversion instruction.
+// BF16: x is first rounded to FP32 by round-to-odd (truncation toward zero,
+// last bit set when inexact), then to BF16 to nearest even; FP32 keeps 16 more
+// bits than BF16 over the whole shared exponent range, so the odd bit only
+// breaks false ties and the result equals the direct rounding of x.
+__device__ __forceinline__ void round_vector_entry(double x, double& x32, double& x16) {
+    const float f = (float)x;
+    const double fd = (double)f;
+    x32 = fd;
+    uint32_t u = __float_as_uint(f);
+    u -= (fabs(fd) > fabs(x)) ? 1u : 0u;  // rounded away from zero: step back to the truncation
+    u |= (fd != x) ? 1u : 0u;             // inexact (NaN stays NaN)
+    const uint32_t b = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    x16 = (double)__uint_as_float(b);
+}
 
 // Issues the loads of a batch's tile entries and of its window records
 // [chunk, chunk+64) (out-of-range record reads return zero). CB: the tile's
@@ -451,7 +474,7 @@ __device__ __forceinline__ void load_batch_regs(const SweepCtx& c, const BatchHd
 // position times the value width, rounded down to 4 bytes (a BF16 lane then
 // takes the half its byte offset selects); the widening is a bitwise blend.
 // Lanes past the batch add their zero product to a private spare accumulator.
-template <typename MetaT, int U, bool CB>
+template <typename MetaT, int U, bool CB, bool P1>
 __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R, int wi, int o0, bool next,
                                            const BatchHdr& Hn, BatchRegs& Rn) {
     int q[U];
@@ -484,13 +507,18 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
     if (next) load_batch_regs<CB>(c, Hn, 0, true, Rn);
     double xv[U];
     int racc[U];
+    int ex[U];  // P1: scale exponent of the lane's column (sentinel lanes read past the end: 0)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int r, col;
         decode_meta<MetaT>(mt[u], r, col);
-        racc[u] = q[u] < c.len ? d[u].y + 8 * r : c.spare;
+        const bool real = q[u] < c.len && (!P1 || r != c.sentinel_row);
+        racc[u] = real ? d[u].y + 8 * r : c.spare;
         const u32x2 xb = __builtin_amdgcn_raw_buffer_load_b64(c.rx, d[u].x + 8 * col, 0, 0);
         xv[u] = __longlong_as_double(((long long)xb.y << 32) | xb.x);
+        ex[u] = 0;
+        if (P1 && c.scale)
+            ex[u] = (int)(int16_t)__builtin_amdgcn_raw_buffer_load_b16(c.rexp, 2 * ((d[u].x >> 3) + col), 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -500,8 +528,18 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
         const uint32_t h = (raw[u].x >> hs[u]) << 16;
         const uint32_t f = d[u].w == 1 ? h : raw[u].x;
         const double v32 = (double)__uint_as_float(f);
-        const double v = d[u].w == 3 ? __longlong_as_double(((long long)raw[u].y << 32) | raw[u].x) : v32;
-        atomicAdd(reinterpret_cast<double*>(c.acc + racc[u]), v * xv[u]);
+        double v = d[u].w == 3 ? __longlong_as_double(((long long)raw[u].y << 32) | raw[u].x) : v32;
+        double xu = xv[u];
+        if (P1) {
+            // Reduced-precision values carry their column's scale 2^e (exact).
+            if (c.scale) v = d[u].w == 3 ? v : ldexp(v, ex[u]);
+            if (c.round_p) {
+                double x32, x16;
+                round_vector_entry(xu, x32, x16);
+                xu = d[u].w == 3 ? xu : d[u].w == 2 ? x32 : x16;
+            }
+        }
+        atomicAdd(reinterpret_cast<double*>(c.acc + racc[u]), v * xu);
     }
     // Every load of the sweep has been consumed; saying so keeps the compiler
     // from guarding the next sweep's loads against this one's.
@@ -513,7 +551,11 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
 //
 // CB = true: the max|p| rule's kernels, where a tile's precision is its column
 // block's code for this product (values from the precision planes).
-template <typename MetaT, int MODE, int MAXROWS, bool CB = false>
+//
+// P1 = true: the paper's own numerics as options (vector entry rounded to the
+// tile's precision, per-column scale of the reduced values, padding entries
+// at row offset R skipped).
+template <typename MetaT, int MODE, int MAXROWS, bool CB = false, bool P1 = false>
 __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, double* __restrict__ y,
                                                                   double* __restrict__ partials) {
     // Row accumulators, then one spare per lane for lanes on a sentinel entry.
@@ -552,6 +594,12 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
                                                 (int)kBufferConfig);
     c.rrec = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.win_tile), (short)0, a.nwin * 4,
                                                (int)kBufferConfig);
+    c.round_p = P1 ? a.p1_round : 0;
+    c.scale = P1 && a.colexp != nullptr;
+    c.sentinel_row = P1 ? a.sentinel_row : -1;
+    if (P1)
+        c.rexp = __builtin_amdgcn_make_buffer_rsrc(const_cast<int16_t*>(a.colexp), (short)0,
+                                                   a.colexp ? a.n * 2 : 0, (int)kBufferConfig);
     double dot = 0.0, p_own = 0.0;
 
     int b = uniform_load(a.gbatch, g0);
@@ -596,15 +644,15 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
         int left = E, wi = 0, o0 = 0;
         for (; left >= kUnroll; left -= kUnroll, wi += kUnroll, o0 += kUnroll * kWave) {
             if (wi > 0 && (wi & (kWave - 1)) == 0) load_batch_regs<CB>(c, H, wi, false, R);  // next 64 records
-            spmv_sweep<MetaT, kUnroll, CB>(c, R, wi, o0, more && wi == 0, Hn, Rn);
+            spmv_sweep<MetaT, kUnroll, CB, P1>(c, R, wi, o0, more && wi == 0, Hn, Rn);
         }
         // The rest is 0 or one power of two below kUnroll (never crossing a record chunk).
         if (wi > 0 && (wi & (kWave - 1)) == 0 && left > 0) load_batch_regs<CB>(c, H, wi, false, R);
         const bool first = more && wi == 0;
-        if (kUnroll > 8 && left == 8) spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1), CB>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 4 && left == 4) spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1), CB>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 2 && left == 2) spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1), CB>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1, CB>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 8 && left == 8) spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1), CB, P1>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 4 && left == 4) spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1), CB, P1>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 2 && left == 2) spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1), CB, P1>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1, CB, P1>(c, R, wi, o0, first, Hn, Rn);
         if (more && E == 0) load_batch_regs<CB>(c, Hn, 0, true, Rn);  // a batch without windows
         wave_lds_sync();
         if (H.flags & kBatchLastOfGroup) {

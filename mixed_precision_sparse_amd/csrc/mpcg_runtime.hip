@@ -43,6 +43,8 @@ struct cg_handle {
     int32_t R = 0, C = 0, G = 0, rows_per_group = 0, ngroups = 0;
     bool meta16 = false;
     bool jacobi = false;
+    int p1 = 0;                    // CG_P1_* options
+    int16_t* colexp = nullptr;     // [n] per-column scale exponents (CG_P1_COLUMN_SCALE)
     int window = 16;
     bool use_graph = true;
     int64_t device_bytes = 0;
@@ -196,37 +198,47 @@ dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t*
     a.ngroups = h->ngroups;
     a.groups_per_wave = h->groups_per_wave;
     a.nwin = (int32_t)h->nwin;
+    a.colexp = (h->p1 & CG_P1_COLUMN_SCALE) ? h->colexp : nullptr;
+    a.p1_round = (h->p1 & CG_P1_ROUND_VECTOR) ? 1 : 0;
+    a.sentinel_row = (h->p1 & CG_P1_PAD_COLUMNS) ? h->R : -1;
     return a;
 }
 
-template <int MODE, bool CB>
+template <int MODE, bool CB, bool P1>
 void launch_spmv_cb(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
     const int grid = spmv_grid(h);
     const bool wide = h->rows_per_group > 64;
     if (h->meta16) {
         if (wide)
-            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, dev::kMaxRows, CB>), dim3(grid),
+            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, dev::kMaxRows, CB, P1>), dim3(grid),
                                dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
         else
-            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, 64, CB>), dim3(grid),
+            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, 64, CB, P1>), dim3(grid),
                                dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
     } else if (wide) {
-        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, dev::kMaxRows, CB>), dim3(grid),
+        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, dev::kMaxRows, CB, P1>), dim3(grid),
                            dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
     } else {
-        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, 64, CB>), dim3(grid), dim3(dev::kSpmvBlock),
-                           0, s, a, a.y, a.partials);
+        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, 64, CB, P1>), dim3(grid),
+                           dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
     }
 }
 
 // The max|p| rule's kernels take the tile precisions from the column-block
-// codes; every other schedule uses the map (or a uniform precision).
+// codes; every other schedule uses the map (or a uniform precision). A handle
+// with any of the paper's own numerics options runs the P1 kernels.
 template <int MODE>
 void launch_spmv(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
-    if (a.cbcode)
-        launch_spmv_cb<MODE, true>(h, a, s);
-    else
-        launch_spmv_cb<MODE, false>(h, a, s);
+    if (h->p1) {
+        if (a.cbcode)
+            launch_spmv_cb<MODE, true, true>(h, a, s);
+        else
+            launch_spmv_cb<MODE, false, true>(h, a, s);
+    } else if (a.cbcode) {
+        launch_spmv_cb<MODE, true, false>(h, a, s);
+    } else {
+        launch_spmv_cb<MODE, false, false>(h, a, s);
+    }
 }
 
 // Column-block codes of the max|p| rule from vector v (solve = 1: in-solve,
@@ -439,12 +451,113 @@ bool ranges_overlap(const void* a, const void* b, size_t bytes) {
 
 }  // namespace
 
+namespace {
+
+// The canonical layout with every odd-length local column closed by a
+// sentinel entry (row offset R, value +0.0), as drawn in Fig. 4(b). Canonical
+// order is kept: the sentinel follows its column's last nonzero.
+void pad_columns(const cg_tilecsc& A, cg_tilecsc& P) {
+    const int64_t T = A.T();
+    P.n = A.n;
+    P.R = A.R;
+    P.C = A.C;
+    P.nrb = A.nrb;
+    P.tile_row_ptr = A.tile_row_ptr;
+    P.tile_col_idx = A.tile_col_idx;
+    std::vector<int64_t> extra(T + 1, 0);
+    mpcg::parallel_for(T, [&](int64_t lo, int64_t hi) {
+        for (int64_t t = lo; t < hi; ++t) {
+            int64_t e = 0, run = 0;
+            for (int64_t k = A.tile_nnz_ptr[t]; k < A.tile_nnz_ptr[t + 1]; ++k) {
+                ++run;
+                if (k + 1 == A.tile_nnz_ptr[t + 1] || A.col_local[k + 1] != A.col_local[k]) {
+                    e += run & 1;
+                    run = 0;
+                }
+            }
+            extra[t] = e;
+        }
+    });
+    P.tile_nnz_ptr.assign(T + 1, 0);
+    int64_t added = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        P.tile_nnz_ptr[t] = A.tile_nnz_ptr[t] + added;
+        added += extra[t];
+    }
+    P.tile_nnz_ptr[T] = A.tile_nnz_ptr[T] + added;
+    const int64_t nnz = P.tile_nnz_ptr[T];
+    P.row_idx.resize(nnz);
+    P.col_local.resize(nnz);
+    P.val.resize(nnz);
+    P.perm.assign(nnz, -1);
+    mpcg::parallel_for(T, [&](int64_t lo, int64_t hi) {
+        for (int64_t t = lo; t < hi; ++t) {
+            int64_t o = P.tile_nnz_ptr[t], run = 0;
+            for (int64_t k = A.tile_nnz_ptr[t]; k < A.tile_nnz_ptr[t + 1]; ++k, ++o) {
+                P.row_idx[o] = A.row_idx[k];
+                P.col_local[o] = A.col_local[k];
+                P.val[o] = A.val[k];
+                P.perm[o] = A.perm.empty() ? -1 : A.perm[k];
+                ++run;
+                if (k + 1 == A.tile_nnz_ptr[t + 1] || A.col_local[k + 1] != A.col_local[k]) {
+                    if (run & 1) {
+                        ++o;
+                        P.row_idx[o] = (uint8_t)A.R;
+                        P.col_local[o] = A.col_local[k];
+                        P.val[o] = 0.0;
+                    }
+                    run = 0;
+                }
+            }
+        }
+    });
+}
+
+// Per-column scale exponents e_j (s_j = 2^e_j, e_j the binary exponent of the
+// column's largest |a_ij|, 0 for a column without a nonzero value) and the
+// scaled values a / s_j in storage order (Sec. 3.3.2).
+void column_scale(const cg_tilecsc& A, std::vector<int16_t>& e, std::vector<double>& scaled) {
+    std::vector<double> colmax(A.n, 0.0);
+    for (int64_t I = 0; I < A.nrb; ++I)
+        for (int64_t t = A.tile_row_ptr[I]; t < A.tile_row_ptr[I + 1]; ++t) {
+            const int64_t c0 = (int64_t)A.tile_col_idx[t] * A.C;
+            for (int64_t k = A.tile_nnz_ptr[t]; k < A.tile_nnz_ptr[t + 1]; ++k)
+                colmax[c0 + A.col_local[k]] = std::max(colmax[c0 + A.col_local[k]], std::fabs(A.val[k]));
+        }
+    e.assign(A.n, 0);
+    for (int64_t j = 0; j < A.n; ++j) {
+        int ej = 0;
+        if (colmax[j] != 0.0) (void)std::frexp(colmax[j], &ej);
+        e[j] = (int16_t)ej;
+    }
+    scaled.resize(A.nnz());
+    mpcg::parallel_for(A.T(), [&](int64_t lo, int64_t hi) {
+        for (int64_t t = lo; t < hi; ++t) {
+            const int64_t c0 = (int64_t)A.tile_col_idx[t] * A.C;
+            for (int64_t k = A.tile_nnz_ptr[t]; k < A.tile_nnz_ptr[t + 1]; ++k)
+                scaled[k] = std::ldexp(A.val[k], -(int)e[c0 + A.col_local[k]]);
+        }
+    });
+}
+
+}  // namespace
+
 extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, const cg_options* opt,
                          void* stream, cg_handle** out) {
     mpcg::clear_error();
     if (!out) return fail(CG_EINVAL, "cg_create: out is NULL");
     *out = nullptr;
     if (!A) return fail(CG_EINVAL, "cg_create: A is NULL");
+    const int p1 = opt ? opt->p1 : 0;
+    if (p1 & ~(CG_P1_ROUND_VECTOR | CG_P1_COLUMN_SCALE | CG_P1_PAD_COLUMNS))
+        return fail(CG_EINVAL, "cg_create: opt->p1 has unknown bits");
+    if ((p1 & CG_P1_PAD_COLUMNS) && A->R > 255)
+        return fail(CG_EINVAL, "cg_create: column padding needs R <= 255 (the sentinel row offset is R)");
+    cg_tilecsc padded;
+    if (p1 & CG_P1_PAD_COLUMNS) {
+        pad_columns(*A, padded);
+        A = &padded;
+    }
     const int64_t T = A->T(), nnz = A->nnz(), n = A->n;
     if (n > INT32_MAX || T > INT32_MAX || nnz > INT32_MAX)
         return fail(CG_EINVAL, "cg_create: n, T and nnz must be below 2^31");
@@ -475,7 +588,9 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     h->R = A->R;
     h->C = A->C;
     h->nrb = A->nrb;
-    h->meta16 = !(A->R <= 16 && A->C <= 16);
+    h->p1 = p1;
+    // Padding stores the sentinel row offset R, which needs the 16-bit form.
+    h->meta16 = !(A->R <= 16 && A->C <= 16) || (p1 & CG_P1_PAD_COLUMNS);
     // Row blocks per wavefront: the largest of 32, 64, 128, 256 rows whose row
     // groups hold at most one batch of tiles on average (at least one row block).
     auto group_rb = [&](int rows) { return std::max(1, std::min(dev::kMaxGroupRB, rows / A->R)); };
@@ -637,6 +752,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         for (int64_t I = 0; I < h->nrb; ++I)
             for (int64_t t = A->tile_row_ptr[I]; t < A->tile_row_ptr[I + 1]; ++t)
                 for (int64_t k = A->tile_nnz_ptr[t]; k < A->tile_nnz_ptr[t + 1]; ++k) {
+                    if (A->row_idx[k] >= A->R) continue;  // padding sentinel
                     int64_t row = I * A->R + A->row_idx[k];
                     int64_t col = (int64_t)A->tile_col_idx[t] * A->C + A->col_local[k];
                     if (row == col) {
@@ -675,6 +791,23 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         h->meta = m;
     }
     TRY(dalloc(h, &h->v64, nnz));
+    std::vector<int16_t> colexp_h;
+    std::vector<double> scaled_h;
+    double* vlow = nullptr;  // set-up only: the scaled values the reduced planes are rounded from
+    if (p1 & CG_P1_COLUMN_SCALE) {
+        column_scale(*A, colexp_h, scaled_h);
+        TRY(dalloc(h, &h->colexp, n));
+        if (hipMalloc(&vlow, sizeof(double) * (size_t)std::max<int64_t>(nnz, 1)) != hipSuccess) {
+            (void)hipGetLastError();
+            return bail(fail(CG_ENOMEM, "cg_create: device allocation of the scaled values failed"));
+        }
+    }
+    struct FreeLater {
+        double* p;
+        ~FreeLater() {
+            if (p) (void)hipFree(p);
+        }
+    } free_vlow{vlow};
     TRY(dalloc(h, &h->planes, h->planes_bytes));
     TRY(dalloc(h, &h->packed, h->planes_bytes));
     TRY(dalloc(h, &h->toff, std::max<int64_t>(T, 1)));
@@ -725,6 +858,10 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
                             (h->meta16 ? 2 : 1) * (size_t)nnz, hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->v64, A->val.data(), sizeof(double) * nnz, hipMemcpyHostToDevice, s)))
         return dev_err(e, "upload");
+    if (vlow &&
+        ((e = hipMemcpyAsync(h->colexp, colexp_h.data(), sizeof(int16_t) * n, hipMemcpyHostToDevice, s)) ||
+         (e = hipMemcpyAsync(vlow, scaled_h.data(), sizeof(double) * nnz, hipMemcpyHostToDevice, s))))
+        return dev_err(e, "upload");
     if (h->jacobi &&
         (e = hipMemcpyAsync(h->dinv, dinv_h.data(), sizeof(double) * n, hipMemcpyHostToDevice, s)))
         return dev_err(e, "upload");
@@ -738,7 +875,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         return dev_err(e, "planes");
     hipLaunchKernelGGL(dev::build_segments_kernel,
                        dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>((h->nbatch + 3) / 4, 8192))),
-                       dim3(dev::kBlock), 0, s, h->btab, h->nbatch, h->v64, h->planes);
+                       dim3(dev::kBlock), 0, s, h->btab, h->nbatch, h->v64, vlow ? vlow : h->v64, h->planes);
     if ((e = hipGetLastError()) != hipSuccess) return dev_err(e, "plane kernel");
     dev::State hs{};
     hs.uprec = -1;
@@ -1012,6 +1149,7 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
         // r0 = b - A x0 with the exact FP64 values.
         dev::SpmvArgs sa = spmv_args(h, x0, h->r, &h->st->zero_prec);
         sa.b = b;
+        sa.p1_round = 0;
         launch_spmv<dev::kSpmvResidual>(h, sa, s);
         va.r_ready = 1;
     }
@@ -1102,6 +1240,15 @@ extern "C" int cg_get_map_trace(const cg_handle* h, int32_t cap, int32_t* k_out,
             }
     }
     return hs.ntrace;
+}
+
+extern "C" int cg_export_column_scale(const cg_handle* h, int32_t* out) {
+    mpcg::clear_error();
+    if (!h || !out) return fail(CG_EINVAL, "cg_export_column_scale: NULL argument");
+    std::vector<int16_t> e(h->n, 0);
+    if (h->colexp) HIP_CHECK(hipMemcpy(e.data(), h->colexp, sizeof(int16_t) * h->n, hipMemcpyDeviceToHost));
+    for (int64_t j = 0; j < h->n; ++j) out[j] = e[j];
+    return CG_OK;
 }
 
 extern "C" int cg_export_layout(const cg_handle* h, int64_t* tile_row_ptr, int32_t* tile_col_idx,

@@ -35,7 +35,8 @@ import numpy as np
 import scipy.sparse as sp
 
 from . import maps as _maps
-from .rounding import to_bf16_value, to_fp32
+from .rounding import stream_values, to_bf16_value, to_fp32
+from .spmv import column_scale_exponents, p1_stored_values
 from .tilecsc import TileCSC
 
 
@@ -126,12 +127,63 @@ class PerturbedOperator:
         return self.M @ p
 
 
+class P1Operator:
+    """The paper's own product: the vector entry rounded with its tile (Eq. 9/10).
+
+    Entry (i, j) of a tile at precision m contributes v_ij * p~_j in FP64,
+    where v_ij is the stored value (scaled per column when column_scale is
+    set, Sec. 3.3.2) and p~_j is p_j rounded to m when round_vector is set.
+    The product is taken as sum over m of A_m p~^(m), A_m holding the entries
+    at precision m.
+    """
+
+    def __init__(self, L: TileCSC, indptr, indices, data, round_vector=True, column_scale=False):
+        self.n = L.n
+        tile_canon = L.tile_of_nnz()
+        self.tile_of_csr = np.empty_like(tile_canon)
+        self.tile_of_csr[L.perm] = tile_canon
+        self.indptr = np.asarray(indptr)
+        self.indices = np.asarray(indices)
+        a = np.asarray(data, dtype=np.float64)
+        e = (column_scale_exponents(L.n, indptr, indices, a)[self.indices] if column_scale
+             else np.zeros(a.size, dtype=np.int64))
+        self.streams = tuple(p1_stored_values(a, np.full(a.size, m, np.uint8), e) for m in (0, 1, 2))
+        self.round_vector = round_vector
+        self.parts = []
+
+    def set_map(self, prec_map):
+        prec_nnz = np.asarray(prec_map, dtype=np.uint8)[self.tile_of_csr]
+        self.parts = []
+        for m in (0, 1, 2):
+            sel = prec_nnz == m
+            if sel.any():
+                Am = sp.csr_matrix((np.where(sel, self.streams[m], 0.0), self.indices, self.indptr),
+                                   shape=(self.n, self.n))
+                self.parts.append((m, Am))
+
+    def __matmul__(self, p):
+        y = np.zeros(self.n)
+        for m, Am in self.parts:
+            pm = stream_values(p, np.full(p.size, m, np.uint8)) if self.round_vector else p
+            y += Am @ pm
+        return y
+
+
 def solve(L: TileCSC, indptr, indices, data, b, schedule, tol, maxit, x0=None,
-          jacobi=False, trace=None, keep_maps=True) -> Result:
+          jacobi=False, trace=None, keep_maps=True, round_vector=False,
+          column_scale=False) -> Result:
+    """CG (or Jacobi-PCG) with the mixed-precision product.
+
+    round_vector / column_scale select the paper's own product (P1Operator);
+    r0 = b - A x0 always uses the exact FP64 matrix.
+    """
     n = L.n
     A = sp.csr_matrix((np.asarray(data, dtype=np.float64), np.asarray(indices),
                        np.asarray(indptr)), shape=(n, n))
-    op = PerturbedOperator(L, indptr, indices, data)
+    if round_vector or column_scale:
+        op = P1Operator(L, indptr, indices, data, round_vector, column_scale)
+    else:
+        op = PerturbedOperator(L, indptr, indices, data)
     b = np.asarray(b, dtype=np.float64)
     x = np.zeros(n) if x0 is None else np.array(x0, dtype=np.float64)
     r = b - A @ x

@@ -287,3 +287,49 @@ def test_p1_fp64_stream_is_not_scaled():
     e = spmv.column_scale_exponents(n, M.indptr, M.indices, M.data)
     y = spmv.spmv_p1_loop(L, M.indptr, M.indices, M.data, prec, x, col_exp=e)
     assert y[3] == 1.0e-300 and y[0] == 1.0e300
+
+
+def _cfg_small(cfg):
+    from gen import make_workload
+    w = make_workload(cfg, "small")
+    A = w.A
+    L = tc.build(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    return w, A, L
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_p1_cg_with_fp64_map_is_the_plain_fp64_run(cfg):
+    """FP64 tiles round nothing and are not scaled: the P1 run equals the plain one bit for bit."""
+    from oracle import cg
+    w, A, L = _cfg_small(cfg)
+    sched = cg.StaticSchedule(np.zeros(L.T, np.uint8))
+    a = cg.solve(L, A.indptr, A.indices, A.data, w.b, sched, w.tol, 300, keep_maps=False,
+                 round_vector=True, column_scale=True)
+    b = cg.solve(L, A.indptr, A.indices, A.data, w.b, sched, w.tol, 300, keep_maps=False)
+    assert (a.K, a.status, a.hist) == (b.K, b.status, b.hist)
+    assert np.array_equal(a.x, b.x)
+
+
+@pytest.mark.parametrize("rv,cs", [(True, False), (True, True), (False, True)])
+def test_p1_cg_uses_the_p1_product_of_each_direction(rv, cs):
+    """Every product inside the P1 CG equals spmv_p1 of the direction it multiplied."""
+    from oracle import cg
+    from gen import configs
+    w, A, L = _cfg_small(3)
+    prec = configs.static_map(configs.tile_scores(L.T))
+    e = spmv.column_scale_exponents(A.n, A.indptr, A.indices, A.data) if cs else None
+    count = [0]
+
+    def hook(k, x, r, p, q, alpha):
+        ref = spmv.spmv_p1(L, A.indptr, A.indices, A.data, prec, p, round_vector=rv, col_exp=e)
+        assert np.array_equal(q, ref)
+        count[0] += 1
+
+    res = cg.solve(L, A.indptr, A.indices, A.data, w.b, cg.StaticSchedule(prec), w.tol, 60, trace=hook,
+                   keep_maps=False, round_vector=rv, column_scale=cs)
+    assert count[0] == res.K == 60
+    if rv:
+        # the rounded vector changes the trajectory against the matrix-only product
+        plain = cg.solve(L, A.indptr, A.indices, A.data, w.b, cg.StaticSchedule(prec), w.tol, 60,
+                         keep_maps=False)
+        assert plain.hist != res.hist
