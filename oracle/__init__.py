@@ -17,10 +17,12 @@ Self-Evolving Precision Control for Faster Conjugate Gradient") computes:
 * ``maps``      -- the precision-map rules used by the workloads.
 * ``cg``        -- textbook CG (Fig. 1, Algorithm 1's solver lines) and
   Jacobi-PCG (Sec. 4.6), with the stopping rule of Sec. 4.1.
+* ``tuning``    -- the row-block height search of Sec. 3.3.3 (non-empty tile
+  counts per row block, their evenness, the tuned R).
 
 Pins (tests marked ``not gpu``) tie every function to something other than
 itself: brute force on tiny inputs, library routines on special cases,
 closed forms and CG invariants. No function here is "parity unpinned".
 """
 
-from . import rounding, tilecsc, spmv, maps, cg  # noqa: F401
+from . import rounding, tilecsc, spmv, maps, cg, tuning  # noqa: F401
