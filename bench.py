@@ -59,6 +59,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile-shapes", default="",
+                    help="comma-separated workloads (e.g. 2,3,4): instead of the CG bench, time cg_spmv "
+                         "(FP64 map) at the workload's tile shape and at the tuned row-block heights "
+                         "(paper Sec. 3.3.3) for C = 64 and the workload's C; prints one JSON line")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="counter run: a 256 MiB copy (the scale reference), then 5 cg_spmv "
                          "launches per map (all FP64, the bench's mixed map, all BF16); no timing")
@@ -75,6 +79,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.tile_shapes:
+        tile_shapes(torch, dev, mpcg, [int(c) for c in args.tile_shapes.split(",")], args.spmv_reps)
+        return
     t0 = time.time()
     w = make_workload(2, "full")
     A = w.A
@@ -274,6 +281,58 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    print(json.dumps(out), flush=True)
+
+
+def tile_shapes(torch, dev, mpcg, cfgs, reps):
+    """cg_spmv under the all-FP64 map at the workload's tile shape and at the tuned heights.
+
+    The tuned height comes from cg_tune_row_height (paper Sec. 3.3.3) with its
+    defaults (R <= 256, at least 1024 row blocks). Maps are per tile and differ
+    between tilings, so every shape is timed with the FP64 map.
+    """
+    from gen import make_workload
+
+    out = {"metric": "tile_csc_spmv_by_tile_shape", "map": "all FP64", "workloads": []}
+    for cfg in cfgs:
+        t0 = time.time()
+        w = make_workload(cfg, "full")
+        A = w.A
+        print(f"# cfg{cfg}: generated in {time.time() - t0:.0f}s, n={A.n} nnz={A.nnz}", file=sys.stderr,
+              flush=True)
+        shapes = [(w.R, w.C, "workload")]
+        for C in (64, w.C):
+            R, rows = mpcg.cg_tune_row_height(A.n, A.indptr, A.indices, C)
+            if (R, C) not in [(s[0], s[1]) for s in shapes]:
+                shapes.append((R, C, f"tuned for C={C}"))
+        res = []
+        for R, C, label in shapes:
+            L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, R, C)
+            S = mpcg.Solver(L, np.zeros(L.T, np.uint8))
+            xin = torch.from_numpy(np.random.default_rng(7).uniform(-1, 1, A.n)).to(dev)
+            y = torch.empty_like(xin)
+            for _ in range(10):
+                S.cg_spmv(xin, y)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                S.cg_spmv(xin, y)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            nbytes = spmv_algorithmic_bytes(L, np.zeros(L.T, np.uint8))
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            counts = np.diff(L.tile_row_ptr)
+            rec = {"R": R, "C": C, "shape": label, "tiles": L.T, "spmv_us": round(ms * 1e3, 2),
+                   "algorithmic_bytes": nbytes, "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                   "row_block_tile_cv": round(float(counts.std() / max(counts.mean(), 1e-300)), 4)}
+            res.append(rec)
+            print(f"# cfg{cfg} {label}: {R}x{C} T={L.T} spmv {ms * 1e3:.1f} us, {gbs:.0f} GB/s", file=sys.stderr,
+                  flush=True)
+            S.close()
+            L.close()
+        out["workloads"].append({"workload": w.description, "n": A.n, "nnz": A.nnz, "shapes": res})
     print(json.dumps(out), flush=True)
 
 

@@ -104,6 +104,36 @@ int cg_tilecsc_perm(const cg_tilecsc* A, int64_t* out);
 void cg_tilecsc_free(cg_tilecsc* A);
 
 /*
+ * Row-block height tuning (Sec. 3.3.3 "Cross-Level Balance Tuning"): the
+ * tile width C stays fixed and the height R is searched over the paper's
+ * candidates 32, 64, ..., 16384 so that row blocks hold similar numbers of
+ * non-empty tiles. The paper names no measure; here it is the coefficient of
+ * variation (population standard deviation over mean) of the non-empty tile
+ * counts of the ceil(n/R) row blocks, computed as sqrt(m S2 - S1^2) / S1 from
+ * the exact integer sums S1 = sum c, S2 = sum c^2 over m row blocks. A
+ * candidate is admissible when R <= max_R (cg_tilecsc_from_csr accepts
+ * R <= 256) and it leaves at least min_row_blocks row blocks; the tuned R is
+ * the admissible candidate with the smallest coefficient of variation (ties
+ * to the smaller R), or 32 when none is admissible.
+ *   n, rowptr, colind : square CSR structure as for cg_tilecsc_from_csr
+ *                       (host; values are not needed).
+ *   C                 : tile width in [1, 256].
+ *   max_R, min_row_blocks : admissibility bounds (min_row_blocks >= 1).
+ *   R_out             : receives the tuned height.
+ *   cap               : entries available in each table array (0 allowed).
+ *   cand_R, cand_nrb, cand_T, cand_cv, cand_max_ratio, cand_ok : one entry per
+ *                       candidate, in candidate order: height, row blocks,
+ *                       non-empty tiles, coefficient of variation, largest
+ *                       count over the mean, admissible (0/1). Any may be NULL.
+ * Returns the number of candidates (10) or a negative error (CG_EINVAL for
+ * bad sizes or a column outside [0, n)).
+ */
+int cg_tune_row_height(int64_t n, const int64_t* rowptr, const int32_t* colind, int32_t C, int32_t max_R,
+                       int64_t min_row_blocks, int32_t* R_out, int32_t cap, int32_t* cand_R,
+                       int64_t* cand_nrb, int64_t* cand_T, double* cand_cv, double* cand_max_ratio,
+                       uint8_t* cand_ok);
+
+/*
  * The paper's own SpMV numerics, as options of cg_create (bits of
  * cg_options.p1; 0 = the default product, which rounds only the matrix):
  *   CG_P1_ROUND_VECTOR : the vector entry p_j is rounded to its tile's

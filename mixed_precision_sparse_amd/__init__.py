@@ -20,7 +20,7 @@ from ._lib import (CG_BF16, CG_BREAKDOWN, CG_EDEVICE, CG_EINVAL, CG_ENOMEM, CG_F
                    CGError, check)
 
 __all__ = [
-    "TileCSC", "Solver", "cg_tilecsc_from_csr", "cg_create", "cg_spmv", "cg_solve",
+    "TileCSC", "Solver", "cg_tilecsc_from_csr", "cg_create", "cg_spmv", "cg_solve", "cg_tune_row_height",
     "cg_version", "library_path", "CGError",
 ]
 
@@ -262,6 +262,28 @@ def cg_create(A: TileCSC, precision_map=None, **kw) -> Solver:
 
 def cg_spmv(h: Solver, x, y, stream=None):
     h.cg_spmv(x, y, stream)
+
+
+def cg_tune_row_height(n, indptr, indices, C, max_R=256, min_row_blocks=1024):
+    """Tuned row-block height and the per-candidate table (see ``cg_tune_row_height`` in mpcg.h).
+
+    Returns ``(R, rows)`` with one dict per candidate height: R, row_blocks,
+    tiles, cv, max_ratio, admissible.
+    """
+    indptr = np.ascontiguousarray(indptr, dtype=np.int64)
+    indices = np.ascontiguousarray(indices, dtype=np.int32)
+    cap = 10
+    cR = np.empty(cap, np.int32)
+    cnrb, cT = np.empty(cap, np.int64), np.empty(cap, np.int64)
+    ccv, cmx = np.empty(cap, np.float64), np.empty(cap, np.float64)
+    cok = np.empty(cap, np.uint8)
+    R = ct.c_int32()
+    m = check(_lib.load().cg_tune_row_height(int(n), _ptr(indptr), _ptr(indices), int(C), int(max_R),
+                                             int(min_row_blocks), ct.byref(R), cap, _ptr(cR), _ptr(cnrb),
+                                             _ptr(cT), _ptr(ccv), _ptr(cmx), _ptr(cok)))
+    rows = [dict(R=int(cR[i]), row_blocks=int(cnrb[i]), tiles=int(cT[i]), cv=float(ccv[i]),
+                 max_ratio=float(cmx[i]), admissible=bool(cok[i])) for i in range(min(m, cap))]
+    return R.value, rows
 
 
 def cg_select_reuse_interval(codes, max_fraction=0.1):

@@ -7,7 +7,8 @@ the search from the trivial answer (a handful of huge row blocks is
 perfectly even and leaves the device idle). The reading taken here:
 
 * evenness is the coefficient of variation (population standard deviation
-  over mean) of the non-empty tile counts of all ceil(n / R) row blocks;
+  over mean) of the non-empty tile counts of all ceil(n / R) row blocks,
+  computed from exact integer sums (see :func:`balance`);
 * a candidate must leave at least ``min_row_blocks`` row blocks, and it must
   not exceed ``max_R`` (the largest height the kernel supports);
 * the tuned R is the admissible candidate with the smallest coefficient of
@@ -18,6 +19,8 @@ Test infrastructure only: see the package docstring.
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -34,12 +37,21 @@ def row_block_tile_counts(n: int, indptr, indices, R: int, C: int) -> np.ndarray
 
 
 def balance(counts: np.ndarray):
-    """(coefficient of variation, max / mean) of a row block's tile counts (0, 0 when all are empty)."""
-    counts = np.asarray(counts, dtype=np.float64)
-    mean = counts.mean()
-    if mean == 0.0:
+    """(coefficient of variation, max / mean) of the row blocks' tile counts (0, 0 when all are empty).
+
+    With m row blocks, S1 = sum c and S2 = sum c^2 (exact integers), the
+    population standard deviation over the mean is sqrt(m S2 - S1^2) / S1 and
+    max / mean is m max(c) / S1. Each is evaluated from the exact integers with
+    one rounding to FP64 per operand and IEEE sqrt and division, so the value,
+    and with it the choice between near-equal candidates, does not depend on a
+    summation order.
+    """
+    c = [int(v) for v in np.asarray(counts).ravel()]
+    m, s1 = len(c), sum(c)
+    if s1 == 0:
         return 0.0, 0.0
-    return float(counts.std() / mean), float(counts.max() / mean)
+    s2 = sum(v * v for v in c)
+    return math.sqrt(float(m * s2 - s1 * s1)) / float(s1), float(m * max(c)) / float(s1)
 
 
 def tune_row_height(n: int, indptr, indices, C: int, max_R: int = 256, min_row_blocks: int = 1024,

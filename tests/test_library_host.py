@@ -139,3 +139,43 @@ def test_select_reuse_interval_matches_oracle():
 def test_select_reuse_interval_rejects_bad_codes():
     with pytest.raises(mpcg.CGError):
         mpcg.cg_select_reuse_interval(np.full((4, 2), 3, np.uint8))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_tune_row_height_matches_oracle(cfg):
+    """The library's row-block height search (host code) against the oracle, bit for bit."""
+    from gen import make_workload
+    from oracle import tuning
+
+    w = make_workload(cfg, "small")
+    A = w.A
+    for C, max_R, min_rb in ((64, 256, 1), (16, 16384, 4), (w.C, 256, 40)):
+        R_ref, table_ref = tuning.tune_row_height(A.n, A.indptr, A.indices, C, max_R, min_rb)
+        R, rows = mpcg.cg_tune_row_height(A.n, A.indptr, A.indices, C, max_R, min_rb)
+        assert R == R_ref
+        got = [(r["R"], r["row_blocks"], r["tiles"], r["cv"], r["max_ratio"], r["admissible"]) for r in rows]
+        assert got == table_ref
+
+
+def test_tune_row_height_skewed_and_errors():
+    from oracle import tuning
+
+    rng = np.random.default_rng(5)
+    n = 3000
+    k = np.minimum((rng.pareto(1.1, n) + 1).astype(np.int64), n)
+    indptr = np.concatenate([[0], np.cumsum(k)]).astype(np.int64)
+    indices = np.concatenate([np.sort(rng.choice(n, kk, replace=False)) for kk in k]).astype(np.int32)
+    for C in (1, 7, 64, 256):
+        R_ref, table_ref = tuning.tune_row_height(n, indptr, indices, C, 16384, 2)
+        R, rows = mpcg.cg_tune_row_height(n, indptr, indices, C, 16384, 2)
+        assert R == R_ref
+        assert [(r["R"], r["row_blocks"], r["tiles"], r["cv"], r["max_ratio"], r["admissible"])
+                for r in rows] == table_ref
+    with pytest.raises(mpcg.CGError):
+        mpcg.cg_tune_row_height(n, indptr, indices, 0)
+    with pytest.raises(mpcg.CGError):
+        mpcg.cg_tune_row_height(n, indptr, indices, 64, 256, 0)
+    bad = indices.copy()
+    bad[3] = n
+    with pytest.raises(mpcg.CGError):
+        mpcg.cg_tune_row_height(n, indptr, bad, 64)
