@@ -123,18 +123,44 @@ __device__ inline double block_sum(double v, double* s_tmp) {
 // Fixed-order sum of nparts partials (component j of NV per part); every
 // thread of the block gets the same value, and every block that calls this
 // on the same data gets the same bits.
+// Sum of nparts per-block partials (NV values each) in a fixed order, so that
+// every block of the calling kernel obtains the same bits. A thread takes
+// partials threadIdx.x + k * blockDim.x; it loads eight of them at once (eight
+// independent loads in flight instead of one at a time) into eight running
+// sums, adds the rest one by one into the first, and the block reduces.
 template <int NV, int NW = kWavesPerBlock>
 __device__ inline void sum_partials(const double* partials, int nparts, double (&out)[NV],
                                     double* s_tmp) {
-    double acc[NV];
+    constexpr int kLoads = 8;
+    double acc[kLoads][NV];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) acc[j] = 0.0;
-    for (int i = threadIdx.x; i < nparts; i += blockDim.x) {
+    for (int u = 0; u < kLoads; ++u)
 #pragma unroll
-        for (int j = 0; j < NV; ++j) acc[j] += partials[(size_t)i * NV + j];
+        for (int j = 0; j < NV; ++j) acc[u][j] = 0.0;
+    const int stride = blockDim.x;
+    int i = threadIdx.x;
+    for (; i + (kLoads - 1) * stride < nparts; i += kLoads * stride) {
+        double v[kLoads][NV];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) v[u][j] = partials[(size_t)(i + u * stride) * NV + j];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) acc[u][j] += v[u][j];
+    }
+    for (; i < nparts; i += stride) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) acc[0][j] += partials[(size_t)i * NV + j];
     }
 #pragma unroll
-    for (int j = 0; j < NV; ++j) out[j] = block_sum<NW>(acc[j], s_tmp);
+    for (int j = 0; j < NV; ++j) {
+        double s = acc[0][j];
+#pragma unroll
+        for (int u = 1; u < kLoads; ++u) s += acc[u][j];
+        out[j] = block_sum<NW>(s, s_tmp);
+    }
 }
 
 // Logical block index that gives every XCD a contiguous range of the work:

@@ -153,7 +153,7 @@ int grid_for(int64_t work, int per_thread, int cap) {
 
 constexpr int kVecGridCap = 1024;
 #ifndef MPCG_SPMV_GRID_CAP
-#define MPCG_SPMV_GRID_CAP 4096
+#define MPCG_SPMV_GRID_CAP 32768
 #endif
 constexpr int kSpmvGridCap = MPCG_SPMV_GRID_CAP;
 
