@@ -48,7 +48,7 @@ struct State {
     int32_t ntrace;
     int32_t trace_cap;
     int32_t period;      // tile-rule window length (0: no tile rule)
-    int32_t pad;
+    int32_t live;        // set by the update kernel: this iteration runs (the direction kernel's gate)
     double hi, lo;       // tile-rule thresholds
 };
 
@@ -827,32 +827,33 @@ constexpr int kVecWaves = kVecBlock / kWave;
 constexpr int kVecPairs = 4;
 
 // alpha = r.z / p.q (p.q summed from the SpMV partials in every block);
-// x += alpha p; r -= alpha q; [z = dinv .* r]; partials of r.r [and r.z].
-// On p.q <= 0 or a non-finite alpha nothing is updated and the breakdown is
-// flagged for the direction kernel.
+// r -= alpha q; [z = dinv .* r]; partials of r.r [and r.z]. x += alpha p is
+// left to the direction kernel, which reads p anyway. On p.q <= 0 or a
+// non-finite alpha nothing is updated and the breakdown is flagged for the
+// direction kernel. `done` does not change during this launch, so every block
+// takes the same decision, and block 0 records it in `live` for the direction
+// kernel.
 template <bool JAC>
 __global__ __launch_bounds__(kVecBlock) void cg_update_kernel(VecArgs a) {
     __shared__ double s_tmp[kVecWaves];
     State* st = a.st;
-    if (load_done(st)) return;
+    const bool live = load_done(st) == 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) st->live = live ? 1 : 0;
+    if (!live) return;
     const int64_t npairs = ((int64_t)a.n + 1) / 2;
     const int64_t stride = (int64_t)gridDim.x * kVecBlock;
     const int64_t tid = (int64_t)blockIdx.x * kVecBlock + threadIdx.x;
-    double2* __restrict__ x2 = reinterpret_cast<double2*>(a.x);
     double2* __restrict__ r2 = reinterpret_cast<double2*>(a.r);
     double2* __restrict__ z2 = reinterpret_cast<double2*>(a.z);
-    const double2* __restrict__ p2 = reinterpret_cast<const double2*>(a.p);
     const double2* __restrict__ q2 = reinterpret_cast<const double2*>(a.q);
     const double2* __restrict__ d2 = reinterpret_cast<const double2*>(a.dinv);
-    double2 xv[kVecPairs], rv[kVecPairs], pv[kVecPairs], qv[kVecPairs], dv[kVecPairs];
+    double2 rv[kVecPairs], qv[kVecPairs], dv[kVecPairs];
     auto load = [&](int64_t base) {
 #pragma unroll
         for (int j = 0; j < kVecPairs; ++j) {
             const int64_t i = base + j * stride + tid;
             if (i < npairs) {
-                xv[j] = x2[i];
                 rv[j] = r2[i];
-                pv[j] = p2[i];
                 qv[j] = q2[i];
                 if (JAC) dv[j] = d2[i];
             }
@@ -872,12 +873,9 @@ __global__ __launch_bounds__(kVecBlock) void cg_update_kernel(VecArgs a) {
             for (int j = 0; j < kVecPairs; ++j) {
                 const int64_t i = base + j * stride + tid;
                 if (i < npairs) {
-                    double2 xn, rn;
-                    xn.x = xv[j].x + alpha * pv[j].x;
-                    xn.y = xv[j].y + alpha * pv[j].y;
+                    double2 rn;
                     rn.x = rv[j].x - alpha * qv[j].x;
                     rn.y = rv[j].y - alpha * qv[j].y;
-                    x2[i] = xn;
                     r2[i] = rn;
                     rr += rn.x * rn.x + rn.y * rn.y;
                     if (JAC) {
@@ -905,16 +903,17 @@ __global__ __launch_bounds__(kVecBlock) void cg_update_kernel(VecArgs a) {
     }
 }
 
-// beta = (r.z)_new / (r.z)_old from the update partials (in every block);
-// p = z + beta p (z = r for plain CG). Thread 0 of block 0 commits
-// rho_{k+1}, the history entry, the stop flag and the schedule stage.
-// Other blocks may read `done` before or after that commit within the final
-// iteration; either way the direction update they skip or make is unused.
+// x += alpha p; beta = (r.z)_new / (r.z)_old from the update partials (in
+// every block); p = z + beta p (z = r for plain CG). Thread 0 of block 0
+// commits rho_{k+1}, the history entry, the stop flag and the schedule stage.
+// The launch runs when the update kernel of this iteration ran (`live`, which
+// no block of this launch writes); `done` may be set by block 0 while other
+// blocks still run, and they must still apply this iteration's x update.
 template <bool JAC>
 __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
     __shared__ double s_tmp[kVecWaves];
     State* st = a.st;
-    if (load_done(st)) return;
+    if (!st->live) return;
     if (st->bd) {
         if (blockIdx.x == 0 && threadIdx.x == 0) store_done(st, 3);
         return;
@@ -923,8 +922,9 @@ __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
     const int64_t stride = (int64_t)gridDim.x * kVecBlock;
     const int64_t tid = (int64_t)blockIdx.x * kVecBlock + threadIdx.x;
     double2* __restrict__ p2 = reinterpret_cast<double2*>(a.p);
+    double2* __restrict__ x2 = reinterpret_cast<double2*>(a.x);
     const double2* __restrict__ z2 = reinterpret_cast<const double2*>(JAC ? a.z : a.r);
-    double2 pv[kVecPairs], zv[kVecPairs];
+    double2 pv[kVecPairs], zv[kVecPairs], xv[kVecPairs];
     auto load = [&](int64_t base) {
 #pragma unroll
         for (int j = 0; j < kVecPairs; ++j) {
@@ -932,6 +932,7 @@ __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
             if (i < npairs) {
                 pv[j] = p2[i];
                 zv[j] = z2[i];
+                xv[j] = x2[i];
             }
         }
     };
@@ -941,15 +942,19 @@ __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
     const double rr_new = tot[0];
     const double rz_new = tot[1];
     const double beta = rz_new / st->rz_prev;
+    const double alpha = st->alpha;
     for (int64_t base = 0; base < npairs; base += stride * kVecPairs) {
         if (base > 0) load(base);
 #pragma unroll
         for (int j = 0; j < kVecPairs; ++j) {
             const int64_t i = base + j * stride + tid;
             if (i < npairs) {
-                double2 pn;
+                double2 pn, xn;
+                xn.x = xv[j].x + alpha * pv[j].x;
+                xn.y = xv[j].y + alpha * pv[j].y;
                 pn.x = zv[j].x + beta * pv[j].x;
                 pn.y = zv[j].y + beta * pv[j].y;
+                x2[i] = xn;
                 p2[i] = pn;
             }
         }
