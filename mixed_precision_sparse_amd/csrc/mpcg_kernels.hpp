@@ -626,6 +626,9 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
     if (P1)
         c.rexp = __builtin_amdgcn_make_buffer_rsrc(const_cast<int16_t*>(a.colexp), (short)0,
                                                    a.colexp ? a.n * 2 : 0, (int)kBufferConfig);
+    // CG mode, groups of at most 64 rows: the lane's own p entry, loaded when
+    // the group starts (larger groups reload p at the group's end: holding
+    // four entries per lane costs more occupancy than the reload).
     double dot = 0.0, p_own = 0.0;
 
     int b = uniform_load(a.gbatch, g0);
@@ -824,7 +827,10 @@ __global__ __launch_bounds__(kBlock) void cg_init_finish_kernel(VecArgs a) {
 // before it sums the previous kernel's partials, which hides that sum.
 constexpr int kVecBlock = 1024;
 constexpr int kVecWaves = kVecBlock / kWave;
-constexpr int kVecPairs = 4;
+#ifndef MPCG_VEC_PAIRS
+#define MPCG_VEC_PAIRS 4
+#endif
+constexpr int kVecPairs = MPCG_VEC_PAIRS;
 
 // alpha = r.z / p.q (p.q summed from the SpMV partials in every block);
 // r -= alpha q; [z = dinv .* r]; partials of r.r [and r.z]. x += alpha p is

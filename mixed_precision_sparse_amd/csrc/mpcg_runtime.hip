@@ -152,6 +152,10 @@ int grid_for(int64_t work, int per_thread, int cap) {
 }
 
 constexpr int kVecGridCap = 1024;
+#ifndef MPCG_UPD_GRID_CAP
+#define MPCG_UPD_GRID_CAP 512
+#endif
+constexpr int kUpdGridCap = MPCG_UPD_GRID_CAP;  // blocks of the update and direction kernels
 #ifndef MPCG_SPMV_GRID_CAP
 #define MPCG_SPMV_GRID_CAP 32768
 #endif
@@ -170,7 +174,7 @@ void plan_grids(cg_handle* h) {
     h->vec_blocks = grid_for(h->n, 8, kVecGridCap);
     const int64_t npairs = (h->n + 1) / 2;
     const int64_t per_block = (int64_t)dev::kVecBlock * dev::kVecPairs;
-    h->upd_blocks = (int)std::max<int64_t>(1, std::min<int64_t>((npairs + per_block - 1) / per_block, 512));
+    h->upd_blocks = (int)std::max<int64_t>(1, std::min<int64_t>((npairs + per_block - 1) / per_block, kUpdGridCap));
 }
 
 dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t* uprec) {
