@@ -63,6 +63,11 @@ def main():
                     help="comma-separated workloads (e.g. 2,3,4): instead of the CG bench, time cg_spmv "
                          "(FP64 map) at the workload's tile shape and at the tuned row-block heights "
                          "(paper Sec. 3.3.3) for C = 64 and the workload's C; prints one JSON line")
+    ap.add_argument("--workloads", default="",
+                    help="comma-separated workloads (e.g. 1,2,3,4,5): instead of the CG bench, report per "
+                         "workload the warm time to solution under the all-FP64 map and under the "
+                         "workload's own map, CG iterations/s, true residuals and SpMV GB/s with their "
+                         "roofline fractions; prints one JSON line")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="counter run: a 256 MiB copy (the scale reference), then 5 cg_spmv "
                          "launches per map (all FP64, the bench's mixed map, all BF16); no timing")
@@ -82,6 +87,9 @@ def main():
     if args.tile_shapes:
         tile_shapes(torch, dev, mpcg, [int(c) for c in args.tile_shapes.split(",")], args.spmv_reps)
         return
+    if args.workloads:
+        all_workloads(torch, dev, mpcg, [int(c) for c in args.workloads.split(",")], args.spmv_reps)
+        return
     t0 = time.time()
     w = make_workload(2, "full")
     A = w.A
@@ -96,7 +104,7 @@ def main():
     x = torch.zeros_like(b)
 
     if args.pmc_probe:
-        pmc_probe(torch, dev, S, L, A, pmap)
+        pmc_probe(torch, dev, S, L, A, pmap, b, w, mpcg)
         return
 
     def run_solves(solver, steps):
@@ -284,6 +292,100 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def configure_map(S, w, L, mpcg_mod):
+    """Apply a workload's own precision map or schedule to a handle; returns the static map or None."""
+    from gen import static_map, tile_scores
+
+    kind = w.map_spec["kind"]
+    scores = tile_scores(L.T, 2)
+    if kind == "static":
+        m = static_map(scores, w.map_spec["frac_bf16"], w.map_spec["frac_fp32"])
+        S.cg_set_precision_map(m)
+        return m
+    if kind == "magnitude":
+        S.cg_map_from_magnitude(w.map_spec["t_bf16"], w.map_spec["t_fp32"])
+        return S.cg_get_active_map()
+    if kind == "ratchet":
+        S.cg_set_schedule_residual(w.map_spec["thresholds"], w.map_spec["prec"])
+    elif kind == "tile_rule":
+        S.cg_set_schedule_tile_rule(w.map_spec["period"], scores, w.map_spec["hi"], w.map_spec["lo"])
+    return None
+
+
+def all_workloads(torch, dev, mpcg, cfgs, reps):
+    """Warm time to solution, iterations/s and SpMV bandwidth per workload, both maps.
+
+    Every solve starts from x0 = 0 on the device with b resident; one untimed
+    solve, then the median of three timed ones. SpMV bytes are the algorithmic
+    count of the map the SpMV runs with (the FP64 map, and the workload's own
+    map where it is a fixed per-tile map); an iteration's bytes add 56n (64n
+    with Jacobi) for the vector step.
+    """
+    from gen import make_workload
+
+    out = {"metric": "cg_time_to_solution_by_workload", "workloads": []}
+    for cfg in cfgs:
+        t0 = time.time()
+        w = make_workload(cfg, "full")
+        A = w.A
+        L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+        print(f"# cfg{cfg}: generated and tiled in {time.time() - t0:.0f}s, n={A.n} nnz={A.nnz} T={L.T}",
+              file=sys.stderr, flush=True)
+        b = torch.from_numpy(w.b).to(dev)
+        x = torch.zeros_like(b)
+        xin = torch.from_numpy(np.random.default_rng(7).uniform(-1, 1, A.n)).to(dev)
+        y = torch.empty_like(xin)
+        vec_bytes = (64 if w.jacobi else 56) * A.n
+        rec = {"workload": w.description, "n": A.n, "nnz": A.nnz, "tiles": L.T, "tol": w.tol, "maxit": w.maxit}
+        maps = [("fp64", None)] + ([("own", w.map_spec["kind"])] if w.map_spec["kind"] != "fp64" else [])
+        for label, kind in maps:
+            S = mpcg.Solver(L, np.zeros(L.T, np.uint8), jacobi=w.jacobi)
+            m = np.zeros(L.T, np.uint8) if kind is None else configure_map(S, w, L, mpcg)
+            r = {"map": "all FP64" if kind is None else kind}
+            if m is not None:
+                for _ in range(5):
+                    S.cg_spmv(xin, y)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    S.cg_spmv(xin, y)
+                e1.record()
+                torch.cuda.synchronize()
+                sp_ms = e0.elapsed_time(e1) / reps
+                nb = spmv_algorithmic_bytes(L, m)
+                r.update(spmv_us=round(sp_ms * 1e3, 2), spmv_gbs=round(nb / (sp_ms * 1e-3) / 1e9, 1),
+                         spmv_frac_hbm=round(nb / (sp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+            S.cg_solve(b, x, w.tol, w.maxit)
+            times = []
+            for _ in range(3):
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                status, K, hist = S.cg_solve(b, x, w.tol, w.maxit)
+                torch.cuda.synchronize()
+                times.append(time.perf_counter() - t1)
+            tts = sorted(times)[1]
+            true_res = float(np.linalg.norm(w.b - A.to_scipy() @ x.cpu().numpy()) / np.linalg.norm(w.b))
+            r.update(status=status, iterations=K, time_to_solution_ms=round(tts * 1e3, 3),
+                     iterations_per_s=round(K / tts, 1), recurrence_residual=float(hist[-1]),
+                     true_residual=true_res)
+            if m is not None:
+                it_gbs = (spmv_algorithmic_bytes(L, m) + vec_bytes) * K / tts / 1e9
+                r.update(iteration_gbs=round(it_gbs, 1), iteration_frac_hbm=round(it_gbs / HBM_PEAK_GBS, 4))
+            rec[label] = r
+            print(f"# cfg{cfg} {r['map']}: {status} K={K} TTS {tts * 1e3:.2f} ms ({K / tts:.0f} it/s), "
+                  f"true residual {true_res:.2e}" + (f", SpMV {r['spmv_us']} us = {r['spmv_frac_hbm']:.2f} of "
+                                                     f"8 TB/s" if 'spmv_us' in r else ""),
+                  file=sys.stderr, flush=True)
+            S.close()
+        if "own" in rec:
+            rec["own_over_fp64_tts_speedup"] = round(rec["fp64"]["time_to_solution_ms"] /
+                                                     rec["own"]["time_to_solution_ms"], 4)
+        L.close()
+        out["workloads"].append(rec)
+    print(json.dumps(out), flush=True)
+
+
 def tile_shapes(torch, dev, mpcg, cfgs, reps):
     """cg_spmv under the all-FP64 map at the workload's tile shape and at the tuned heights.
 
@@ -336,9 +438,11 @@ def tile_shapes(torch, dev, mpcg, cfgs, reps):
     print(json.dumps(out), flush=True)
 
 
-def pmc_probe(torch, dev, S, L, A, pmap):
+def pmc_probe(torch, dev, S, L, A, pmap, b, w, mpcg):
     """Launch sequence for the HBM counter runs: the copy of known size first, then the
-    SpMV under each map. Counters are read per dispatch by rocprofv3."""
+    SpMV under each map, then five CG iterations on the mixed map launched one by one
+    (no graph), so that the update and direction kernels are counted too. Counters are
+    read per dispatch by rocprofv3."""
     src = torch.empty(COPY_BYTES // 8, dtype=torch.float64, device=dev).uniform_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -353,6 +457,13 @@ def pmc_probe(torch, dev, S, L, A, pmap):
         torch.cuda.synchronize()
         print(f"# pmc probe: 5 cg_spmv launches, {name} map, algorithmic bytes "
               f"{spmv_algorithmic_bytes(L, m)}", file=sys.stderr, flush=True)
+    Sc = mpcg.Solver(L, pmap, use_graph=0)
+    x = torch.zeros_like(b)
+    Sc.cg_solve(b, x, 0.0, 5)
+    torch.cuda.synchronize()
+    Sc.close()
+    print(f"# pmc probe: 5 CG iterations, mixed map, vector bytes per iteration: update {24 * A.n}, "
+          f"direction {40 * A.n}", file=sys.stderr, flush=True)
 
 
 def cpu_baseline(w, pmap, budget_s):

@@ -280,7 +280,9 @@ __global__ __launch_bounds__(kBlock) void build_segments_kernel(const int32_t* _
 // wavefront per batch: lane l sizes tile l and a wave prefix sum places it,
 // then the lanes copy the batch's values 64 at a time, each finding its tile
 // from the window records. Rerun at every map change; in a solve (solve = 1)
-// only at the start of a tile-rule window.
+// only at the start of a tile-rule window, and then only for the batches the
+// tile rule marked dirty (each batch's segment is self-contained). Every
+// batch it rebuilds is marked clean.
 struct RepackArgs {
     const int32_t* btab;
     const int32_t* tptr;
@@ -291,8 +293,10 @@ struct RepackArgs {
     const uint64_t* win_mask;
     const int32_t* win_tile;
     const State* st;
+    uint8_t* dirty;      // per batch: packed values out of date (cleared here)
     int64_t nbatch;
     int32_t solve;
+    int32_t only_dirty;  // 1: rebuild only the batches marked dirty; 0: every batch
 };
 
 __global__ __launch_bounds__(kBlock) void repack_kernel(RepackArgs a) {
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(kBlock) void repack_kernel(RepackArgs a) {
     for (int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + w; b < a.nbatch; b += waves) {
         const int32_t* e = a.btab + b * kBtFields;
         const int tb = e[kBtTile], nt = e[kBtTiles], first = e[kBtFirstNnz], len = e[kBtLen];
-        if (nt == 0) continue;
+        if (nt == 0 || (a.only_dirty && !a.dirty[b])) continue;
         const bool valid = lane < nt;
         const int p = valid ? min((int)a.map[tb + lane], 2) : 0;
         const int sh = 3 - p;
@@ -350,6 +354,7 @@ __global__ __launch_bounds__(kBlock) void repack_kernel(RepackArgs a) {
                     *reinterpret_cast<uint16_t*>(dst + to) = *reinterpret_cast<const uint16_t*>(src + from);
             }
         }
+        if (lane == 0) a.dirty[b] = 0;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -998,7 +1003,10 @@ struct MapArgs {
     const double* hist;
     int32_t* trace_k;
     int32_t* trace_counts;
+    const int32_t* btab;  // tile rule: batches of the SpMV (a partition of the tiles)
+    uint8_t* dirty;       // tile rule: per batch, set when a tile of the batch changed precision
     int64_t T;
+    int64_t nbatch;
     double rho;     // explicit rho (eval mode)
     int32_t solve;  // 1: in-solve window step (reads k and rho_k from the state)
 };
@@ -1016,6 +1024,9 @@ __device__ inline void block_counts_out(unsigned c0, unsigned c1, unsigned c2, i
 
 // Windowed tile rule: at k % period == 0 every tile's precision is re-selected
 // from its score and rho_k, and the window's precision counts are recorded.
+// One wavefront per SpMV batch (lane l: the batch's tile l); a batch with a
+// tile whose code changed is marked dirty, so that the repack that follows
+// rebuilds only those batches' packed values.
 __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
     State* st = a.st;
     double rho = a.rho;
@@ -1029,13 +1040,22 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
         if (slot >= st->trace_cap) slot = -1;
     }
     unsigned c0 = 0, c1 = 0, c2 = 0;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < a.T;
-         t += (int64_t)gridDim.x * blockDim.x) {
-        const int code = tile_rule_code(a.scores[t], rho, st->hi, st->lo);
-        a.map[t] = (uint8_t)code;
-        c0 += code == 0;
-        c1 += code == 1;
-        c2 += code == 2;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    for (int64_t b = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; b < a.nbatch; b += waves) {
+        const int32_t* e = a.btab + b * kBtFields;
+        const int tb = e[kBtTile], nt = e[kBtTiles];
+        bool changed = false;
+        if (lane < nt) {
+            const int64_t t = (int64_t)tb + lane;
+            const int code = tile_rule_code(a.scores[t], rho, st->hi, st->lo);
+            changed = code != (int)a.map[t];
+            a.map[t] = (uint8_t)code;
+            c0 += code == 0;
+            c1 += code == 1;
+            c2 += code == 2;
+        }
+        if (__any(changed) && lane == 0) a.dirty[b] = 1;
     }
     if (slot >= 0) {
         block_counts_out(c0, c1, c2, a.trace_counts + ((size_t)slot * kTraceBlocks + blockIdx.x) * 3);

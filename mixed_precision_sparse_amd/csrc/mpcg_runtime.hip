@@ -66,6 +66,7 @@ struct cg_handle {
     char* planes = nullptr;        // per-batch value segments (FP64, FP32, BF16)
     char* packed = nullptr;        // per-batch packed values of the active map (same offsets)
     int32_t* toff = nullptr;       // [T] packed start of every tile (see repack_kernel)
+    uint8_t* dirty = nullptr;      // [nbatch] packed segment out of date (tile rule -> repack)
     int64_t planes_bytes = 0;
     std::vector<int32_t> btab_host;  // host copy of the batch table
     double* dinv = nullptr;
@@ -282,8 +283,10 @@ void launch_repack(cg_handle* h, int solve, hipStream_t s) {
     a.win_mask = h->win_mask;
     a.win_tile = h->win_tile;
     a.st = h->st;
+    a.dirty = h->dirty;
     a.nbatch = h->nbatch;
     a.solve = solve;
+    a.only_dirty = solve;  // in a solve the tile rule has just marked the batches it changed
     const int64_t blocks = (h->nbatch + dev::kWavesPerBlock - 1) / dev::kWavesPerBlock;
     hipLaunchKernelGGL(dev::repack_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 16384))),
                        dim3(dev::kBlock), 0, s, a);
@@ -329,7 +332,10 @@ dev::MapArgs map_args(cg_handle* h, double rho, int solve) {
     a.hist = h->hist;
     a.trace_k = h->trace_k;
     a.trace_counts = h->trace_counts;
+    a.btab = h->btab;
+    a.dirty = h->dirty;
     a.T = h->T;
+    a.nbatch = h->nbatch;
     a.rho = rho;
     a.solve = solve;
     return a;
@@ -815,6 +821,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     TRY(dalloc(h, &h->planes, h->planes_bytes));
     TRY(dalloc(h, &h->packed, h->planes_bytes));
     TRY(dalloc(h, &h->toff, std::max<int64_t>(T, 1)));
+    TRY(dalloc(h, &h->dirty, std::max<int64_t>(h->nbatch, 1)));
     // CG vectors padded with zeros to an even length (the vector kernels work
     // in 16-byte pairs); nothing writes the padding.
     const int64_t n_pad = n + (n & 1);
@@ -874,7 +881,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     } else if ((e = hipMemsetAsync(h->map, 0, T, s))) {
         return dev_err(e, "map");
     }
-    if ((e = hipMemsetAsync(h->planes, 0, h->planes_bytes, s)) ||
+    if ((e = hipMemsetAsync(h->dirty, 0, (size_t)std::max<int64_t>(h->nbatch, 1), s)) ||
+        (e = hipMemsetAsync(h->planes, 0, h->planes_bytes, s)) ||
         (e = hipMemsetAsync(h->packed, 0, h->planes_bytes, s)))
         return dev_err(e, "planes");
     hipLaunchKernelGGL(dev::build_segments_kernel,

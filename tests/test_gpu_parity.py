@@ -356,3 +356,25 @@ def test_cg_launch_modes_agree(graph, window, dev):
     assert torch.equal(x3, xd)
     S.close()
     S2.close()
+
+
+def test_tile_rule_packed_values_follow_the_map_after_a_solve(dev):
+    """In a solve the tile rule repacks only the batches whose tiles changed
+    precision; afterwards cg_spmv under the final map matches the oracle."""
+    w = make_workload(5, "small")
+    A = w.A
+    L, Lo = build_both(w)
+    s = tile_scores(L.T, 2)
+    S = mpcg.Solver(L)
+    S.cg_set_schedule_tile_rule(10, s, w.map_spec["hi"], w.map_spec["lo"])
+    bd = torch.from_numpy(w.b).to(dev)
+    for maxit in (35, 120, 400):
+        xd = torch.zeros_like(bd)
+        S.cg_solve(bd, xd, w.tol, maxit)
+        ks, counts = S.cg_get_map_trace()
+        m = S.cg_get_active_map()
+        log(f"tile rule, maxit {maxit}: {len(ks)} windows, final counts {np.bincount(m, minlength=3).tolist()}")
+        assert len(ks) >= 2 and len({tuple(c) for c in counts.tolist()}) >= 2  # the map really changed
+        x = np.random.default_rng(maxit).uniform(-1, 1, A.n)
+        spmv_check(S, Lo, A, m, x, dev)
+    S.close()
