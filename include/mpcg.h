@@ -183,15 +183,19 @@ typedef struct {
 int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, const cg_options* opt,
               void* stream, cg_handle** out);
 
+/* Free a handle and all its device memory; waits for the device first.
+ * NULL is accepted. The handle must not be used afterwards. */
 int cg_destroy(cg_handle* h);
 
 /* Replace the active per-tile map (uint8[T], codes 0..2) without touching the
  * value planes (Sec. 3.3.2: switching reads another stream, nothing is
- * re-uploaded); only the SpMV's per-map sweep plan (16 bytes per tile and 12
- * per window of 64 nonzeros) is rebuilt on the device. on_device = 0: host
- * pointer; 1: device pointer (copied through the host and validated like a
- * host map). Clears any schedule. Synchronous with respect to the host.
- * Errors: CG_EINVAL (NULL argument, a code > 2), CG_EDEVICE. */
+ * re-uploaded from the host). The SpMV reads a packed copy of the selected
+ * values (each tile's values at its map precision, tile after tile), which is
+ * rebuilt on the device from the planes, together with one 4-byte offset per
+ * tile. on_device = 0: host pointer; 1: device pointer (copied through the
+ * host and validated like a host map). Clears any schedule. Synchronous with
+ * respect to the host. Errors: CG_EINVAL (NULL argument, a code > 2),
+ * CG_EDEVICE. */
 int cg_set_precision_map(cg_handle* h, const uint8_t* map, int32_t on_device);
 
 /* Copy the active map to host uint8[T]. Under a uniform residual schedule the
@@ -264,7 +268,10 @@ int cg_clear_schedule(cg_handle* h);
 /*
  * y = (A + E(map)) x (Eq. (5)): each tile's values are read from the plane
  * its active map entry selects, widened exactly, and every product and sum is
- * formed in FP64.
+ * formed in FP64. The map is the active map, or under a schedule: the first
+ * stage's precision (residual schedule), the max|p| rule applied to x, the
+ * tile rule's current map. With the handle's CG_P1_* options the product
+ * follows them (x_j rounded to the tile's precision, column scale, padding).
  *   x, y : device double[n]; y must not overlap x. Asynchronous on stream.
  * Errors: CG_EINVAL on NULL or overlapping pointers.
  */
@@ -318,7 +325,11 @@ int cg_get_sizes(const cg_handle* h, int64_t* n, int64_t* T, int64_t* nnz, int32
 /* Device-resident bytes held by the handle (matrix, planes, map, vectors). */
 int64_t cg_device_bytes(const cg_handle* h);
 
+/* Message of the calling thread's last failed call ("" when the last call
+ * succeeded); owned by the library, valid until that thread's next call. */
 const char* cg_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
 int cg_version(void);
 
 #ifdef __cplusplus
