@@ -830,7 +830,10 @@ __global__ __launch_bounds__(kBlock) void cg_init_finish_kernel(VecArgs a) {
 // per chunk). The handle's vectors are padded with zeros to an even length,
 // so pairs need no tail handling. Each kernel issues its first chunk's loads
 // before it sums the previous kernel's partials, which hides that sum.
-constexpr int kVecBlock = 1024;
+#ifndef MPCG_VEC_BLOCK
+#define MPCG_VEC_BLOCK 512
+#endif
+constexpr int kVecBlock = MPCG_VEC_BLOCK;
 constexpr int kVecWaves = kVecBlock / kWave;
 #ifndef MPCG_VEC_PAIRS
 #define MPCG_VEC_PAIRS 4

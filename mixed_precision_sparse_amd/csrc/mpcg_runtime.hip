@@ -154,7 +154,7 @@ int grid_for(int64_t work, int per_thread, int cap) {
 
 constexpr int kVecGridCap = 1024;
 #ifndef MPCG_UPD_GRID_CAP
-#define MPCG_UPD_GRID_CAP 512
+#define MPCG_UPD_GRID_CAP 1024
 #endif
 constexpr int kUpdGridCap = MPCG_UPD_GRID_CAP;  // blocks of the update and direction kernels
 #ifndef MPCG_SPMV_GRID_CAP

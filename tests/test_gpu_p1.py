@@ -246,26 +246,32 @@ def _agree(tr, tr_ref, tol):
     return abs(a - b) <= 1e-2 * b
 
 
-@pytest.mark.parametrize("cfg,flags", [(1, RV | PAD), (2, RV), (2, RV | CS | PAD), (3, RV), (3, RV | CS | PAD)])
+@pytest.mark.parametrize("cfg,flags", [(1, RV | PAD), (2, RV), (2, RV | CS | PAD), (3, RV), (3, RV | CS | PAD),
+                                       (2, CS | PAD)])
 def test_p1_cg_matches_oracle(cfg, flags, dev):
     w = make_workload(cfg, "small")
     A = w.A
     L, Lo = _both(A, w.R, w.C)
     prec = static_map(tile_scores(L.T, 2))
     maxit = min(w.maxit, 3000)
-    log(f"p1 cg cfg{cfg} flags={flags} n={w.n}")
-    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, w.b, ocg.StaticSchedule(prec), w.tol, maxit,
+    # With the vector rounded the true residual floors near 1e-3 on these
+    # matrices while the recurrence keeps falling through rounding noise, where
+    # K and the final iterate depend on summation order; those runs stop at a
+    # tolerance above the floor.
+    tol = 1e-2 if flags & RV else w.tol
+    log(f"p1 cg cfg{cfg} flags={flags} n={w.n} tol={tol}")
+    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, w.b, ocg.StaticSchedule(prec), tol, maxit,
                     keep_maps=False, round_vector=bool(flags & RV), column_scale=bool(flags & CS))
     S = mpcg.Solver(L, precision_map=prec, p1=flags)
     bd = torch.from_numpy(w.b).to(dev)
     xd = torch.zeros_like(bd)
-    status, K, hist = S.cg_solve(bd, xd, w.tol, maxit)
+    status, K, hist = S.cg_solve(bd, xd, tol, maxit)
     x = xd.cpu().numpy()
     tr = float(np.linalg.norm(w.b - A.to_scipy() @ x) / np.linalg.norm(w.b))
     log(f"  gpu {status} K={K} true={tr:.3e}; oracle {ref.status} K={ref.K} true={ref.true_residual:.3e}")
-    assert status == ref.status
+    assert status == ref.status == "converged"
     assert _k_close(K, ref.K), (K, ref.K)
-    assert _agree(tr, ref.true_residual, w.tol), (tr, ref.true_residual)
+    assert _agree(tr, ref.true_residual, tol), (tr, ref.true_residual)
     m = min(K, ref.K, 20)
     assert np.allclose(hist[: m + 1], ref.hist[: m + 1], rtol=1e-6, atol=0)
     S.close()
