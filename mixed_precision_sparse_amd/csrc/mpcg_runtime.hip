@@ -603,15 +603,24 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     h->meta16 = !(A->R <= 16 && A->C <= 16) || (p1 & CG_P1_PAD_COLUMNS);
     // Row blocks per wavefront: the largest of 32, 64, 128, 256 rows whose row
     // groups hold at most one batch of tiles on average (at least one row block).
+    // A small matrix would then leave too few groups (wavefronts) to spread its
+    // product over the chip: below kMinGroups groups the group shrinks to the
+    // largest size that reaches kMinGroups, down to one row block.
     auto group_rb = [&](int rows) { return std::max(1, std::min(dev::kMaxGroupRB, rows / A->R)); };
+    auto groups_of = [&](int G) { return (h->nrb + G - 1) / G; };
     if (dev::kGroupRows > 0) {
         h->G = group_rb(dev::kGroupRows);
     } else {
         h->G = group_rb(32);
         for (int rows : {64, 128, 256}) {
             const int G = group_rb(rows);
-            const int64_t groups = (h->nrb + G - 1) / G;
-            if (groups > 0 && T <= (int64_t)dev::kTileBatch * groups) h->G = G;
+            if (groups_of(G) > 0 && T <= (int64_t)dev::kTileBatch * groups_of(G)) h->G = G;
+        }
+        constexpr int64_t kMinGroups = 1024;
+        if (groups_of(h->G) < kMinGroups) {
+            int G = h->G;
+            while (G > 1 && groups_of(G) < kMinGroups) G = std::max(1, G / 2);
+            h->G = G;
         }
     }
     h->rows_per_group = h->G * A->R;
