@@ -558,7 +558,12 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
         // shift 3.
         const uint32_t h = (raw[u].x >> hs[u]) << 16;
         const uint32_t f = d[u].w == 1 ? h : raw[u].x;
-        const double v32 = (double)__uint_as_float(f);
+        double v32 = (double)__uint_as_float(f);
+        // Materialise the widened value in every lane (an empty statement that
+        // emits nothing), so that the choice below stays two selects: left to
+        // itself the compiler branches around the conversion, which costs five
+        // scalar and control instructions per window in an issue-bound loop.
+        asm volatile("" : "+v"(v32));
         double v = d[u].w == 3 ? __longlong_as_double(((long long)raw[u].y << 32) | raw[u].x) : v32;
         double xu = xv[u];
         if (P1) {
