@@ -7,8 +7,12 @@ residual, plus the map trace and, where the layout is cheap to hash, SHA-256
 digests of the canonical Tile-CSC arrays.
 
 Usage: python tests/golden/make_golden.py CFG [CFG ...]
+       python tests/golden/make_golden.py --only LABEL CFG   (one map: fp64 or mixed,
+                                                               written to a part file)
+       python tests/golden/make_golden.py --merge CFG        (part files -> the result)
 Each run is single-threaded and takes from about a minute (cfg2) to more
-than an hour (cfg5, two 5000-iteration solves).
+than an hour (cfg5, two 5000-iteration solves); the two maps of one
+workload can run as two processes with --only, then --merge.
 """
 
 import hashlib
@@ -39,7 +43,7 @@ def layout_digest(L):
                 col_local=sha(L.col_local, np.uint8))
 
 
-def run(cfg, scale="full"):
+def run(cfg, scale="full", only=None):
     t0 = time.time()
     w = make_workload(cfg, scale)
     A = w.A
@@ -55,6 +59,8 @@ def run(cfg, scale="full"):
     specs = [("fp64", dict(kind="fp64"))]
     if w.map_spec["kind"] != "fp64":
         specs.append(("mixed", w.map_spec))
+    if only is not None:
+        specs = [s for s in specs if s[0] == only]
     for label, spec in specs:
         t1 = time.time()
         sched = cg.schedule_for(spec, L, scores=scores, static=static)
@@ -71,12 +77,35 @@ def run(cfg, scale="full"):
                                   true_residual=res.true_residual, seconds=el, windows=wins)
         print(f"  {label}: K={res.K} {res.status} rho={res.hist[-1]:.3e} "
               f"true={res.true_residual:.3e} ({el:.1f}s)", flush=True)
-    path = os.path.join(HERE, f"cg_cfg{cfg}_{scale}.json")
+    path = os.path.join(HERE, f"cg_cfg{cfg}_{scale}.json" if only is None else f"cg_cfg{cfg}_{scale}.{only}.part")
     with open(path, "w") as f:
         json.dump(out, f)
     print(f"wrote {path}", flush=True)
 
 
+def merge(cfg, scale="full"):
+    """Combine the per-map part files of one workload into its result file."""
+    parts = [os.path.join(HERE, f"cg_cfg{cfg}_{scale}.{label}.part") for label in ("fp64", "mixed")]
+    docs = [json.load(open(p)) for p in parts if os.path.exists(p)]
+    if not docs:
+        raise SystemExit("no part files")
+    out = docs[0]
+    for d in docs[1:]:
+        if d["input_hash"] != out["input_hash"] or d["layout"] != out["layout"]:
+            raise SystemExit("part files disagree on the inputs")
+        out["runs"].update(d["runs"])
+    path = os.path.join(HERE, f"cg_cfg{cfg}_{scale}.json")
+    with open(path, "w") as f:
+        json.dump(out, f)
+    print(f"wrote {path} with runs {sorted(out['runs'])}", flush=True)
+
+
 if __name__ == "__main__":
-    for a in sys.argv[1:]:
-        run(int(a))
+    args = sys.argv[1:]
+    if args and args[0] == "--only":
+        run(int(args[2]), only=args[1])
+    elif args and args[0] == "--merge":
+        merge(int(args[1]))
+    else:
+        for a in args:
+            run(int(a))
