@@ -68,6 +68,13 @@ def main():
                          "workload the warm time to solution under the all-FP64 map and under the "
                          "workload's own map, CG iterations/s, true residuals and SpMV GB/s with their "
                          "roofline fractions; prints one JSON line")
+    ap.add_argument("--col-slices", default="",
+                    help="with --workloads or --spmv-probe: comma-separated column-slice counts (e.g. 8,16) whose handles "
+                         "are timed beside the unsliced ones")
+    ap.add_argument("--spmv-probe", default="",
+                    help="counter run on comma-separated workloads (e.g. 4,5): a 256 MiB copy (the scale "
+                         "reference), then per workload 5 cg_spmv launches under the all-FP64 map on the "
+                         "unsliced handle and on one per --col-slices count; no timing")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="counter run: a 256 MiB copy (the scale reference), then 5 cg_spmv "
                          "launches per map (all FP64, the bench's mixed map, all BF16); no timing")
@@ -87,8 +94,13 @@ def main():
     if args.tile_shapes:
         tile_shapes(torch, dev, mpcg, [int(c) for c in args.tile_shapes.split(",")], args.spmv_reps)
         return
+    if args.spmv_probe:
+        spmv_probe(torch, dev, mpcg, [int(c) for c in args.spmv_probe.split(",")],
+                   [int(c) for c in args.col_slices.split(",") if c])
+        return
     if args.workloads:
-        all_workloads(torch, dev, mpcg, [int(c) for c in args.workloads.split(",")], args.spmv_reps)
+        all_workloads(torch, dev, mpcg, [int(c) for c in args.workloads.split(",")], args.spmv_reps,
+                      [int(c) for c in args.col_slices.split(",") if c])
         return
     t0 = time.time()
     w = make_workload(2, "full")
@@ -312,14 +324,15 @@ def configure_map(S, w, L, mpcg_mod):
     return None
 
 
-def all_workloads(torch, dev, mpcg, cfgs, reps):
+def all_workloads(torch, dev, mpcg, cfgs, reps, slices=()):
     """Warm time to solution, iterations/s and SpMV bandwidth per workload, both maps.
 
     Every solve starts from x0 = 0 on the device with b resident; one untimed
     solve, then the median of three timed ones. SpMV bytes are the algorithmic
     count of the map the SpMV runs with (the FP64 map, and the workload's own
     map where it is a fixed per-tile map); an iteration's bytes add 56n (64n
-    with Jacobi) for the vector step.
+    with Jacobi) for the vector step. Every count in ``slices`` adds the same
+    runs on a handle with that many column slices.
     """
     from gen import make_workload
 
@@ -337,11 +350,22 @@ def all_workloads(torch, dev, mpcg, cfgs, reps):
         y = torch.empty_like(xin)
         vec_bytes = (64 if w.jacobi else 56) * A.n
         rec = {"workload": w.description, "n": A.n, "nnz": A.nnz, "tiles": L.T, "tol": w.tol, "maxit": w.maxit}
-        maps = [("fp64", None)] + ([("own", w.map_spec["kind"])] if w.map_spec["kind"] != "fp64" else [])
-        for label, kind in maps:
-            S = mpcg.Solver(L, np.zeros(L.T, np.uint8), jacobi=w.jacobi)
-            m = np.zeros(L.T, np.uint8) if kind is None else configure_map(S, w, L, mpcg)
-            r = {"map": "all FP64" if kind is None else kind}
+        own = w.map_spec["kind"]
+        runs = [("fp64", None, 0)] + ([("own", own, 0)] if own != "fp64" else [])
+        for ns in slices:  # column-sliced handles (the tile rule needs canonical order)
+            runs += [(f"fp64_slices{ns}", None, ns)] + \
+                ([(f"own_slices{ns}", own, ns)] if own not in ("fp64", "tile_rule") else [])
+        static_own = None  # the magnitude rule's map, set as a fixed map on sliced handles
+        for label, kind, ns in runs:
+            S = mpcg.Solver(L, np.zeros(L.T, np.uint8), jacobi=w.jacobi, col_slices=ns)
+            if kind == "magnitude" and ns > 0:
+                S.cg_set_precision_map(static_own)
+                m = static_own
+            else:
+                m = np.zeros(L.T, np.uint8) if kind is None else configure_map(S, w, L, mpcg)
+                if kind == "magnitude":
+                    static_own = m
+            r = {"map": "all FP64" if kind is None else kind, "col_slices": ns}
             if m is not None:
                 for _ in range(5):
                     S.cg_spmv(xin, y)
@@ -373,7 +397,7 @@ def all_workloads(torch, dev, mpcg, cfgs, reps):
                 it_gbs = (spmv_algorithmic_bytes(L, m) + vec_bytes) * K / tts / 1e9
                 r.update(iteration_gbs=round(it_gbs, 1), iteration_frac_hbm=round(it_gbs / HBM_PEAK_GBS, 4))
             rec[label] = r
-            print(f"# cfg{cfg} {r['map']}: {status} K={K} TTS {tts * 1e3:.2f} ms ({K / tts:.0f} it/s), "
+            print(f"# cfg{cfg} {label}: {status} K={K} TTS {tts * 1e3:.2f} ms ({K / tts:.0f} it/s), "
                   f"true residual {true_res:.2e}" + (f", SpMV {r['spmv_us']} us = {r['spmv_frac_hbm']:.2f} of "
                                                      f"8 TB/s" if 'spmv_us' in r else ""),
                   file=sys.stderr, flush=True)
@@ -464,6 +488,35 @@ def pmc_probe(torch, dev, S, L, A, pmap, b, w, mpcg):
     Sc.close()
     print(f"# pmc probe: 5 CG iterations, mixed map, vector bytes per iteration: update {24 * A.n}, "
           f"direction {40 * A.n}", file=sys.stderr, flush=True)
+
+
+def spmv_probe(torch, dev, mpcg, cfgs, slices):
+    """Launch sequence for counter runs of the SpMV on any workload: the copy of known
+    size, then per workload and column-slice count (0 = unsliced) five cg_spmv launches
+    under the all-FP64 map. With slices the combine kernel follows every SpMV."""
+    from gen import make_workload
+
+    src = torch.empty(COPY_BYTES // 8, dtype=torch.float64, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    for cfg in cfgs:
+        w = make_workload(cfg, "full")
+        A = w.A
+        L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+        m = np.zeros(L.T, np.uint8)
+        xin = torch.from_numpy(np.random.default_rng(7).uniform(-1, 1, A.n)).to(dev)
+        y = torch.empty_like(xin)
+        for ns in [0] + list(slices):
+            S = mpcg.Solver(L, m, col_slices=ns)
+            for _ in range(5):
+                S.cg_spmv(xin, y)
+            torch.cuda.synchronize()
+            S.close()
+            print(f"# spmv probe: cfg{cfg}, {ns} column slices, 5 cg_spmv launches, all-FP64 map, "
+                  f"algorithmic bytes {spmv_algorithmic_bytes(L, m)}", file=sys.stderr, flush=True)
+        L.close()
 
 
 def cpu_baseline(w, pmap, budget_s):

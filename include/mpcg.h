@@ -164,8 +164,24 @@ typedef struct {
     int32_t use_graph;   /* 1: replay each window as a captured HIP graph; 0 = plain launches;
                             -1 = default (graph) */
     int32_t p1;          /* CG_P1_* bits: the paper's own SpMV numerics (above); 0 = off */
-    int32_t reserved[4];
+    int32_t col_slices;  /* column slices S in [0, 64]; 0 or 1 = none (below) */
+    int32_t reserved[3];
 } cg_options;
+
+/*
+ * Column slices (cg_options.col_slices = S > 1): the SpMV takes the tiles in S
+ * groups of consecutive column blocks, one after the other, so that the part
+ * of x a group gathers can stay in the L2 of the XCDs that sweep it. This is
+ * for matrices whose columns scatter over an x much larger than one XCD's
+ * L2, such as random sparsity. Each slice writes its own partial product
+ * (S * 8n more bytes written, and read once more, per product). The sums are
+ * formed in a fixed order: the SpMV result equals the unsliced one within
+ * rounding. Supported with static maps, the residual schedule, Jacobi and the
+ * CG_P1_* options; cg_map_from_magnitude and the tile and max|p| rules return
+ * CG_EINVAL on such a handle. The device keeps the tiles in slice order;
+ * maps, the map trace and cg_export_layout use the canonical tile order as
+ * everywhere else.
+ */
 
 /*
  * Create a solver handle on the current HIP device.
@@ -178,7 +194,7 @@ typedef struct {
  *   stream        : stream for the set-up copies and kernels.
  * Errors: CG_EINVAL (map code > 2, bad layout, n >= 2^28 or T or nnz >= 2^31,
  * Jacobi with a zero or missing diagonal entry, unknown p1 bits, padding with
- * R = 256), CG_ENOMEM, CG_EDEVICE.
+ * R = 256, col_slices outside [0, 64]), CG_ENOMEM, CG_EDEVICE.
  */
 int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, const cg_options* opt,
               void* stream, cg_handle** out);

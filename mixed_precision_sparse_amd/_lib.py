@@ -31,7 +31,8 @@ class cg_tilecsc_view(ct.Structure):
 
 
 class cg_options(ct.Structure):
-    _fields_ = [("jacobi", i32), ("window", i32), ("use_graph", i32), ("p1", i32), ("reserved", i32 * 4)]
+    _fields_ = [("jacobi", i32), ("window", i32), ("use_graph", i32), ("p1", i32), ("col_slices", i32),
+                ("reserved", i32 * 3)]
 
 
 # name -> (restype, argtypes)

@@ -241,6 +241,9 @@ __host__ __device__ inline int batch_records(int len) { return sweep_windows((le
 // has one entry with no tiles, so its rows are still written.
 enum BatchField { kBtTile = 0, kBtTiles, kBtFirstNnz, kBtLen, kBtRecords, kBtGroup, kBtFlags, kBtSegment, kBtFields };
 constexpr int kBatchFirstOfGroup = 1, kBatchLastOfGroup = 2;
+// Bits from kBatchSliceShift up: the column slice of the batch's segment,
+// whose rows go to partial product number slice (stride SpmvArgs.ystride).
+constexpr int kBatchSliceShift = 8;
 
 // Value planes, stored per batch: one 16-byte aligned segment holds the
 // batch's FP64 values (8*len bytes), then its FP32 values (4*len), then its
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(kBlock) void repack_kernel(RepackArgs a) {
 
 struct SpmvArgs {
     const int32_t* btab;    // [nbatch][8] batch table
-    const int32_t* gbatch;  // [ngroups+1] first batch of every row group
+    const int32_t* gbatch;  // [ngroups+1] first batch of every segment (a row group, per column slice)
     const int2* tent;       // [T] per tile: x byte offset of its column block, accumulator byte offset of its rows
     const uint8_t* map;     // [T] active precision map
     const int32_t* toff;    // [T] per tile: its values' start in the packed segment minus position << width shift
@@ -382,6 +385,7 @@ struct SpmvArgs {
     double* partials;      // CG mode: one p.q partial per block
     const int16_t* colexp;  // P1 kernels: per column e_j of the scale 2^e_j (NULL: no scale)
     int32_t n, rows_per_group, ngroups, groups_per_wave, nwin;
+    int32_t ystride;       // column slices: distance between two slices' partial products
     int32_t p1_round;      // P1 kernels: round the vector entry to the tile's precision
     int32_t sentinel_row;  // P1 kernels: row offset of padding entries (R), or -1
 };
@@ -695,15 +699,17 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
         if (more && E == 0) load_batch_regs<CB>(c, Hn, 0, true, Rn);  // a batch without windows
         wave_lds_sync();
         if (H.flags & kBatchLastOfGroup) {
+            // This segment's partial product (the product itself without column slices).
+            double* __restrict__ yo = y + (size_t)(H.flags >> kBatchSliceShift) * a.ystride;
             for (int i = lane; i < nrows; i += kWave) {
                 const double acc = s_acc[w][i];
                 if (MODE == kSpmvPlain) {
-                    y[row0 + i] = acc;
+                    yo[row0 + i] = acc;
                 } else if (MODE == kSpmvCg) {
-                    y[row0 + i] = acc;
+                    yo[row0 + i] = acc;
                     dot += (MAXROWS <= kWave ? p_own : a.x[row0 + i]) * acc;
                 } else {
-                    y[row0 + i] = a.b[row0 + i] - acc;
+                    yo[row0 + i] = a.b[row0 + i] - acc;
                 }
             }
             wave_lds_sync();
@@ -736,7 +742,7 @@ struct VecArgs {
     double* x;
     double* r;
     double* p;
-    const double* q;
+    const double* q;      // the product q, or its column-slice partial products (nq of them)
     double* z;            // Jacobi only (z = dinv .* r)
     const double* dinv;   // Jacobi only
     const double* b;
@@ -752,6 +758,8 @@ struct VecArgs {
     int32_t n;
     int32_t jacobi;
     int32_t r_ready;         // init: r already holds b - A x0
+    int32_t nq;              // partial products summed into q (column slices), >= 1
+    int64_t qstride;         // distance between two partial products
 };
 
 __device__ inline void trace_uniform(State* st, int32_t* trace_k, int32_t* trace_counts, int k,
@@ -874,6 +882,11 @@ __global__ __launch_bounds__(kVecBlock) void cg_update_kernel(VecArgs a) {
             if (i < npairs) {
                 rv[j] = r2[i];
                 qv[j] = q2[i];
+                for (int s = 1; s < a.nq; ++s) {  // column slices: q is the sum of the partials
+                    const double2 qs = q2[s * (a.qstride / 2) + i];
+                    qv[j].x += qs.x;
+                    qv[j].y += qs.y;
+                }
                 if (JAC) dv[j] = d2[i];
             }
         }
@@ -992,6 +1005,17 @@ __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
         else if (k >= st->maxit) done = 2;
         else if (st->nstage > 0) advance_stage(st, a.trace_k, a.trace_counts, k, rho, a.T, false);
         if (done) store_done(st, done);
+    }
+}
+
+// Column slices: y = sum of the nparts partial products (or b minus it).
+__global__ __launch_bounds__(kBlock) void combine_kernel(const double* __restrict__ parts, int nparts, int64_t stride,
+                                                        const double* __restrict__ b, double* __restrict__ y,
+                                                        int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        double acc = parts[i];
+        for (int s = 1; s < nparts; ++s) acc += parts[s * stride + i];
+        y[i] = b ? b[i] - acc : acc;
     }
 }
 

@@ -41,6 +41,10 @@ struct cg_handle {
     hipStream_t stream = nullptr;  // internal stream for the solve loop
     int64_t n = 0, T = 0, nnz = 0, nrb = 0;
     int32_t R = 0, C = 0, G = 0, rows_per_group = 0, ngroups = 0;
+    int32_t S = 1;                 // column slices (cg_options.col_slices)
+    int64_t nseg = 0;              // SpMV segments: S * ngroups (slice-major)
+    std::vector<int32_t> dperm;    // S > 1: device tile -> canonical tile
+    double* qpart = nullptr;       // S > 1: [S][n_pad] partial products of the slices
     bool meta16 = false;
     bool jacobi = false;
     int p1 = 0;                    // CG_P1_* options
@@ -55,7 +59,7 @@ struct cg_handle {
     int64_t nwin = 0;
     int2* tent = nullptr;          // [T] SpMV tile entries: x byte offset, accumulator byte offset
     int32_t* btab = nullptr;       // [nbatch][8] SpMV batch table
-    int32_t* gbatch = nullptr;     // [ngroups+1] first batch of every row group
+    int32_t* gbatch = nullptr;     // [nseg+1] first batch of every segment (row group, slice)
     int64_t nbatch = 0;
     int32_t* trp = nullptr;
     int32_t* tcol = nullptr;
@@ -168,9 +172,9 @@ int spmv_grid(const cg_handle* h) { return h->spmv_blocks; }
 // Every SpMV wavefront takes a contiguous range of row groups (a capped grid:
 // a wavefront pipelines its batches); vector kernels use a capped grid.
 void plan_grids(cg_handle* h) {
-    const int64_t waves = std::max<int64_t>(1, std::min<int64_t>(h->ngroups, (int64_t)kSpmvGridCap * dev::kSpmvWaves));
-    h->groups_per_wave = (int)std::max<int64_t>(1, (h->ngroups + waves - 1) / waves);
-    const int64_t used = (h->ngroups + h->groups_per_wave - 1) / h->groups_per_wave;
+    const int64_t waves = std::max<int64_t>(1, std::min<int64_t>(h->nseg, (int64_t)kSpmvGridCap * dev::kSpmvWaves));
+    h->groups_per_wave = (int)std::max<int64_t>(1, (h->nseg + waves - 1) / waves);
+    const int64_t used = (h->nseg + h->groups_per_wave - 1) / h->groups_per_wave;
     h->spmv_blocks = (int)std::max<int64_t>(1, (used + dev::kSpmvWaves - 1) / dev::kSpmvWaves);
     h->vec_blocks = grid_for(h->n, 8, kVecGridCap);
     const int64_t npairs = (h->n + 1) / 2;
@@ -200,7 +204,8 @@ dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t*
     a.partials = h->part_spmv;
     a.n = (int32_t)h->n;
     a.rows_per_group = h->rows_per_group;
-    a.ngroups = h->ngroups;
+    a.ngroups = (int32_t)h->nseg;
+    a.ystride = (int32_t)(h->n + (h->n & 1));
     a.groups_per_wave = h->groups_per_wave;
     a.nwin = (int32_t)h->nwin;
     a.colexp = (h->p1 & CG_P1_COLUMN_SCALE) ? h->colexp : nullptr;
@@ -244,6 +249,12 @@ void launch_spmv(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
     } else {
         launch_spmv_cb<MODE, false, false>(h, a, s);
     }
+}
+
+// Column slices: y = sum of the partial products in qpart (b - sum with b).
+void launch_combine(cg_handle* h, const double* b, double* y, hipStream_t s) {
+    hipLaunchKernelGGL(dev::combine_kernel, dim3(grid_for(h->n, 4, 4096)), dim3(dev::kBlock), 0, s, h->qpart,
+                       h->S, (int64_t)(h->n + (h->n & 1)), b, y, h->n);
 }
 
 // Column-block codes of the max|p| rule from vector v (solve = 1: in-solve,
@@ -305,7 +316,9 @@ dev::VecArgs vec_args(cg_handle* h, const double* b, const double* x0) {
     a.x = h->x;
     a.r = h->r;
     a.p = h->p;
-    a.q = h->q;
+    a.q = h->S > 1 ? h->qpart : h->q;  // with column slices the SpMV leaves partial products
+    a.nq = h->S;
+    a.qstride = h->n + (h->n & 1);
     a.z = h->z;
     a.dinv = h->dinv;
     a.b = b;
@@ -400,7 +413,7 @@ void enqueue_iteration(cg_handle* h, int i, hipStream_t s, bool rule_at_end = fa
         hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, s, ma);
         launch_repack(h, 1, s);
     }
-    dev::SpmvArgs sa = spmv_args(h, h->p, h->q, &h->st->uprec);
+    dev::SpmvArgs sa = spmv_args(h, h->p, h->S > 1 ? h->qpart : h->q, &h->st->uprec);
     launch_spmv<dev::kSpmvCg>(h, sa, s);
     dev::VecArgs va = vec_args(h, nullptr, nullptr);
     va.part_in = h->part_spmv;
@@ -528,12 +541,11 @@ void pad_columns(const cg_tilecsc& A, cg_tilecsc& P) {
 // scaled values a / s_j in storage order (Sec. 3.3.2).
 void column_scale(const cg_tilecsc& A, std::vector<int16_t>& e, std::vector<double>& scaled) {
     std::vector<double> colmax(A.n, 0.0);
-    for (int64_t I = 0; I < A.nrb; ++I)
-        for (int64_t t = A.tile_row_ptr[I]; t < A.tile_row_ptr[I + 1]; ++t) {
-            const int64_t c0 = (int64_t)A.tile_col_idx[t] * A.C;
-            for (int64_t k = A.tile_nnz_ptr[t]; k < A.tile_nnz_ptr[t + 1]; ++k)
-                colmax[c0 + A.col_local[k]] = std::max(colmax[c0 + A.col_local[k]], std::fabs(A.val[k]));
-        }
+    for (int64_t t = 0; t < A.T(); ++t) {
+        const int64_t c0 = (int64_t)A.tile_col_idx[t] * A.C;
+        for (int64_t k = A.tile_nnz_ptr[t]; k < A.tile_nnz_ptr[t + 1]; ++k)
+            colmax[c0 + A.col_local[k]] = std::max(colmax[c0 + A.col_local[k]], std::fabs(A.val[k]));
+    }
     e.assign(A.n, 0);
     for (int64_t j = 0; j < A.n; ++j) {
         int ej = 0;
@@ -546,6 +558,71 @@ void column_scale(const cg_tilecsc& A, std::vector<int16_t>& e, std::vector<doub
             const int64_t c0 = (int64_t)A.tile_col_idx[t] * A.C;
             for (int64_t k = A.tile_nnz_ptr[t]; k < A.tile_nnz_ptr[t + 1]; ++k)
                 scaled[k] = std::ldexp(A.val[k], -(int)e[c0 + A.col_local[k]]);
+        }
+    });
+}
+
+// Device order of the tiles with S column slices: slice s holds the column
+// blocks [ceil(s ncb / S), ceil((s+1) ncb / S)); the tiles are listed slice by
+// slice, then row group by row group (segment s * ngroups + g), then in
+// canonical order. D receives the layout in that order (tile_row_ptr left
+// canonical), trb the row block of every device tile, seg_t0 the first device
+// tile of every segment (nseg + 1 entries), dperm device tile -> canonical.
+void build_slices(const cg_tilecsc& A, int S, int G, int64_t ngroups, cg_tilecsc& D, std::vector<int32_t>& trb,
+                  std::vector<int64_t>& seg_t0, std::vector<int32_t>& dperm) {
+    const int64_t T = A.T(), nrb = A.nrb, ncb = (A.n + A.C - 1) / A.C;
+    auto jlo = [&](int64_t s) { return (s * ncb + S - 1) / S; };
+    // Tiles of row block I in slice s: [lb(I, jlo(s)), lb(I, jlo(s+1))).
+    auto lb = [&](int64_t I, int64_t j) {
+        const int32_t* b = A.tile_col_idx.data() + A.tile_row_ptr[I];
+        const int32_t* e = A.tile_col_idx.data() + A.tile_row_ptr[I + 1];
+        return (int64_t)(std::lower_bound(b, e, (int32_t)j) - A.tile_col_idx.data());
+    };
+    const int64_t nseg = (int64_t)S * ngroups;
+    std::vector<int64_t> cnt(nseg, 0);
+    mpcg::parallel_for(ngroups, [&](int64_t lo, int64_t hi) {
+        for (int64_t g = lo; g < hi; ++g)
+            for (int64_t I = g * G; I < std::min<int64_t>((g + 1) * G, nrb); ++I)
+                for (int64_t s = 0; s < S; ++s) cnt[s * ngroups + g] += lb(I, jlo(s + 1)) - lb(I, jlo(s));
+    });
+    seg_t0.assign(nseg + 1, 0);
+    for (int64_t v = 0; v < nseg; ++v) seg_t0[v + 1] = seg_t0[v] + cnt[v];
+    dperm.assign(T, 0);
+    trb.assign(std::max<int64_t>(T, 1), 0);
+    mpcg::parallel_for(ngroups, [&](int64_t lo, int64_t hi) {
+        for (int64_t g = lo; g < hi; ++g)
+            for (int64_t s = 0; s < S; ++s) {
+                int64_t d = seg_t0[s * ngroups + g];
+                for (int64_t I = g * G; I < std::min<int64_t>((g + 1) * G, nrb); ++I)
+                    for (int64_t t = lb(I, jlo(s)); t < lb(I, jlo(s + 1)); ++t, ++d) {
+                        dperm[d] = (int32_t)t;
+                        trb[d] = (int32_t)I;
+                    }
+            }
+    });
+    D.n = A.n;
+    D.R = A.R;
+    D.C = A.C;
+    D.nrb = A.nrb;
+    D.tile_row_ptr = A.tile_row_ptr;
+    D.tile_col_idx.resize(T);
+    D.tile_nnz_ptr.assign(T + 1, 0);
+    for (int64_t d = 0; d < T; ++d) {
+        const int64_t t = dperm[d];
+        D.tile_col_idx[d] = A.tile_col_idx[t];
+        D.tile_nnz_ptr[d + 1] = D.tile_nnz_ptr[d] + (A.tile_nnz_ptr[t + 1] - A.tile_nnz_ptr[t]);
+    }
+    const int64_t nnz = A.nnz();
+    D.row_idx.resize(nnz);
+    D.col_local.resize(nnz);
+    D.val.resize(nnz);
+    mpcg::parallel_for(T, [&](int64_t lo, int64_t hi) {
+        for (int64_t d = lo; d < hi; ++d) {
+            const int64_t t = dperm[d], k0 = A.tile_nnz_ptr[t], len = A.tile_nnz_ptr[t + 1] - k0;
+            const int64_t o = D.tile_nnz_ptr[d];
+            std::memcpy(&D.row_idx[o], &A.row_idx[k0], len);
+            std::memcpy(&D.col_local[o], &A.col_local[k0], len);
+            std::memcpy(&D.val[o], &A.val[k0], sizeof(double) * len);
         }
     });
 }
@@ -629,88 +706,113 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         h->jacobi = opt->jacobi != 0;
         if (opt->window > 0) h->window = std::min(opt->window, 4096);
         if (opt->use_graph >= 0) h->use_graph = opt->use_graph != 0;
+        if (opt->col_slices < 0 || opt->col_slices > 64)
+            return bail(fail(CG_EINVAL, "cg_create: col_slices must lie in [0, 64]"));
+        h->S = std::max(1, opt->col_slices);
     }
 
+    // Device order of the tiles: canonical, or slice by slice (col_slices).
+    // D is the layout in device order; segment v (slice v / ngroups, row group
+    // v % ngroups) owns device tiles [seg_t0[v], seg_t0[v + 1]).
+    h->nseg = (int64_t)h->S * h->ngroups;
+    cg_tilecsc sliced;
+    const cg_tilecsc* D = A;
+    std::vector<int32_t> trb;
+    std::vector<int64_t> seg_t0;
+    if (h->S > 1) {
+        build_slices(*A, h->S, h->G, h->ngroups, sliced, trb, seg_t0, h->dperm);
+        D = &sliced;
+    } else {
+        trb.assign(std::max<int64_t>(T, 1), 0);
+        mpcg::parallel_for(h->nrb, [&](int64_t lo, int64_t hi) {
+            for (int64_t I = lo; I < hi; ++I)
+                for (int64_t t = A->tile_row_ptr[I]; t < A->tile_row_ptr[I + 1]; ++t) trb[t] = (int32_t)I;
+        });
+        seg_t0.assign(h->nseg + 1, 0);
+        for (int64_t g = 0; g <= h->ngroups; ++g)
+            seg_t0[g] = A->tile_row_ptr[std::min<int64_t>(g * h->G, h->nrb)];
+    }
+    auto seg_group = [&](int64_t v) { return v % h->ngroups; };
+    auto seg_slice = [&](int64_t v) { return v / h->ngroups; };
     // Host-side packing of the device layout: 32-bit offsets and packed (row, col).
     std::vector<int32_t> trp(h->nrb + 1), tptr(T + 1);
     for (int64_t i = 0; i <= h->nrb; ++i) trp[i] = (int32_t)A->tile_row_ptr[i];
-    for (int64_t i = 0; i <= T; ++i) tptr[i] = (int32_t)A->tile_nnz_ptr[i];
+    for (int64_t i = 0; i <= T; ++i) tptr[i] = (int32_t)D->tile_nnz_ptr[i];
     std::vector<uint8_t> meta8;
     std::vector<uint16_t> meta16;
     if (h->meta16) {
         meta16.resize(nnz);
         mpcg::parallel_for(nnz, [&](int64_t lo, int64_t hi) {
             for (int64_t k = lo; k < hi; ++k)
-                meta16[k] = (uint16_t)((A->row_idx[k] << 8) | A->col_local[k]);
+                meta16[k] = (uint16_t)((D->row_idx[k] << 8) | D->col_local[k]);
         });
     } else {
         meta8.resize(nnz);
         mpcg::parallel_for(nnz, [&](int64_t lo, int64_t hi) {
-            for (int64_t k = lo; k < hi; ++k) meta8[k] = (uint8_t)((A->row_idx[k] << 4) | A->col_local[k]);
+            for (int64_t k = lo; k < hi; ++k) meta8[k] = (uint8_t)((D->row_idx[k] << 4) | D->col_local[k]);
         });
     }
-    // Window records of the SpMV sweep: row group g's tiles are taken in batches
+    // Window records of the SpMV sweep: a segment's tiles are taken in batches
     // of kTileBatch and every batch owns batch_records(len) records: its windows
     // of 64 nonzeros, then padding up to the sweep sizes the kernel runs.
-    std::vector<int32_t> win_base(h->ngroups + 1, 0);
+    std::vector<int32_t> win_base(h->nseg + 1, 0);
     {
-        std::vector<int64_t> cnt(h->ngroups, 0);
-        mpcg::parallel_for(h->ngroups, [&](int64_t lo, int64_t hi) {
-            for (int64_t g = lo; g < hi; ++g) {
-                const int64_t rb0 = g * h->G, rb1 = std::min<int64_t>(rb0 + h->G, h->nrb);
-                const int64_t t0 = A->tile_row_ptr[rb0], t1 = A->tile_row_ptr[rb1];
+        std::vector<int64_t> cnt(h->nseg, 0);
+        mpcg::parallel_for(h->nseg, [&](int64_t lo, int64_t hi) {
+            for (int64_t v = lo; v < hi; ++v) {
+                const int64_t t0 = seg_t0[v], t1 = seg_t0[v + 1];
                 int64_t c = 0;
                 for (int64_t tb = t0; tb < t1; tb += dev::kTileBatch) {
                     const int64_t nt = std::min<int64_t>(dev::kTileBatch, t1 - tb);
-                    c += dev::batch_records((int)(A->tile_nnz_ptr[tb + nt] - A->tile_nnz_ptr[tb]));
+                    c += dev::batch_records((int)(D->tile_nnz_ptr[tb + nt] - D->tile_nnz_ptr[tb]));
                 }
-                cnt[g] = c;
+                cnt[v] = c;
             }
         });
         int64_t acc = 0;
-        for (int64_t g = 0; g < h->ngroups; ++g) {
-            win_base[g] = (int32_t)acc;
-            acc += cnt[g];
+        for (int64_t v = 0; v < h->nseg; ++v) {
+            win_base[v] = (int32_t)acc;
+            acc += cnt[v];
             if (acc > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: too many SpMV windows"));
         }
-        win_base[h->ngroups] = (int32_t)acc;
+        win_base[h->nseg] = (int32_t)acc;
         h->nwin = acc;
     }
     if (h->nwin >= (int64_t(1) << 28)) return bail(fail(CG_EINVAL, "cg_create: too many SpMV windows"));
-    // Batch table: every row group's batches in order; a group without tiles
-    // gets one entry without tiles so that its rows are written.
-    std::vector<int32_t> gbatch(h->ngroups + 1, 0);
+    // Batch table: every segment's batches in order; a segment without tiles
+    // gets one entry without tiles so that its rows are written. The flags hold
+    // the segment's slice above bit 8 (its rows go to that partial product).
+    std::vector<int32_t> gbatch(h->nseg + 1, 0);
     std::vector<int32_t> btab;
     {
         int64_t nb = 0;
-        for (int64_t g = 0; g < h->ngroups; ++g) {
-            gbatch[g] = (int32_t)nb;
-            const int64_t rb0 = g * h->G, rb1 = std::min<int64_t>(rb0 + h->G, h->nrb);
-            const int64_t ntile = A->tile_row_ptr[rb1] - A->tile_row_ptr[rb0];
+        for (int64_t v = 0; v < h->nseg; ++v) {
+            gbatch[v] = (int32_t)nb;
+            const int64_t ntile = seg_t0[v + 1] - seg_t0[v];
             nb += std::max<int64_t>(1, (ntile + dev::kTileBatch - 1) / dev::kTileBatch);
             if (nb > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: too many SpMV batches"));
         }
-        gbatch[h->ngroups] = (int32_t)nb;
+        gbatch[h->nseg] = (int32_t)nb;
         h->nbatch = nb;
         btab.assign((size_t)nb * dev::kBtFields, 0);
-        mpcg::parallel_for(h->ngroups, [&](int64_t lo, int64_t hi) {
-            for (int64_t g = lo; g < hi; ++g) {
-                const int64_t rb0 = g * h->G, rb1 = std::min<int64_t>(rb0 + h->G, h->nrb);
-                const int64_t t0 = A->tile_row_ptr[rb0], t1 = A->tile_row_ptr[rb1];
-                int64_t b = gbatch[g], rec = win_base[g];
-                const int64_t b_last = gbatch[g + 1] - 1;
+        mpcg::parallel_for(h->nseg, [&](int64_t lo, int64_t hi) {
+            for (int64_t v = lo; v < hi; ++v) {
+                const int64_t t0 = seg_t0[v], t1 = seg_t0[v + 1];
+                int64_t b = gbatch[v], rec = win_base[v];
+                const int64_t b_last = gbatch[v + 1] - 1;
                 for (int64_t tb = t0; b <= b_last; tb += dev::kTileBatch, ++b) {
                     int32_t* e = &btab[(size_t)b * dev::kBtFields];
                     const int64_t nt = std::max<int64_t>(0, std::min<int64_t>(dev::kTileBatch, t1 - tb));
-                    const int64_t len = nt ? A->tile_nnz_ptr[tb + nt] - A->tile_nnz_ptr[tb] : 0;
+                    const int64_t len = nt ? D->tile_nnz_ptr[tb + nt] - D->tile_nnz_ptr[tb] : 0;
                     e[dev::kBtTile] = nt ? (int32_t)tb : 0;
                     e[dev::kBtTiles] = (int32_t)nt;
-                    e[dev::kBtFirstNnz] = nt ? (int32_t)A->tile_nnz_ptr[tb] : 0;
+                    e[dev::kBtFirstNnz] = nt ? (int32_t)D->tile_nnz_ptr[tb] : 0;
                     e[dev::kBtLen] = (int32_t)len;
                     e[dev::kBtRecords] = (int32_t)rec;
-                    e[dev::kBtGroup] = (int32_t)g;
-                    e[dev::kBtFlags] = (b == gbatch[g] ? dev::kBatchFirstOfGroup : 0) |
-                                       (b == b_last ? dev::kBatchLastOfGroup : 0);
+                    e[dev::kBtGroup] = (int32_t)seg_group(v);
+                    e[dev::kBtFlags] = (b == gbatch[v] ? dev::kBatchFirstOfGroup : 0) |
+                                       (b == b_last ? dev::kBatchLastOfGroup : 0) |
+                                       (int32_t)(seg_slice(v) << dev::kBatchSliceShift);
                     if (nt) rec += dev::batch_records((int)len);
                 }
             }
@@ -732,17 +834,16 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     std::vector<int2> tent(std::max<int64_t>(T, 1), make_int2(0, 0));
     std::vector<uint64_t> win_mask(std::max<int64_t>(h->nwin, 1), 0);
     std::vector<int32_t> win_tile(std::max<int64_t>(h->nwin, 1), 0);
-    mpcg::parallel_for(h->nrb, [&](int64_t lo, int64_t hi) {
-        for (int64_t I = lo; I < hi; ++I)
-            for (int64_t t = A->tile_row_ptr[I]; t < A->tile_row_ptr[I + 1]; ++t)
-                tent[t] = make_int2((int)(A->tile_col_idx[t] * A->C * 8), (int)((I % h->G) * A->R * 8));
+    mpcg::parallel_for(T, [&](int64_t lo, int64_t hi) {
+        for (int64_t t = lo; t < hi; ++t)
+            tent[t] = make_int2((int)(D->tile_col_idx[t] * A->C * 8), (int)((trb[t] % h->G) * A->R * 8));
     });
     mpcg::parallel_for(h->nbatch, [&](int64_t lo, int64_t hi) {
         for (int64_t b = lo; b < hi; ++b) {
             const int32_t* e = &btab[(size_t)b * dev::kBtFields];
             const int64_t tb = e[dev::kBtTile], nt = e[dev::kBtTiles], len = e[dev::kBtLen];
             if (!nt) continue;
-            const int64_t kb = A->tile_nnz_ptr[tb], nw = (len + 63) / 64, E = dev::batch_records((int)len);
+            const int64_t kb = D->tile_nnz_ptr[tb], nw = (len + 63) / 64, E = dev::batch_records((int)len);
             int64_t j = 0;
             for (int64_t v = 0; v < E; ++v) {
                 const int64_t wi = e[dev::kBtRecords] + v;
@@ -751,11 +852,11 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
                     continue;
                 }
                 const int64_t w0 = v * 64;
-                while (j + 1 < nt && A->tile_nnz_ptr[tb + j + 1] - kb <= w0) ++j;
+                while (j + 1 < nt && D->tile_nnz_ptr[tb + j + 1] - kb <= w0) ++j;
                 win_tile[wi] = (int32_t)j;
                 uint64_t m = 0;
                 for (int64_t jn = j + 1; jn <= nt; ++jn) {
-                    const int64_t start = (jn < nt ? A->tile_nnz_ptr[tb + jn] - kb : len);
+                    const int64_t start = (jn < nt ? D->tile_nnz_ptr[tb + jn] - kb : len);
                     if (start >= w0 + 64) break;
                     m |= 1ull << (start - w0 - 1);
                 }
@@ -796,7 +897,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     TRY(dalloc(h, &h->win_tile, h->nwin));
     TRY(dalloc(h, &h->tent, std::max<int64_t>(T, 1)));
     TRY(dalloc(h, &h->btab, (int64_t)btab.size()));
-    TRY(dalloc(h, &h->gbatch, h->ngroups + 1));
+    TRY(dalloc(h, &h->gbatch, h->nseg + 1));
     TRY(dalloc(h, &h->tcol, T));
     TRY(dalloc(h, &h->tptr, T + 1));
     TRY(dalloc(h, &h->map, T));
@@ -814,7 +915,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     std::vector<double> scaled_h;
     double* vlow = nullptr;  // set-up only: the scaled values the reduced planes are rounded from
     if (p1 & CG_P1_COLUMN_SCALE) {
-        column_scale(*A, colexp_h, scaled_h);
+        column_scale(*D, colexp_h, scaled_h);
         TRY(dalloc(h, &h->colexp, n));
         if (hipMalloc(&vlow, sizeof(double) * (size_t)std::max<int64_t>(nnz, 1)) != hipSuccess) {
             (void)hipGetLastError();
@@ -838,6 +939,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     TRY(dalloc(h, &h->r, n_pad));
     TRY(dalloc(h, &h->p, n_pad));
     TRY(dalloc(h, &h->q, n_pad));
+    if (h->S > 1) TRY(dalloc(h, &h->qpart, (int64_t)h->S * n_pad));
     if (h->jacobi) {
         TRY(dalloc(h, &h->z, n_pad));
         TRY(dalloc(h, &h->dinv, n_pad));
@@ -866,17 +968,21 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
 
     for (double* v : {h->x, h->r, h->p, h->q, h->z, h->dinv})
         if (v && (e = hipMemsetAsync(v, 0, sizeof(double) * (size_t)n_pad, s))) return dev_err(e, "vectors");
+    // The SpMV never writes a slice's padding entry n, which the pair-wise
+    // update kernel reads: it stays zero.
+    if (h->qpart && (e = hipMemsetAsync(h->qpart, 0, sizeof(double) * (size_t)n_pad * h->S, s)))
+        return dev_err(e, "vectors");
     if ((e = hipMemcpyAsync(h->win_mask, win_mask.data(), sizeof(uint64_t) * win_mask.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->win_tile, win_tile.data(), sizeof(int32_t) * win_tile.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tent, tent.data(), sizeof(int2) * tent.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->trp, trp.data(), sizeof(int32_t) * trp.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->btab, btab.data(), sizeof(int32_t) * btab.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->gbatch, gbatch.data(), sizeof(int32_t) * gbatch.size(), hipMemcpyHostToDevice, s)) ||
-        (e = hipMemcpyAsync(h->tcol, A->tile_col_idx.data(), sizeof(int32_t) * T, hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->tcol, D->tile_col_idx.data(), sizeof(int32_t) * T, hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tptr, tptr.data(), sizeof(int32_t) * tptr.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->meta, h->meta16 ? (const void*)meta16.data() : (const void*)meta8.data(),
                             (h->meta16 ? 2 : 1) * (size_t)nnz, hipMemcpyHostToDevice, s)) ||
-        (e = hipMemcpyAsync(h->v64, A->val.data(), sizeof(double) * nnz, hipMemcpyHostToDevice, s)))
+        (e = hipMemcpyAsync(h->v64, D->val.data(), sizeof(double) * nnz, hipMemcpyHostToDevice, s)))
         return dev_err(e, "upload");
     if (vlow &&
         ((e = hipMemcpyAsync(h->colexp, colexp_h.data(), sizeof(int16_t) * n, hipMemcpyHostToDevice, s)) ||
@@ -886,7 +992,13 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         (e = hipMemcpyAsync(h->dinv, dinv_h.data(), sizeof(double) * n, hipMemcpyHostToDevice, s)))
         return dev_err(e, "upload");
     if (precision_map) {
-        if ((e = hipMemcpyAsync(h->map, precision_map, T, hipMemcpyHostToDevice, s))) return dev_err(e, "upload");
+        if (h->S > 1) {
+            std::vector<uint8_t> dm(T);
+            for (int64_t d = 0; d < T; ++d) dm[d] = precision_map[h->dperm[d]];
+            if ((e = hipMemcpy(h->map, dm.data(), T, hipMemcpyHostToDevice))) return dev_err(e, "upload");
+        } else if ((e = hipMemcpyAsync(h->map, precision_map, T, hipMemcpyHostToDevice, s))) {
+            return dev_err(e, "upload");
+        }
     } else if ((e = hipMemsetAsync(h->map, 0, T, s))) {
         return dev_err(e, "map");
     }
@@ -950,7 +1062,13 @@ extern "C" int cg_set_precision_map(cg_handle* h, const uint8_t* map, int32_t on
     for (int64_t t = 0; t < h->T; ++t)
         if (map[t] > 2)
             return fail(CG_EINVAL, "cg_set_precision_map: map[" + std::to_string(t) + "] is not 0, 1 or 2");
-    HIP_CHECK(hipMemcpy(h->map, map, h->T, hipMemcpyHostToDevice));
+    if (h->S > 1) {  // device order of the tiles
+        std::vector<uint8_t> dm(h->T);
+        for (int64_t d = 0; d < h->T; ++d) dm[d] = map[h->dperm[d]];
+        HIP_CHECK(hipMemcpy(h->map, dm.data(), h->T, hipMemcpyHostToDevice));
+    } else {
+        HIP_CHECK(hipMemcpy(h->map, map, h->T, hipMemcpyHostToDevice));
+    }
     HIP_CHECK(repack(h));
     h->sched = kSchedStatic;
     return upload_schedule(h);
@@ -973,6 +1091,12 @@ extern "C" int cg_get_active_map(const cg_handle* h, uint8_t* out) {
         for (int64_t t = 0; t < h->T; ++t) out[t] = code[tcol[t]];
         return CG_OK;
     }
+    if (h->S > 1) {  // device order of the tiles
+        std::vector<uint8_t> dm(h->T);
+        HIP_CHECK(hipMemcpy(dm.data(), h->map, h->T, hipMemcpyDeviceToHost));
+        for (int64_t d = 0; d < h->T; ++d) out[h->dperm[d]] = dm[d];
+        return CG_OK;
+    }
     HIP_CHECK(hipMemcpy(out, h->map, h->T, hipMemcpyDeviceToHost));
     return CG_OK;
 }
@@ -981,6 +1105,7 @@ extern "C" int cg_map_from_magnitude(cg_handle* h, double t_bf16, double t_fp32)
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_map_from_magnitude: h is NULL");
     if (!(t_bf16 <= t_fp32)) return fail(CG_EINVAL, "cg_map_from_magnitude: need t_bf16 <= t_fp32");
+    if (h->S > 1) return fail(CG_EINVAL, "cg_map_from_magnitude: not available with column slices");
     HIP_CHECK(hipMemset(h->scratch_u64, 0, sizeof(unsigned long long)));
     const int g = grid_for(h->T, 1, 8192);
     hipLaunchKernelGGL(dev::diag_absmax_kernel, dim3(g), dim3(dev::kBlock), 0, h->stream, h->trp, h->tcol,
@@ -1016,6 +1141,7 @@ extern "C" int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const dou
                                          double lo) {
     mpcg::clear_error();
     if (!h || !scores) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: NULL argument");
+    if (h->S > 1) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: not available with column slices");
     if (period < 1) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: period must be >= 1");
     if (!(lo <= hi)) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: need lo <= hi");
     if (!h->scores) {
@@ -1033,6 +1159,7 @@ extern "C" int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const dou
 extern "C" int cg_set_schedule_pmag(cg_handle* h, double lo, double hi, int32_t period) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_set_schedule_pmag: h is NULL");
+    if (h->S > 1) return fail(CG_EINVAL, "cg_set_schedule_pmag: not available with column slices");
     if (std::isnan(lo) || std::isnan(hi) || !(lo <= hi))
         return fail(CG_EINVAL, "cg_set_schedule_pmag: need lo <= hi (no NaN)");
     if (period < 1) return fail(CG_EINVAL, "cg_set_schedule_pmag: period must be >= 1");
@@ -1098,8 +1225,14 @@ extern "C" int cg_spmv(cg_handle* h, const double* x, double* y, void* stream) {
     if (!h || !x || !y) return fail(CG_EINVAL, "cg_spmv: NULL argument");
     if (ranges_overlap(x, y, sizeof(double) * h->n)) return fail(CG_EINVAL, "cg_spmv: y overlaps x");
     if (h->sched == kSchedPMag) launch_pmag(h, x, 0, static_cast<hipStream_t>(stream));  // map from x
-    dev::SpmvArgs a = spmv_args(h, x, y, &h->st->spmv_uprec);
-    launch_spmv<dev::kSpmvPlain>(h, a, static_cast<hipStream_t>(stream));
+    if (h->S > 1) {  // the slices' partial products, then their sum
+        dev::SpmvArgs a = spmv_args(h, x, h->qpart, &h->st->spmv_uprec);
+        launch_spmv<dev::kSpmvPlain>(h, a, static_cast<hipStream_t>(stream));
+        launch_combine(h, nullptr, y, static_cast<hipStream_t>(stream));
+    } else {
+        dev::SpmvArgs a = spmv_args(h, x, y, &h->st->spmv_uprec);
+        launch_spmv<dev::kSpmvPlain>(h, a, static_cast<hipStream_t>(stream));
+    }
     HIP_CHECK(hipGetLastError());
     return CG_OK;
 }
@@ -1168,10 +1301,17 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
     dev::VecArgs va = vec_args(h, b, x0);
     if (x0) {
         // r0 = b - A x0 with the exact FP64 values.
-        dev::SpmvArgs sa = spmv_args(h, x0, h->r, &h->st->zero_prec);
-        sa.b = b;
-        sa.p1_round = 0;
-        launch_spmv<dev::kSpmvResidual>(h, sa, s);
+        if (h->S > 1) {
+            dev::SpmvArgs sa = spmv_args(h, x0, h->qpart, &h->st->zero_prec);
+            sa.p1_round = 0;
+            launch_spmv<dev::kSpmvPlain>(h, sa, s);
+            launch_combine(h, b, h->r, s);
+        } else {
+            dev::SpmvArgs sa = spmv_args(h, x0, h->r, &h->st->zero_prec);
+            sa.b = b;
+            sa.p1_round = 0;
+            launch_spmv<dev::kSpmvResidual>(h, sa, s);
+        }
         va.r_ready = 1;
     }
     hipLaunchKernelGGL(dev::cg_init_kernel, dim3(vec_grid(h)), dim3(dev::kBlock), 0, s, va);
@@ -1277,46 +1417,79 @@ extern "C" int cg_export_layout(const cg_handle* h, int64_t* tile_row_ptr, int32
                                 float* val32, uint16_t* bf16) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_export_layout: h is NULL");
+    const int64_t T = h->T, nnz = h->nnz;
     if (tile_row_ptr) {
         std::vector<int32_t> t(h->nrb + 1);
         HIP_CHECK(hipMemcpy(t.data(), h->trp, sizeof(int32_t) * t.size(), hipMemcpyDeviceToHost));
         for (size_t i = 0; i < t.size(); ++i) tile_row_ptr[i] = t[i];
     }
-    if (tile_col_idx) HIP_CHECK(hipMemcpy(tile_col_idx, h->tcol, sizeof(int32_t) * h->T, hipMemcpyDeviceToHost));
-    if (tile_nnz_ptr) {
-        std::vector<int32_t> t(h->T + 1);
-        HIP_CHECK(hipMemcpy(t.data(), h->tptr, sizeof(int32_t) * t.size(), hipMemcpyDeviceToHost));
-        for (size_t i = 0; i < t.size(); ++i) tile_nnz_ptr[i] = t[i];
+    // Device order of tiles and nonzeros; with column slices it is mapped back
+    // to the canonical order (device tile d is canonical tile dperm[d]).
+    std::vector<int32_t> dt(T + 1);
+    HIP_CHECK(hipMemcpy(dt.data(), h->tptr, sizeof(int32_t) * dt.size(), hipMemcpyDeviceToHost));
+    const bool sliced = h->S > 1;
+    std::vector<int64_t> ct;  // canonical tile pointers
+    if (sliced) {
+        ct.assign(T + 1, 0);
+        for (int64_t d = 0; d < T; ++d) ct[h->dperm[d] + 1] = dt[d + 1] - dt[d];
+        for (int64_t t = 0; t < T; ++t) ct[t + 1] += ct[t];
     }
+    // Copies a per-nonzero array from device order into canonical order.
+    auto to_canonical = [&](const char* src, char* dst, size_t w) {
+        if (!sliced) {
+            std::memcpy(dst, src, w * (size_t)nnz);
+            return;
+        }
+        for (int64_t d = 0; d < T; ++d)
+            std::memcpy(dst + w * (size_t)ct[h->dperm[d]], src + w * (size_t)dt[d], w * (size_t)(dt[d + 1] - dt[d]));
+    };
+    if (tile_col_idx) {
+        std::vector<int32_t> c(std::max<int64_t>(T, 1));
+        if (T) HIP_CHECK(hipMemcpy(c.data(), h->tcol, sizeof(int32_t) * T, hipMemcpyDeviceToHost));
+        for (int64_t d = 0; d < T; ++d) tile_col_idx[sliced ? h->dperm[d] : d] = c[d];
+    }
+    if (tile_nnz_ptr)
+        for (int64_t t = 0; t <= T; ++t) tile_nnz_ptr[t] = sliced ? ct[t] : dt[t];
     if (row_idx || col_local) {
+        std::vector<uint8_t> r(std::max<int64_t>(nnz, 1)), c(std::max<int64_t>(nnz, 1));
         if (h->meta16) {
-            std::vector<uint16_t> m(h->nnz);
-            HIP_CHECK(hipMemcpy(m.data(), h->meta, 2 * (size_t)h->nnz, hipMemcpyDeviceToHost));
-            for (int64_t k = 0; k < h->nnz; ++k) {
-                if (row_idx) row_idx[k] = (uint8_t)(m[k] >> 8);
-                if (col_local) col_local[k] = (uint8_t)(m[k] & 255);
+            std::vector<uint16_t> m(std::max<int64_t>(nnz, 1));
+            HIP_CHECK(hipMemcpy(m.data(), h->meta, 2 * (size_t)nnz, hipMemcpyDeviceToHost));
+            for (int64_t k = 0; k < nnz; ++k) {
+                r[k] = (uint8_t)(m[k] >> 8);
+                c[k] = (uint8_t)(m[k] & 255);
             }
         } else {
-            std::vector<uint8_t> m(h->nnz);
-            HIP_CHECK(hipMemcpy(m.data(), h->meta, (size_t)h->nnz, hipMemcpyDeviceToHost));
-            for (int64_t k = 0; k < h->nnz; ++k) {
-                if (row_idx) row_idx[k] = (uint8_t)(m[k] >> 4);
-                if (col_local) col_local[k] = (uint8_t)(m[k] & 15);
+            std::vector<uint8_t> m(std::max<int64_t>(nnz, 1));
+            HIP_CHECK(hipMemcpy(m.data(), h->meta, (size_t)nnz, hipMemcpyDeviceToHost));
+            for (int64_t k = 0; k < nnz; ++k) {
+                r[k] = (uint8_t)(m[k] >> 4);
+                c[k] = (uint8_t)(m[k] & 15);
             }
         }
+        if (row_idx) to_canonical((const char*)r.data(), (char*)row_idx, 1);
+        if (col_local) to_canonical((const char*)c.data(), (char*)col_local, 1);
     }
-    if (val64) HIP_CHECK(hipMemcpy(val64, h->v64, sizeof(double) * h->nnz, hipMemcpyDeviceToHost));
+    if (val64) {
+        std::vector<double> v(std::max<int64_t>(nnz, 1));
+        HIP_CHECK(hipMemcpy(v.data(), h->v64, sizeof(double) * nnz, hipMemcpyDeviceToHost));
+        to_canonical((const char*)v.data(), (char*)val64, sizeof(double));
+    }
     if (val32 || bf16) {
         // The reduced planes live in the per-batch segments.
         std::vector<char> seg(h->planes_bytes);
         HIP_CHECK(hipMemcpy(seg.data(), h->planes, seg.size(), hipMemcpyDeviceToHost));
+        std::vector<float> v32(std::max<int64_t>(nnz, 1));
+        std::vector<uint16_t> v16(std::max<int64_t>(nnz, 1));
         for (int64_t b = 0; b < h->nbatch; ++b) {
             const int32_t* e = &h->btab_host[(size_t)b * dev::kBtFields];
             const int64_t first = e[dev::kBtFirstNnz], len = e[dev::kBtLen];
             const char* base = seg.data() + (int64_t)e[dev::kBtSegment] * 16;
-            if (val32) std::memcpy(val32 + first, base + 8 * len, 4 * len);
-            if (bf16) std::memcpy(bf16 + first, base + 12 * len, 2 * len);
+            std::memcpy(v32.data() + first, base + 8 * len, 4 * len);
+            std::memcpy(v16.data() + first, base + 12 * len, 2 * len);
         }
+        if (val32) to_canonical((const char*)v32.data(), (char*)val32, 4);
+        if (bf16) to_canonical((const char*)v16.data(), (char*)bf16, 2);
     }
     return CG_OK;
 }
