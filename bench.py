@@ -71,6 +71,11 @@ def main():
     ap.add_argument("--col-slices", default="",
                     help="with --workloads or --spmv-probe: comma-separated column-slice counts (e.g. 8,16) whose handles "
                          "are timed beside the unsliced ones")
+    ap.add_argument("--small-systems", action="store_true",
+                    help="instead of the CG bench, time CG (FP64 map, tol 1e-10) on 2D 5-point and 3D "
+                         "7-point Laplacians of a few hundred to a few thousand rows, on one workgroup "
+                         "(single_block=1) and with three launches per iteration (single_block=-1); "
+                         "prints one JSON line")
     ap.add_argument("--spmv-probe", default="",
                     help="counter run on comma-separated workloads (e.g. 4,5): a 256 MiB copy (the scale "
                          "reference), then per workload 5 cg_spmv launches under the all-FP64 map on the "
@@ -93,6 +98,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.tile_shapes:
         tile_shapes(torch, dev, mpcg, [int(c) for c in args.tile_shapes.split(",")], args.spmv_reps)
+        return
+    if args.small_systems:
+        small_systems(torch, dev, mpcg)
         return
     if args.spmv_probe:
         spmv_probe(torch, dev, mpcg, [int(c) for c in args.spmv_probe.split(",")],
@@ -488,6 +496,46 @@ def pmc_probe(torch, dev, S, L, A, pmap, b, w, mpcg):
     Sc.close()
     print(f"# pmc probe: 5 CG iterations, mixed map, vector bytes per iteration: update {24 * A.n}, "
           f"direction {40 * A.n}", file=sys.stderr, flush=True)
+
+
+def small_systems(torch, dev, mpcg):
+    """Time per CG iteration of the single-workgroup and the multi-launch solve.
+
+    Laplacians (16x16 tiles, FP64 map, b = A x*, x* ~ U[-1, 1] seed 0, x0 = 0,
+    tol 1e-10): one untimed solve, then the best of three timed ones per path.
+    """
+    from gen.matrices import laplace2d_5pt, laplace3d_7pt
+
+    out = {"metric": "cg_us_per_iteration_small_systems", "cases": []}
+    cases = [("2D 5-point", m, laplace2d_5pt) for m in (8, 16, 24, 32, 40, 48, 64)] + \
+        [("3D 7-point", m, laplace3d_7pt) for m in (6, 8, 10, 12, 14, 16)]
+    for name, m, gen_fn in cases:
+        A = gen_fn(m)
+        L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, 16, 16)
+        b = torch.from_numpy(A.to_scipy() @ np.random.default_rng(0).uniform(-1, 1, A.n)).to(dev)
+        rec = {"matrix": f"{name} Laplacian {m}^{2 if name.startswith('2D') else 3}", "n": A.n, "nnz": A.nnz}
+        for label, sb in (("single_workgroup", 1), ("multi_launch", -1)):
+            S = mpcg.Solver(L, single_block=sb)
+            x = torch.zeros_like(b)
+            S.cg_solve(b, x, 1e-10, 20000)
+            best = float("inf")
+            for _ in range(3):
+                torch.cuda.synchronize()
+                t = time.perf_counter()
+                st, K, _ = S.cg_solve(b, x, 1e-10, 20000)
+                torch.cuda.synchronize()
+                best = min(best, time.perf_counter() - t)
+            rec[label] = {"status": st, "iterations": K, "time_to_solution_ms": round(best * 1e3, 3),
+                          "us_per_iteration": round(best / max(K, 1) * 1e6, 2)}
+            S.close()
+        L.close()
+        rec["speedup"] = round(rec["multi_launch"]["time_to_solution_ms"] /
+                               rec["single_workgroup"]["time_to_solution_ms"], 3)
+        print(f"# {rec['matrix']}: n={A.n} nnz={A.nnz} one workgroup "
+              f"{rec['single_workgroup']['us_per_iteration']} us/it, three launches "
+              f"{rec['multi_launch']['us_per_iteration']} us/it", file=sys.stderr, flush=True)
+        out["cases"].append(rec)
+    print(json.dumps(out), flush=True)
 
 
 def spmv_probe(torch, dev, mpcg, cfgs, slices):

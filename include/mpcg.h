@@ -165,7 +165,9 @@ typedef struct {
                             -1 = default (graph) */
     int32_t p1;          /* CG_P1_* bits: the paper's own SpMV numerics (above); 0 = off */
     int32_t col_slices;  /* column slices S in [0, 64]; 0 or 1 = none (below) */
-    int32_t reserved[3];
+    int32_t single_block; /* cg_solve on one workgroup: 0 = automatic for small
+                             systems, 1 = whenever supported, -1 = never (below) */
+    int32_t reserved[2];
 } cg_options;
 
 /*
@@ -184,6 +186,21 @@ typedef struct {
  */
 
 /*
+ * Single-workgroup solve (cg_options.single_block): cg_solve runs all its
+ * iterations in one kernel launch of one 1024-thread workgroup, with
+ * workgroup barriers between the SpMV, update and direction phases instead of
+ * three launches per iteration. For systems so small that launch latency, not
+ * bandwidth, bounds an iteration. Same arithmetic, stop tests, history,
+ * breakdown rule and map trace as the multi-launch solve. Supported with
+ * static maps (including the magnitude rule's), the residual schedule and
+ * Jacobi, without column slices or CG_P1_* options; elsewhere cg_solve uses
+ * the multi-launch path whatever the option says. Automatic (0) picks it for
+ * at most 8192 stored entries and 4096 rows, where it is the faster path; a
+ * single workgroup scales with the entries, so larger systems run faster on
+ * the multi-launch path.
+ */
+
+/*
  * Create a solver handle on the current HIP device.
  *   A             : canonical matrix; copied to library-owned device memory
  *                   (index arrays, the FP64 values, and the FP32 and BF16 value
@@ -194,7 +211,8 @@ typedef struct {
  *   stream        : stream for the set-up copies and kernels.
  * Errors: CG_EINVAL (map code > 2, bad layout, n >= 2^28 or T or nnz >= 2^31,
  * Jacobi with a zero or missing diagonal entry, unknown p1 bits, padding with
- * R = 256, col_slices outside [0, 64]), CG_ENOMEM, CG_EDEVICE.
+ * R = 256, col_slices outside [0, 64], single_block outside [-1, 1]),
+ * CG_ENOMEM, CG_EDEVICE.
  */
 int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, const cg_options* opt,
               void* stream, cg_handle** out);

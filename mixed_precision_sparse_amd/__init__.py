@@ -132,7 +132,7 @@ class Solver:
     """Device-resident solver handle (owns a ``cg_handle``)."""
 
     def __init__(self, A: TileCSC, precision_map=None, jacobi=False, window=0, use_graph=-1,
-                 p1=0, col_slices=0, stream=None):
+                 p1=0, col_slices=0, single_block=0, stream=None):
         lib = _lib.load()
         opt = _lib.cg_options()
         opt.jacobi = 1 if jacobi else 0
@@ -140,6 +140,7 @@ class Solver:
         opt.use_graph = int(use_graph)
         opt.p1 = int(p1)
         opt.col_slices = int(col_slices)
+        opt.single_block = int(single_block)
         pm = None
         if precision_map is not None:
             pm = np.ascontiguousarray(precision_map, dtype=np.uint8)

@@ -32,7 +32,7 @@ class cg_tilecsc_view(ct.Structure):
 
 class cg_options(ct.Structure):
     _fields_ = [("jacobi", i32), ("window", i32), ("use_graph", i32), ("p1", i32), ("col_slices", i32),
-                ("reserved", i32 * 3)]
+                ("single_block", i32), ("reserved", i32 * 2)]
 
 
 # name -> (restype, argtypes)

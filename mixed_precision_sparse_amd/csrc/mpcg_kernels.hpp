@@ -595,25 +595,16 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
 // P1 = true: the paper's own numerics as options (vector entry rounded to the
 // tile's precision, per-column scale of the reduced values, padding entries
 // at row offset R skipped).
-template <typename MetaT, int MODE, int MAXROWS, bool CB = false, bool P1 = false>
-__global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, double* __restrict__ y,
-                                                                  double* __restrict__ partials) {
-    // Row accumulators, then one spare per lane for lanes on a sentinel entry.
-    __shared__ double s_acc[kSpmvWaves][MAXROWS + kWave];
-    __shared__ int4 s_desc[kSpmvWaves][kDescSlots];
-    __shared__ double s_tmp[kSpmvWaves];
-
-    if (MODE == kSpmvCg && load_done(a.st)) return;
-
-    const int lane = threadIdx.x & (kWave - 1);
-    // The wavefront index is uniform across the wave; saying so keeps every
-    // per-batch and per-window quantity in scalar registers.
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int gw = xcd_contiguous_block(blockIdx.x, gridDim.x) * kSpmvWaves + w;
-    const int g0 = min(gw * a.groups_per_wave, a.ngroups);
-    const int g1 = min(g0 + a.groups_per_wave, a.ngroups);
+//
+// spmv_wave is one wavefront's share: the batches of row groups (segments)
+// [g0, g1), with the wave's LDS row accumulators `acc` (MAXROWS + kWave
+// doubles: the rows, then one spare per lane for lanes on a sentinel entry)
+// and tile descriptors `desc` (kDescSlots). uprec is the uniform precision, or
+// -1 for the per-tile map. Returns the lane's part of p.q in CG mode, else 0.
+template <typename MetaT, int MODE, int MAXROWS, bool CB, bool P1>
+__device__ __forceinline__ double spmv_wave(const SpmvArgs& a, double* __restrict__ y, int g0, int g1, int uprec,
+                                            double* acc, int4* desc, int lane) {
     SweepCtx c;
-    const int uprec = *a.uprec;
     c.lane = lane;
     c.tent = a.tent;
     c.map = a.map;
@@ -624,8 +615,8 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
     // max|p| rule (which changes the map every iteration), else from the map's
     // packed segment.
     const bool from_planes = CB || uprec >= 0;
-    c.desc = &s_desc[w][0];
-    c.acc = reinterpret_cast<char*>(&s_acc[w][0]);
+    c.desc = desc;
+    c.acc = reinterpret_cast<char*>(acc);
     c.spare = (MAXROWS + lane) * 8;
     // Byte offsets are 32-bit: n < 2^28 and the record count < 2^28 are
     // checked when the handle is created.
@@ -660,7 +651,7 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
         const int row0 = H.group * a.rows_per_group;
         const int nrows = min(a.rows_per_group, a.n - row0);
         if (H.flags & kBatchFirstOfGroup) {
-            for (int i = lane; i < a.rows_per_group; i += kWave) s_acc[w][i] = 0.0;
+            for (int i = lane; i < a.rows_per_group; i += kWave) acc[i] = 0.0;
             if (MODE == kSpmvCg && MAXROWS <= kWave && lane < nrows) p_own = a.x[row0 + lane];
         }
         // Tile entries, the sentinel past the batch's tiles.
@@ -672,8 +663,8 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
             e.y = R.entry.y;
             e.z = !tile ? kSentinelPlane : from_planes ? p * (10 - 2 * p) * H.len : R.toff;
             e.w = tile ? 3 - p : 3;
-            s_desc[w][lane] = e;
-            if (lane == 0) s_desc[w][kTileBatch] = make_int4(kSentinelColumn, 0, kSentinelPlane, 3);
+            desc[lane] = e;
+            if (lane == 0) desc[kTileBatch] = make_int4(kSentinelColumn, 0, kSentinelPlane, 3);
         }
         c.rv = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char*>((from_planes ? a.planes : a.packed) + (int64_t)H.segment * 16), (short)0,
@@ -702,14 +693,14 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
             // This segment's partial product (the product itself without column slices).
             double* __restrict__ yo = y + (size_t)(H.flags >> kBatchSliceShift) * a.ystride;
             for (int i = lane; i < nrows; i += kWave) {
-                const double acc = s_acc[w][i];
+                const double v = acc[i];
                 if (MODE == kSpmvPlain) {
-                    yo[row0 + i] = acc;
+                    yo[row0 + i] = v;
                 } else if (MODE == kSpmvCg) {
-                    yo[row0 + i] = acc;
-                    dot += (MAXROWS <= kWave ? p_own : a.x[row0 + i]) * acc;
+                    yo[row0 + i] = v;
+                    dot += (MAXROWS <= kWave ? p_own : a.x[row0 + i]) * v;
                 } else {
-                    yo[row0 + i] = a.b[row0 + i] - acc;
+                    yo[row0 + i] = a.b[row0 + i] - v;
                 }
             }
             wave_lds_sync();
@@ -717,7 +708,26 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
         H = Hn;
         R = Rn;
     }
+    return dot;
+}
 
+template <typename MetaT, int MODE, int MAXROWS, bool CB = false, bool P1 = false>
+__global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, double* __restrict__ y,
+                                                                  double* __restrict__ partials) {
+    __shared__ double s_acc[kSpmvWaves][MAXROWS + kWave];
+    __shared__ int4 s_desc[kSpmvWaves][kDescSlots];
+    __shared__ double s_tmp[kSpmvWaves];
+
+    if (MODE == kSpmvCg && load_done(a.st)) return;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    // The wavefront index is uniform across the wave; saying so keeps every
+    // per-batch and per-window quantity in scalar registers.
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int gw = xcd_contiguous_block(blockIdx.x, gridDim.x) * kSpmvWaves + w;
+    const int g0 = min(gw * a.groups_per_wave, a.ngroups);
+    const int g1 = min(g0 + a.groups_per_wave, a.ngroups);
+    double dot = spmv_wave<MetaT, MODE, MAXROWS, CB, P1>(a, y, g0, g1, *a.uprec, &s_acc[w][0], &s_desc[w][0], lane);
     if (MODE == kSpmvCg) {
         dot = wave_sum(dot);
         __syncthreads();
@@ -762,9 +772,16 @@ struct VecArgs {
     int64_t qstride;         // distance between two partial products
 };
 
+// st->ntrace and st->stage are read with atomic loads: the single-workgroup
+// solver writes them and reads them back within one launch, and such loads
+// are never served by the scalar cache, which does not see vector stores.
+__device__ inline int load_i32(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ inline void trace_uniform(State* st, int32_t* trace_k, int32_t* trace_counts, int k,
                                      int prec, int64_t T) {
-    const int i = st->ntrace;
+    const int i = load_i32(&st->ntrace);
     if (i < st->trace_cap) {
         trace_k[i] = k;
         for (int p = 0; p < 3; ++p) trace_counts[(size_t)i * kTraceBlocks * 3 + p] = (p == prec) ? (int32_t)T : 0;
@@ -776,9 +793,10 @@ __device__ inline void trace_uniform(State* st, int32_t* trace_k, int32_t* trace
 __device__ inline void advance_stage(State* st, int32_t* trace_k, int32_t* trace_counts, int k,
                                      double rho, int64_t T, bool first) {
     if (st->nstage <= 0) return;
-    int s = st->stage;
+    const int s0 = load_i32(&st->stage);
+    int s = s0;
     while (s < st->nstage - 1 && rho <= st->thresholds[s]) ++s;
-    if (s != st->stage || first) {
+    if (s != s0 || first) {
         st->stage = s;
         st->uprec = st->stage_prec[s];
         trace_uniform(st, trace_k, trace_counts, k, st->uprec, T);
@@ -1005,6 +1023,121 @@ __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
         else if (k >= st->maxit) done = 2;
         else if (st->nstage > 0) advance_stage(st, a.trace_k, a.trace_counts, k, rho, a.T, false);
         if (done) store_done(st, done);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Single-workgroup CG for small systems. One launch of kSmallBlock threads
+// runs the iterations that the SpMV, update and direction kernels run one
+// launch each, with workgroup barriers between the phases; small systems are
+// bound by launch latency, not bandwidth. Same state, history, stop tests,
+// breakdown rule and residual schedule as those kernels; the per-tile map is
+// fixed during the launch (static maps, uniform stages). Wavefront w takes the
+// row groups [w G / W, (w + 1) G / W). Scalars that change during the launch
+// are passed through LDS: the scalar cache does not see vector stores.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallBlock = kSmallWaves * kWave;
+
+template <typename MetaT, int MAXROWS, bool JAC>
+__global__ __launch_bounds__(kSmallBlock) void cg_small_kernel(SpmvArgs sa, VecArgs va) {
+    __shared__ double s_acc[kSmallWaves][MAXROWS + kWave];
+    __shared__ int4 s_desc[kSmallWaves][kDescSlots];
+    __shared__ double s_tmp[kSmallWaves];
+    __shared__ int s_done, s_uprec, s_k;
+    State* st = va.st;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int g0 = (int)((int64_t)sa.ngroups * w / kSmallWaves);
+    const int g1 = (int)((int64_t)sa.ngroups * (w + 1) / kSmallWaves);
+    const int64_t npairs = ((int64_t)va.n + 1) / 2;
+    double2* r2 = reinterpret_cast<double2*>(va.r);
+    double2* z2 = reinterpret_cast<double2*>(va.z);
+    double2* p2 = reinterpret_cast<double2*>(va.p);
+    double2* x2 = reinterpret_cast<double2*>(va.x);
+    const double2* q2 = reinterpret_cast<const double2*>(va.q);
+    const double2* d2 = reinterpret_cast<const double2*>(va.dinv);
+    if (threadIdx.x == 0) {
+        s_done = load_done(st);
+        s_uprec = st->uprec;
+        s_k = st->k;
+    }
+    __syncthreads();
+    const int maxit = st->maxit;
+    double rz_old = st->rz;  // then carried in registers (every thread gets the same sums)
+    // Every thread leaves the loop at the same iteration: the exit reads LDS
+    // values written before the barrier that ends the previous iteration.
+    for (int k = s_k; k < maxit && s_done == 0; k = s_k) {
+        // q = A p and p.q.
+        const double pq = block_sum<kSmallWaves>(
+            spmv_wave<MetaT, kSpmvCg, MAXROWS, false, false>(sa, sa.y, g0, g1, s_uprec, &s_acc[w][0],
+                                                              &s_desc[w][0], lane),
+            s_tmp);
+        const double alpha = rz_old / pq;
+        if (!(pq > 0.0) || !isfinite(pq) || !isfinite(alpha)) {  // breakdown: nothing is updated
+            if (threadIdx.x == 0) {
+                st->pq = pq;
+                st->bd = 1;
+                store_done(st, 3);
+            }
+            break;
+        }
+        // r -= alpha q; [z = dinv .* r]; r.r [and r.z].
+        double rr = 0.0, rz = 0.0;
+        for (int64_t i = threadIdx.x; i < npairs; i += kSmallBlock) {
+            const double2 qv = q2[i];
+            double2 rn = r2[i];
+            rn.x -= alpha * qv.x;
+            rn.y -= alpha * qv.y;
+            r2[i] = rn;
+            rr += rn.x * rn.x + rn.y * rn.y;
+            if (JAC) {
+                const double2 dv = d2[i];
+                double2 zn;
+                zn.x = dv.x * rn.x;
+                zn.y = dv.y * rn.y;
+                z2[i] = zn;
+                rz += rn.x * zn.x + rn.y * zn.y;
+            }
+        }
+        const double rr_new = block_sum<kSmallWaves>(rr, s_tmp);
+        const double rz_new = JAC ? block_sum<kSmallWaves>(rz, s_tmp) : rr_new;
+        const double beta = rz_new / rz_old;
+        // x += alpha p; p = z + beta p (z = r for plain CG): each thread reads
+        // back only the r or z entries it has just written.
+        const double2* zsrc = reinterpret_cast<const double2*>(JAC ? va.z : va.r);
+        for (int64_t i = threadIdx.x; i < npairs; i += kSmallBlock) {
+            const double2 pv = p2[i], zv = zsrc[i];
+            double2 xv = x2[i], pn;
+            xv.x += alpha * pv.x;
+            xv.y += alpha * pv.y;
+            pn.x = zv.x + beta * pv.x;
+            pn.y = zv.y + beta * pv.y;
+            x2[i] = xv;
+            p2[i] = pn;
+        }
+        if (threadIdx.x == 0) {
+            const int kn = k + 1;
+            const double rho = sqrt(rr_new) / st->norm0;
+            va.hist[kn] = rho;
+            st->pq = pq;
+            st->alpha = alpha;
+            st->rz_prev = rz_old;
+            st->k = kn;
+            st->rr = rr_new;
+            st->rz = rz_new;
+            st->beta = beta;
+            int done = 0;
+            if (!isfinite(beta) || !isfinite(rho)) done = 3;
+            else if (rho <= st->tol) done = 1;
+            else if (kn >= maxit) done = 2;
+            else if (st->nstage > 0) advance_stage(st, va.trace_k, va.trace_counts, kn, rho, va.T, false);
+            if (done) store_done(st, done);
+            s_done = done;
+            s_uprec = load_i32(&st->uprec);
+            s_k = kn;
+        }
+        rz_old = rz_new;
+        __syncthreads();
     }
 }
 

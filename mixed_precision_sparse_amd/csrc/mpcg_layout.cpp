@@ -27,7 +27,7 @@ void mpcg::clear_error() { g_last_error.clear(); }
 
 extern "C" const char* cg_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int cg_version(void) { return 10200; }  // 1.2.0
+extern "C" int cg_version(void) { return 10300; }  // 1.3.0
 
 namespace {
 

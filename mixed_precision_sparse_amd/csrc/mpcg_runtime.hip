@@ -42,6 +42,7 @@ struct cg_handle {
     int64_t n = 0, T = 0, nnz = 0, nrb = 0;
     int32_t R = 0, C = 0, G = 0, rows_per_group = 0, ngroups = 0;
     int32_t S = 1;                 // column slices (cg_options.col_slices)
+    int32_t single_block = 0;      // cg_options.single_block: 0 auto, 1 when supported, -1 never
     int64_t nseg = 0;              // SpMV segments: S * ngroups (slice-major)
     std::vector<int32_t> dperm;    // S > 1: device tile -> canonical tile
     double* qpart = nullptr;       // S > 1: [S][n_pad] partial products of the slices
@@ -161,6 +162,12 @@ constexpr int kVecGridCap = 1024;
 #define MPCG_UPD_GRID_CAP 1024
 #endif
 constexpr int kUpdGridCap = MPCG_UPD_GRID_CAP;  // blocks of the update and direction kernels
+#ifndef MPCG_SMALL_AUTO_NNZ
+#define MPCG_SMALL_AUTO_NNZ 8192
+#endif
+#ifndef MPCG_SMALL_AUTO_N
+#define MPCG_SMALL_AUTO_N 4096
+#endif
 #ifndef MPCG_SPMV_GRID_CAP
 #define MPCG_SPMV_GRID_CAP 32768
 #endif
@@ -432,6 +439,48 @@ void enqueue_iteration(cg_handle* h, int i, hipStream_t s, bool rule_at_end = fa
     if (h->sched == kSchedPMag) {  // the map of the next window (iteration i + 1 starts it)
         if (pmag_split(h) ? (rule_at_end && i == h->window - 1) : (i + 1) % h->pm_period == 0)
             launch_pmag(h, h->p, 1, s);
+    }
+}
+
+// The single-workgroup solver runs schedules whose per-tile map is fixed for
+// the whole solve (static maps and the residual stages, which are uniform),
+// without column slices or the P1 numerics. Chosen automatically up to
+// kSmallAutoNnz stored entries and kSmallAutoN rows: below that one workgroup
+// beats three launches per iteration (measured on 2D and 3D Laplacians; at
+// 20K entries it is twice as slow, each wavefront then walking 16 row groups
+// one after the other).
+constexpr int64_t kSmallAutoNnz = MPCG_SMALL_AUTO_NNZ;
+constexpr int64_t kSmallAutoN = MPCG_SMALL_AUTO_N;
+
+bool single_block_solve(const cg_handle* h) {
+    const bool supported = h->S == 1 && h->p1 == 0 && (h->sched == kSchedStatic || h->sched == kSchedResidual);
+    if (!supported || h->single_block < 0) return false;
+    return h->single_block > 0 || (h->nnz <= kSmallAutoNnz && h->n <= kSmallAutoN);
+}
+
+template <typename MetaT, int MAXROWS>
+void launch_small_m(cg_handle* h, const dev::SpmvArgs& sa, const dev::VecArgs& va, hipStream_t s) {
+    if (h->jacobi)
+        hipLaunchKernelGGL((dev::cg_small_kernel<MetaT, MAXROWS, true>), dim3(1), dim3(dev::kSmallBlock), 0, s, sa, va);
+    else
+        hipLaunchKernelGGL((dev::cg_small_kernel<MetaT, MAXROWS, false>), dim3(1), dim3(dev::kSmallBlock), 0, s, sa,
+                           va);
+}
+
+// Every iteration of the solve in one launch of one workgroup.
+void launch_small(cg_handle* h, hipStream_t s) {
+    const dev::SpmvArgs sa = spmv_args(h, h->p, h->q, &h->st->uprec);
+    const dev::VecArgs va = vec_args(h, nullptr, nullptr);
+    const bool wide = h->rows_per_group > 64;
+    if (h->meta16) {
+        if (wide)
+            launch_small_m<uint16_t, dev::kMaxRows>(h, sa, va, s);
+        else
+            launch_small_m<uint16_t, 64>(h, sa, va, s);
+    } else if (wide) {
+        launch_small_m<uint8_t, dev::kMaxRows>(h, sa, va, s);
+    } else {
+        launch_small_m<uint8_t, 64>(h, sa, va, s);
     }
 }
 
@@ -709,6 +758,9 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         if (opt->col_slices < 0 || opt->col_slices > 64)
             return bail(fail(CG_EINVAL, "cg_create: col_slices must lie in [0, 64]"));
         h->S = std::max(1, opt->col_slices);
+        if (opt->single_block < -1 || opt->single_block > 1)
+            return bail(fail(CG_EINVAL, "cg_create: single_block must be -1, 0 or 1"));
+        h->single_block = opt->single_block;
     }
 
     // Device order of the tiles: canonical, or slice by slice (col_slices).
@@ -1324,10 +1376,16 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
                            h->trace_k, h->trace_counts);
     }
 
-    // Iterate in windows; poll the device stop flag of the previous window
-    // while the current one runs.
+    // Small systems: every iteration in one launch. Otherwise iterate in
+    // windows and poll the device stop flag of the previous window while the
+    // current one runs.
+    const bool small = single_block_solve(h);
+    if (small) {
+        launch_small(h, s);
+        HIP_CHECK(hipGetLastError());
+    }
     int polled = 0;
-    if (h->use_graph) {
+    if (h->use_graph && !small) {
         int rc = ensure_graph(h);
         if (rc != CG_OK) return rc;
     }
@@ -1335,7 +1393,7 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
     int32_t done = 0, kdone = 0;
     const int W = solve_window(h);
     const int64_t max_windows = (int64_t)maxit / W + 2;
-    while (true) {
+    while (!small) {
         if (windows < max_windows) {
             // Split max|p| rule: window w ends at k = (w + 1) W; evaluate when that is a
             // multiple of the period.

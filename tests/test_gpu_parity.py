@@ -257,14 +257,17 @@ def true_residuals_agree(tr, tr_ref, tol, rel=1e-2):
     return abs(a - b) <= rel * b
 
 
+# single_block: -1 = the multi-launch solve, 1 = one workgroup where the
+# schedule allows it (static maps, residual stages), else the multi-launch one.
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("which", ["fp64", "mixed"])
-def test_cg_parity_small(cfg, which, dev):
+@pytest.mark.parametrize("single_block", [-1, 1])
+def test_cg_parity_small(cfg, which, single_block, dev):
     w = make_workload(cfg, "small")
     A = w.A
-    log(f"cg cfg{cfg} small map={which} n={w.n}")
+    log(f"cg cfg{cfg} small map={which} single_block={single_block} n={w.n}")
     L, Lo = build_both(w)
-    S = mpcg.Solver(L, jacobi=w.jacobi)
+    S = mpcg.Solver(L, jacobi=w.jacobi, single_block=single_block)
     if which == "mixed":
         sched = _configure(S, w, L, Lo)
     else:
@@ -297,11 +300,12 @@ def test_cg_parity_small(cfg, which, dev):
     S.close()
 
 
-def test_cg_initial_guess_and_degenerate_cases(dev):
+@pytest.mark.parametrize("single_block", [-1, 1])
+def test_cg_initial_guess_and_degenerate_cases(single_block, dev):
     w = make_workload(1, "small")
     A = w.A
     L, Lo = build_both(w)
-    S = mpcg.Solver(L)
+    S = mpcg.Solver(L, single_block=single_block)
     bd = torch.from_numpy(w.b).to(dev)
     # Nonzero initial guess; x may alias x0.
     x0 = np.random.default_rng(1).uniform(-1, 1, A.n)
@@ -321,11 +325,12 @@ def test_cg_initial_guess_and_degenerate_cases(dev):
     S.close()
 
 
-def test_cg_breakdown_on_indefinite_matrix(dev):
+@pytest.mark.parametrize("single_block", [-1, 1])
+def test_cg_breakdown_on_indefinite_matrix(single_block, dev):
     n = 2
     L = mpcg.cg_tilecsc_from_csr(n, np.array([0, 1, 2]), np.array([0, 1], np.int32),
                                  np.array([1.0, -1.0]), 16, 16)
-    S = mpcg.Solver(L)
+    S = mpcg.Solver(L, single_block=single_block)
     bd = torch.ones(2, dtype=torch.float64, device=dev)
     xd = torch.zeros_like(bd)
     st, K, hist = S.cg_solve(bd, xd, 1e-10, 10)
@@ -340,11 +345,11 @@ def test_cg_launch_modes_agree(graph, window, dev):
     w = make_workload(2, "small")
     A = w.A
     L, Lo = build_both(w)
-    S = mpcg.Solver(L, use_graph=graph, window=window)
+    S = mpcg.Solver(L, use_graph=graph, window=window, single_block=-1)
     bd = torch.from_numpy(w.b).to(dev)
     xd = torch.zeros_like(bd)
     st, K, hist = S.cg_solve(bd, xd, w.tol, w.maxit)
-    S2 = mpcg.Solver(L, use_graph=0, window=16)
+    S2 = mpcg.Solver(L, use_graph=0, window=16, single_block=-1)
     x2 = torch.zeros_like(bd)
     st2, K2, hist2 = S2.cg_solve(bd, x2, w.tol, w.maxit)
     torch.cuda.synchronize()

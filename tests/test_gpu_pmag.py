@@ -106,7 +106,9 @@ def test_pmag_reduces_to_static_maps_bit_for_bit(cfg, dev):
         S1.cg_set_schedule_pmag(lo, lo)
         x1 = torch.zeros_like(bd)
         st1, K1, h1 = S1.cg_solve(bd, x1, w.tol, 400)
-        S2 = mpcg.Solver(L, np.full(L.T, code, np.uint8))
+        # The same multi-launch kernels (a small static-map handle could
+        # otherwise solve on one workgroup, with another summation order).
+        S2 = mpcg.Solver(L, np.full(L.T, code, np.uint8), single_block=-1)
         x2 = torch.zeros_like(bd)
         st2, K2, h2 = S2.cg_solve(bd, x2, w.tol, 400)
         log(f"cfg{cfg} pmag lo=hi={lo}: {st1} K={K1}; static code {code}: {st2} K={K2}")

@@ -28,6 +28,17 @@ def _declared_functions():
     return sorted(set(names))
 
 
+def test_options_struct_matches_header():
+    """The binding's cg_options has the header's fields, in order, with their sizes."""
+    text = open(os.path.join(ROOT, "include", "mpcg.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} cg_options;", text, flags=re.S).group(1)
+    fields = [(name, int(count) if count else 1) for name, count in re.findall(r"int32_t\s+(\w+)(?:\[(\d+)\])?;", body)]
+    ours = [(name, ct.sizeof(typ) // 4) for name, typ in _lib.cg_options._fields_]
+    assert fields == ours
+    assert ct.sizeof(_lib.cg_options) == 4 * sum(c for _, c in fields)
+
+
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = _declared_functions()
