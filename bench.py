@@ -507,8 +507,8 @@ def small_systems(torch, dev, mpcg):
     from gen.matrices import laplace2d_5pt, laplace3d_7pt
 
     out = {"metric": "cg_us_per_iteration_small_systems", "cases": []}
-    cases = [("2D 5-point", m, laplace2d_5pt) for m in (8, 16, 24, 32, 40, 48, 64)] + \
-        [("3D 7-point", m, laplace3d_7pt) for m in (6, 8, 10, 12, 14, 16)]
+    cases = [("2D 5-point", m, laplace2d_5pt) for m in (8, 16, 32, 48, 64, 96, 128, 192)] + \
+        [("3D 7-point", m, laplace3d_7pt) for m in (6, 8, 12, 16, 21, 28, 36)]
     for name, m, gen_fn in cases:
         A = gen_fn(m)
         L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, 16, 16)

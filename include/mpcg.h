@@ -193,11 +193,13 @@ typedef struct {
  * bandwidth, bounds an iteration. Same arithmetic, stop tests, history,
  * breakdown rule and map trace as the multi-launch solve. Supported with
  * static maps (including the magnitude rule's), the residual schedule and
- * Jacobi, without column slices or CG_P1_* options; elsewhere cg_solve uses
- * the multi-launch path whatever the option says. Automatic (0) picks it for
- * at most 8192 stored entries and 4096 rows, where it is the faster path; a
- * single workgroup scales with the entries, so larger systems run faster on
- * the multi-launch path.
+ * Jacobi, without column slices or CG_P1_* options, for at most 12288 rows
+ * (the workgroup keeps p in LDS); elsewhere cg_solve uses the multi-launch
+ * path whatever the option says. The option also sizes the handle's row
+ * groups for one workgroup (about 16 groups of up to 256 rows). Automatic
+ * (0) picks it for at most 24576 stored entries and 8192 rows, where it is
+ * no slower than three launches per iteration; its time grows with the
+ * entries, so larger systems run faster on the multi-launch path.
  */
 
 /*

@@ -454,6 +454,8 @@ struct SweepCtx {
     const int32_t* toff;
     const int32_t* tcol;
     const uint8_t* cbcode;
+    const double* xs;  // XL sweeps: the vector in LDS (entries 0 .. xmax)
+    int xmax;
     int len, lane;
     int spare;  // byte offset of this lane's spare accumulator
     int round_p, scale, sentinel_row;  // P1 options (wave-uniform)
@@ -509,7 +511,10 @@ __device__ __forceinline__ void load_batch_regs(const SweepCtx& c, const BatchHd
 // position times the value width, rounded down to 4 bytes (a BF16 lane then
 // takes the half its byte offset selects); the widening is a bitwise blend.
 // Lanes past the batch add their zero product to a private spare accumulator.
-template <typename MetaT, int U, bool CB, bool P1>
+//
+// XL: the vector entries come from the LDS copy c.xs (lanes on a sentinel
+// entry read its last entry, and add their zero product to the spare).
+template <typename MetaT, int U, bool CB, bool P1, bool XL = false>
 __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R, int wi, int o0, bool next,
                                            const BatchHdr& Hn, BatchRegs& Rn) {
     int q[U];
@@ -549,8 +554,12 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
         decode_meta<MetaT>(mt[u], r, col);
         const bool real = q[u] < c.len && (!P1 || r != c.sentinel_row);
         racc[u] = real ? d[u].y + 8 * r : c.spare;
-        const u32x2 xb = __builtin_amdgcn_raw_buffer_load_b64(c.rx, d[u].x + 8 * col, 0, 0);
-        xv[u] = __longlong_as_double(((long long)xb.y << 32) | xb.x);
+        if (XL) {
+            xv[u] = c.xs[min((d[u].x >> 3) + col, c.xmax)];
+        } else {
+            const u32x2 xb = __builtin_amdgcn_raw_buffer_load_b64(c.rx, d[u].x + 8 * col, 0, 0);
+            xv[u] = __longlong_as_double(((long long)xb.y << 32) | xb.x);
+        }
         ex[u] = 0;
         if (P1 && c.scale)
             ex[u] = (int)(int16_t)__builtin_amdgcn_raw_buffer_load_b16(c.rexp, 2 * ((d[u].x >> 3) + col), 0, 0);
@@ -601,11 +610,17 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
 // doubles: the rows, then one spare per lane for lanes on a sentinel entry)
 // and tile descriptors `desc` (kDescSlots). uprec is the uniform precision, or
 // -1 for the per-tile map. Returns the lane's part of p.q in CG mode, else 0.
-template <typename MetaT, int MODE, int MAXROWS, bool CB, bool P1>
+// U: windows per full sweep (kUnroll, or a larger power of two for latency-
+// bound callers; a batch's leftover whole kUnroll sweeps then run one by one).
+// XL: vector entries from the LDS copy xs[0 .. n-1] instead of a.x.
+template <typename MetaT, int MODE, int MAXROWS, bool CB, bool P1, int U = kUnroll, bool XL = false>
 __device__ __forceinline__ double spmv_wave(const SpmvArgs& a, double* __restrict__ y, int g0, int g1, int uprec,
-                                            double* acc, int4* desc, int lane) {
+                                            double* acc, int4* desc, int lane, const double* xs = nullptr) {
+    static_assert(U >= kUnroll && U % kUnroll == 0 && (U & (U - 1)) == 0 && U <= kWave, "sweep size");
     SweepCtx c;
     c.lane = lane;
+    c.xs = xs;
+    c.xmax = a.n - 1;
     c.tent = a.tent;
     c.map = a.map;
     c.toff = a.toff;
@@ -676,17 +691,26 @@ __device__ __forceinline__ double spmv_wave(const SpmvArgs& a, double* __restric
         // The first sweep of the batch also starts the next batch's loads.
         BatchRegs Rn{};
         int left = E, wi = 0, o0 = 0;
-        for (; left >= kUnroll; left -= kUnroll, wi += kUnroll, o0 += kUnroll * kWave) {
+        for (; left >= U; left -= U, wi += U, o0 += U * kWave) {
             if (wi > 0 && (wi & (kWave - 1)) == 0) load_batch_regs<CB>(c, H, wi, false, R);  // next 64 records
-            spmv_sweep<MetaT, kUnroll, CB, P1>(c, R, wi, o0, more && wi == 0, Hn, Rn);
+            spmv_sweep<MetaT, U, CB, P1, XL>(c, R, wi, o0, more && wi == 0, Hn, Rn);
+        }
+        if (U > kUnroll) {
+            for (; left >= kUnroll; left -= kUnroll, wi += kUnroll, o0 += kUnroll * kWave) {
+                if (wi > 0 && (wi & (kWave - 1)) == 0) load_batch_regs<CB>(c, H, wi, false, R);
+                spmv_sweep<MetaT, kUnroll, CB, P1, XL>(c, R, wi, o0, more && wi == 0, Hn, Rn);
+            }
         }
         // The rest is 0 or one power of two below kUnroll (never crossing a record chunk).
         if (wi > 0 && (wi & (kWave - 1)) == 0 && left > 0) load_batch_regs<CB>(c, H, wi, false, R);
         const bool first = more && wi == 0;
-        if (kUnroll > 8 && left == 8) spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1), CB, P1>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 4 && left == 4) spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1), CB, P1>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 2 && left == 2) spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1), CB, P1>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1, CB, P1>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 8 && left == 8)
+            spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1), CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 4 && left == 4)
+            spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1), CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 2 && left == 2)
+            spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1), CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
+        if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1, CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
         if (more && E == 0) load_batch_regs<CB>(c, Hn, 0, true, Rn);  // a batch without windows
         wave_lds_sync();
         if (H.flags & kBatchLastOfGroup) {
@@ -1037,12 +1061,24 @@ __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
 // are passed through LDS: the scalar cache does not see vector stores.
 constexpr int kSmallWaves = 16;
 constexpr int kSmallBlock = kSmallWaves * kWave;
+#ifndef MPCG_SMALL_UNROLL
+#define MPCG_SMALL_UNROLL 4
+#endif
+#ifndef MPCG_SMALL_XLDS
+#define MPCG_SMALL_XLDS 1
+#endif
+constexpr int kSmallUnroll = MPCG_SMALL_UNROLL;  // windows per sweep: a latency-bound SpMV
+constexpr bool kSmallXLds = MPCG_SMALL_XLDS != 0;  // gather p from an LDS copy
+// Rows the LDS copy of p holds: with the widest accumulators the workgroup
+// then uses 154 of gfx950's 160 KB of LDS.
+constexpr int kSmallMaxN = 12288;
 
 template <typename MetaT, int MAXROWS, bool JAC>
 __global__ __launch_bounds__(kSmallBlock) void cg_small_kernel(SpmvArgs sa, VecArgs va) {
     __shared__ double s_acc[kSmallWaves][MAXROWS + kWave];
     __shared__ int4 s_desc[kSmallWaves][kDescSlots];
     __shared__ double s_tmp[kSmallWaves];
+    __shared__ double s_p[kSmallXLds ? kSmallMaxN : 1];  // p, for the SpMV's gathers
     __shared__ int s_done, s_uprec, s_k;
     State* st = va.st;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1061,6 +1097,8 @@ __global__ __launch_bounds__(kSmallBlock) void cg_small_kernel(SpmvArgs sa, VecA
         s_uprec = st->uprec;
         s_k = st->k;
     }
+    if (kSmallXLds)
+        for (int i = threadIdx.x; i < va.n; i += kSmallBlock) s_p[i] = va.p[i];
     __syncthreads();
     const int maxit = st->maxit;
     double rz_old = st->rz;  // then carried in registers (every thread gets the same sums)
@@ -1069,8 +1107,8 @@ __global__ __launch_bounds__(kSmallBlock) void cg_small_kernel(SpmvArgs sa, VecA
     for (int k = s_k; k < maxit && s_done == 0; k = s_k) {
         // q = A p and p.q.
         const double pq = block_sum<kSmallWaves>(
-            spmv_wave<MetaT, kSpmvCg, MAXROWS, false, false>(sa, sa.y, g0, g1, s_uprec, &s_acc[w][0],
-                                                              &s_desc[w][0], lane),
+            spmv_wave<MetaT, kSpmvCg, MAXROWS, false, false, kSmallUnroll, kSmallXLds>(
+                sa, sa.y, g0, g1, s_uprec, &s_acc[w][0], &s_desc[w][0], lane, s_p),
             s_tmp);
         const double alpha = rz_old / pq;
         if (!(pq > 0.0) || !isfinite(pq) || !isfinite(alpha)) {  // breakdown: nothing is updated
@@ -1114,6 +1152,10 @@ __global__ __launch_bounds__(kSmallBlock) void cg_small_kernel(SpmvArgs sa, VecA
             pn.y = zv.y + beta * pv.y;
             x2[i] = xv;
             p2[i] = pn;
+            if (kSmallXLds) {  // 2i < n always; for odd n the padding entry n has no slot
+                s_p[2 * i] = pn.x;
+                if (2 * i + 1 < va.n) s_p[2 * i + 1] = pn.y;
+            }
         }
         if (threadIdx.x == 0) {
             const int kn = k + 1;

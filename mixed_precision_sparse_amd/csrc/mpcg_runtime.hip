@@ -163,10 +163,10 @@ constexpr int kVecGridCap = 1024;
 #endif
 constexpr int kUpdGridCap = MPCG_UPD_GRID_CAP;  // blocks of the update and direction kernels
 #ifndef MPCG_SMALL_AUTO_NNZ
-#define MPCG_SMALL_AUTO_NNZ 8192
+#define MPCG_SMALL_AUTO_NNZ 24576
 #endif
 #ifndef MPCG_SMALL_AUTO_N
-#define MPCG_SMALL_AUTO_N 4096
+#define MPCG_SMALL_AUTO_N 8192
 #endif
 #ifndef MPCG_SPMV_GRID_CAP
 #define MPCG_SPMV_GRID_CAP 32768
@@ -175,6 +175,20 @@ constexpr int kSpmvGridCap = MPCG_SPMV_GRID_CAP;
 
 int vec_grid(const cg_handle* h) { return h->vec_blocks; }
 int spmv_grid(const cg_handle* h) { return h->spmv_blocks; }
+
+constexpr int64_t kSmallAutoNnz = MPCG_SMALL_AUTO_NNZ;
+constexpr int64_t kSmallAutoN = MPCG_SMALL_AUTO_N;
+
+// Whether the handle solves on one workgroup when its schedule allows it (the
+// option, or automatically up to kSmallAutoNnz stored entries and kSmallAutoN
+// rows, where one workgroup was measured no slower than three launches per
+// iteration on 2D and 3D Laplacians); fixed when the handle is created, as its
+// row groups are sized for it.
+bool small_layout(const cg_handle* h) {
+    if (h->single_block < 0 || h->S != 1 || h->p1 != 0) return false;
+    if (dev::kSmallXLds && h->n > dev::kSmallMaxN) return false;  // p must fit the LDS copy
+    return h->single_block > 0 || (h->nnz <= kSmallAutoNnz && h->n <= kSmallAutoN);
+}
 
 // Every SpMV wavefront takes a contiguous range of row groups (a capped grid:
 // a wavefront pipelines its batches); vector kernels use a capped grid.
@@ -444,18 +458,11 @@ void enqueue_iteration(cg_handle* h, int i, hipStream_t s, bool rule_at_end = fa
 
 // The single-workgroup solver runs schedules whose per-tile map is fixed for
 // the whole solve (static maps and the residual stages, which are uniform),
-// without column slices or the P1 numerics. Chosen automatically up to
-// kSmallAutoNnz stored entries and kSmallAutoN rows: below that one workgroup
-// beats three launches per iteration (measured on 2D and 3D Laplacians; at
-// 20K entries it is twice as slow, each wavefront then walking 16 row groups
-// one after the other).
-constexpr int64_t kSmallAutoNnz = MPCG_SMALL_AUTO_NNZ;
-constexpr int64_t kSmallAutoN = MPCG_SMALL_AUTO_N;
+// on handles whose row groups were sized for it (small_layout).
 
 bool single_block_solve(const cg_handle* h) {
     const bool supported = h->S == 1 && h->p1 == 0 && (h->sched == kSchedStatic || h->sched == kSchedResidual);
-    if (!supported || h->single_block < 0) return false;
-    return h->single_block > 0 || (h->nnz <= kSmallAutoNnz && h->n <= kSmallAutoN);
+    return supported && small_layout(h);
 }
 
 template <typename MetaT, int MAXROWS>
@@ -727,6 +734,17 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     h->p1 = p1;
     // Padding stores the sentinel row offset R, which needs the 16-bit form.
     h->meta16 = !(A->R <= 16 && A->C <= 16) || (p1 & CG_P1_PAD_COLUMNS);
+    if (opt) {
+        h->jacobi = opt->jacobi != 0;
+        if (opt->window > 0) h->window = std::min(opt->window, 4096);
+        if (opt->use_graph >= 0) h->use_graph = opt->use_graph != 0;
+        if (opt->col_slices < 0 || opt->col_slices > 64)
+            return bail(fail(CG_EINVAL, "cg_create: col_slices must lie in [0, 64]"));
+        h->S = std::max(1, opt->col_slices);
+        if (opt->single_block < -1 || opt->single_block > 1)
+            return bail(fail(CG_EINVAL, "cg_create: single_block must be -1, 0 or 1"));
+        h->single_block = opt->single_block;
+    }
     // Row blocks per wavefront: the largest of 32, 64, 128, 256 rows whose row
     // groups hold at most one batch of tiles on average (at least one row block).
     // A small matrix would then leave too few groups (wavefronts) to spread its
@@ -736,6 +754,12 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     auto groups_of = [&](int G) { return (h->nrb + G - 1) / G; };
     if (dev::kGroupRows > 0) {
         h->G = group_rb(dev::kGroupRows);
+    } else if (small_layout(h)) {
+        // A handle that solves on one workgroup: about one group of up to 256
+        // rows per wavefront, so that each wavefront pays the latency of a
+        // batch over many windows.
+        h->G = std::min<int>(group_rb(256),
+                             (int)std::max<int64_t>(1, (h->nrb + dev::kSmallWaves - 1) / dev::kSmallWaves));
     } else {
         h->G = group_rb(32);
         for (int rows : {64, 128, 256}) {
@@ -751,17 +775,6 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     }
     h->rows_per_group = h->G * A->R;
     h->ngroups = (int32_t)((h->nrb + h->G - 1) / h->G);
-    if (opt) {
-        h->jacobi = opt->jacobi != 0;
-        if (opt->window > 0) h->window = std::min(opt->window, 4096);
-        if (opt->use_graph >= 0) h->use_graph = opt->use_graph != 0;
-        if (opt->col_slices < 0 || opt->col_slices > 64)
-            return bail(fail(CG_EINVAL, "cg_create: col_slices must lie in [0, 64]"));
-        h->S = std::max(1, opt->col_slices);
-        if (opt->single_block < -1 || opt->single_block > 1)
-            return bail(fail(CG_EINVAL, "cg_create: single_block must be -1, 0 or 1"));
-        h->single_block = opt->single_block;
-    }
 
     // Device order of the tiles: canonical, or slice by slice (col_slices).
     // D is the layout in device order; segment v (slice v / ngroups, row group

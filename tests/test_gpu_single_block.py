@@ -6,8 +6,9 @@ residual history within 1e-6 relative over the first 20 entries, true
 residual within 1e-2 relative after clamping at the tolerance) and with the
 multi-launch solve. The cases cover odd n, ragged tiles, one- and two-byte
 index packing, both accumulator widths (row groups of at most 64 and of up
-to 256 rows), mixed per-tile maps, Jacobi, the iteration cap, a 1 x 1 system
-and repeated solves on one handle.
+to 256 rows), mixed per-tile maps, the magnitude rule, the residual stages,
+Jacobi, the iteration cap, a 1 x 1 system, repeated solves on one handle, and
+a handle too large for the workgroup's LDS copy of p (multi-launch instead).
 """
 
 import math
@@ -103,7 +104,57 @@ def test_single_block_random_spd(R, C, jacobi, dev):
     S.close()
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 4])
+@pytest.mark.parametrize("jacobi", [False, True])
+def test_single_block_residual_stages(jacobi, dev):
+    """BF16 until rho <= 1e-3, FP32 until 1e-6, then FP64: stages, trace and history as the oracle's."""
+    A = _spd(1001, 0.006, 71)
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, 16, 16)
+    Lo = otc.build(A.n, A.indptr, A.indices, A.data, 16, 16)
+    b = A.to_scipy() @ np.random.default_rng(0).uniform(-1, 1, A.n)
+    thresholds, prec = (1e-3, 1e-6), (2, 1, 0)
+    S = mpcg.Solver(L, jacobi=jacobi, single_block=1)
+    S.cg_set_schedule_residual(thresholds, prec)
+    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, b, ocg.RatchetSchedule(thresholds, prec), 1e-10, 2000,
+                    jacobi=jacobi, keep_maps=False)
+    bd = torch.from_numpy(b).to(dev)
+    xd = torch.zeros_like(bd)
+    st, K, hist = S.cg_solve(bd, xd, 1e-10, 2000)
+    tr = _true_res(A, xd.cpu().numpy(), b)
+    log(f"stages jacobi={jacobi}: gpu {st} K={K} true={tr:.3e}; oracle {ref.status} K={ref.K}")
+    assert st == ref.status and _k_close(K, ref.K), (K, ref.K)
+    assert _agree(tr, ref.true_residual, 1e-10)
+    m = min(K, ref.K, 20)
+    assert np.allclose(hist[: m + 1], ref.hist[: m + 1], rtol=1e-6, atol=0)
+    ks, counts = S.cg_get_map_trace()
+    assert ks.tolist() == [wk for (wk, _, _) in ref.windows]
+    assert counts.tolist() == [c for (_, c, _) in ref.windows]
+    assert len(ks) == 3
+    S.close()
+
+
+def test_single_block_beyond_the_lds_copy_runs_multi_launch(dev):
+    """A forced handle larger than the LDS copy of p solves on the multi-launch path."""
+    from gen.matrices import laplace2d_5pt
+    A = laplace2d_5pt(128)  # n = 16384
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, 16, 16)
+    Lo = otc.build(A.n, A.indptr, A.indices, A.data, 16, 16)
+    b = A.to_scipy() @ np.random.default_rng(0).uniform(-1, 1, A.n)
+    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, b, ocg.StaticSchedule(np.zeros(L.T, np.uint8)), 1e-8, 2000,
+                    keep_maps=False)
+    bd = torch.from_numpy(b).to(dev)
+    res = []
+    for sb in (1, -1):
+        S = mpcg.Solver(L, single_block=sb)
+        xd = torch.zeros_like(bd)
+        res.append(S.cg_solve(bd, xd, 1e-8, 2000))
+        torch.cuda.synchronize()
+        S.close()
+    (st1, K1, h1), (st2, K2, h2) = res
+    assert (st1, K1) == (st2, K2) == (ref.status, K1) and _k_close(K1, ref.K)
+    assert np.array_equal(h1, h2)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_single_block_agrees_with_multi_launch(cfg, dev):
     w = make_workload(cfg, "small")
     A = w.A
@@ -115,6 +166,8 @@ def test_single_block_agrees_with_multi_launch(cfg, dev):
             S.cg_set_schedule_residual(w.map_spec["thresholds"], w.map_spec["prec"])
         elif w.map_spec["kind"] == "static":
             S.cg_set_precision_map(static_map(tile_scores(L.T, 2)))
+        elif w.map_spec["kind"] == "magnitude":
+            S.cg_map_from_magnitude(w.map_spec["t_bf16"], w.map_spec["t_fp32"])
         bd = torch.from_numpy(w.b).to(dev)
         xd = torch.zeros_like(bd)
         st, K, hist = S.cg_solve(bd, xd, w.tol, w.maxit)
@@ -123,9 +176,10 @@ def test_single_block_agrees_with_multi_launch(cfg, dev):
         S.close()
     (st1, K1, h1, x1, k1, c1), (st2, K2, h2, x2, k2, c2) = res
     log(f"cfg{cfg}: single block {st1} K={K1}; multi-launch {st2} K={K2}")
-    assert st1 == st2 and abs(K1 - K2) <= 1
-    m = min(K1, K2, 40)
-    assert np.allclose(h1[: m + 1], h2[: m + 1], rtol=1e-9, atol=0)
+    # Summation orders differ between the paths: the usual bars, not bits.
+    assert st1 == st2 and _k_close(K1, K2), (K1, K2)
+    m = min(K1, K2, 20)
+    assert np.allclose(h1[: m + 1], h2[: m + 1], rtol=1e-6, atol=0)
     assert k1 == k2 and c1 == c2
     assert _agree(_true_res(A, x1, w.b), _true_res(A, x2, w.b), w.tol)
 
