@@ -1,5 +1,6 @@
 // Device code for gfx950: value-plane builder, mixed-precision Tile-CSC SpMV,
-// fused CG vector updates with single-pass grid reductions, and map kernels.
+// fused CG vector updates with single-pass grid reductions, a single-workgroup
+// CG loop for small systems, the column-slice combine, and map kernels.
 //
 // Method: EvoCG paper ("EvoCG: Self-Evolving Precision Control for Faster
 // Conjugate Gradient"): Tile-CSC and value streams (Sec. 3.3, Fig. 4), the
@@ -24,7 +25,9 @@ constexpr int kMaxGroupRB = 63;  // row blocks per wavefront at most (boundaries
 
 // Solver scalars, resident on the device for the whole solve. Each field has
 // one writer per kernel launch (thread 0 of block 0) and no other block of
-// that launch reads it, except `done` (see cg_direction_kernel).
+// that launch reads it, except `done` (see cg_direction_kernel). In the
+// single-workgroup loop thread 0 writes them and reads back only its own
+// stores (stage and trace counters through atomic loads; cg_small_kernel).
 struct State {
     double rz;        // r.z of the current iterate (r.r for plain CG)
     double rz_prev;   // r.z before the current update (copied by the update kernel)
@@ -120,11 +123,9 @@ __device__ inline double block_sum(double v, double* s_tmp) {
     return t;
 }
 
-// Fixed-order sum of nparts partials (component j of NV per part); every
-// thread of the block gets the same value, and every block that calls this
-// on the same data gets the same bits.
-// Sum of nparts per-block partials (NV values each) in a fixed order, so that
-// every block of the calling kernel obtains the same bits. A thread takes
+// Sum of nparts per-block partials (NV values each) in a fixed order: every
+// thread of the block gets the same value, and every block that calls this on
+// the same data gets the same bits. A thread takes
 // partials threadIdx.x + k * blockDim.x; it loads eight of them at once (eight
 // independent loads in flight instead of one at a time) into eight running
 // sums, adds the rest one by one into the first, and the block reduces.
@@ -180,8 +181,9 @@ __device__ inline void wave_lds_sync() {
 // Mixed-precision Tile-CSC SpMV.
 //
 // One wavefront owns a run of row groups; a row group is G consecutive row
-// blocks (G*R rows: the largest of 32, 64, 128 or 256 rows whose groups hold
-// one batch of tiles on average, and at least one row block).
+// blocks (at most 256 rows; G is chosen per handle when it is created). With
+// column slices the unit is a segment, the tiles of one row group within one
+// slice, and each segment writes its own partial product.
 // Its tiles are taken in batches of up to 64 in storage order, and the 64
 // lanes sweep a batch's nonzeros 64 at a time ("windows"), several windows
 // at once. Products of the widened stored value and the FP64 vector entry are
@@ -195,8 +197,9 @@ __device__ inline void wave_lds_sync() {
 // record per window built with the layout (the tile of the window's first
 // nonzero and a bit mask of the tiles that start inside the window, so the
 // lookup is a prefix popcount). Each lane then reads its value with one
-// 8-byte load from its tile's plane: no branch, and a map change costs
-// nothing but the map itself. Lanes past a batch's end land on a sentinel
+// 8-byte load, from its precision's plane under a uniform precision or from
+// the map's packed segment (rebuilt by repack_kernel when the map changes):
+// no branch on the precision. Lanes past a batch's end land on a sentinel
 // entry whose offsets are past the end of every buffer; the hardware answers
 // those loads with zero and no memory access.
 //
@@ -204,7 +207,8 @@ __device__ inline void wave_lds_sync() {
 // while it sweeps the current one. A block of kSpmvWaves wavefronts handles a
 // contiguous range of row groups (blocks are spread so that each XCD gets a
 // contiguous part of the matrix); in CG mode each block also writes its part
-// of p.q.
+// of p.q. The single-workgroup solver runs the same per-wavefront code
+// (spmv_wave) on its 16 wavefronts.
 // ---------------------------------------------------------------------------
 enum SpmvMode { kSpmvPlain = 0, kSpmvCg = 1, kSpmvResidual = 2 };
 #ifndef MPCG_SPMV_UNROLL
@@ -237,8 +241,9 @@ __host__ __device__ inline int sweep_windows(int nw) {
 __host__ __device__ inline int batch_records(int len) { return sweep_windows((len + kWave - 1) / kWave); }
 
 // Batch table entry (8 int32, one scalar load): the wave's work is a run of
-// consecutive batches covering whole row groups. A row group without tiles
-// has one entry with no tiles, so its rows are still written.
+// consecutive batches covering whole row groups (segments, with column
+// slices). A segment without tiles has one entry with no tiles, so its rows
+// are still written.
 enum BatchField { kBtTile = 0, kBtTiles, kBtFirstNnz, kBtLen, kBtRecords, kBtGroup, kBtFlags, kBtSegment, kBtFields };
 constexpr int kBatchFirstOfGroup = 1, kBatchLastOfGroup = 2;
 // Bits from kBatchSliceShift up: the column slice of the batch's segment,
