@@ -244,11 +244,19 @@ def main():
               f"true residual {truep:.3e}", file=sys.stderr, flush=True)
         Sp.close()
 
-    traffic = None
+    # Counter results (rocprofv3 runs of --pmc-probe), reported only while they
+    # describe the kernels as built from the current sources.
+    traffic, l2 = None, None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
         if tr.get("kernel_source_hash") == kernel_source_hash():
             traffic = tr.get("bytes_per_launch")
+            c = tr.get("l2", {})
+            if c:
+                l2 = {"spmv_hit_rate_mixed_map": c["mixed"]["hit_rate"],
+                      "spmv_hit_rate_fp64_map": c["fp64"]["hit_rate"],
+                      "x_gather_hit_rate_estimate": c.get("x_gather_estimate", {}).get("hit_rate"),
+                      "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -307,6 +315,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": bytes_spmv,
         },
+        "l2": l2,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
