@@ -116,6 +116,24 @@ def test_sliced_spmv_matches_oracle(name, slices, dev):
     S.close()
 
 
+@pytest.mark.parametrize("slices", [16, 64])
+def test_more_slices_than_column_blocks(slices, dev):
+    """Slices without any column block (ncb < S) still write their zero partials."""
+    A = _random(100, 0.05, 54)  # C = 16: 7 column blocks
+    L, Lo = _both(A, 16, 16)
+    prec = np.random.default_rng(5).integers(0, 3, L.T).astype(np.uint8)
+    S = mpcg.Solver(L, precision_map=prec, col_slices=slices)
+    x = np.random.default_rng(6).uniform(-1, 1, A.n)
+    y = _spmv(S, x, dev)
+    y_ref = ospmv.spmv(Lo, A.indptr, A.indices, prec, x)
+    bound = 1e-13 * ospmv.abs_bound(A.indptr, A.indices, A.data, x)
+    assert np.all(np.abs(y - y_ref) <= bound)
+    e = S.cg_export_layout()
+    assert np.array_equal(e["tile_col_idx"], Lo.tile_col_idx) and np.array_equal(e["row_idx"], Lo.row_idx)
+    assert np.array_equal(S.cg_get_active_map(), prec)
+    S.close()
+
+
 def test_sliced_spmv_with_paper_numerics(dev):
     A = _random(2000, 0.004, 53)
     L, Lo = _both(A, 16, 16)
