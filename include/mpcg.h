@@ -298,6 +298,17 @@ int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const double* scores
  * make the result the active map (the schedule stays set). */
 int cg_eval_tile_rule(cg_handle* h, double rho);
 
+/* Window maps of the windowed per-tile rule (Sec. 3.4: a map chosen at a
+ * window start holds for the window), recorded by later solves for tests and
+ * analysis. cg_record_window_maps(h, cap) keeps the map of each of the first
+ * cap windows of every solve in cap * T bytes of device memory (cap = 0 stops
+ * recording and frees them). cg_get_window_maps copies the first min(cap,
+ * recorded) maps of the last solve to host uint8[windows][T] (canonical tile
+ * order; out may be NULL) and returns the number recorded; 0 without the tile
+ * rule or without recording. Errors: CG_EINVAL (NULL h, cap < 0), CG_ENOMEM. */
+int cg_record_window_maps(cg_handle* h, int32_t cap);
+int cg_get_window_maps(const cg_handle* h, int32_t cap, uint8_t* out);
+
 /* Remove any schedule; the active map stays as it is. */
 int cg_clear_schedule(cg_handle* h);
 

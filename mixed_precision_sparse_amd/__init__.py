@@ -199,6 +199,16 @@ class Solver:
         check(_lib.load().cg_get_column_codes(self._h, int(out.shape[0]), _ptr(out)))
         return out
 
+    def cg_record_window_maps(self, cap):
+        check(_lib.load().cg_record_window_maps(self._h, int(cap)))
+
+    def cg_get_window_maps(self, cap=100000):
+        """Tile-rule maps of the last solve's windows, uint8[windows][T] (canonical tile order)."""
+        n = check(_lib.load().cg_get_window_maps(self._h, 0, None))
+        out = np.empty((min(n, cap), self.T), dtype=np.uint8)
+        check(_lib.load().cg_get_window_maps(self._h, int(out.shape[0]), _ptr(out)))
+        return out
+
     def cg_eval_tile_rule(self, rho):
         check(_lib.load().cg_eval_tile_rule(self._h, float(rho)))
 

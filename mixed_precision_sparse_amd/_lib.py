@@ -47,6 +47,8 @@ SIGNATURES = {
     "cg_set_precision_map": (ct.c_int, [vp, vp, i32]),
     "cg_get_active_map": (ct.c_int, [vp, vp]),
     "cg_map_from_magnitude": (ct.c_int, [vp, f64, f64]),
+    "cg_record_window_maps": (ct.c_int, [vp, i32]),
+    "cg_get_window_maps": (ct.c_int, [vp, i32, vp]),
     "cg_set_schedule_residual": (ct.c_int, [vp, i32, vp, vp]),
     "cg_set_schedule_tile_rule": (ct.c_int, [vp, i32, vp, f64, f64]),
     "cg_eval_tile_rule": (ct.c_int, [vp, f64]),

@@ -1217,10 +1217,12 @@ struct MapArgs {
     int32_t* trace_counts;
     const int32_t* btab;  // tile rule: batches of the SpMV (a partition of the tiles)
     uint8_t* dirty;       // tile rule: per batch, set when a tile of the batch changed precision
+    uint8_t* winmaps;     // tile rule, recording on: [window][T] map of every window (else NULL)
     int64_t T;
     int64_t nbatch;
-    double rho;     // explicit rho (eval mode)
-    int32_t solve;  // 1: in-solve window step (reads k and rho_k from the state)
+    double rho;          // explicit rho (eval mode)
+    int32_t solve;       // 1: in-solve window step (reads k and rho_k from the state)
+    int32_t winmap_cap;  // windows winmaps holds
 };
 
 __device__ inline void block_counts_out(unsigned c0, unsigned c1, unsigned c2, int32_t* out) {
@@ -1263,6 +1265,7 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
             const int code = tile_rule_code(a.scores[t], rho, st->hi, st->lo);
             changed = code != (int)a.map[t];
             a.map[t] = (uint8_t)code;
+            if (slot >= 0 && slot < a.winmap_cap) a.winmaps[(size_t)slot * a.T + t] = (uint8_t)code;
             c0 += code == 0;
             c1 += code == 1;
             c2 += code == 2;

@@ -43,6 +43,8 @@ struct cg_handle {
     int32_t R = 0, C = 0, G = 0, rows_per_group = 0, ngroups = 0;
     int32_t S = 1;                 // column slices (cg_options.col_slices)
     int32_t single_block = 0;      // cg_options.single_block: 0 auto, 1 when supported, -1 never
+    uint8_t* winmaps = nullptr;    // cg_record_window_maps: [winmap_cap][T] tile-rule window maps
+    int32_t winmap_cap = 0;
     int64_t nseg = 0;              // SpMV segments: S * ngroups (slice-major)
     std::vector<int32_t> dperm;    // S > 1: device tile -> canonical tile
     double* qpart = nullptr;       // S > 1: [S][n_pad] partial products of the slices
@@ -368,6 +370,8 @@ dev::MapArgs map_args(cg_handle* h, double rho, int solve) {
     a.trace_counts = h->trace_counts;
     a.btab = h->btab;
     a.dirty = h->dirty;
+    a.winmaps = h->winmaps;
+    a.winmap_cap = h->winmap_cap;
     a.T = h->T;
     a.nbatch = h->nbatch;
     a.rho = rho;
@@ -1265,6 +1269,37 @@ extern "C" int cg_get_column_codes(const cg_handle* h, int32_t cap, uint8_t* out
     const int64_t n = std::min<int64_t>(std::min<int64_t>(hs.ntrace, h->cbhist_rows), std::max(cap, 0));
     if (n > 0 && out) HIP_CHECK(hipMemcpy(out, h->cbhist, (size_t)(n * h->ncb), hipMemcpyDeviceToHost));
     return (int)std::min<int64_t>(hs.ntrace, h->cbhist_rows);
+}
+
+extern "C" int cg_record_window_maps(cg_handle* h, int32_t cap) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_record_window_maps: h is NULL");
+    if (cap < 0) return fail(CG_EINVAL, "cg_record_window_maps: cap must be >= 0");
+    if (h->winmaps) {
+        HIP_CHECK(hipDeviceSynchronize());
+        dfree(h, h->winmaps);
+        h->winmaps = nullptr;
+        h->winmap_cap = 0;
+    }
+    if (cap > 0) {
+        const int rc = dalloc(h, &h->winmaps, (int64_t)cap * h->T);
+        if (rc != CG_OK) return rc;
+        h->winmap_cap = cap;
+    }
+    drop_graph(h);  // the captured tile-rule launches carry the buffer
+    return CG_OK;
+}
+
+extern "C" int cg_get_window_maps(const cg_handle* h, int32_t cap, uint8_t* out) {
+    mpcg::clear_error();
+    if (!h) return fail(CG_EINVAL, "cg_get_window_maps: h is NULL");
+    if (h->sched != kSchedTileRule || !h->winmaps) return 0;
+    dev::State hs{};
+    HIP_CHECK(hipMemcpy(&hs, h->st, sizeof(hs), hipMemcpyDeviceToHost));
+    const int64_t avail = std::min<int64_t>(hs.ntrace, h->winmap_cap);
+    const int64_t m = std::min<int64_t>(avail, std::max(cap, 0));
+    if (m > 0 && out) HIP_CHECK(hipMemcpy(out, h->winmaps, (size_t)(m * h->T), hipMemcpyDeviceToHost));
+    return (int)avail;
 }
 
 extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {

@@ -363,6 +363,35 @@ def test_cg_launch_modes_agree(graph, window, dev):
     S2.close()
 
 
+def test_tile_rule_window_maps_bit_exact(dev):
+    """Every recorded window map of the per-tile rule equals the oracle's, tile by tile,
+    while the two trajectories agree (rho at the window start equal to 1e-9 relative)."""
+    w = make_workload(5, "small")
+    A = w.A
+    L, Lo = build_both(w)
+    S = mpcg.Solver(L)
+    sched = _configure(S, w, L, Lo)
+    S.cg_record_window_maps(w.maxit // w.map_spec["period"] + 2)
+    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, w.b, sched, w.tol, w.maxit)
+    bd = torch.from_numpy(w.b).to(dev)
+    xd = torch.zeros_like(bd)
+    st, K, hist = S.cg_solve(bd, xd, w.tol, w.maxit)
+    maps = S.cg_get_window_maps()
+    ks, counts = S.cg_get_map_trace()
+    assert len(maps) == len(ks) > 1
+    checked = 0
+    for i, (wk, c, m) in enumerate(ref.windows):
+        if i >= len(ks) or wk > min(K, ref.K) or abs(hist[wk] - ref.hist[wk]) > 1e-9 * ref.hist[wk]:
+            break
+        assert ks[i] == wk and np.array_equal(maps[i], m), (i, wk)
+        assert np.bincount(maps[i], minlength=3).tolist() == counts[i].tolist()
+        checked += 1
+    log(f"tile rule: {checked} of {len(ks)} window maps compared bit for bit")
+    assert checked >= 3
+    S.cg_record_window_maps(0)
+    S.close()
+
+
 def test_tile_rule_packed_values_follow_the_map_after_a_solve(dev):
     """In a solve the tile rule repacks only the batches whose tiles changed
     precision; afterwards cg_spmv under the final map matches the oracle."""
