@@ -203,6 +203,12 @@ typedef struct {
  */
 
 /*
+ * Threads: handles share no state, so different handles may be used at the
+ * same time from different host threads; calls on one handle must not
+ * overlap. cg_last_error reports the calling thread's last error.
+ */
+
+/*
  * Create a solver handle on the current HIP device.
  *   A             : canonical matrix; copied to library-owned device memory
  *                   (index arrays, the FP64 values, and the FP32 and BF16 value
