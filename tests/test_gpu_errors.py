@@ -1,0 +1,112 @@
+"""Argument validation of the device-side calls and handle lifetime.
+
+Every rejected call returns CG_EINVAL with a message naming the call, leaves
+the handle usable (a solve after the errors gives the same result as before
+them), and creating and destroying handles returns all of their device
+memory."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from gen import make_workload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mpcg = pytest.importorskip("mixed_precision_sparse_amd")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    return torch.device("cuda:0")
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _rejects(fn, name):
+    with pytest.raises(mpcg.CGError) as e:
+        fn()
+    assert name in str(e.value), str(e.value)
+
+
+def test_invalid_arguments_leave_the_handle_usable(dev):
+    w = make_workload(2, "small")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    S = mpcg.Solver(L, single_block=-1)
+    b = torch.from_numpy(w.b).to(dev)
+    x = torch.zeros_like(b)
+    ref = S.cg_solve(b, x, w.tol, w.maxit)
+    lib = mpcg._lib.load()
+    y = torch.empty_like(b)
+    # cg_spmv: y must not overlap x
+    _rejects(lambda: S.cg_spmv(b, b), "cg_spmv")
+    assert lib.cg_spmv(S._h, None, mpcg._dev_ptr(y), None) < 0
+    # cg_solve: tolerance, iteration cap, NULL vectors
+    _rejects(lambda: S.cg_solve(b, x, -1.0, 10), "cg_solve")
+    _rejects(lambda: S.cg_solve(b, x, 1e-8, -1), "cg_solve")
+    assert lib.cg_solve(S._h, None, None, 1e-8, 10, mpcg._dev_ptr(x), None, None, None) < 0
+    # maps and schedules
+    _rejects(lambda: S.cg_set_precision_map(np.full(L.T, 3, np.uint8)), "cg_set_precision_map")
+    with pytest.raises(ValueError):
+        S.cg_set_precision_map(np.zeros(L.T + 1, np.uint8))
+    _rejects(lambda: S.cg_map_from_magnitude(1e-2, 1e-4), "cg_map_from_magnitude")
+    _rejects(lambda: S.cg_set_schedule_residual((1e-3,), (2, 1, 0, 0, 0, 0, 0, 0, 0)), "cg_set_schedule_residual")
+    _rejects(lambda: S.cg_set_schedule_residual((1e-3, 1e-6), (2, 5, 0)), "cg_set_schedule_residual")
+    _rejects(lambda: S.cg_set_schedule_residual((np.nan, 1e-6), (2, 1, 0)), "cg_set_schedule_residual")
+    scores = np.random.default_rng(2).uniform(0, 1, L.T)
+    _rejects(lambda: S.cg_set_schedule_tile_rule(0, scores, 1e-3, 1e-6), "cg_set_schedule_tile_rule")
+    _rejects(lambda: S.cg_set_schedule_tile_rule(10, scores, 1e-6, 1e-3), "cg_set_schedule_tile_rule")
+    _rejects(lambda: S.cg_set_schedule_pmag(1.0, 0.5), "cg_set_schedule_pmag")
+    _rejects(lambda: S.cg_set_schedule_pmag(1e-9, 1e-8, period=0), "cg_set_schedule_pmag")
+    _rejects(lambda: S.cg_record_window_maps(-1), "cg_record_window_maps")
+    _rejects(lambda: S.cg_eval_tile_rule(1.0), "cg_eval_tile_rule")  # no tile rule set
+    # the handle still solves exactly as before
+    x2 = torch.zeros_like(b)
+    got = S.cg_solve(b, x2, w.tol, w.maxit)
+    torch.cuda.synchronize()
+    assert got[:2] == ref[:2] and np.array_equal(got[2], ref[2]) and torch.equal(x, x2)
+    S.close()
+
+
+def test_invalid_create_options(dev):
+    w = make_workload(1, "small")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    _rejects(lambda: mpcg.Solver(L, precision_map=np.full(L.T, 7, np.uint8)), "cg_create")
+    _rejects(lambda: mpcg.Solver(L, p1=1 << 7), "cg_create")
+    _rejects(lambda: mpcg.Solver(L, col_slices=-1), "cg_create")
+    _rejects(lambda: mpcg.Solver(L, single_block=-2), "cg_create")
+
+
+def test_handles_return_their_device_memory(dev):
+    w = make_workload(3, "small")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    b = torch.from_numpy(w.b).to(dev)
+    x = torch.zeros_like(b)
+    torch.cuda.synchronize()
+    S = mpcg.Solver(L, jacobi=True, single_block=-1)  # warm up the runtime's own allocations
+    S.cg_solve(b, x, w.tol, 50)
+    S.close()
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    held = 0
+    for i in range(10):
+        S = mpcg.Solver(L, jacobi=True, single_block=-1, col_slices=2 if i % 2 else 0)
+        held = max(held, S.device_bytes())
+        S.cg_solve(b, x, w.tol, 50)
+        S.close()
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    log(f"device bytes per handle {held}, free memory change {free0 - free1} bytes")
+    assert held > 0
+    assert free0 - free1 <= 4 << 20  # allocator granularity, not leaked handles
