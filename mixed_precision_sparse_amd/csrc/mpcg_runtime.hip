@@ -1,7 +1,9 @@
 // HIP runtime behind the C ABI: device-resident Tile-CSC matrix with its
 // three value planes, the precision map and schedules, cg_spmv, and the
 // cg_solve loop (device-resident scalars, window-wise stop polling, optional
-// HIP-graph replay of each window).
+// HIP-graph replay of each window, or one single-workgroup launch for small
+// systems). Optional column slices reorder the tiles on the device; every
+// map, trace and export is translated back to the canonical tile order.
 //
 // EvoCG paper: value-stream selection without re-quantisation (Sec. 3.3.2,
 // Sec. 4.8), the per-iteration CG step (Sec. 2.1, Fig. 1), interval reuse of
@@ -1002,7 +1004,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     TRY(dalloc(h, &h->toff, std::max<int64_t>(T, 1)));
     TRY(dalloc(h, &h->dirty, std::max<int64_t>(h->nbatch, 1)));
     // CG vectors padded with zeros to an even length (the vector kernels work
-    // in 16-byte pairs); nothing writes the padding.
+    // in 16-byte pairs); the padding entry stays zero, as every update of it
+    // combines zeros (q's padding is never written by the SpMV).
     const int64_t n_pad = n + (n & 1);
     TRY(dalloc(h, &h->x, n_pad));
     TRY(dalloc(h, &h->r, n_pad));
