@@ -1225,15 +1225,34 @@ struct MapArgs {
     int32_t winmap_cap;  // windows winmaps holds
 };
 
+// The block's totals of three per-thread counts, returned in thread c for
+// count c (c < 3; other threads get 0). Each wavefront sums with shuffles and
+// leaves one slot per count in LDS: an LDS atomic from every lane on one
+// address would run its 64 lanes one after another.
+__device__ inline unsigned block_count3(unsigned c0, unsigned c1, unsigned c2) {
+    __shared__ unsigned s_part[kWavesPerBlock][3];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        c0 += __shfl_xor(c0, off, kWave);
+        c1 += __shfl_xor(c1, off, kWave);
+        c2 += __shfl_xor(c2, off, kWave);
+    }
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        s_part[w][0] = c0;
+        s_part[w][1] = c1;
+        s_part[w][2] = c2;
+    }
+    __syncthreads();
+    unsigned t = 0;
+    if (threadIdx.x < 3)
+        for (int v = 0; v < (int)(blockDim.x / kWave); ++v) t += s_part[v][threadIdx.x];
+    return t;
+}
+
 __device__ inline void block_counts_out(unsigned c0, unsigned c1, unsigned c2, int32_t* out) {
-    __shared__ unsigned s_cnt[3];
-    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
-    __syncthreads();
-    atomicAdd(&s_cnt[0], c0);  // LDS atomics
-    atomicAdd(&s_cnt[1], c1);
-    atomicAdd(&s_cnt[2], c2);
-    __syncthreads();
-    if (threadIdx.x < 3) out[threadIdx.x] = (int32_t)s_cnt[threadIdx.x];
+    const unsigned t = block_count3(c0, c1, c2);
+    if (threadIdx.x < 3) out[threadIdx.x] = (int32_t)t;
 }
 
 // Windowed tile rule: at k % period == 0 every tile's precision is re-selected
@@ -1307,20 +1326,41 @@ struct PMagArgs {
 __device__ inline double nan_max(double a, double b) { return (a > b || a != a) ? a : b; }
 __device__ inline int pmag_code(double m, double lo, double hi) { return m < lo ? 2 : (m < hi ? 1 : 0); }
 
-__global__ __launch_bounds__(kBlock) void pmag_kernel(PMagArgs a) {
-    __shared__ unsigned s_cnt[3];
-    int slot = -1;
-    int k = 0;
-    if (a.solve) {
-        if (load_done(a.st)) return;
-        k = a.st->k;
-        if (k % a.period != 0) return;
-        slot = k / a.period;
-        if (slot >= a.trace_cap) slot = -1;
+// In a solve the rule runs at iterations k that are multiples of the period
+// and writes trace entry k / period; returns false where this launch has
+// nothing to do (the solve has stopped, or k is not a multiple).
+__device__ inline bool pmag_slot(const PMagArgs& a, int& k, int& slot) {
+    slot = -1;
+    k = 0;
+    if (!a.solve) return true;
+    if (load_done(a.st)) return false;
+    k = a.st->k;
+    if (k % a.period != 0) return false;
+    slot = k / a.period;
+    if (slot >= a.trace_cap) slot = -1;
+    return true;
+}
+
+// The block's tile counts per code into the trace entry (slot b % kTraceBlocks
+// of entry `slot`); block 0 also records the entry's iteration.
+__device__ inline void pmag_counts_out(const PMagArgs& a, const unsigned (&cnt)[3], int slot, int k) {
+    if (slot < 0) return;
+    const unsigned t = block_count3(cnt[0], cnt[1], cnt[2]);
+    if (threadIdx.x < 3) {
+        int32_t* out = a.trace_counts + ((size_t)slot * kTraceBlocks + blockIdx.x % kTraceBlocks) * 3;
+        atomicAdd(&out[threadIdx.x], (int32_t)t);
     }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.trace_k[slot] = k;
+        a.st->ntrace = slot + 1;
+    }
+}
+
+// One thread per column block.
+__global__ __launch_bounds__(kBlock) void pmag_kernel(PMagArgs a) {
+    int k, slot;
+    if (!pmag_slot(a, k, slot)) return;
     uint8_t* hist = slot >= 0 && a.history ? a.history + (size_t)slot * a.ncb : nullptr;
-    if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0u;
-    __syncthreads();
     unsigned cnt[3] = {0u, 0u, 0u};
     const bool pairs = (a.C & 1) == 0 && ((uintptr_t)a.p & 15) == 0;
     for (int64_t J = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; J < a.ncb;
@@ -1343,20 +1383,7 @@ __global__ __launch_bounds__(kBlock) void pmag_kernel(PMagArgs a) {
         if (hist) hist[J] = (uint8_t)code;
         cnt[code] += tiles;
     }
-    if (slot >= 0) {
-        atomicAdd(&s_cnt[0], cnt[0]);  // LDS atomics
-        atomicAdd(&s_cnt[1], cnt[1]);
-        atomicAdd(&s_cnt[2], cnt[2]);
-        __syncthreads();
-        if (threadIdx.x < 3) {
-            int32_t* out = a.trace_counts + ((size_t)slot * kTraceBlocks + blockIdx.x % kTraceBlocks) * 3;
-            atomicAdd(&out[threadIdx.x], (int32_t)s_cnt[threadIdx.x]);
-        }
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-            a.trace_k[slot] = k;
-            a.st->ntrace = slot + 1;
-        }
-    }
+    pmag_counts_out(a, cnt, slot, k);
 }
 
 // Precision counts of the active map into trace entry 0 (static maps).

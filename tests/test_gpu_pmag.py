@@ -47,7 +47,11 @@ def _random_spd(n, density, seed, R, C):
     return M
 
 
-CASES = [("cfg2", None), ("cfg3", None), ("cfg5", None), ("C12", (300, 0.02, 8, 12)), ("C128", (700, 0.01, 64, 128))]
+# Beyond the workloads: C12 (segments of 12 entries, 16-byte loads of 6 pairs),
+# C128 (the largest column blocks, a short last one) and C8odd (n odd: the
+# last column block is short and ends on a single entry).
+CASES = [("cfg2", None), ("cfg3", None), ("cfg5", None), ("C12", (300, 0.02, 8, 12)), ("C128", (700, 0.01, 64, 128)),
+         ("C8odd", (301, 0.03, 8, 8))]
 
 
 def _case(name, spec):
@@ -91,6 +95,35 @@ def test_pmag_spmv_and_map_match_oracle(name, spec, dev):
         assert np.all(np.abs(yd.cpu().numpy() - y_ref) <= bound)
         if trial == 0:
             assert set(np.unique(ref_map)) == {0, 1, 2}
+    S.close()
+
+
+@pytest.mark.parametrize("C", [8, 16])
+def test_pmag_map_independent_of_vector_alignment(C, dev):
+    """x at an 8-byte offset (scalar loads) and at 16-byte offsets (pairs) gives the
+    oracle's map; a NaN makes its column block FP64."""
+    n, ip, ind, val, R, _ = _case("x", (333, 0.03, 8, C))
+    L = mpcg.cg_tilecsc_from_csr(n, ip, ind, val, R, C)
+    Lo = otc.build(n, ip, ind, val, R, C)
+    S = mpcg.Solver(L)
+    lo, hi = 1e-4, 1e-2
+    S.cg_set_schedule_pmag(lo, hi)
+    ncb = -(-n // C)
+    rng = np.random.default_rng(3)
+    scale = np.array([1.0, 1e-3, 1e-5])[np.arange(ncb) % 3]
+    x = rng.uniform(-1, 1, n) * np.repeat(scale, C)[:n]
+    x[2 * C + 1] = np.nan  # block 2 is a BF16 block by scale
+    ref_map = omaps.pmag_rule(x, C, Lo.tile_col_idx, lo, hi)
+    assert ref_map[Lo.tile_col_idx == 2].tolist() == [0] * int(np.sum(Lo.tile_col_idx == 2))
+    buf = torch.zeros(n + 2, dtype=torch.float64, device=dev)
+    for off in (1, 2, 0):
+        xd = buf[off:off + n]
+        xd.copy_(torch.from_numpy(x))
+        log(f"pmag alignment C={C} offset {8 * off} bytes, address % 16 = {xd.data_ptr() % 16}")
+        yd = torch.empty(n, dtype=torch.float64, device=dev)
+        S.cg_spmv(xd, yd)
+        torch.cuda.synchronize()
+        assert np.array_equal(S.cg_get_active_map(), ref_map), off
     S.close()
 
 
