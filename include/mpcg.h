@@ -339,8 +339,9 @@ int cg_spmv(cg_handle* h, const double* x, double* y, void* stream);
  *   tol        : stop when ||r_k||/||r_0|| <= tol (recurrence residual), tol >= 0.
  *   maxit      : iteration cap, maxit >= 0.
  *   x          : device double[n] receiving the last iterate; may equal x0.
- *                b, x0 and x start on 16-byte boundaries (any hipMalloc'd
- *                buffer or torch tensor does).
+ *                b, x0 and x need only the alignment of a double: the
+ *                solve reads b and x0 and writes x entry by entry, and runs
+ *                its iterations on the handle's own vectors.
  *   iterations : host int32, completed iterations K.
  *   res_hist   : host double[maxit+1] receiving rho_0 .. rho_K (rho_0 = 1;
  *                a zero r0 gives K = 0 and rho_0 = 0), or NULL.
@@ -348,8 +349,8 @@ int cg_spmv(cg_handle* h, const double* x, double* y, void* stream);
  *                returns when the solve has finished.
  * Returns CG_OK (converged), CG_NOT_CONVERGED (K = maxit), CG_BREAKDOWN
  * (p.q <= 0 or non-finite alpha/beta; x holds the last iterate), or an error:
- * CG_EINVAL (NULL h, b, x or iterations, a misaligned vector, tol < 0,
- * maxit < 0), CG_ENOMEM, CG_EDEVICE.
+ * CG_EINVAL (NULL h, b, x or iterations, tol < 0, maxit < 0), CG_ENOMEM,
+ * CG_EDEVICE.
  */
 int cg_solve(cg_handle* h, const double* b, const double* x0, double tol, int32_t maxit,
              double* x, int32_t* iterations, double* res_hist, void* stream);

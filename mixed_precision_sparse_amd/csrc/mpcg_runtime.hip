@@ -1344,9 +1344,6 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
                         double* x, int32_t* iterations, double* res_hist, void* stream) {
     mpcg::clear_error();
     if (!h || !b || !x || !iterations) return fail(CG_EINVAL, "cg_solve: NULL argument");
-    // The vector kernels move pairs of entries with 16-byte loads and stores.
-    if (((reinterpret_cast<uintptr_t>(b) | reinterpret_cast<uintptr_t>(x0) | reinterpret_cast<uintptr_t>(x)) & 15) != 0)
-        return fail(CG_EINVAL, "cg_solve: b, x0 and x must be 16-byte aligned");
     if (!(tol >= 0.0)) return fail(CG_EINVAL, "cg_solve: tol must be >= 0");
     if (maxit < 0) return fail(CG_EINVAL, "cg_solve: maxit must be >= 0");
     hipStream_t user = static_cast<hipStream_t>(stream);

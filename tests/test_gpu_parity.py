@@ -326,6 +326,36 @@ def test_cg_initial_guess_and_degenerate_cases(single_block, dev):
 
 
 @pytest.mark.parametrize("single_block", [-1, 1])
+def test_cg_vectors_at_8_byte_offsets(single_block, dev):
+    """b, x0 and x as views that start 8 bytes into their buffers (odd n, so the
+    last entry is the buffer's last double) give the aligned solve's bits."""
+    n = 1001  # 1D Laplacian, tridiag(-1, 2, -1)
+    ip = np.concatenate([[0], np.cumsum([2] + [3] * (n - 2) + [2])]).astype(np.int64)
+    ind = np.concatenate([[0, 1]] + [[i - 1, i, i + 1] for i in range(1, n - 1)] + [[n - 2, n - 1]]).astype(np.int32)
+    val = np.concatenate([[2.0, -1.0]] + [[-1.0, 2.0, -1.0]] * (n - 2) + [[-1.0, 2.0]])
+    L = mpcg.cg_tilecsc_from_csr(n, ip, ind, val, 16, 16)
+    S = mpcg.Solver(L, single_block=single_block)
+    rng = np.random.default_rng(5)
+    x0 = rng.uniform(-1, 1, n)
+    ref_b = torch.from_numpy(rng.uniform(-1, 1, n)).to(dev)
+    ref_x0 = torch.from_numpy(x0).to(dev)
+    ref_x = torch.zeros_like(ref_b)
+    ref = S.cg_solve(ref_b, ref_x, 1e-10, 2000, x0=ref_x0)
+    assert ref[0] == "converged"
+    bufs = [torch.zeros(n + 1, dtype=torch.float64, device=dev) for _ in range(3)]
+    b1, x01, x1 = (t[1:] for t in bufs)
+    b1.copy_(ref_b)
+    x01.copy_(ref_x0)
+    assert all(t.data_ptr() % 16 == 8 for t in (b1, x01, x1))
+    got = S.cg_solve(b1, x1, 1e-10, 2000, x0=x01)
+    torch.cuda.synchronize()
+    log(f"offset vectors single_block={single_block}: {got[0]} K={got[1]}")
+    assert got[:2] == ref[:2] and np.array_equal(got[2], ref[2]) and torch.equal(x1, ref_x)
+    assert bufs[2][0].item() == 0.0  # nothing written before the view
+    S.close()
+
+
+@pytest.mark.parametrize("single_block", [-1, 1])
 def test_cg_breakdown_on_indefinite_matrix(single_block, dev):
     n = 2
     L = mpcg.cg_tilecsc_from_csr(n, np.array([0, 1, 2]), np.array([0, 1], np.int32),
