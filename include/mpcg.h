@@ -218,7 +218,7 @@ typedef struct {
  *   opt           : NULL for defaults.
  *   stream        : stream for the set-up copies and kernels.
  * Errors: CG_EINVAL (map code > 2, bad layout, n >= 2^28 or T or nnz >= 2^31,
- * Jacobi with a zero or missing diagonal entry, unknown p1 bits, padding with
+ * no nonzeros, Jacobi with a zero or missing diagonal entry, unknown p1 bits, padding with
  * R = 256, col_slices outside [0, 64], single_block outside [-1, 1]),
  * CG_ENOMEM, CG_EDEVICE.
  */

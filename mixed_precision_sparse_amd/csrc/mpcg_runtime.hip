@@ -712,6 +712,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         return fail(CG_EINVAL, "cg_create: n, T and nnz must be below 2^31");
     if (n >= (int64_t(1) << 28))
         return fail(CG_EINVAL, "cg_create: n must be below 2^28 (x is addressed with 32-bit byte offsets)");
+    if (nnz == 0) return fail(CG_EINVAL, "cg_create: the matrix has no nonzeros (it cannot be SPD)");
     if (precision_map) {
         for (int64_t t = 0; t < T; ++t)
             if (precision_map[t] > 2)

@@ -91,6 +91,12 @@ def test_host_layout_empty_matrix():
                                  np.zeros(0), 4, 4)
     assert L.T == 0 and L.nnz == 0
     assert L.tile_row_ptr.tolist() == [0, 0, 0, 0]
+    # The layout is valid, but no handle is made for it: a matrix without
+    # nonzeros is not SPD. The check precedes every device call.
+    lib = _lib.load()
+    out = ct.c_void_p()
+    assert lib.cg_create(L._h, None, None, None, ct.byref(out)) == mpcg.CG_EINVAL
+    assert b"no nonzeros" in lib.cg_last_error() and not out.value
 
 
 @pytest.mark.parametrize("case", ["unsorted", "duplicate", "out_of_range", "nan", "bad_R", "bad_C",
