@@ -48,10 +48,11 @@ def _random_spd(n, density, seed, R, C):
 
 
 # Beyond the workloads: C12 (segments of 12 entries, 16-byte loads of 6 pairs),
-# C128 (the largest column blocks, a short last one) and C8odd (n odd: the
-# last column block is short and ends on a single entry).
+# C128 (the largest column blocks, a short last one), C8odd (n odd: the last
+# column block is short and ends on a single entry) and C7 (odd C and R: the
+# segments are read entry by entry).
 CASES = [("cfg2", None), ("cfg3", None), ("cfg5", None), ("C12", (300, 0.02, 8, 12)), ("C128", (700, 0.01, 64, 128)),
-         ("C8odd", (301, 0.03, 8, 8))]
+         ("C8odd", (301, 0.03, 8, 8)), ("C7", (257, 0.03, 9, 7))]
 
 
 def _case(name, spec):
