@@ -3,7 +3,9 @@
 // non-empty R x C tiles of each row block, how evenly they spread (coefficient
 // of variation), and the tuned R: the admissible candidate (R <= max_R, at
 // least min_row_blocks row blocks) with the smallest coefficient of variation,
-// ties to the smaller R. Host code only.
+// ties to the smaller R. Candidates are compared exactly (integer arithmetic
+// on the squared coefficient), not through the rounded values. Host code
+// only.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -19,10 +21,33 @@ namespace {
 
 constexpr int kCandidates = 10;  // 32 << 0 .. 32 << 9
 
+typedef unsigned __int128 u128;
+
 struct Balance {
     int64_t nrb = 0, tiles = 0;
     double cv = 0.0, max_ratio = 0.0;
+    u128 var = 0, s1sq = 1;  // cv^2 = var / s1sq exactly (var = m S2 - S1^2, s1sq = S1^2; 0 / 1 when empty)
 };
+
+// p / q < r / s for p, r >= 0 and q, s > 0, exactly: compare the integer
+// parts; when they agree, compare the reciprocals of the remainders (a
+// continued-fraction step), which never overflows.
+bool frac_less(u128 p, u128 q, u128 r, u128 s) {
+    for (;;) {
+        const u128 a = p / q, b = r / s;
+        if (a != b) return a < b;
+        p -= a * q;
+        r -= b * s;
+        if (p == 0) return r != 0;
+        if (r == 0) return false;
+        // p / q < r / s  <=>  s / r < q / p
+        const u128 np = s, nq = r, nr = q, ns = p;
+        p = np;
+        q = nq;
+        r = nr;
+        s = ns;
+    }
+}
 
 // Tile counts of every row block of height R (one stamp array of column
 // blocks per worker), then the balance measures from exact integer sums: with
@@ -59,6 +84,8 @@ Balance row_block_balance(int64_t n, const int64_t* rowptr, const int32_t* colin
     b.tiles = s1;
     if (s1 > 0) {
         const unsigned __int128 var = (unsigned __int128)nrb * s2 - (unsigned __int128)s1 * (unsigned __int128)s1;
+        b.var = var;
+        b.s1sq = (u128)s1 * (u128)s1;
         b.cv = std::sqrt((double)var) / (double)s1;
         b.max_ratio = (double)((unsigned __int128)nrb * (unsigned __int128)mx) / (double)s1;
     }
@@ -86,14 +113,14 @@ extern "C" int cg_tune_row_height(int64_t n, const int64_t* rowptr, const int32_
         if (colind[k] < 0 || colind[k] >= n)
             return fail(CG_EINVAL, "cg_tune_row_height: colind[" + std::to_string(k) + "] is outside [0, n)");
     int32_t best = -1;
-    double best_cv = 0.0;
+    Balance best_b;
     for (int i = 0; i < kCandidates; ++i) {
         const int32_t R = 32 << i;
         const Balance b = row_block_balance(n, rowptr, colind, R, C);
         const bool ok = R <= max_R && b.nrb >= min_row_blocks;
-        if (ok && (best < 0 || b.cv < best_cv)) {
+        if (ok && (best < 0 || frac_less(b.var, b.s1sq, best_b.var, best_b.s1sq))) {
             best = R;
-            best_cv = b.cv;
+            best_b = b;
         }
         if (i < cap) {
             if (cand_R) cand_R[i] = R;

@@ -7,8 +7,10 @@ the search from the trivial answer (a handful of huge row blocks is
 perfectly even and leaves the device idle). The reading taken here:
 
 * evenness is the coefficient of variation (population standard deviation
-  over mean) of the non-empty tile counts of all ceil(n / R) row blocks,
-  computed from exact integer sums (see :func:`balance`);
+  over mean) of the non-empty tile counts of all ceil(n / R) row blocks;
+  candidates are compared by its exact square (rational arithmetic, see
+  :func:`cv_squared`), so that two candidates a floating-point evaluation
+  cannot tell apart are still ordered correctly;
 * a candidate must leave at least ``min_row_blocks`` row blocks, and it must
   not exceed ``max_R`` (the largest height the kernel supports);
 * the tuned R is the admissible candidate with the smallest coefficient of
@@ -21,6 +23,7 @@ Test infrastructure only: see the package docstring.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -36,34 +39,62 @@ def row_block_tile_counts(n: int, indptr, indices, R: int, C: int) -> np.ndarray
     return np.bincount(keys // ncb, minlength=-(-n // R)).astype(np.int64)
 
 
+def cv_squared(counts) -> Fraction:
+    """Exact square of the coefficient of variation of ``counts`` (0 when all are zero).
+
+    Written from the definition: mean = sum(c) / m, population variance =
+    sum((c - mean)^2) / m, and cv^2 = variance / mean^2, all in rational
+    arithmetic. Equal counts are grouped first (a library primitive), which
+    changes nothing in the exact sum.
+    """
+    values, mult = np.unique(np.asarray(counts, dtype=np.int64).ravel(), return_counts=True)
+    m = int(mult.sum())
+    total = sum(int(v) * int(k) for v, k in zip(values, mult))
+    if m == 0 or total == 0:
+        return Fraction(0)
+    mean = Fraction(total, m)
+    var = sum(int(k) * (int(v) - mean) ** 2 for v, k in zip(values, mult)) / m
+    return var / (mean * mean)
+
+
 def balance(counts: np.ndarray):
     """(coefficient of variation, max / mean) of the row blocks' tile counts (0, 0 when all are empty).
 
-    With m row blocks, S1 = sum c and S2 = sum c^2 (exact integers), the
-    population standard deviation over the mean is sqrt(m S2 - S1^2) / S1 and
-    max / mean is m max(c) / S1. Each is evaluated from the exact integers with
-    one rounding to FP64 per operand and IEEE sqrt and division, so the value,
-    and with it the choice between near-equal candidates, does not depend on a
-    summation order.
+    Both are the exact values rounded to FP64 (the square root of the exact
+    cv^2 rounded once, then one IEEE square root); the selection compares the
+    exact cv^2 itself.
     """
-    c = [int(v) for v in np.asarray(counts).ravel()]
-    m, s1 = len(c), sum(c)
-    if s1 == 0:
+    c = np.asarray(counts, dtype=np.int64).ravel()
+    total = int(c.sum())
+    if total == 0:
         return 0.0, 0.0
-    s2 = sum(v * v for v in c)
-    return math.sqrt(float(m * s2 - s1 * s1)) / float(s1), float(m * max(c)) / float(s1)
+    return math.sqrt(float(cv_squared(c))), float(Fraction(len(c) * int(c.max()), total))
+
+
+def select_height(candidates, max_R: int = 256, min_row_blocks: int = 1024) -> int:
+    """The tuned R from (R, counts) pairs in candidate order (Sec. 3.3.3 reading above).
+
+    Admissible: R <= max_R and at least ``min_row_blocks`` row blocks. The
+    smallest exact cv^2 wins; on equal cv^2 the earlier (smaller) R stays;
+    with no admissible candidate, the first candidate's R.
+    """
+    best = None
+    for R, counts in candidates:
+        if R <= max_R and len(counts) >= min_row_blocks:
+            v = cv_squared(counts)
+            if best is None or v < best[1]:
+                best = (R, v)
+    return best[0] if best is not None else candidates[0][0]
 
 
 def tune_row_height(n: int, indptr, indices, C: int, max_R: int = 256, min_row_blocks: int = 1024,
                     candidates=CANDIDATES):
     """Tuned R and one table row per candidate: (R, row blocks, tiles, cv, max/mean, admissible)."""
-    table = []
-    best = None
+    table, pairs = [], []
     for R in candidates:
         counts = row_block_tile_counts(n, indptr, indices, R, C)
         cv, mx = balance(counts)
         ok = R <= max_R and counts.size >= min_row_blocks
         table.append((R, int(counts.size), int(counts.sum()), cv, mx, ok))
-        if ok and (best is None or cv < best[1]):
-            best = (R, cv)
-    return (best[0] if best is not None else candidates[0]), table
+        pairs.append((R, counts))
+    return select_height(pairs, max_R, min_row_blocks), table

@@ -160,7 +160,10 @@ def test_select_reuse_interval_rejects_bad_codes():
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_tune_row_height_matches_oracle(cfg):
-    """The library's row-block height search (host code) against the oracle, bit for bit."""
+    """The library's row-block height search (host code) against the oracle: the chosen R and
+    every count exactly (both sides compare candidates by the exact squared coefficient of
+    variation); the reported coefficient and max/mean are two roundings of the same exact
+    values, so they agree within a few units in the last place."""
     from gen import make_workload
     from oracle import tuning
 
@@ -170,8 +173,11 @@ def test_tune_row_height_matches_oracle(cfg):
         R_ref, table_ref = tuning.tune_row_height(A.n, A.indptr, A.indices, C, max_R, min_rb)
         R, rows = mpcg.cg_tune_row_height(A.n, A.indptr, A.indices, C, max_R, min_rb)
         assert R == R_ref
-        got = [(r["R"], r["row_blocks"], r["tiles"], r["cv"], r["max_ratio"], r["admissible"]) for r in rows]
-        assert got == table_ref
+        got = [(r["R"], r["row_blocks"], r["tiles"], r["admissible"]) for r in rows]
+        assert got == [(t[0], t[1], t[2], t[5]) for t in table_ref]
+        for r, t in zip(rows, table_ref):
+            assert r["cv"] == pytest.approx(t[3], rel=4 * 2.0 ** -52, abs=0.0)
+            assert r["max_ratio"] == pytest.approx(t[4], rel=4 * 2.0 ** -52, abs=0.0)
 
 
 def test_tune_row_height_skewed_and_errors():
@@ -186,8 +192,11 @@ def test_tune_row_height_skewed_and_errors():
         R_ref, table_ref = tuning.tune_row_height(n, indptr, indices, C, 16384, 2)
         R, rows = mpcg.cg_tune_row_height(n, indptr, indices, C, 16384, 2)
         assert R == R_ref
-        assert [(r["R"], r["row_blocks"], r["tiles"], r["cv"], r["max_ratio"], r["admissible"])
-                for r in rows] == table_ref
+        assert [(r["R"], r["row_blocks"], r["tiles"], r["admissible"]) for r in rows] == \
+            [(t[0], t[1], t[2], t[5]) for t in table_ref]
+        for r, t in zip(rows, table_ref):
+            assert r["cv"] == pytest.approx(t[3], rel=4 * 2.0 ** -52, abs=0.0)
+            assert r["max_ratio"] == pytest.approx(t[4], rel=4 * 2.0 ** -52, abs=0.0)
     with pytest.raises(mpcg.CGError):
         mpcg.cg_tune_row_height(n, indptr, indices, 0)
     with pytest.raises(mpcg.CGError):

@@ -126,3 +126,53 @@ def test_selection_minimises_cv_not_max_ratio():
         assert R == best[0]
         disagree += min(adm, key=lambda row: (row[4], row[0]))[0] != R
     assert disagree > 0
+
+
+def test_cv_squared_exact_against_the_definition():
+    """cv^2 in rational arithmetic equals the textbook population variance over the squared
+    mean written element by element, and matches FP64 NumPy where NumPy is accurate."""
+    from fractions import Fraction
+
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        c = rng.integers(0, 50, rng.integers(1, 40))
+        if c.sum() == 0:
+            continue
+        m = len(c)
+        mean = Fraction(int(c.sum()), m)
+        var = sum((Fraction(int(v)) - mean) ** 2 for v in c) / m
+        assert tuning.cv_squared(c) == var / mean ** 2
+        assert math.sqrt(float(tuning.cv_squared(c))) == pytest.approx(float(np.std(c) / np.mean(c)), rel=1e-12)
+    assert tuning.cv_squared(np.zeros(4, dtype=np.int64)) == 0
+    assert tuning.cv_squared(np.array([5, 5, 5])) == 0
+
+
+def test_selection_orders_a_near_tie_exactly():
+    """A hand-built near tie: counts (p, p+1) against (q, q, q, q, q+1) with 5q = 4p + 2.
+    Exactly cv_a^2 = 1/(2p+1)^2 and cv_b^2 = 4/(4p+3)^2, so b is smaller, by a relative
+    1/(4p) ~ 2.5e-18: below FP64 resolution, where the usual formulas tie (and so would
+    pick the smaller height, a). The selection must still take b."""
+    from fractions import Fraction
+
+    p = 10 ** 17 + 2
+    q = (4 * p + 2) // 5
+    assert 5 * q == 4 * p + 2
+    a = np.array([p, p + 1], dtype=np.int64)
+    b = np.array([q, q, q, q, q + 1], dtype=np.int64)
+    assert tuning.cv_squared(a) == Fraction(1, (2 * p + 1) ** 2)
+    assert tuning.cv_squared(b) == Fraction(4, (4 * p + 3) ** 2)
+    # FP64 cannot tell them apart: the rounded measures and NumPy's std/mean agree bit for bit
+    def fp64_cv(c):  # sqrt(m S2 - S1^2) / S1 with the exact integers rounded once each
+        c = [int(v) for v in c]
+        m, s1, s2 = len(c), sum(c), sum(v * v for v in c)
+        return math.sqrt(float(m * s2 - s1 * s1)) / float(s1)
+
+    assert fp64_cv(a) == fp64_cv(b)
+    assert float(np.std(a.astype(np.float64)) / np.mean(a.astype(np.float64))) == \
+        float(np.std(b.astype(np.float64)) / np.mean(b.astype(np.float64)))
+    assert tuning.balance(a)[0] == tuning.balance(b)[0]
+    # the exact comparison orders them, whichever comes first
+    assert tuning.select_height([(32, a), (64, b)], max_R=64, min_row_blocks=1) == 64
+    assert tuning.select_height([(32, b), (64, a)], max_R=64, min_row_blocks=1) == 32
+    # equal exact values keep the smaller height
+    assert tuning.select_height([(32, a), (64, a.copy())], max_R=64, min_row_blocks=1) == 32
