@@ -223,6 +223,11 @@ def solve(L: TileCSC, indptr, indices, data, b, schedule, tol, maxit, x0=None,
             status = "breakdown"
             break
         alpha = rz / pq
+        if not math.isfinite(alpha):
+            # p.q > 0 but so small that r.z / p.q overflows: a breakdown found
+            # before the update, so the iterate and K stay as they are.
+            status = "breakdown"
+            break
         if trace is not None:
             trace(k, x, r, p, q, alpha)
         x += alpha * p
@@ -235,7 +240,7 @@ def solve(L: TileCSC, indptr, indices, data, b, schedule, tol, maxit, x0=None,
             z = r
             rz_new = rr_new
         beta = rz_new / rz
-        if not (math.isfinite(alpha) and math.isfinite(beta)):
+        if not math.isfinite(beta):
             status = "breakdown"
             k += 1
             hist.append(math.sqrt(rr_new) / norm0)

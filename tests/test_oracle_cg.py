@@ -137,6 +137,34 @@ def test_breakdown_on_indefinite_matrix():
     assert res.status == "breakdown" and res.K == 0
 
 
+def test_overflowing_alpha_stops_before_the_update():
+    """p.q > 0 but subnormal: alpha = r.r / p.q overflows. The solve stops with breakdown
+    before touching the iterate (K = 0, x = x0, one history entry), which is what the
+    library does and what its header promises (x holds the last iterate)."""
+    M = _csr(np.diag([1e-310, 1.0, 1.0, 1.0]))
+    b = np.array([1.0, 0.0, 0.0, 0.0])
+    q = M @ b
+    assert 0.0 < float(b @ q) < 2.3e-308 and math.isinf(1.0 / float(b @ q))  # the premise
+    res = _solve(M, b, 1e-10, 10)
+    assert res.status == "breakdown" and res.K == 0 and res.hist == [1.0]
+    assert np.array_equal(res.x, np.zeros(4))
+    x0 = np.array([0.0, 0.5, -0.25, 2.0])
+    r2 = _solve(M, b + M @ x0, 1e-10, 10, x0=x0)
+    assert r2.status == "breakdown" and r2.K == 0 and np.array_equal(r2.x, x0)
+
+
+def test_non_finite_beta_counts_the_update():
+    """A finite alpha with an overflowing r_new.r_new gives a non-finite beta: the update of
+    that iteration has been applied, so it is counted (K = 1) before the solve stops."""
+    # alpha = (1e200 + 1) / (1e-50 + 1) = 1e200; x = alpha b = (1e300, 1e200) stays finite;
+    # r_new = (1e100 (1 - 1e-50), 1 - 1e200), whose square overflows, so beta = inf
+    M = _csr(np.diag([1e-250, 1.0]))
+    b = np.array([1e100, 1.0])
+    res = _solve(M, b, 1e-30, 10)
+    assert res.status == "breakdown" and res.K == 1 and len(res.hist) == 2
+    assert np.all(np.isfinite(res.x)) and res.x[0] == pytest.approx(1e300, rel=1e-12)
+
+
 def test_degenerate_inputs():
     M = _csr(np.diag([2.0, 3.0, 4.0]))
     z = _solve(M, np.zeros(3), 1e-10, 10)
