@@ -167,8 +167,22 @@ typedef struct {
     int32_t col_slices;  /* column slices S in [0, 64]; 0 or 1 = none (below) */
     int32_t single_block; /* cg_solve on one workgroup: 0 = automatic for small
                              systems, 1 = whenever supported, -1 = never (below) */
-    int32_t reserved[2];
+    int32_t stage_x;     /* 1: stage each SpMV batch's vector segments in LDS (below); 0 = off */
+    int32_t reserved[1];
 } cg_options;
+
+/*
+ * Vector segments staged in LDS (cg_options.stage_x = 1): before the SpMV
+ * sweeps a batch of up to 64 tiles, it copies the x segments of the batch's
+ * distinct column blocks (C entries each) into LDS, and the sweep reads every
+ * x_j from there instead of gathering it from memory (Sec. 3.3.2 "Intra-Tile
+ * CSC Execution" amortises the x_j loads of a column in the same way). Only
+ * batches whose distinct column blocks hold no more entries than the batch has
+ * nonzeros and fit 8 KiB are staged; the others gather as usual. Requires C a
+ * power of two and none of the CG_P1_* options (otherwise ignored). Results are
+ * the same products in the same order. On MI355X the gathers mostly hit the
+ * L2 and the stage costs occupancy, so it is off by default.
+ */
 
 /*
  * Column slices (cg_options.col_slices = S > 1): the SpMV takes the tiles in S

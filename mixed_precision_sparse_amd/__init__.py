@@ -132,7 +132,7 @@ class Solver:
     """Device-resident solver handle (owns a ``cg_handle``)."""
 
     def __init__(self, A: TileCSC, precision_map=None, jacobi=False, window=0, use_graph=-1,
-                 p1=0, col_slices=0, single_block=0, stream=None):
+                 p1=0, col_slices=0, single_block=0, stage_x=0, stream=None):
         lib = _lib.load()
         opt = _lib.cg_options()
         opt.jacobi = 1 if jacobi else 0
@@ -141,6 +141,7 @@ class Solver:
         opt.p1 = int(p1)
         opt.col_slices = int(col_slices)
         opt.single_block = int(single_block)
+        opt.stage_x = int(stage_x)
         pm = None
         if precision_map is not None:
             pm = np.ascontiguousarray(precision_map, dtype=np.uint8)

@@ -32,7 +32,7 @@ class cg_tilecsc_view(ct.Structure):
 
 class cg_options(ct.Structure):
     _fields_ = [("jacobi", i32), ("window", i32), ("use_graph", i32), ("p1", i32), ("col_slices", i32),
-                ("single_block", i32), ("reserved", i32 * 2)]
+                ("single_block", i32), ("stage_x", i32), ("reserved", i32 * 1)]
 
 
 # name -> (restype, argtypes)

@@ -237,15 +237,42 @@ __host__ __device__ inline int sweep_windows(int nw) {
     while (t < r) t <<= 1;
     return full + t;
 }
+// Batches whose vector segments are staged in LDS run pipelined sweeps of
+// kStagedU windows each: their records are padded to a multiple of kStagedU
+// and fit one chunk of 64 records.
+constexpr int kStagedU = 4;
+// Largest LDS vector stage of one wavefront (bytes; 0 turns staging off), and
+// the largest staged entries per nonzero of a batch, in percent.
+#ifndef MPCG_STAGE_MAX_BYTES
+#define MPCG_STAGE_MAX_BYTES 8192
+#endif
+#ifndef MPCG_STAGE_RATIO_PCT
+#define MPCG_STAGE_RATIO_PCT 100
+#endif
+constexpr int kStageMaxBytes = MPCG_STAGE_MAX_BYTES;
+// Sweeps of a staged batch in flight at once (1 or 2).
+#ifndef MPCG_STAGED_PIPE
+#define MPCG_STAGED_PIPE 2
+#endif
+constexpr int kStagedPipe = MPCG_STAGED_PIPE;
+constexpr int kStageRatioPct = MPCG_STAGE_RATIO_PCT;
 // Window records of a batch of len nonzeros.
-__host__ __device__ inline int batch_records(int len) { return sweep_windows((len + kWave - 1) / kWave); }
+__host__ __device__ inline int batch_records(int len, bool staged = false) {
+    const int nw = (len + kWave - 1) / kWave;
+    return staged ? (nw + kStagedU - 1) / kStagedU * kStagedU : sweep_windows(nw);
+}
 
-// Batch table entry (8 int32, one scalar load): the wave's work is a run of
+// Batch table entry (int32 fields, scalar loads): the wave's work is a run of
 // consecutive batches covering whole row groups (segments, with column
 // slices). A segment without tiles has one entry with no tiles, so its rows
-// are still written.
-enum BatchField { kBtTile = 0, kBtTiles, kBtFirstNnz, kBtLen, kBtRecords, kBtGroup, kBtFlags, kBtSegment, kBtFields };
-constexpr int kBatchFirstOfGroup = 1, kBatchLastOfGroup = 2;
+// are still written. A staged batch (flag kBatchStaged) lists the distinct
+// column blocks its tiles touch in xcb[kBtXList .. kBtXList + kBtXCount);
+// its tiles' vector offsets then point into the LDS copy of those segments.
+enum BatchField {
+    kBtTile = 0, kBtTiles, kBtFirstNnz, kBtLen, kBtRecords, kBtGroup, kBtFlags, kBtSegment, kBtPacked, kBtXList,
+    kBtXCount, kBtFields
+};
+constexpr int kBatchFirstOfGroup = 1, kBatchLastOfGroup = 2, kBatchStaged = 4;
 // Bits from kBatchSliceShift up: the column slice of the batch's segment,
 // whose rows go to partial product number slice (stride SpmvArgs.ystride).
 constexpr int kBatchSliceShift = 8;
@@ -255,6 +282,12 @@ constexpr int kBatchSliceShift = 8;
 // BF16 values (2*len), all in storage order, and 16 spare bytes. Plane code p
 // starts at byte p*(10-2p)*len of the segment.
 __host__ __device__ inline int64_t segment_bytes(int64_t len) { return (14 * len + 16 + 15) / 16 * 16; }
+// The active map's values of a batch (see repack_kernel) take at most 8 bytes
+// per value: each tile starts on 8 bytes and its values are 8, 4 or 2 bytes
+// wide. They sit in a buffer of their own, batch after batch (kBtPacked, in
+// 16-byte units), with 16 spare bytes each for the 8-byte loads of the last
+// values.
+__host__ __device__ inline int64_t packed_bytes(int64_t len) { return (8 * len + 16 + 15) / 16 * 16; }
 
 // Builds every batch's segment from the FP64 values, rounding to nearest even
 // (one wavefront per batch). The FP32 and BF16 planes are rounded from vlow:
@@ -281,15 +314,15 @@ __global__ __launch_bounds__(kBlock) void build_segments_kernel(const int32_t* _
     }
 }
 
-// Packed values of a per-tile map: inside every batch's packed segment, tile
-// after tile in storage order, each tile's values at its precision, every
+// Packed values of a per-tile map: inside every batch's packed part (its own
+// buffer, packed_bytes apart), tile after tile in storage order, each tile's values at its precision, every
 // tile starting on an 8-byte boundary; toff[t] = start of tile t's values
 // minus (its position in the batch << log2 of its value width). One
 // wavefront per batch: lane l sizes tile l and a wave prefix sum places it,
 // then the lanes copy the batch's values 64 at a time, each finding its tile
 // from the window records. Rerun at every map change; in a solve (solve = 1)
 // only at the start of a tile-rule window, and then only for the batches the
-// tile rule marked dirty (each batch's segment is self-contained). Every
+// tile rule marked dirty (each batch's part is self-contained). Every
 // batch it rebuilds is marked clean.
 struct RepackArgs {
     const int32_t* btab;
@@ -343,7 +376,7 @@ __global__ __launch_bounds__(kBlock) void repack_kernel(RepackArgs a) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const char* src = a.planes + (int64_t)e[kBtSegment] * 16;
-        char* dst = a.packed + (int64_t)e[kBtSegment] * 16;
+        char* dst = a.packed + (int64_t)e[kBtPacked] * 16;
         for (int o = 0, v = e[kBtRecords]; o < len; o += kWave, ++v) {
             const uint64_t m = a.win_mask[v];
             const int j = a.win_tile[v] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -389,10 +422,14 @@ struct SpmvArgs {
     const State* st;
     double* partials;      // CG mode: one p.q partial per block
     const int16_t* colexp;  // P1 kernels: per column e_j of the scale 2^e_j (NULL: no scale)
-    int32_t n, rows_per_group, ngroups, groups_per_wave, nwin;
+    const int32_t* xcb;     // staged batches: their distinct column blocks (see kBtXList)
+    int32_t n, rows_per_group, ngroups, nwin;
     int32_t ystride;       // column slices: distance between two slices' partial products
     int32_t p1_round;      // P1 kernels: round the vector entry to the tile's precision
     int32_t sentinel_row;  // P1 kernels: row offset of padding entries (R), or -1
+    int32_t C;             // tile width
+    int32_t stage_shift;   // staged batches: log2 of the 16-byte chunks per column block (C / 2)
+    int32_t stage_doubles; // LDS doubles of one wavefront's vector stage (0: no staged batch)
 };
 
 template <typename MetaT>
@@ -408,12 +445,39 @@ __device__ inline void decode_meta<uint16_t>(uint32_t m, int& r, int& c) {
     c = (int)(m & 255u);
 }
 
+// A buffer resource over a batch's part of a stream. Its fields come from
+// wave-uniform values; reading them through readfirstlane says so, so that
+// the loads through it stay single instructions (a resource the compiler
+// cannot prove uniform is used in a loop over its distinct values).
+__device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    char* q = reinterpret_cast<char*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+    return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, __builtin_amdgcn_readfirstlane(bytes), (int)kBufferConfig);
+}
+
 __device__ inline __amdgpu_buffer_rsrc_t batch_rsrc(const void* base, int64_t first, int width, int count) {
-    const char* p = static_cast<const char*>(base) + first * width;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, count * width, (int)kBufferConfig);
+    return uniform_rsrc(static_cast<const char*>(base) + first * width, count * width);
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Cache policy of the streamed value and index loads. The non-temporal hint
+// (2) suits bytes read once per product, but it measured slower on every
+// workload on MI355X, so the default policy (0) is used.
+#ifndef MPCG_SPMV_NT
+#define MPCG_SPMV_NT 0
+#endif
+constexpr int kStreamAux = MPCG_SPMV_NT ? 2 : 0;
+
+// Packed (row, column) of the nonzero at batch position q (buffer loads: past
+// the batch they return zero).
+template <typename MetaT>
+__device__ __forceinline__ uint32_t load_meta(__amdgpu_buffer_rsrc_t r, int q) {
+    return sizeof(MetaT) == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, q, 0, kStreamAux)
+                              : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, 2 * q, 0, kStreamAux);
+}
 
 // Wave-uniform reads of data no kernel here writes while the SpMV runs: read
 // through the constant address space so they become scalar loads.
@@ -424,7 +488,7 @@ __device__ inline T uniform_load(const T* p, int i) {
 
 // One batch's header in scalar registers.
 struct BatchHdr {
-    int tile, tiles, first, len, records, group, flags, segment;
+    int tile, tiles, first, len, records, group, flags, segment, packed, xlist, xcount;
 };
 __device__ __forceinline__ BatchHdr load_hdr(const int32_t* btab, int b) {
     const int32_t* e = btab + (size_t)b * kBtFields;
@@ -437,6 +501,9 @@ __device__ __forceinline__ BatchHdr load_hdr(const int32_t* btab, int b) {
     h.group = uniform_load(e, kBtGroup);
     h.flags = uniform_load(e, kBtFlags);
     h.segment = uniform_load(e, kBtSegment);
+    h.packed = uniform_load(e, kBtPacked);
+    h.xlist = uniform_load(e, kBtXList);
+    h.xcount = uniform_load(e, kBtXCount);
     return h;
 }
 
@@ -447,6 +514,7 @@ struct BatchRegs {
     int prec, toff;
     uint32_t mlo, mhi;
     int rec;
+    int xcb;  // staged batch: column block of stage slot `lane` (lane < kBtXCount)
 };
 
 struct SweepCtx {
@@ -459,7 +527,8 @@ struct SweepCtx {
     const int32_t* toff;
     const int32_t* tcol;
     const uint8_t* cbcode;
-    const double* xs;  // XL sweeps: the vector in LDS (entries 0 .. xmax)
+    const int32_t* xcb;
+    const double* xs;  // XL sweeps: the vector in LDS (entries 0 .. xmax); staged batches: the stage
     int xmax;
     int len, lane;
     int spare;  // byte offset of this lane's spare accumulator
@@ -499,6 +568,8 @@ __device__ __forceinline__ void load_batch_regs(const SweepCtx& c, const BatchHd
             r.prec = c.map[t];
             r.toff = c.toff[t];
         }
+        r.xcb = 0;
+        if (h.flags & kBatchStaged) r.xcb = c.xcb[h.xlist + min(c.lane, h.xcount - 1)];
     }
     const int wi = h.records + chunk + c.lane;
     const u32x2 m = __builtin_amdgcn_raw_buffer_load_b64(c.rmask, 8 * wi, 0, 0);
@@ -536,9 +607,7 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
     }
     uint32_t mt[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-        mt[u] = sizeof(MetaT) == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(c.rmt, q[u], 0, 0)
-                                   : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(c.rmt, 2 * q[u], 0, 0);
+    for (int u = 0; u < U; ++u) mt[u] = load_meta<MetaT>(c.rmt, q[u]);
     // Stored values, issued before the vector gathers (which wait for the
     // packed indices).
     u32x2 raw[U];
@@ -547,7 +616,7 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
     for (int u = 0; u < U; ++u) {
         const int off = d[u].z + (q[u] << d[u].w);
         hs[u] = (off & 2) << 3;
-        raw[u] = __builtin_amdgcn_raw_buffer_load_b64(c.rv, off & ~3, 0, 0);
+        raw[u] = __builtin_amdgcn_raw_buffer_load_b64(c.rv, off & ~3, 0, kStreamAux);
     }
     if (next) load_batch_regs<CB>(c, Hn, 0, true, Rn);
     double xv[U];
@@ -600,6 +669,148 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
+// All window records of one batch on the gather path (vector entries loaded
+// from x, or from the LDS copy with XL): whole sweeps of U windows, leftover
+// whole kUnroll sweeps, then one sweep of the power of two that covers the
+// rest. The first sweep also starts the loads of the next batch (header Hn)
+// into Rn when `more`.
+template <typename MetaT, bool CB, bool P1, int U, bool XL>
+__device__ __forceinline__ void sweep_batch_gather(const SweepCtx& c, const BatchHdr& H, BatchRegs& R, bool more,
+                                                   const BatchHdr& Hn, BatchRegs& Rn) {
+    const int E = batch_records(H.len);
+    int left = E, wi = 0, o0 = 0;
+    for (; left >= U; left -= U, wi += U, o0 += U * kWave) {
+        if (wi > 0 && (wi & (kWave - 1)) == 0) load_batch_regs<CB>(c, H, wi, false, R);  // next 64 records
+        spmv_sweep<MetaT, U, CB, P1, XL>(c, R, wi, o0, more && wi == 0, Hn, Rn);
+    }
+    if (U > kUnroll) {
+        for (; left >= kUnroll; left -= kUnroll, wi += kUnroll, o0 += kUnroll * kWave) {
+            if (wi > 0 && (wi & (kWave - 1)) == 0) load_batch_regs<CB>(c, H, wi, false, R);
+            spmv_sweep<MetaT, kUnroll, CB, P1, XL>(c, R, wi, o0, more && wi == 0, Hn, Rn);
+        }
+    }
+    // The rest is 0 or one power of two below kUnroll (never crossing a record chunk).
+    if (wi > 0 && (wi & (kWave - 1)) == 0 && left > 0) load_batch_regs<CB>(c, H, wi, false, R);
+    const bool first = more && wi == 0;
+    if (kUnroll > 8 && left == 8)
+        spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1), CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
+    if (kUnroll > 4 && left == 4)
+        spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1), CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
+    if (kUnroll > 2 && left == 2)
+        spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1), CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
+    if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1, CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
+    if (more && E == 0) load_batch_regs<CB>(c, Hn, 0, true, Rn);  // a batch without windows
+}
+
+// Staged batches. At the batch start the x segments of the batch's distinct
+// column blocks (C entries each, listed in xcb) are copied into the wave's
+// LDS stage by LDS-direct buffer loads (16 bytes per lane, no registers), in
+// slot order: the tile entries of such a batch hold their block's slot
+// offset in the stage instead of an offset in x. The sweeps then read every
+// vector entry from LDS, so a sweep waits on one round trip to memory (the
+// packed indices and the values, issued together) instead of two.
+//
+// The sweeps are pipelined: the loads of sweep s + 1 are issued before sweep
+// s is accumulated, so every wave keeps two sweeps of stream loads in flight.
+struct StagedSweep {
+    uint32_t mt[kStagedU];
+    u32x2 raw[kStagedU];
+    uint32_t cw[kStagedU];  // stage offset | accumulator offset << 16 | width shift << 28 | BF16 high half << 30
+};
+
+template <typename MetaT>
+__device__ __forceinline__ void staged_issue(const SweepCtx& c, const BatchRegs& R, int s, StagedSweep& S) {
+#pragma unroll
+    for (int u = 0; u < kStagedU; ++u) {
+        const int wi = s * kStagedU + u;  // < 64: a staged batch's records fit one chunk
+        const uint32_t mlo = __builtin_amdgcn_readlane(R.mlo, wi);
+        const uint32_t mhi = __builtin_amdgcn_readlane(R.mhi, wi);
+        const int j = __builtin_amdgcn_readlane(R.rec, wi) +
+                      (int)__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+        const int4 d = c.desc[j];
+        const int q = wi * kWave + c.lane;
+        S.mt[u] = load_meta<MetaT>(c.rmt, q);
+        const int off = d.z + (q << d.w);
+        S.raw[u] = __builtin_amdgcn_raw_buffer_load_b64(c.rv, off & ~3, 0, kStreamAux);
+        S.cw[u] = (uint32_t)d.x | ((uint32_t)d.y << 16) | ((uint32_t)d.w << 28) | ((uint32_t)(off & 2) << 29);
+    }
+}
+
+template <typename MetaT>
+__device__ __forceinline__ void staged_consume(const SweepCtx& c, const StagedSweep& S, int s) {
+    double xv[kStagedU];
+    int racc[kStagedU];
+#pragma unroll
+    for (int u = 0; u < kStagedU; ++u) {
+        int r, col;
+        decode_meta<MetaT>(S.mt[u], r, col);
+        const int q = (s * kStagedU + u) * kWave + c.lane;
+        racc[u] = q < c.len ? (int)((S.cw[u] >> 16) & 0xFFFu) + 8 * r : c.spare;
+        xv[u] = c.xs[(int)((S.cw[u] & 0xFFFFu) >> 3) + col];
+    }
+#pragma unroll
+    for (int u = 0; u < kStagedU; ++u) {
+        const int w = (int)((S.cw[u] >> 28) & 3u);
+        const uint32_t h = (S.raw[u].x >> ((S.cw[u] >> 26) & 16u)) << 16;
+        const uint32_t f = w == 1 ? h : S.raw[u].x;
+        double v32 = (double)__uint_as_float(f);
+        asm volatile("" : "+v"(v32));  // keep the choice below two selects (see spmv_sweep)
+        const double v = w == 3 ? __longlong_as_double(((long long)S.raw[u].y << 32) | S.raw[u].x) : v32;
+        atomicAdd(reinterpret_cast<double*>(c.acc + racc[u]), v * xv[u]);
+    }
+}
+
+// The x segments of a staged batch into the stage: chunk i (16 bytes) of the
+// stage is chunk i & (C/2 - 1) of column block xcb[i >> stage_shift]; lanes
+// past the batch's chunks are masked off.
+__device__ __forceinline__ void stage_x(const SweepCtx& c, const BatchRegs& R, int xcount, int shift, int C8,
+                                        double* stage) {
+    const int chunks = xcount << shift;
+    const int mask = (1 << shift) - 1;
+    for (int j = 0; j < chunks; j += kWave) {
+        const int i = j + c.lane;
+        const int blk = __builtin_amdgcn_ds_bpermute(4 * min(i >> shift, kWave - 1), R.xcb);
+        if (i < chunks)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (__attribute__((address_space(3))) void*)(stage + 2 * j),
+                                                     16, blk * C8 + ((i & mask) << 4), 0, 0, 0);
+    }
+}
+
+// A staged batch: stage the vector segments, then the pipelined sweeps. The
+// first sweep's loads are issued together with the staging; the next batch's
+// loads (header Hn) go out after the second sweep's.
+template <typename MetaT, bool CB>
+__device__ __forceinline__ void sweep_batch_staged(const SweepCtx& c, const SpmvArgs& a, const BatchHdr& H,
+                                                   const BatchRegs& R, bool more, const BatchHdr& Hn, BatchRegs& Rn) {
+    stage_x(c, R, H.xcount, a.stage_shift, a.C * 8, const_cast<double*>(c.xs));
+    const int nsw = batch_records(H.len, true) / kStagedU;
+    if (nsw == 0) {
+        if (more) load_batch_regs<CB>(c, Hn, 0, true, Rn);
+        return;
+    }
+    StagedSweep A, B;
+    staged_issue<MetaT>(c, R, 0, A);
+    if (kStagedPipe == 1) {  // one sweep in flight at a time
+        if (more) load_batch_regs<CB>(c, Hn, 0, true, Rn);
+        for (int s = 0;;) {
+            staged_consume<MetaT>(c, A, s);
+            if (++s >= nsw) break;
+            staged_issue<MetaT>(c, R, s, A);
+        }
+        return;
+    }
+    if (nsw > 1) staged_issue<MetaT>(c, R, 1, B);
+    if (more) load_batch_regs<CB>(c, Hn, 0, true, Rn);
+    for (int s = 0;;) {
+        staged_consume<MetaT>(c, A, s);
+        if (++s >= nsw) break;
+        if (s + 1 < nsw) staged_issue<MetaT>(c, R, s + 1, A);
+        staged_consume<MetaT>(c, B, s);
+        if (++s >= nsw) break;
+        if (s + 1 < nsw) staged_issue<MetaT>(c, R, s + 1, B);
+    }
+}
+
 // The outputs are separate restrict arguments: the compiler may then treat
 // every other array as read-only for the whole launch.
 //
@@ -621,7 +832,8 @@ __device__ __forceinline__ void spmv_sweep(const SweepCtx& c, const BatchRegs& R
 template <typename MetaT, int MODE, int MAXROWS, bool CB, bool P1, int U = kUnroll, bool XL = false>
 __device__ __forceinline__ double spmv_wave(const SpmvArgs& a, double* __restrict__ y, int g0, int g1, int uprec,
                                             double* acc, int4* desc, int lane, const double* xs = nullptr) {
-    static_assert(U >= kUnroll && U % kUnroll == 0 && (U & (U - 1)) == 0 && U <= kWave, "sweep size");
+    // The sweep-ordered indices are laid out for sweeps of kUnroll windows.
+    static_assert(U == kUnroll, "sweep size");
     SweepCtx c;
     c.lane = lane;
     c.xs = xs;
@@ -631,6 +843,7 @@ __device__ __forceinline__ double spmv_wave(const SpmvArgs& a, double* __restric
     c.toff = a.toff;
     c.tcol = a.tcol;
     c.cbcode = a.cbcode;
+    c.xcb = a.xcb;
     // Values come from the precision planes under a uniform precision or the
     // max|p| rule (which changes the map every iteration), else from the map's
     // packed segment.
@@ -687,36 +900,13 @@ __device__ __forceinline__ double spmv_wave(const SpmvArgs& a, double* __restric
             if (lane == 0) desc[kTileBatch] = make_int4(kSentinelColumn, 0, kSentinelPlane, 3);
         }
         c.rv = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char*>((from_planes ? a.planes : a.packed) + (int64_t)H.segment * 16), (short)0,
-            (int)segment_bytes(H.len), (int)kBufferConfig);
+            const_cast<char*>(from_planes ? a.planes + (int64_t)H.segment * 16 : a.packed + (int64_t)H.packed * 16),
+            (short)0, (int)(from_planes ? segment_bytes(H.len) : packed_bytes(H.len)), (int)kBufferConfig);
         c.rmt = batch_rsrc(a.meta, H.first, (int)sizeof(MetaT), H.len);
         c.len = H.len;
-        const int E = batch_records(H.len);
         wave_lds_sync();
-        // The first sweep of the batch also starts the next batch's loads.
         BatchRegs Rn{};
-        int left = E, wi = 0, o0 = 0;
-        for (; left >= U; left -= U, wi += U, o0 += U * kWave) {
-            if (wi > 0 && (wi & (kWave - 1)) == 0) load_batch_regs<CB>(c, H, wi, false, R);  // next 64 records
-            spmv_sweep<MetaT, U, CB, P1, XL>(c, R, wi, o0, more && wi == 0, Hn, Rn);
-        }
-        if (U > kUnroll) {
-            for (; left >= kUnroll; left -= kUnroll, wi += kUnroll, o0 += kUnroll * kWave) {
-                if (wi > 0 && (wi & (kWave - 1)) == 0) load_batch_regs<CB>(c, H, wi, false, R);
-                spmv_sweep<MetaT, kUnroll, CB, P1, XL>(c, R, wi, o0, more && wi == 0, Hn, Rn);
-            }
-        }
-        // The rest is 0 or one power of two below kUnroll (never crossing a record chunk).
-        if (wi > 0 && (wi & (kWave - 1)) == 0 && left > 0) load_batch_regs<CB>(c, H, wi, false, R);
-        const bool first = more && wi == 0;
-        if (kUnroll > 8 && left == 8)
-            spmv_sweep<MetaT, (kUnroll > 8 ? 8 : 1), CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 4 && left == 4)
-            spmv_sweep<MetaT, (kUnroll > 4 ? 4 : 1), CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 2 && left == 2)
-            spmv_sweep<MetaT, (kUnroll > 2 ? 2 : 1), CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
-        if (kUnroll > 1 && left == 1) spmv_sweep<MetaT, 1, CB, P1, XL>(c, R, wi, o0, first, Hn, Rn);
-        if (more && E == 0) load_batch_regs<CB>(c, Hn, 0, true, Rn);  // a batch without windows
+        sweep_batch_gather<MetaT, CB, P1, U, XL>(c, H, R, more, Hn, Rn);
         wave_lds_sync();
         if (H.flags & kBatchLastOfGroup) {
             // This segment's partial product (the product itself without column slices).
@@ -740,12 +930,135 @@ __device__ __forceinline__ double spmv_wave(const SpmvArgs& a, double* __restric
     return dot;
 }
 
-template <typename MetaT, int MODE, int MAXROWS, bool CB = false, bool P1 = false>
+// One wavefront's share in the multi-launch product: the segments g, g +
+// gstride, ... below gend (the kernel interleaves an XCD's segments over its
+// wavefronts), each a run of batches. The next batch's header, tile entries,
+// window records and stage list are loaded while the current batch is swept,
+// also across segments. Batches flagged kBatchStaged run the staged,
+// pipelined sweeps with the vector segments in LDS (`stage`); the others
+// gather the vector from memory. Returns the lane's part of p.q in CG mode.
+template <typename MetaT, int MODE, int MAXROWS, bool CB, bool P1, bool STAGE>
+__device__ __forceinline__ double spmv_wave_multi(const SpmvArgs& a, double* __restrict__ y, int g, int gstride,
+                                                  int gend, int uprec, double* acc, int4* desc, double* stage,
+                                                  int lane) {
+    SweepCtx c;
+    c.lane = lane;
+    c.xs = stage;
+    c.xmax = a.n - 1;
+    c.tent = a.tent;
+    c.map = a.map;
+    c.toff = a.toff;
+    c.tcol = a.tcol;
+    c.cbcode = a.cbcode;
+    c.xcb = a.xcb;
+    const bool from_planes = CB || uprec >= 0;
+    c.desc = desc;
+    c.acc = reinterpret_cast<char*>(acc);
+    c.spare = (MAXROWS + lane) * 8;
+    c.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<double*>(a.x), (short)0, a.n * 8, (int)kBufferConfig);
+    c.rmask = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(a.win_mask), (short)0, a.nwin * 8,
+                                                (int)kBufferConfig);
+    c.rrec = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.win_tile), (short)0, a.nwin * 4,
+                                               (int)kBufferConfig);
+    c.round_p = P1 ? a.p1_round : 0;
+    c.scale = P1 && a.colexp != nullptr;
+    c.sentinel_row = P1 ? a.sentinel_row : -1;
+    if (P1)
+        c.rexp = __builtin_amdgcn_make_buffer_rsrc(const_cast<int16_t*>(a.colexp), (short)0,
+                                                   a.colexp ? a.n * 2 : 0, (int)kBufferConfig);
+    double dot = 0.0, p_own = 0.0;
+    if (g >= gend) return 0.0;
+    int b = uniform_load(a.gbatch, g);
+    int bend = uniform_load(a.gbatch, g + 1);
+    BatchHdr H = load_hdr(a.btab, b);
+    BatchRegs R{};
+    load_batch_regs<CB>(c, H, 0, true, R);
+    for (;;) {
+        // The successor: the next batch of this segment, else the first batch
+        // of this wave's next segment.
+        int bn = b + 1, bendn = bend, gn = g;
+        bool more = true;
+        if (bn >= bend) {
+            gn = g + gstride;
+            more = gn < gend;
+            if (more) {
+                bn = uniform_load(a.gbatch, gn);
+                bendn = uniform_load(a.gbatch, gn + 1);
+            }
+        }
+        BatchHdr Hn{};
+        if (more) Hn = load_hdr(a.btab, bn);
+        const int row0 = H.group * a.rows_per_group;
+        const int nrows = min(a.rows_per_group, a.n - row0);
+        if (H.flags & kBatchFirstOfGroup) {
+            for (int i = lane; i < a.rows_per_group; i += kWave) acc[i] = 0.0;
+            if (MODE == kSpmvCg && MAXROWS <= kWave && lane < nrows) p_own = a.x[row0 + lane];
+        }
+        const bool staged = STAGE && (H.flags & kBatchStaged) != 0;
+        {
+            const int p = uprec >= 0 ? uprec : R.prec;
+            const bool tile = lane < H.tiles;
+            const int none = staged ? 0 : kSentinelColumn;  // a staged sentinel reads stage entry 0
+            int4 e;
+            e.x = tile ? R.entry.x : none;
+            e.y = R.entry.y;
+            e.z = !tile ? kSentinelPlane : from_planes ? p * (10 - 2 * p) * H.len : R.toff;
+            e.w = tile ? 3 - p : 3;
+            desc[lane] = e;
+            if (lane == 0) desc[kTileBatch] = make_int4(none, 0, kSentinelPlane, 3);
+        }
+        c.rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(from_planes ? a.planes + (int64_t)H.segment * 16 : a.packed + (int64_t)H.packed * 16),
+            (short)0, (int)(from_planes ? segment_bytes(H.len) : packed_bytes(H.len)), (int)kBufferConfig);
+        c.rmt = batch_rsrc(a.meta, H.first, (int)sizeof(MetaT), H.len);
+        c.len = H.len;
+        wave_lds_sync();
+        BatchRegs Rn{};
+        if (STAGE && staged)
+            sweep_batch_staged<MetaT, CB>(c, a, H, R, more, Hn, Rn);
+        else
+            sweep_batch_gather<MetaT, CB, P1, kUnroll, false>(c, H, R, more, Hn, Rn);
+        wave_lds_sync();
+        if (H.flags & kBatchLastOfGroup) {
+            // This segment's partial product (the product itself without column slices).
+            double* __restrict__ yo = y + (size_t)(H.flags >> kBatchSliceShift) * a.ystride;
+            for (int i = lane; i < nrows; i += kWave) {
+                const double v = acc[i];
+                if (MODE == kSpmvPlain) {
+                    yo[row0 + i] = v;
+                } else if (MODE == kSpmvCg) {
+                    yo[row0 + i] = v;
+                    dot += (MAXROWS <= kWave ? p_own : a.x[row0 + i]) * v;
+                } else {
+                    yo[row0 + i] = a.b[row0 + i] - v;
+                }
+            }
+            wave_lds_sync();
+        }
+        if (!more) break;
+        H = Hn;
+        R = Rn;
+        b = bn;
+        bend = bendn;
+        g = gn;
+    }
+    return dot;
+}
+
+// The multi-launch product. Blocks are dealt to the XCDs round robin; XCD x
+// takes a contiguous range of segments in proportion to its blocks and
+// interleaves it over its wavefronts (wavefront i takes segments i, i + W,
+// ... of the range), so that the XCD's wavefronts sweep neighbouring
+// segments together (shared vector segments stay in its L2) and finish
+// together whatever the grid size. The grid is at most what the chip holds
+// at once. Dynamic LDS: a vector stage of a.stage_doubles per wavefront.
+template <typename MetaT, int MODE, int MAXROWS, bool CB = false, bool P1 = false, bool STAGE = false>
 __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, double* __restrict__ y,
                                                                   double* __restrict__ partials) {
     __shared__ double s_acc[kSpmvWaves][MAXROWS + kWave];
     __shared__ int4 s_desc[kSpmvWaves][kDescSlots];
     __shared__ double s_tmp[kSpmvWaves];
+    extern __shared__ __attribute__((aligned(16))) double s_stage[];
 
     if (MODE == kSpmvCg && load_done(a.st)) return;
 
@@ -753,10 +1066,16 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
     // The wavefront index is uniform across the wave; saying so keeps every
     // per-batch and per-window quantity in scalar registers.
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int gw = xcd_contiguous_block(blockIdx.x, gridDim.x) * kSpmvWaves + w;
-    const int g0 = min(gw * a.groups_per_wave, a.ngroups);
-    const int g1 = min(g0 + a.groups_per_wave, a.ngroups);
-    double dot = spmv_wave<MetaT, MODE, MAXROWS, CB, P1>(a, y, g0, g1, *a.uprec, &s_acc[w][0], &s_desc[w][0], lane);
+    const int nb = gridDim.x, bx = blockIdx.x;
+    const int xcd = bx & 7, q = nb >> 3, r = nb & 7;
+    const int nbx = q + (xcd < r ? 1 : 0);          // blocks on this XCD
+    const int b0 = xcd * q + (xcd < r ? xcd : r);   // its first block in XCD-contiguous order
+    const int s0 = (int)((int64_t)a.ngroups * b0 / nb);
+    const int s1 = (int)((int64_t)a.ngroups * (b0 + nbx) / nb);
+    const int wx = (bx >> 3) * kSpmvWaves + w;
+    double dot = spmv_wave_multi<MetaT, MODE, MAXROWS, CB, P1, STAGE>(a, y, s0 + wx, nbx * kSpmvWaves, s1, *a.uprec,
+                                                              &s_acc[w][0], &s_desc[w][0],
+                                                              s_stage + (size_t)w * a.stage_doubles, lane);
     if (MODE == kSpmvCg) {
         dot = wave_sum(dot);
         __syncthreads();

@@ -45,6 +45,7 @@ struct cg_handle {
     int32_t R = 0, C = 0, G = 0, rows_per_group = 0, ngroups = 0;
     int32_t S = 1;                 // column slices (cg_options.col_slices)
     int32_t single_block = 0;      // cg_options.single_block: 0 auto, 1 when supported, -1 never
+    bool stage_x = false;          // cg_options.stage_x: vector segments staged in LDS per batch
     uint8_t* winmaps = nullptr;    // cg_record_window_maps: [winmap_cap][T] tile-rule window maps
     int32_t winmap_cap = 0;
     int64_t nseg = 0;              // SpMV segments: S * ngroups (slice-major)
@@ -66,6 +67,9 @@ struct cg_handle {
     int32_t* btab = nullptr;       // [nbatch][8] SpMV batch table
     int32_t* gbatch = nullptr;     // [nseg+1] first batch of every segment (row group, slice)
     int64_t nbatch = 0;
+    int32_t* xcb = nullptr;        // staged batches' distinct column blocks
+    int64_t stage_doubles = 0;     // LDS vector stage of one SpMV wavefront (doubles)
+    int32_t stage_shift = 0;       // log2(C / 2)
     int32_t* trp = nullptr;
     int32_t* tcol = nullptr;
     int32_t* tptr = nullptr;
@@ -76,7 +80,7 @@ struct cg_handle {
     char* packed = nullptr;        // per-batch packed values of the active map (same offsets)
     int32_t* toff = nullptr;       // [T] packed start of every tile (see repack_kernel)
     uint8_t* dirty = nullptr;      // [nbatch] packed segment out of date (tile rule -> repack)
-    int64_t planes_bytes = 0;
+    int64_t planes_bytes = 0, packed_bytes = 0;
     std::vector<int32_t> btab_host;  // host copy of the batch table
     double* dinv = nullptr;
 
@@ -84,7 +88,7 @@ struct cg_handle {
     double *x = nullptr, *r = nullptr, *p = nullptr, *q = nullptr, *z = nullptr;
     double* part_spmv = nullptr;  // one p.q partial per SpMV block
     double* part_vec = nullptr;   // two partials per vector-kernel block
-    int spmv_blocks = 0, groups_per_wave = 0, vec_blocks = 0, upd_blocks = 0;
+    int spmv_blocks = 0, vec_blocks = 0, upd_blocks = 0;
     dev::State* st = nullptr;
     double* hist = nullptr;
     int64_t hist_cap = 0;
@@ -176,9 +180,17 @@ constexpr int kUpdGridCap = MPCG_UPD_GRID_CAP;  // blocks of the update and dire
 #define MPCG_SPMV_GRID_CAP 32768
 #endif
 constexpr int kSpmvGridCap = MPCG_SPMV_GRID_CAP;
+// SpMV grid: at most kSpmvPersist times the blocks the chip holds at once
+// (0: one wavefront per segment up to the cap).
+#ifndef MPCG_SPMV_PERSIST
+#define MPCG_SPMV_PERSIST 0
+#endif
+constexpr int kSpmvPersist = MPCG_SPMV_PERSIST;
 
 int vec_grid(const cg_handle* h) { return h->vec_blocks; }
 int spmv_grid(const cg_handle* h) { return h->spmv_blocks; }
+// Dynamic LDS of an SpMV block: one vector stage per wavefront.
+size_t spmv_dyn_lds(const cg_handle* h) { return (size_t)h->stage_doubles * 8 * dev::kSpmvWaves; }
 
 constexpr int64_t kSmallAutoNnz = MPCG_SMALL_AUTO_NNZ;
 constexpr int64_t kSmallAutoN = MPCG_SMALL_AUTO_N;
@@ -194,13 +206,38 @@ bool small_layout(const cg_handle* h) {
     return h->single_block > 0 || (h->nnz <= kSmallAutoNnz && h->n <= kSmallAutoN);
 }
 
-// Every SpMV wavefront takes a contiguous range of row groups (a capped grid:
-// a wavefront pipelines its batches); vector kernels use a capped grid.
+// Row-accumulator capacity of the SpMV instantiation a handle uses.
+int spmv_maxrows(const cg_handle* h) { return h->rows_per_group > 128 ? 256 : h->rows_per_group > 64 ? 128 : 64; }
+
+template <typename MetaT, int MODE, int MAXROWS, bool CB, bool P1>
+const void* spmv_kernel_fn() {
+    return reinterpret_cast<const void*>(&dev::spmv_tilecsc_kernel<MetaT, MODE, MAXROWS, CB, P1>);
+}
+
+// The SpMV grid: one wavefront per segment, but no more blocks than the chip
+// holds at once (each XCD's wavefronts then take several segments each,
+// interleaved; see spmv_tilecsc_kernel). Vector kernels use capped grids.
 void plan_grids(cg_handle* h) {
-    const int64_t waves = std::max<int64_t>(1, std::min<int64_t>(h->nseg, (int64_t)kSpmvGridCap * dev::kSpmvWaves));
-    h->groups_per_wave = (int)std::max<int64_t>(1, (h->nseg + waves - 1) / waves);
-    const int64_t used = (h->nseg + h->groups_per_wave - 1) / h->groups_per_wave;
-    h->spmv_blocks = (int)std::max<int64_t>(1, (used + dev::kSpmvWaves - 1) / dev::kSpmvWaves);
+    const int64_t want = std::max<int64_t>(1, (h->nseg + dev::kSpmvWaves - 1) / dev::kSpmvWaves);
+    int64_t cap = kSpmvGridCap;
+    if (kSpmvPersist) {
+        const void* fn = h->meta16 ? (spmv_maxrows(h) == 256   ? spmv_kernel_fn<uint16_t, dev::kSpmvPlain, 256, false, false>()
+                                      : spmv_maxrows(h) == 128 ? spmv_kernel_fn<uint16_t, dev::kSpmvPlain, 128, false, false>()
+                                                               : spmv_kernel_fn<uint16_t, dev::kSpmvPlain, 64, false, false>())
+                                   : (spmv_maxrows(h) == 256   ? spmv_kernel_fn<uint8_t, dev::kSpmvPlain, 256, false, false>()
+                                      : spmv_maxrows(h) == 128 ? spmv_kernel_fn<uint8_t, dev::kSpmvPlain, 128, false, false>()
+                                                               : spmv_kernel_fn<uint8_t, dev::kSpmvPlain, 64, false, false>());
+        int per_cu = 0, cus = 0;
+        hipDeviceProp_t prop;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, dev::kSpmvBlock, spmv_dyn_lds(h)) == hipSuccess &&
+            hipGetDeviceProperties(&prop, h->device) == hipSuccess && per_cu > 0) {
+            cus = prop.multiProcessorCount;
+            cap = std::min<int64_t>(cap, (int64_t)per_cu * cus * kSpmvPersist);
+        } else {
+            (void)hipGetLastError();
+        }
+    }
+    h->spmv_blocks = (int)std::max<int64_t>(1, std::min<int64_t>(want, cap));
     h->vec_blocks = grid_for(h->n, 8, kVecGridCap);
     const int64_t npairs = (h->n + 1) / 2;
     const int64_t per_block = (int64_t)dev::kVecBlock * dev::kVecPairs;
@@ -231,31 +268,41 @@ dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t*
     a.rows_per_group = h->rows_per_group;
     a.ngroups = (int32_t)h->nseg;
     a.ystride = (int32_t)(h->n + (h->n & 1));
-    a.groups_per_wave = h->groups_per_wave;
     a.nwin = (int32_t)h->nwin;
     a.colexp = (h->p1 & CG_P1_COLUMN_SCALE) ? h->colexp : nullptr;
     a.p1_round = (h->p1 & CG_P1_ROUND_VECTOR) ? 1 : 0;
     a.sentinel_row = (h->p1 & CG_P1_PAD_COLUMNS) ? h->R : -1;
+    a.xcb = h->xcb;
+    a.C = h->C;
+    a.stage_shift = h->stage_shift;
+    a.stage_doubles = (int32_t)h->stage_doubles;
     return a;
+}
+
+template <typename MetaT, int MODE, int MAXROWS, bool CB, bool P1>
+void launch_spmv_m(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
+    if constexpr (!P1) {
+        if (h->stage_doubles > 0) {  // vector segments staged in LDS (cg_options.stage_x)
+            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<MetaT, MODE, MAXROWS, CB, false, true>), dim3(spmv_grid(h)),
+                               dim3(dev::kSpmvBlock), spmv_dyn_lds(h), s, a, a.y, a.partials);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<MetaT, MODE, MAXROWS, CB, P1>), dim3(spmv_grid(h)),
+                       dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
 }
 
 template <int MODE, bool CB, bool P1>
 void launch_spmv_cb(cg_handle* h, const dev::SpmvArgs& a, hipStream_t s) {
-    const int grid = spmv_grid(h);
-    const bool wide = h->rows_per_group > 64;
+    const int m = spmv_maxrows(h);
     if (h->meta16) {
-        if (wide)
-            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, dev::kMaxRows, CB, P1>), dim3(grid),
-                               dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
-        else
-            hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint16_t, MODE, 64, CB, P1>), dim3(grid),
-                               dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
-    } else if (wide) {
-        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, dev::kMaxRows, CB, P1>), dim3(grid),
-                           dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
+        if (m == 256) launch_spmv_m<uint16_t, MODE, 256, CB, P1>(h, a, s);
+        else if (m == 128) launch_spmv_m<uint16_t, MODE, 128, CB, P1>(h, a, s);
+        else launch_spmv_m<uint16_t, MODE, 64, CB, P1>(h, a, s);
     } else {
-        hipLaunchKernelGGL((dev::spmv_tilecsc_kernel<uint8_t, MODE, 64, CB, P1>), dim3(grid),
-                           dim3(dev::kSpmvBlock), 0, s, a, a.y, a.partials);
+        if (m == 256) launch_spmv_m<uint8_t, MODE, 256, CB, P1>(h, a, s);
+        else if (m == 128) launch_spmv_m<uint8_t, MODE, 128, CB, P1>(h, a, s);
+        else launch_spmv_m<uint8_t, MODE, 64, CB, P1>(h, a, s);
     }
 }
 
@@ -751,6 +798,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         if (opt->single_block < -1 || opt->single_block > 1)
             return bail(fail(CG_EINVAL, "cg_create: single_block must be -1, 0 or 1"));
         h->single_block = opt->single_block;
+        if (opt->stage_x < 0 || opt->stage_x > 1) return bail(fail(CG_EINVAL, "cg_create: stage_x must be 0 or 1"));
+        h->stage_x = opt->stage_x != 0;
     }
     // Row blocks per wavefront: the largest of 32, 64, 128, 256 rows whose row
     // groups hold at most one batch of tiles on average (at least one row block).
@@ -824,38 +873,9 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
             for (int64_t k = lo; k < hi; ++k) meta8[k] = (uint8_t)((D->row_idx[k] << 4) | D->col_local[k]);
         });
     }
-    // Window records of the SpMV sweep: a segment's tiles are taken in batches
-    // of kTileBatch and every batch owns batch_records(len) records: its windows
-    // of 64 nonzeros, then padding up to the sweep sizes the kernel runs.
-    std::vector<int32_t> win_base(h->nseg + 1, 0);
-    {
-        std::vector<int64_t> cnt(h->nseg, 0);
-        mpcg::parallel_for(h->nseg, [&](int64_t lo, int64_t hi) {
-            for (int64_t v = lo; v < hi; ++v) {
-                const int64_t t0 = seg_t0[v], t1 = seg_t0[v + 1];
-                int64_t c = 0;
-                for (int64_t tb = t0; tb < t1; tb += dev::kTileBatch) {
-                    const int64_t nt = std::min<int64_t>(dev::kTileBatch, t1 - tb);
-                    c += dev::batch_records((int)(D->tile_nnz_ptr[tb + nt] - D->tile_nnz_ptr[tb]));
-                }
-                cnt[v] = c;
-            }
-        });
-        int64_t acc = 0;
-        for (int64_t v = 0; v < h->nseg; ++v) {
-            win_base[v] = (int32_t)acc;
-            acc += cnt[v];
-            if (acc > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: too many SpMV windows"));
-        }
-        win_base[h->nseg] = (int32_t)acc;
-        h->nwin = acc;
-    }
-    if (h->nwin >= (int64_t(1) << 28)) return bail(fail(CG_EINVAL, "cg_create: too many SpMV windows"));
-    // Batch table: every segment's batches in order; a segment without tiles
-    // gets one entry without tiles so that its rows are written. The flags hold
-    // the segment's slice above bit 8 (its rows go to that partial product).
+    // Batches: a segment's tiles are taken kTileBatch at a time; a segment
+    // without tiles gets one batch without tiles so that its rows are written.
     std::vector<int32_t> gbatch(h->nseg + 1, 0);
-    std::vector<int32_t> btab;
     {
         int64_t nb = 0;
         for (int64_t v = 0; v < h->nseg; ++v) {
@@ -866,56 +886,114 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         }
         gbatch[h->nseg] = (int32_t)nb;
         h->nbatch = nb;
-        btab.assign((size_t)nb * dev::kBtFields, 0);
-        mpcg::parallel_for(h->nseg, [&](int64_t lo, int64_t hi) {
-            for (int64_t v = lo; v < hi; ++v) {
-                const int64_t t0 = seg_t0[v], t1 = seg_t0[v + 1];
-                int64_t b = gbatch[v], rec = win_base[v];
-                const int64_t b_last = gbatch[v + 1] - 1;
-                for (int64_t tb = t0; b <= b_last; tb += dev::kTileBatch, ++b) {
-                    int32_t* e = &btab[(size_t)b * dev::kBtFields];
-                    const int64_t nt = std::max<int64_t>(0, std::min<int64_t>(dev::kTileBatch, t1 - tb));
-                    const int64_t len = nt ? D->tile_nnz_ptr[tb + nt] - D->tile_nnz_ptr[tb] : 0;
-                    e[dev::kBtTile] = nt ? (int32_t)tb : 0;
-                    e[dev::kBtTiles] = (int32_t)nt;
-                    e[dev::kBtFirstNnz] = nt ? (int32_t)D->tile_nnz_ptr[tb] : 0;
-                    e[dev::kBtLen] = (int32_t)len;
-                    e[dev::kBtRecords] = (int32_t)rec;
-                    e[dev::kBtGroup] = (int32_t)seg_group(v);
-                    e[dev::kBtFlags] = (b == gbatch[v] ? dev::kBatchFirstOfGroup : 0) |
-                                       (b == b_last ? dev::kBatchLastOfGroup : 0) |
-                                       (int32_t)(seg_slice(v) << dev::kBatchSliceShift);
-                    if (nt) rec += dev::batch_records((int)len);
+    }
+    const int64_t nb = h->nbatch;
+    std::vector<int32_t> btab((size_t)nb * dev::kBtFields, 0);
+    // First tile, tiles and nonzeros of every batch, and whether its vector
+    // segments are staged in LDS: the handle supports it (multi-launch
+    // product, C a power of two, none of the paper's numerics options), the
+    // batch's distinct column blocks fit the stage and hold no more entries
+    // than the batch has nonzeros (each staged entry is used once or more on
+    // average), and its padded records fit one chunk of 64.
+    const bool stage_ok = h->stage_x && dev::kStageMaxBytes > 0 && !small_layout(h) && p1 == 0 && A->C >= 2 &&
+                          (A->C & (A->C - 1)) == 0;
+    std::vector<int32_t> bnx(nb, 0);  // distinct column blocks of a staged batch (0: not staged)
+    mpcg::parallel_for(h->nseg, [&](int64_t lo, int64_t hi) {
+        int32_t cols[dev::kTileBatch];
+        for (int64_t v = lo; v < hi; ++v) {
+            const int64_t t0 = seg_t0[v], t1 = seg_t0[v + 1];
+            int64_t tb = t0;
+            for (int64_t b = gbatch[v]; b < gbatch[v + 1]; ++b, tb += dev::kTileBatch) {
+                int32_t* e = &btab[(size_t)b * dev::kBtFields];
+                const int64_t nt = std::max<int64_t>(0, std::min<int64_t>(dev::kTileBatch, t1 - tb));
+                const int64_t len = nt ? D->tile_nnz_ptr[tb + nt] - D->tile_nnz_ptr[tb] : 0;
+                e[dev::kBtTile] = nt ? (int32_t)tb : 0;
+                e[dev::kBtTiles] = (int32_t)nt;
+                e[dev::kBtFirstNnz] = nt ? (int32_t)D->tile_nnz_ptr[tb] : 0;
+                e[dev::kBtLen] = (int32_t)len;
+                e[dev::kBtGroup] = (int32_t)seg_group(v);
+                e[dev::kBtFlags] = (b == gbatch[v] ? dev::kBatchFirstOfGroup : 0) |
+                                   (b == gbatch[v + 1] - 1 ? dev::kBatchLastOfGroup : 0) |
+                                   (int32_t)(seg_slice(v) << dev::kBatchSliceShift);
+                if (!stage_ok || nt == 0) continue;
+                for (int64_t k = 0; k < nt; ++k) cols[k] = D->tile_col_idx[tb + k];
+                std::sort(cols, cols + nt);
+                const int64_t nx = std::unique(cols, cols + nt) - cols;
+                const int64_t entries = nx * A->C;
+                if (entries * 8 <= dev::kStageMaxBytes && entries * 100 <= len * dev::kStageRatioPct &&
+                    dev::batch_records((int)len, true) <= dev::kWave) {
+                    bnx[b] = (int32_t)nx;
+                    e[dev::kBtFlags] |= dev::kBatchStaged;
                 }
             }
-        });
-        // Value segments in batch order (16-byte units).
-        int64_t off = 0;
+        }
+    });
+    // Stage lists (xcb) and window records, in batch order.
+    std::vector<int64_t> xbase(nb + 1, 0);
+    int64_t nwin = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+        int32_t* e = &btab[(size_t)b * dev::kBtFields];
+        xbase[b + 1] = xbase[b] + bnx[b];
+        e[dev::kBtXList] = (int32_t)xbase[b];
+        e[dev::kBtXCount] = bnx[b];
+        e[dev::kBtRecords] = (int32_t)nwin;
+        if (e[dev::kBtTiles]) nwin += dev::batch_records(e[dev::kBtLen], bnx[b] > 0);
+        if (nwin > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: too many SpMV windows"));
+    }
+    h->nwin = nwin;
+    if (h->nwin >= (int64_t(1) << 28)) return bail(fail(CG_EINVAL, "cg_create: too many SpMV windows"));
+    if (xbase[nb] > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: too many staged column blocks"));
+    std::vector<int32_t> xcb(std::max<int64_t>(xbase[nb], 1), 0);
+    h->stage_doubles = 0;
+    for (int64_t b = 0; b < nb; ++b) h->stage_doubles = std::max<int64_t>(h->stage_doubles, (int64_t)bnx[b] * A->C);
+    h->stage_shift = 0;
+    while ((2 << h->stage_shift) < A->C) ++h->stage_shift;
+    // Value segments (three planes) and packed parts (the active map's
+    // values), each in batch order, in 16-byte units.
+    {
+        int64_t off = 0, poff = 0;
         for (int64_t b = 0; b < nb; ++b) {
             int32_t* e = &btab[(size_t)b * dev::kBtFields];
             e[dev::kBtSegment] = (int32_t)(off / 16);
+            e[dev::kBtPacked] = (int32_t)(poff / 16);
             off += e[dev::kBtLen] ? dev::segment_bytes(e[dev::kBtLen]) : 0;
+            poff += e[dev::kBtLen] ? dev::packed_bytes(e[dev::kBtLen]) : 0;
             if (off / 16 > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: value planes above 32 GiB"));
         }
         h->planes_bytes = std::max<int64_t>(off, 16);
+        h->packed_bytes = std::max<int64_t>(poff, 16);
     }
-    // Tile entries and window records. A record holds the batch tile of the
-    // window's first nonzero and a mask whose bit q says that nonzero q+1 of the
-    // window starts a tile; the batch's end counts as the start of the sentinel
-    // (tile index nt), which is also where padding records point.
+    // Tile entries and window records. A tile entry holds the byte offset of
+    // its column block's segment (in x, or in the stage of a staged batch:
+    // slot * C * 8 with the slot the block's rank among the batch's distinct
+    // blocks) and of its rows in the row-group accumulators. A record holds
+    // the batch tile of the window's first nonzero and a mask whose bit q says
+    // that nonzero q+1 of the window starts a tile; the batch's end counts as
+    // the start of the sentinel (tile index nt), which is also where padding
+    // records point.
     std::vector<int2> tent(std::max<int64_t>(T, 1), make_int2(0, 0));
     std::vector<uint64_t> win_mask(std::max<int64_t>(h->nwin, 1), 0);
     std::vector<int32_t> win_tile(std::max<int64_t>(h->nwin, 1), 0);
-    mpcg::parallel_for(T, [&](int64_t lo, int64_t hi) {
-        for (int64_t t = lo; t < hi; ++t)
-            tent[t] = make_int2((int)(D->tile_col_idx[t] * A->C * 8), (int)((trb[t] % h->G) * A->R * 8));
-    });
     mpcg::parallel_for(h->nbatch, [&](int64_t lo, int64_t hi) {
         for (int64_t b = lo; b < hi; ++b) {
             const int32_t* e = &btab[(size_t)b * dev::kBtFields];
             const int64_t tb = e[dev::kBtTile], nt = e[dev::kBtTiles], len = e[dev::kBtLen];
             if (!nt) continue;
-            const int64_t kb = D->tile_nnz_ptr[tb], nw = (len + 63) / 64, E = dev::batch_records((int)len);
+            const bool staged = bnx[b] > 0;
+            int32_t list[dev::kTileBatch];
+            if (staged) {
+                for (int64_t k = 0; k < nt; ++k) list[k] = D->tile_col_idx[tb + k];
+                std::sort(list, list + nt);
+                (void)std::unique(list, list + nt);  // the first bnx[b] entries
+                std::copy(list, list + bnx[b], xcb.data() + xbase[b]);
+            }
+            for (int64_t t = tb; t < tb + nt; ++t) {
+                int xoff = (int)(D->tile_col_idx[t] * A->C * 8);
+                if (staged)
+                    xoff = (int)((std::lower_bound(list, list + bnx[b], D->tile_col_idx[t]) - list) * A->C * 8);
+                tent[t] = make_int2(xoff, (int)((trb[t] % h->G) * A->R * 8));
+            }
+            const int64_t kb = D->tile_nnz_ptr[tb], nw = (len + 63) / 64, E = dev::batch_records((int)len, staged);
             int64_t j = 0;
             for (int64_t v = 0; v < E; ++v) {
                 const int64_t wi = e[dev::kBtRecords] + v;
@@ -970,6 +1048,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     TRY(dalloc(h, &h->tent, std::max<int64_t>(T, 1)));
     TRY(dalloc(h, &h->btab, (int64_t)btab.size()));
     TRY(dalloc(h, &h->gbatch, h->nseg + 1));
+    TRY(dalloc(h, &h->xcb, (int64_t)xcb.size()));
     TRY(dalloc(h, &h->tcol, T));
     TRY(dalloc(h, &h->tptr, T + 1));
     TRY(dalloc(h, &h->map, T));
@@ -1001,7 +1080,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         }
     } free_vlow{vlow};
     TRY(dalloc(h, &h->planes, h->planes_bytes));
-    TRY(dalloc(h, &h->packed, h->planes_bytes));
+    TRY(dalloc(h, &h->packed, h->packed_bytes));
     TRY(dalloc(h, &h->toff, std::max<int64_t>(T, 1)));
     TRY(dalloc(h, &h->dirty, std::max<int64_t>(h->nbatch, 1)));
     // CG vectors padded with zeros to an even length (the vector kernels work
@@ -1051,6 +1130,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         (e = hipMemcpyAsync(h->trp, trp.data(), sizeof(int32_t) * trp.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->btab, btab.data(), sizeof(int32_t) * btab.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->gbatch, gbatch.data(), sizeof(int32_t) * gbatch.size(), hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->xcb, xcb.data(), sizeof(int32_t) * xcb.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tcol, D->tile_col_idx.data(), sizeof(int32_t) * T, hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tptr, tptr.data(), sizeof(int32_t) * tptr.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->meta, h->meta16 ? (const void*)meta16.data() : (const void*)meta8.data(),
@@ -1077,7 +1157,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     }
     if ((e = hipMemsetAsync(h->dirty, 0, (size_t)std::max<int64_t>(h->nbatch, 1), s)) ||
         (e = hipMemsetAsync(h->planes, 0, h->planes_bytes, s)) ||
-        (e = hipMemsetAsync(h->packed, 0, h->planes_bytes, s)))
+        (e = hipMemsetAsync(h->packed, 0, h->packed_bytes, s)))
         return dev_err(e, "planes");
     hipLaunchKernelGGL(dev::build_segments_kernel,
                        dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>((h->nbatch + 3) / 4, 8192))),
