@@ -369,6 +369,32 @@ int cg_spmv(cg_handle* h, const double* x, double* y, void* stream);
 int cg_solve(cg_handle* h, const double* b, const double* x0, double tol, int32_t maxit,
              double* x, int32_t* iterations, double* res_hist, void* stream);
 
+/*
+ * True relative residual ||b - A x||_2 / ||b||_2 with the exact FP64 matrix
+ * values (EvoCG paper Sec. 4.3: the final residual is recomputed in FP64
+ * after the solve, outside the timed region), whatever the active map or
+ * schedule; ||b - A x||_2 when b = 0.
+ *   b, x   : device double[n] (any double alignment; not modified).
+ *   out    : host double receiving the value.
+ *   stream : the computation is ordered after prior work on stream; the call
+ *            returns when the value is on the host.
+ * The per-block partial sums live in the handle's memory (allocated by
+ * cg_create). Errors: CG_EINVAL (NULL argument), CG_EDEVICE.
+ */
+int cg_true_residual(cg_handle* h, const double* b, const double* x, double* out, void* stream);
+
+/*
+ * Bandwidth references (measurement aids for benchmarks; no part of the
+ * method): cg_stream_read reads `bytes` from src once with 16-byte
+ * non-temporal loads and writes one sum per block to sink[blocks];
+ * cg_stream_copy copies `bytes` from src to dst. Both are asynchronous on
+ * stream, with a grid of `blocks` 256-thread blocks. bytes must be a positive
+ * multiple of 16 and the pointers 16-byte aligned device memory.
+ * Errors: CG_EINVAL, CG_EDEVICE.
+ */
+int cg_stream_read(const void* src, int64_t bytes, double* sink, int32_t blocks, void* stream);
+int cg_stream_copy(const void* src, void* dst, int64_t bytes, int32_t blocks, void* stream);
+
 /* Map trace of the last cg_solve: one entry per map change (the first at
  * k = 0). Writes up to cap entries: k_out[i] (iteration the map took effect)
  * and counts_out[3*i + p] (tiles at precision p). Returns the number of

@@ -21,7 +21,7 @@ from ._lib import (CG_BF16, CG_BREAKDOWN, CG_EDEVICE, CG_EINVAL, CG_ENOMEM, CG_F
 
 __all__ = [
     "TileCSC", "Solver", "cg_tilecsc_from_csr", "cg_create", "cg_spmv", "cg_solve", "cg_tune_row_height",
-    "cg_version", "library_path", "CGError",
+    "cg_version", "library_path", "CGError", "cg_stream_read", "cg_stream_copy",
 ]
 
 STATUS = {CG_OK: "converged", CG_NOT_CONVERGED: "maxit", CG_BREAKDOWN: "breakdown"}
@@ -231,6 +231,13 @@ class Solver:
                                         ct.byref(it), _ptr(hist), ct.c_void_p(_stream(stream))))
         return STATUS[rc], int(it.value), hist[: it.value + 1].copy()
 
+    def cg_true_residual(self, b, x, stream=None) -> float:
+        """||b - A x|| / ||b|| with the exact FP64 values (device vectors in, host float out)."""
+        out = ct.c_double()
+        check(_lib.load().cg_true_residual(self._h, ct.c_void_p(_dev_ptr(b)), ct.c_void_p(_dev_ptr(x)),
+                                           ct.byref(out), ct.c_void_p(_stream(stream))))
+        return float(out.value)
+
     def cg_get_map_trace(self, cap=100000):
         ks = np.empty(cap, dtype=np.int32)
         cnt = np.empty(3 * cap, dtype=np.int64)
@@ -316,3 +323,28 @@ def cg_select_reuse_interval(codes, max_fraction=0.1):
 
 def cg_solve(h: Solver, b, x0, tol, maxit, x, stream=None):
     return h.cg_solve(b, x, tol, maxit, x0=x0, stream=stream)
+
+
+def _bytes_ptr(t):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+        raise TypeError("expected a contiguous torch tensor on a GPU")
+    return t.data_ptr(), t.numel() * t.element_size()
+
+
+def cg_stream_read(src, sink, blocks, stream=None):
+    """Bandwidth reference: read all of src once (sink: float64 tensor of at least `blocks` entries)."""
+    p, nbytes = _bytes_ptr(src)
+    check(_lib.load().cg_stream_read(ct.c_void_p(p), nbytes, ct.c_void_p(_dev_ptr(sink)), int(blocks),
+                                     ct.c_void_p(_stream(stream))))
+
+
+def cg_stream_copy(src, dst, blocks, stream=None):
+    """Bandwidth reference: copy src into dst (same byte size)."""
+    p, nbytes = _bytes_ptr(src)
+    q, nb2 = _bytes_ptr(dst)
+    if nb2 != nbytes:
+        raise ValueError("src and dst must have the same size")
+    check(_lib.load().cg_stream_copy(ct.c_void_p(p), ct.c_void_p(q), nbytes, int(blocks),
+                                     ct.c_void_p(_stream(stream))))

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libmpcg.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["mpcg_layout.cpp", "mpcg_reuse.cpp", "mpcg_tuning.cpp", "mpcg_runtime.hip"]
+SOURCES = ["mpcg_layout.cpp", "mpcg_reuse.cpp", "mpcg_tuning.cpp", "mpcg_runtime.hip", "mpcg_stream.hip"]
 
 # Packed-FP32 instructions are disabled for all device code (no v_pk_*_f32).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

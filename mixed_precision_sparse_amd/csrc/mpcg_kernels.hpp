@@ -210,7 +210,9 @@ __device__ inline void wave_lds_sync() {
 // of p.q. The single-workgroup solver runs the same per-wavefront code
 // (spmv_wave) on its 16 wavefronts.
 // ---------------------------------------------------------------------------
-enum SpmvMode { kSpmvPlain = 0, kSpmvCg = 1, kSpmvResidual = 2 };
+// Plain: y = A x. Cg: y = A p and per-block partials of p.q. Residual:
+// y = b - A x. ResNorm: no y; per-block partials of ||b - A x||^2 and ||b||^2.
+enum SpmvMode { kSpmvPlain = 0, kSpmvCg = 1, kSpmvResidual = 2, kSpmvResNorm = 3 };
 #ifndef MPCG_SPMV_UNROLL
 #define MPCG_SPMV_UNROLL 4
 #endif
@@ -940,7 +942,7 @@ __device__ __forceinline__ double spmv_wave(const SpmvArgs& a, double* __restric
 template <typename MetaT, int MODE, int MAXROWS, bool CB, bool P1, bool STAGE>
 __device__ __forceinline__ double spmv_wave_multi(const SpmvArgs& a, double* __restrict__ y, int g, int gstride,
                                                   int gend, int uprec, double* acc, int4* desc, double* stage,
-                                                  int lane) {
+                                                  int lane, double& dot2) {
     SweepCtx c;
     c.lane = lane;
     c.xs = stage;
@@ -967,6 +969,7 @@ __device__ __forceinline__ double spmv_wave_multi(const SpmvArgs& a, double* __r
         c.rexp = __builtin_amdgcn_make_buffer_rsrc(const_cast<int16_t*>(a.colexp), (short)0,
                                                    a.colexp ? a.n * 2 : 0, (int)kBufferConfig);
     double dot = 0.0, p_own = 0.0;
+    dot2 = 0.0;
     if (g >= gend) return 0.0;
     int b = uniform_load(a.gbatch, g);
     int bend = uniform_load(a.gbatch, g + 1);
@@ -1029,8 +1032,12 @@ __device__ __forceinline__ double spmv_wave_multi(const SpmvArgs& a, double* __r
                 } else if (MODE == kSpmvCg) {
                     yo[row0 + i] = v;
                     dot += (MAXROWS <= kWave ? p_own : a.x[row0 + i]) * v;
-                } else {
+                } else if (MODE == kSpmvResidual) {
                     yo[row0 + i] = a.b[row0 + i] - v;
+                } else {
+                    const double bi = a.b[row0 + i], ri = bi - v;
+                    dot += ri * ri;
+                    dot2 += bi * bi;
                 }
             }
             wave_lds_sync();
@@ -1073,9 +1080,10 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
     const int s0 = (int)((int64_t)a.ngroups * b0 / nb);
     const int s1 = (int)((int64_t)a.ngroups * (b0 + nbx) / nb);
     const int wx = (bx >> 3) * kSpmvWaves + w;
+    double dot2;
     double dot = spmv_wave_multi<MetaT, MODE, MAXROWS, CB, P1, STAGE>(a, y, s0 + wx, nbx * kSpmvWaves, s1, *a.uprec,
                                                               &s_acc[w][0], &s_desc[w][0],
-                                                              s_stage + (size_t)w * a.stage_doubles, lane);
+                                                              s_stage + (size_t)w * a.stage_doubles, lane, dot2);
     if (MODE == kSpmvCg) {
         dot = wave_sum(dot);
         __syncthreads();
@@ -1086,6 +1094,46 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
             for (int i = 0; i < kSpmvWaves; ++i) t += s_tmp[i];
             partials[blockIdx.x] = t;
         }
+    } else if (MODE == kSpmvResNorm) {
+        const double t1 = block_sum<kSpmvWaves>(dot, s_tmp);
+        const double t2 = block_sum<kSpmvWaves>(dot2, s_tmp);
+        if (threadIdx.x == 0) {
+            partials[2 * blockIdx.x] = t1;
+            partials[2 * blockIdx.x + 1] = t2;
+        }
+    }
+}
+
+// The relative true residual from nparts (||b - A x||^2, ||b||^2) partials:
+// out[0] = ||b - A x|| / ||b|| (||b - A x|| when b = 0), summed in a fixed
+// order (one block).
+__global__ __launch_bounds__(kBlock) void resnorm_finish_kernel(const double* __restrict__ partials, int nparts,
+                                                               double* __restrict__ out) {
+    __shared__ double s_tmp[kWavesPerBlock];
+    double tot[2];
+    sum_partials<2>(partials, nparts, tot, s_tmp);
+    if (threadIdx.x == 0) out[0] = tot[1] > 0.0 ? sqrt(tot[0]) / sqrt(tot[1]) : sqrt(tot[0]);
+}
+
+// Column slices: the residual from the slices' partial products (r_i = b_i -
+// their sum) straight into (||r||^2, ||b||^2) block partials.
+__global__ __launch_bounds__(kBlock) void combine_resnorm_kernel(const double* __restrict__ parts, int nparts,
+                                                                int64_t stride, const double* __restrict__ b,
+                                                                int64_t n, double* __restrict__ partials) {
+    __shared__ double s_tmp[kWavesPerBlock];
+    double rr = 0.0, bb = 0.0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        double acc = parts[i];
+        for (int s = 1; s < nparts; ++s) acc += parts[s * stride + i];
+        const double r = b[i] - acc;
+        rr += r * r;
+        bb += b[i] * b[i];
+    }
+    const double t1 = block_sum(rr, s_tmp);
+    const double t2 = block_sum(bb, s_tmp);
+    if (threadIdx.x == 0) {
+        partials[2 * blockIdx.x] = t1;
+        partials[2 * blockIdx.x + 1] = t2;
     }
 }
 

@@ -116,6 +116,15 @@ struct cg_handle {
     // Host staging for polling.
     int32_t* pinned = nullptr;  // [2 windows][2 ints] (done, k)
     hipEvent_t ev[2] = {nullptr, nullptr};
+    // The last cg_spmv / cg_true_residual launch on a caller's stream: calls
+    // that rewrite the map, the packed values or the scalar state wait for it.
+    hipEvent_t ev_user = nullptr;
+    bool user_pending = false;
+    // cg_true_residual: (||r||^2, ||b||^2) partials per block and the result.
+    double* part_res = nullptr;
+    int64_t part_res_cap = 0;
+    double* res_out = nullptr;
+    double* res_host = nullptr;  // pinned
 
     // Captured window graph.
     hipGraphExec_t graph = nullptr;
@@ -180,6 +189,7 @@ constexpr int kUpdGridCap = MPCG_UPD_GRID_CAP;  // blocks of the update and dire
 #define MPCG_SPMV_GRID_CAP 32768
 #endif
 constexpr int kSpmvGridCap = MPCG_SPMV_GRID_CAP;
+constexpr int kResGridCap = 4096;  // blocks of the column-slice residual-norm kernel
 // SpMV grid: at most kSpmvPersist times the blocks the chip holds at once
 // (0: one wavefront per segment up to the cap).
 #ifndef MPCG_SPMV_PERSIST
@@ -544,6 +554,32 @@ void launch_small(cg_handle* h, hipStream_t s) {
     }
 }
 
+// ||b - A x|| / ||b|| with the exact FP64 values into out[0] (device),
+// asynchronously on s; partials: 2 doubles per block of the launch (at most
+// 2 * max(SpMV grid, kResGridCap)).
+int launch_true_residual(cg_handle* h, const double* b, const double* x, double* partials, double* out,
+                         hipStream_t s) {
+    dev::SpmvArgs sa = spmv_args(h, x, nullptr, &h->st->zero_prec);
+    sa.cbcode = nullptr;  // exact FP64 values, whatever the schedule
+    sa.p1_round = 0;
+    sa.b = b;
+    int nparts = 0;
+    if (h->S > 1) {  // the slices' partial products, then the residual and its norms
+        sa.y = h->qpart;
+        launch_spmv<dev::kSpmvPlain>(h, sa, s);
+        nparts = grid_for(h->n, 4, kResGridCap);
+        hipLaunchKernelGGL(dev::combine_resnorm_kernel, dim3(nparts), dim3(dev::kBlock), 0, s, h->qpart, h->S,
+                           (int64_t)(h->n + (h->n & 1)), b, (int64_t)h->n, partials);
+    } else {
+        sa.partials = partials;
+        launch_spmv<dev::kSpmvResNorm>(h, sa, s);
+        nparts = spmv_grid(h);
+    }
+    hipLaunchKernelGGL(dev::resnorm_finish_kernel, dim3(1), dim3(dev::kBlock), 0, s, partials, nparts, out);
+    HIP_CHECK(hipGetLastError());
+    return CG_OK;
+}
+
 int ensure_graph(cg_handle* h) {
     const int W = solve_window(h);
     const int period = h->sched == kSchedPMag ? h->pm_period : h->period;
@@ -573,6 +609,17 @@ int ensure_graph(cg_handle* h) {
     h->graph_period = period;
     h->graph_sched = h->sched;
     return CG_OK;
+}
+
+// Waits until the last launch made on a caller's stream (cg_spmv,
+// cg_true_residual) has finished, before a call rewrites what it reads (the
+// map, the packed values, the column codes, the scalar state). Those calls
+// use the handle's own stream or blocking copies, which are not ordered after
+// a caller's non-blocking stream.
+hipError_t order_after_user(cg_handle* h) {
+    if (!h->user_pending) return hipSuccess;
+    h->user_pending = false;
+    return hipEventSynchronize(h->ev_user);
 }
 
 bool ranges_overlap(const void* a, const void* b, size_t bytes) {
@@ -773,6 +820,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         for (auto& e : h->ev)
             if (e) (void)hipEventDestroy(e);
         if (h->pinned) (void)hipHostFree(h->pinned);
+        if (h->res_host) (void)hipHostFree(h->res_host);
+        if (h->ev_user) (void)hipEventDestroy(h->ev_user);
         if (h->stream) (void)hipStreamDestroy(h->stream);
         delete h;
         return rc;
@@ -1099,6 +1148,9 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     plan_grids(h);
     TRY(dalloc(h, &h->part_spmv, spmv_grid(h)));
     TRY(dalloc(h, &h->part_vec, 2 * std::max(vec_grid(h), h->upd_blocks)));
+    h->part_res_cap = 2 * (int64_t)std::max(spmv_grid(h), kResGridCap);
+    TRY(dalloc(h, &h->part_res, h->part_res_cap));
+    TRY(dalloc(h, &h->res_out, 4));
     TRY(dalloc(h, &h->st, 1));
     TRY(dalloc(h, &h->scratch_u64, 4));
     h->trace_cap = 16;
@@ -1117,6 +1169,9 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
             return dev_err(e, "event");
     if ((e = hipHostMalloc((void**)&h->pinned, 4 * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess)
         return dev_err(e, "pinned host memory");
+    if ((e = hipHostMalloc((void**)&h->res_host, 4 * sizeof(double), hipHostMallocDefault)) != hipSuccess)
+        return dev_err(e, "pinned host memory");
+    if ((e = hipEventCreateWithFlags(&h->ev_user, hipEventDisableTiming)) != hipSuccess) return dev_err(e, "event");
 
     for (double* v : {h->x, h->r, h->p, h->q, h->z, h->dinv})
         if (v && (e = hipMemsetAsync(v, 0, sizeof(double) * (size_t)n_pad, s))) return dev_err(e, "vectors");
@@ -1183,6 +1238,8 @@ extern "C" int cg_destroy(cg_handle* h) {
     for (auto& e : h->ev)
         if (e) (void)hipEventDestroy(e);
     if (h->pinned) (void)hipHostFree(h->pinned);
+    if (h->res_host) (void)hipHostFree(h->res_host);
+    if (h->ev_user) (void)hipEventDestroy(h->ev_user);
     if (h->stream) (void)hipStreamDestroy(h->stream);
     delete h;  // frees device buffers
     return CG_OK;
@@ -1205,6 +1262,7 @@ extern "C" int64_t cg_device_bytes(const cg_handle* h) { return h ? h->device_by
 extern "C" int cg_set_precision_map(cg_handle* h, const uint8_t* map, int32_t on_device) {
     mpcg::clear_error();
     if (!h || !map) return fail(CG_EINVAL, "cg_set_precision_map: NULL argument");
+    HIP_CHECK(order_after_user(h));
     // A device map is staged through the host so that it is validated like a host map.
     std::vector<uint8_t> staged;
     if (on_device) {
@@ -1257,6 +1315,7 @@ extern "C" int cg_get_active_map(const cg_handle* h, uint8_t* out) {
 extern "C" int cg_map_from_magnitude(cg_handle* h, double t_bf16, double t_fp32) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_map_from_magnitude: h is NULL");
+    HIP_CHECK(order_after_user(h));
     if (!(t_bf16 <= t_fp32)) return fail(CG_EINVAL, "cg_map_from_magnitude: need t_bf16 <= t_fp32");
     if (h->S > 1) return fail(CG_EINVAL, "cg_map_from_magnitude: not available with column slices");
     HIP_CHECK(hipMemset(h->scratch_u64, 0, sizeof(unsigned long long)));
@@ -1276,6 +1335,7 @@ extern "C" int cg_set_schedule_residual(cg_handle* h, int32_t nstage, const doub
                                         const uint8_t* prec) {
     mpcg::clear_error();
     if (!h || !prec) return fail(CG_EINVAL, "cg_set_schedule_residual: NULL argument");
+    HIP_CHECK(order_after_user(h));
     if (nstage < 1 || nstage > 8) return fail(CG_EINVAL, "cg_set_schedule_residual: nstage must lie in [1, 8]");
     if (nstage > 1 && !thresholds) return fail(CG_EINVAL, "cg_set_schedule_residual: thresholds is NULL");
     h->thresholds.assign(thresholds, thresholds + (nstage - 1));
@@ -1294,6 +1354,7 @@ extern "C" int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const dou
                                          double lo) {
     mpcg::clear_error();
     if (!h || !scores) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: NULL argument");
+    HIP_CHECK(order_after_user(h));
     if (h->S > 1) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: not available with column slices");
     if (period < 1) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: period must be >= 1");
     if (!(lo <= hi)) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: need lo <= hi");
@@ -1312,6 +1373,7 @@ extern "C" int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const dou
 extern "C" int cg_set_schedule_pmag(cg_handle* h, double lo, double hi, int32_t period) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_set_schedule_pmag: h is NULL");
+    HIP_CHECK(order_after_user(h));
     if (h->S > 1) return fail(CG_EINVAL, "cg_set_schedule_pmag: not available with column slices");
     if (std::isnan(lo) || std::isnan(hi) || !(lo <= hi))
         return fail(CG_EINVAL, "cg_set_schedule_pmag: need lo <= hi (no NaN)");
@@ -1339,6 +1401,7 @@ extern "C" int cg_set_schedule_pmag(cg_handle* h, double lo, double hi, int32_t 
 extern "C" int cg_record_column_codes(cg_handle* h, int32_t enable) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_record_column_codes: h is NULL");
+    HIP_CHECK(order_after_user(h));
     h->rec_cb = enable != 0;
     drop_graph(h);
     return CG_OK;
@@ -1358,6 +1421,7 @@ extern "C" int cg_get_column_codes(const cg_handle* h, int32_t cap, uint8_t* out
 extern "C" int cg_record_window_maps(cg_handle* h, int32_t cap) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_record_window_maps: h is NULL");
+    HIP_CHECK(order_after_user(h));
     if (cap < 0) return fail(CG_EINVAL, "cg_record_window_maps: cap must be >= 0");
     if (h->winmaps) {
         HIP_CHECK(hipDeviceSynchronize());
@@ -1389,6 +1453,7 @@ extern "C" int cg_get_window_maps(const cg_handle* h, int32_t cap, uint8_t* out)
 extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_eval_tile_rule: h is NULL");
+    HIP_CHECK(order_after_user(h));
     if (h->sched != kSchedTileRule) return fail(CG_EINVAL, "cg_eval_tile_rule: no tile rule is set");
     dev::MapArgs ma = map_args(h, rho, 0);
     hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, h->stream, ma);
@@ -1400,6 +1465,7 @@ extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {
 extern "C" int cg_clear_schedule(cg_handle* h) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_clear_schedule: h is NULL");
+    HIP_CHECK(order_after_user(h));
     h->sched = kSchedStatic;
     return upload_schedule(h);
 }
@@ -1418,6 +1484,21 @@ extern "C" int cg_spmv(cg_handle* h, const double* x, double* y, void* stream) {
         launch_spmv<dev::kSpmvPlain>(h, a, static_cast<hipStream_t>(stream));
     }
     HIP_CHECK(hipGetLastError());
+    HIP_CHECK(hipEventRecord(h->ev_user, static_cast<hipStream_t>(stream)));
+    h->user_pending = true;
+    return CG_OK;
+}
+
+extern "C" int cg_true_residual(cg_handle* h, const double* b, const double* x, double* out, void* stream) {
+    mpcg::clear_error();
+    if (!h || !b || !x || !out) return fail(CG_EINVAL, "cg_true_residual: NULL argument");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HIP_CHECK(order_after_user(h));  // the result is copied through the handle's pinned buffer
+    int rc = launch_true_residual(h, b, x, h->part_res, h->res_out, s);
+    if (rc != CG_OK) return rc;
+    HIP_CHECK(hipMemcpyAsync(h->res_host, h->res_out, sizeof(double), hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    *out = h->res_host[0];
     return CG_OK;
 }
 
@@ -1464,7 +1545,8 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
         drop_graph(h);
     }
 
-    // Order after the caller's prior work.
+    // Order after the caller's prior work (and a cg_spmv on another stream).
+    HIP_CHECK(order_after_user(h));
     HIP_CHECK(hipEventRecord(h->ev[0], user));
     HIP_CHECK(hipStreamWaitEvent(s, h->ev[0], 0));
 

@@ -1,0 +1,126 @@
+"""GPU tests of cg_true_residual (EvoCG paper Sec. 4.3: the final residual
+||b - A x|| / ||b|| recomputed with the exact FP64 matrix) against the oracle,
+and of the ordering of map changes after a cg_spmv still in flight.
+
+Bound: every entry of b - A x is within 2e-13 ((|A||x|)_i + |b_i|) of the
+oracle's (the SpMV bar plus the subtraction), so the relative residuals agree
+within 2e-13 * || |A||x| + |b| || / ||b|| (times a small slack for the norms).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from gen import make_workload, static_map, tile_scores
+from oracle import cg as ocg, spmv as ospmv, tilecsc as otc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mpcg = pytest.importorskip("mixed_precision_sparse_amd")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    return torch.device("cuda:0")
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def ref_residual(A, b, x):
+    r = b - A.to_scipy() @ x
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(r) / nb) if nb > 0 else float(np.linalg.norm(r))
+
+
+def bound(A, b, x):
+    s = ospmv.abs_bound(A.indptr, A.indices, A.data, x) + np.abs(b)
+    nb = np.linalg.norm(b)
+    return 2.5e-13 * float(np.linalg.norm(s)) / (nb if nb > 0 else 1.0)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", ["plain", "slices", "pmag", "p1"])
+def test_true_residual_matches_oracle(cfg, variant, dev):
+    w = make_workload(cfg, "small")
+    A = w.A
+    log(f"true residual cfg{cfg} small {variant}")
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    opts = {"plain": {}, "slices": {"col_slices": 4}, "pmag": {},
+            "p1": {"p1": mpcg.CG_P1_ROUND_VECTOR | mpcg.CG_P1_COLUMN_SCALE}}[variant]
+    S = mpcg.Solver(L, static_map(tile_scores(L.T, 2), 0.2, 0.3), jacobi=w.jacobi, **opts)
+    if variant == "pmag":
+        S.cg_set_schedule_pmag(1e-3, 1e-1, 1)
+    rng = np.random.default_rng(cfg)
+    bd = torch.from_numpy(w.b).to(dev)
+    xs = [rng.uniform(-1, 1, A.n), w.xstar.copy(), np.zeros(A.n)]
+    x = torch.zeros_like(bd)
+    S.cg_solve(bd, x, w.tol, min(w.maxit, 400))
+    xs.append(x.cpu().numpy())
+    for xv in xs:
+        got = S.cg_true_residual(bd, torch.from_numpy(xv).to(dev))
+        want = ref_residual(A, w.b, xv)
+        assert abs(got - want) <= bound(A, w.b, xv) + 1e-15 * want, (got, want)
+    # b = 0: the plain norm ||A x||
+    z = torch.zeros_like(bd)
+    got = S.cg_true_residual(z, torch.from_numpy(xs[0]).to(dev))
+    want = float(np.linalg.norm(A.to_scipy() @ xs[0]))
+    assert abs(got - want) <= 2.5e-13 * float(np.linalg.norm(ospmv.abs_bound(A.indptr, A.indices, A.data, xs[0])))
+    S.close()
+
+
+def test_true_residual_after_solve_matches_oracle_solve(dev):
+    """The library's residual of its own iterate against the oracle solve's reported true residual."""
+    w = make_workload(2, "small")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    Lo = otc.build(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    m = static_map(tile_scores(L.T, 2), 0.2, 0.3)
+    S = mpcg.Solver(L, m)
+    bd = torch.from_numpy(w.b).to(dev)
+    x = torch.zeros_like(bd)
+    status, K, _ = S.cg_solve(bd, x, w.tol, w.maxit)
+    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, w.b, ocg.StaticSchedule(m), w.tol, w.maxit)
+    got = S.cg_true_residual(bd, x)
+    assert status == ref.status and abs(K - ref.K) <= max(1, int(0.02 * ref.K))
+    assert abs(max(got, w.tol) - max(ref.true_residual, w.tol)) <= 1e-2 * max(ref.true_residual, w.tol)
+    S.close()
+
+
+def test_map_change_waits_for_spmv_in_flight(dev):
+    """cg_spmv on a non-blocking stream, then the tile rule rewrites the map with no host
+    synchronisation in between: y must be the product under the map the SpMV was launched
+    with (the map change waits for it)."""
+    w = make_workload(5, "small")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    Lo = otc.build(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    scores = tile_scores(L.T, 2)
+    S = mpcg.Solver(L)
+    S.cg_set_schedule_tile_rule(10, scores, 1e-3, 1e-6)
+    S.cg_eval_tile_rule(1.0)  # mostly BF16
+    m_old = S.cg_get_active_map()
+    s = torch.cuda.Stream()
+    x = np.random.default_rng(4).uniform(-1, 1, A.n)
+    xd = torch.from_numpy(x).to(dev)
+    ys = [torch.full_like(xd, float("nan")) for _ in range(8)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for y in ys:
+            S.cg_spmv(xd, y, stream=s)
+    S.cg_eval_tile_rule(1e-9)  # all FP64
+    m_new = S.cg_get_active_map()
+    assert not np.array_equal(m_old, m_new)
+    torch.cuda.synchronize()
+    y_ref = ospmv.spmv(Lo, A.indptr, A.indices, m_old, x)
+    bnd = 1e-13 * ospmv.abs_bound(A.indptr, A.indices, A.data, x)
+    for y in ys:
+        assert np.all(np.abs(y.cpu().numpy() - y_ref) <= bnd)
+    S.close()
