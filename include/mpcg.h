@@ -384,6 +384,21 @@ int cg_solve(cg_handle* h, const double* b, const double* x0, double tol, int32_
 int cg_true_residual(cg_handle* h, const double* b, const double* x, double* out, void* stream);
 
 /*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): cg_true_residual without
+ * any allocation or host synchronisation. Same value as cg_true_residual,
+ * from the same kernels, written to out, a caller-owned device double, and
+ * enqueued on stream (the call returns at once; read out after the stream).
+ * The per-block partial sums live in a static device array of 65,536 doubles
+ * (512 KiB) per GPU, held until the process ends: every call on one GPU
+ * shares it, so calls that overlap on one GPU (other streams, other host
+ * threads) race. A launch needing more than 65,536 partial sums is rejected
+ * with CG_EINVAL (no handle built by cg_create needs that many).
+ * Errors: CG_EINVAL (NULL argument, too many partial sums), CG_EDEVICE.
+ */
+int cg_true_residual_noalloc(cg_handle* h, const double* b, const double* x, double* out, void* stream);
+
+/*
  * Bandwidth references (measurement aids for benchmarks; no part of the
  * method): cg_stream_read reads `bytes` from src once with 16-byte
  * non-temporal loads and writes one sum per block to sink[blocks];

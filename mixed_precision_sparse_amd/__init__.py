@@ -238,6 +238,12 @@ class Solver:
                                            ct.byref(out), ct.c_void_p(_stream(stream))))
         return float(out.value)
 
+    def cg_true_residual_noalloc(self, b, x, out, stream=None):
+        """The same value as cg_true_residual, written into the device float64 tensor `out`
+        (first entry) on the stream, with no allocation and no synchronisation."""
+        check(_lib.load().cg_true_residual_noalloc(self._h, ct.c_void_p(_dev_ptr(b)), ct.c_void_p(_dev_ptr(x)),
+                                                   ct.c_void_p(_dev_ptr(out)), ct.c_void_p(_stream(stream))))
+
     def cg_get_map_trace(self, cap=100000):
         ks = np.empty(cap, dtype=np.int32)
         cnt = np.empty(3 * cap, dtype=np.int64)

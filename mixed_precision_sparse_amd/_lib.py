@@ -60,6 +60,7 @@ SIGNATURES = {
     "cg_spmv": (ct.c_int, [vp, vp, vp, vp]),
     "cg_solve": (ct.c_int, [vp, vp, vp, f64, i32, vp, ct.POINTER(i32), vp, vp]),
     "cg_true_residual": (ct.c_int, [vp, vp, vp, ct.POINTER(f64), vp]),
+    "cg_true_residual_noalloc": (ct.c_int, [vp, vp, vp, vp, vp]),
     "cg_stream_read": (ct.c_int, [vp, i64, vp, i32, vp]),
     "cg_stream_copy": (ct.c_int, [vp, vp, i64, i32, vp]),
     "cg_get_map_trace": (ct.c_int, [vp, i32, vp, vp]),

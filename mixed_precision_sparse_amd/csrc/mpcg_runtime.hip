@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -611,6 +612,36 @@ int ensure_graph(cg_handle* h) {
     return CG_OK;
 }
 
+// Scratch of cg_true_residual_noalloc: the per-block partial sums (two per
+// block of the residual-norm launch) live in this file-scope device array, one
+// copy per GPU, held until the process ends. In host code `scratch` only names
+// the symbol; its address on each device comes from hipGetSymbolAddress, taken
+// once per device (with that device current) by the first cg_create there.
+constexpr int64_t kNoAllocScratchDoubles = 2 * (int64_t)std::max(kSpmvGridCap, kResGridCap);
+static __device__ __align__(256) double scratch[kNoAllocScratchDoubles];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (device d), looked
+// up the first time and kept.
+int scratch_address(int d, double** out) {
+    *out = nullptr;
+    if (d < 0 || d >= kMaxDevices) return fail(CG_EDEVICE, "device index " + std::to_string(d) + " out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[d]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(CG_EDEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        }
+        g_scratch_ptr[d] = static_cast<double*>(p);
+    }
+    *out = g_scratch_ptr[d];
+    return CG_OK;
+}
+
 // Waits until the last launch made on a caller's stream (cg_spmv,
 // cg_true_residual) has finished, before a call rewrites what it reads (the
 // map, the packed values, the column codes, the scalar state). Those calls
@@ -828,6 +859,11 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     };
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (hipGetDevice(&h->device) != hipSuccess) return bail(fail(CG_EDEVICE, "cg_create: no HIP device"));
+    {
+        double* sp = nullptr;  // the static scratch of cg_true_residual_noalloc on this device
+        const int rc = scratch_address(h->device, &sp);
+        if (rc != CG_OK) return bail(rc);
+    }
     h->n = n;
     h->T = T;
     h->nnz = nnz;
@@ -1500,6 +1536,23 @@ extern "C" int cg_true_residual(cg_handle* h, const double* b, const double* x, 
     HIP_CHECK(hipStreamSynchronize(s));
     *out = h->res_host[0];
     return CG_OK;
+}
+
+extern "C" int cg_true_residual_noalloc(cg_handle* h, const double* b, const double* x, double* out, void* stream) {
+    mpcg::clear_error();
+    if (!h || !b || !x || !out) return fail(CG_EINVAL, "cg_true_residual_noalloc: NULL argument");
+    double* sp = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (h->device >= 0 && h->device < kMaxDevices) sp = g_scratch_ptr[h->device];
+    }
+    if (!sp) return fail(CG_EDEVICE, "cg_true_residual_noalloc: no scratch address for the handle's device");
+    const int64_t parts = h->S > 1 ? grid_for(h->n, 4, kResGridCap) : spmv_grid(h);
+    if (2 * parts > kNoAllocScratchDoubles)
+        return fail(CG_EINVAL, "cg_true_residual_noalloc: " + std::to_string(2 * parts) +
+                                   " partial sums exceed the static scratch of " +
+                                   std::to_string(kNoAllocScratchDoubles));
+    return launch_true_residual(h, b, x, sp, out, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double tol, int32_t maxit,
