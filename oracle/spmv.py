@@ -61,6 +61,27 @@ def spmv(L: TileCSC, indptr, indices, prec_of_tile, x) -> np.ndarray:
     return perturbed_operator(L, indptr, indices, prec_of_tile) @ np.asarray(x, dtype=np.float64)
 
 
+def spmv_full(n: int, indptr, indices, data, R: int, C: int, prec_of_tile, x, keys=None) -> np.ndarray:
+    """Same as :func:`spmv`, for full-size matrices without the whole Tile-CSC object.
+
+    Every CSR entry's tile is found from the sorted tile keys (I * ncb + J, see
+    :func:`oracle.tilecsc.tile_numbering`; pass ``keys`` to reuse them), its value is
+    replaced by its tile's stored value, and the rounded matrix multiplies x in FP64
+    (SciPy's serial CSR product, in CSR order).
+    """
+    from .tilecsc import tile_numbering, tile_of
+
+    indptr = np.asarray(indptr, dtype=np.int64)
+    if keys is None:
+        keys, _ = tile_numbering(n, indptr, indices, R, C)
+    rows = np.repeat(np.arange(n, dtype=np.int64), np.diff(indptr))
+    prec = np.asarray(prec_of_tile, dtype=np.uint8)[tile_of(keys, n, R, C, rows, indices)]
+    del rows
+    vals = stream_values(np.asarray(data, dtype=np.float64), prec)
+    M = sp.csr_matrix((vals, np.asarray(indices), indptr), shape=(n, n))
+    return M @ np.asarray(x, dtype=np.float64)
+
+
 def spmv_loop(L: TileCSC, indptr, indices, prec_of_tile, x) -> np.ndarray:
     """Same as :func:`spmv`, written as plain loops (small inputs only)."""
     vals = rounded_csr_values(L, prec_of_tile)

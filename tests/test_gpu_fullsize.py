@@ -2,8 +2,11 @@
 
 Expected values come from the oracle: the layout digests, map digests and
 CG results in tests/golden/cg_cfg*_full.json (written by
-tests/golden/make_golden.py, which calls only gen and oracle), and SpMV
-rows computed one by one by the oracle on a sample of rows.
+tests/golden/make_golden.py, which calls only gen and oracle), and the SpMV
+compared on every row with the oracle's product of the rounded matrix
+(oracle.spmv.spmv_full), under the FP64 map, a random mixed map and the
+workload's own map (for the windowed tile rule: the map and packed values
+left by a short solve whose later windows rebuild only changed batches).
 """
 
 import hashlib
@@ -83,43 +86,63 @@ def test_fullsize_layout_and_spmv(cfg, dev):
     del e
     log(f"cfg{cfg}: device layout digests equal the oracle's")
 
-    # Sampled rows at full size, in the launch configuration cg_spmv uses.
+    # Every row at full size, in the launch configuration cg_spmv uses, against the
+    # oracle's product of the rounded matrix (oracle.spmv.spmv_full).
     t = time.time()
     keys, _ = otc.tile_numbering(A.n, A.indptr, A.indices, w.R, w.C)
     log(f"cfg{cfg}: oracle tile numbering in {time.time() - t:.1f}s")
     rng = np.random.default_rng(100 + cfg)
-    rows = np.unique(np.concatenate([rng.integers(0, A.n, 1500), [0, A.n - 1],
-                                     np.argsort(np.diff(A.indptr))[-20:]]))
     x = rng.uniform(-1, 1, A.n)
     xd = torch.from_numpy(x).to(dev)
     yd = torch.empty_like(xd)
-    bound_all = ospmv.abs_bound(A.indptr, A.indices, A.data, x)
-    rand_map = static_map(tile_scores(L.T, 7))
-    for name, m in (("fp64", np.zeros(L.T, np.uint8)), ("mixed", rand_map)):
-        S.cg_set_precision_map(m)
+    bound_all = 1e-13 * ospmv.abs_bound(A.indptr, A.indices, A.data, x)
+
+    def check_all_rows(name, m):
         S.cg_spmv(xd, yd)
         torch.cuda.synchronize()
         y = yd.cpu().numpy()
-        y_ref = ospmv.spmv_rows(A.indptr, A.indices, A.data, rows,
-                                lambda i, cols: m[otc.tile_of(keys, A.n, w.R, w.C, np.full(cols.size, i), cols)],
-                                x)
-        err = np.abs(y[rows] - y_ref)
-        assert np.all(err <= 1e-13 * bound_all[rows]), (name, float((err / bound_all[rows]).max()))
-        log(f"cfg{cfg}: SpMV {name} map, {rows.size} sampled rows within 1e-13*(|A||x|)")
+        t0 = time.time()
+        y_ref = ospmv.spmv_full(A.n, A.indptr, A.indices, A.data, w.R, w.C, m, x, keys=keys)
+        bad = np.nonzero(~(np.abs(y - y_ref) <= bound_all))[0]
+        assert bad.size == 0, (name, int(bad.size), bad[:5].tolist())
+        log(f"cfg{cfg}: SpMV {name} map, all {A.n} rows within 1e-13*(|A||x|) (oracle {time.time() - t0:.1f}s)")
 
-    # The workload's own map rule at full size.
+    for name, m in (("fp64", np.zeros(L.T, np.uint8)), ("random mixed", static_map(tile_scores(L.T, 7)))):
+        S.cg_set_precision_map(m)
+        check_all_rows(name, m)
+
+    # The workload's own map at full size: the map itself against the oracle's rule, then
+    # every row of the product under it.
     kind = w.map_spec["kind"]
+    sc = tile_scores(L.T, 2)
+    if kind == "static":
+        m = static_map(sc, w.map_spec["frac_bf16"], w.map_spec["frac_fp32"])
+        S.cg_set_precision_map(m)
+        check_all_rows("own static", m)
     if kind == "magnitude":
         S.cg_map_from_magnitude(w.map_spec["t_bf16"], w.map_spec["t_fp32"])
-        assert sha(S.cg_get_active_map(), np.uint8) == g["runs"]["mixed"]["windows"][0]["sha"]
+        m = S.cg_get_active_map()
+        assert sha(m, np.uint8) == g["runs"]["mixed"]["windows"][0]["sha"]
         log(f"cfg{cfg}: magnitude-rule map equals the oracle's")
+        check_all_rows("magnitude rule", m)
+    if kind == "ratchet":
+        S.cg_set_schedule_residual(w.map_spec["thresholds"], w.map_spec["prec"])  # cg_spmv: the first stage
+        check_all_rows("ratchet first stage", np.full(L.T, w.map_spec["prec"][0], np.uint8))
     if kind == "tile_rule":
-        sc = tile_scores(L.T, 2)
         S.cg_set_schedule_tile_rule(10, sc, w.map_spec["hi"], w.map_spec["lo"])
         for rho in (1.0, 2.5e-3, 4e-6, 1e-9):
             S.cg_eval_tile_rule(rho)
             assert np.array_equal(S.cg_get_active_map(), omaps.tile_rule(sc, rho, w.map_spec["hi"], w.map_spec["lo"]))
         log(f"cfg{cfg}: tile-rule maps equal the oracle's")
+        # A short solve: its windows at k = 10 and 20 rebuild only the batches whose tiles
+        # changed precision; the product afterwards reads that packed state.
+        bd = torch.from_numpy(w.b).to(dev)
+        xs = torch.zeros_like(bd)
+        st, K, hist = S.cg_solve(bd, xs, w.tol, 25)
+        assert K == 25
+        m = S.cg_get_active_map()
+        assert np.array_equal(m, omaps.tile_rule(sc, hist[20], w.map_spec["hi"], w.map_spec["lo"]))
+        check_all_rows("tile rule window k=20 (after partial repacks)", m)
     S.close()
 
 

@@ -163,3 +163,24 @@ def test_spmv_rows_matches_full_product():
     yr = spmv.spmv_rows(M.indptr, M.indices, M.data, rows,
                         lambda i, cols: prec[tc.tile_of(keys, 90, R, C, np.full(cols.size, i), cols)], x)
     assert np.allclose(yr, y[rows], rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("n,R,C,seed", [(45, 8, 8, 1), (70, 16, 8, 3), (97, 32, 16, 5)])
+def test_spmv_full_matches_dense_tile_lookup_and_spmv(n, R, C, seed):
+    """The full-size form (tiles from sorted keys, no Tile-CSC object) against the dense
+    tile-by-tile reference, and bit for bit against spmv (same CSR order, same rounding)."""
+    M = _fp32_exact_matrix(n, 0.1, seed)
+    M.data = M.data * (1.0 + 2.0 ** -30)  # values no longer FP32-exact: the rounding matters
+    L = tc.build(n, M.indptr, M.indices, M.data, R, C)
+    prec = np.random.default_rng(seed + 100).integers(0, 3, L.T).astype(np.uint8)
+    x = np.random.default_rng(seed + 200).uniform(-1, 1, n)
+    y = spmv.spmv_full(n, M.indptr, M.indices, M.data, R, C, prec, x)
+    assert np.array_equal(y, spmv.spmv(L, M.indptr, M.indices, prec, x))
+    M2 = _fp32_exact_matrix(n, 0.1, seed)
+    L2 = tc.build(n, M2.indptr, M2.indices, M2.data, R, C)
+    D = _dense_reference(M2, R, C, L2, prec)
+    y2 = spmv.spmv_full(n, M2.indptr, M2.indices, M2.data, R, C, prec, x)
+    assert np.all(np.abs(y2 - D @ x) <= 1e-13 * (np.abs(D) @ np.abs(x)))
+    # the tile of every entry matters: a map shifted by one tile changes the product
+    y3 = spmv.spmv_full(n, M.indptr, M.indices, M.data, R, C, np.roll(prec, 1), x)
+    assert not np.array_equal(y3, y)
