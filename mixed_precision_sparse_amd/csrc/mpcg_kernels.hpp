@@ -942,7 +942,7 @@ __device__ __forceinline__ double spmv_wave(const SpmvArgs& a, double* __restric
 template <typename MetaT, int MODE, int MAXROWS, bool CB, bool P1, bool STAGE>
 __device__ __forceinline__ double spmv_wave_multi(const SpmvArgs& a, double* __restrict__ y, int g, int gstride,
                                                   int gend, int uprec, double* acc, int4* desc, double* stage,
-                                                  int lane, double& dot2) {
+                                                  double* pown, int lane, double& dot2) {
     SweepCtx c;
     c.lane = lane;
     c.xs = stage;
@@ -996,6 +996,15 @@ __device__ __forceinline__ double spmv_wave_multi(const SpmvArgs& a, double* __r
         if (H.flags & kBatchFirstOfGroup) {
             for (int i = lane; i < a.rows_per_group; i += kWave) acc[i] = 0.0;
             if (MODE == kSpmvCg && MAXROWS <= kWave && lane < nrows) p_own = a.x[row0 + lane];
+            if (MODE == kSpmvCg && MAXROWS > kWave) {
+                // The group's own p entries (for p.q at the group's end) go to LDS
+                // now, 16 bytes per lane by LDS-direct loads; the sweeps' waits
+                // cover them. Entries past n read as zero.
+                for (int j = 0; j < a.rows_per_group / 2; j += kWave)
+                    if (j + lane < a.rows_per_group / 2)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (__attribute__((address_space(3))) void*)(pown + 2 * j),
+                                                                 16, row0 * 8 + (j + lane) * 16, 0, 0, 0);
+            }
         }
         const bool staged = STAGE && (H.flags & kBatchStaged) != 0;
         {
@@ -1031,7 +1040,7 @@ __device__ __forceinline__ double spmv_wave_multi(const SpmvArgs& a, double* __r
                     yo[row0 + i] = v;
                 } else if (MODE == kSpmvCg) {
                     yo[row0 + i] = v;
-                    dot += (MAXROWS <= kWave ? p_own : a.x[row0 + i]) * v;
+                    dot += (MAXROWS <= kWave ? p_own : pown[i]) * v;
                 } else if (MODE == kSpmvResidual) {
                     yo[row0 + i] = a.b[row0 + i] - v;
                 } else {
@@ -1065,6 +1074,9 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
     __shared__ double s_acc[kSpmvWaves][MAXROWS + kWave];
     __shared__ int4 s_desc[kSpmvWaves][kDescSlots];
     __shared__ double s_tmp[kSpmvWaves];
+    // CG mode, groups above 64 rows: each wavefront's copy of its group's p entries.
+    constexpr int kPown = (MODE == kSpmvCg && MAXROWS > kWave) ? MAXROWS : 2;
+    __shared__ __attribute__((aligned(16))) double s_pown[kSpmvWaves][kPown];
     extern __shared__ __attribute__((aligned(16))) double s_stage[];
 
     if (MODE == kSpmvCg && load_done(a.st)) return;
@@ -1083,7 +1095,8 @@ __global__ __launch_bounds__(kSpmvBlock) void spmv_tilecsc_kernel(SpmvArgs a, do
     double dot2;
     double dot = spmv_wave_multi<MetaT, MODE, MAXROWS, CB, P1, STAGE>(a, y, s0 + wx, nbx * kSpmvWaves, s1, *a.uprec,
                                                               &s_acc[w][0], &s_desc[w][0],
-                                                              s_stage + (size_t)w * a.stage_doubles, lane, dot2);
+                                                              s_stage + (size_t)w * a.stage_doubles, &s_pown[w][0],
+                                                              lane, dot2);
     if (MODE == kSpmvCg) {
         dot = wave_sum(dot);
         __syncthreads();

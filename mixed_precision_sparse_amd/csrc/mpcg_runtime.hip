@@ -187,7 +187,7 @@ constexpr int kUpdGridCap = MPCG_UPD_GRID_CAP;  // blocks of the update and dire
 #define MPCG_SMALL_AUTO_N 8192
 #endif
 #ifndef MPCG_SPMV_GRID_CAP
-#define MPCG_SPMV_GRID_CAP 32768
+#define MPCG_SPMV_GRID_CAP 16384
 #endif
 constexpr int kSpmvGridCap = MPCG_SPMV_GRID_CAP;
 constexpr int kResGridCap = 4096;  // blocks of the column-slice residual-norm kernel
