@@ -66,11 +66,11 @@ typedef struct {
     int64_t n;                    /* rows (= columns) */
     int64_t T;                    /* non-empty tiles */
     int64_t nnz;
-    int32_t R, C;                 /* tile height and width, each in [1, 256] */
+    int32_t R, C;                 /* tile height in [1, 16384], width in [1, 256] */
     const int64_t* tile_row_ptr;  /* [ceil(n/R) + 1] */
     const int32_t* tile_col_idx;  /* [T] column-block index */
     const int64_t* tile_nnz_ptr;  /* [T + 1] */
-    const uint8_t* row_idx;       /* [nnz] row offset inside the row block */
+    const uint16_t* row_idx;      /* [nnz] row offset inside the row block */
     const uint8_t* col_local;     /* [nnz] column offset inside the tile */
     const double* val;            /* [nnz] FP64 values in canonical order */
 } cg_tilecsc_view;
@@ -81,7 +81,8 @@ typedef struct {
  *   rowptr  : host int64[n+1], rowptr[0] = 0, non-decreasing.
  *   colind  : host int32[nnz], strictly increasing inside each row, in [0, n).
  *   val     : host double[nnz], finite (explicit zeros are kept as entries).
- *   R, C    : tile shape, each in [1, 256].
+ *   R, C    : tile shape: height R in [1, 16384] (the paper's candidates of
+ *             Sec. 3.3.3 reach 16384), width C in [1, 256].
  *   out     : receives a library-owned object; free with cg_tilecsc_free.
  * Inputs are read only and may be freed after the call.
  * Errors: CG_EINVAL (bad sizes, unsorted or duplicate columns, non-finite
@@ -111,8 +112,9 @@ void cg_tilecsc_free(cg_tilecsc* A);
  * variation (population standard deviation over mean) of the non-empty tile
  * counts of the ceil(n/R) row blocks, computed as sqrt(m S2 - S1^2) / S1 from
  * the exact integer sums S1 = sum c, S2 = sum c^2 over m row blocks. A
- * candidate is admissible when R <= max_R (cg_tilecsc_from_csr accepts
- * R <= 256) and it leaves at least min_row_blocks row blocks; the tuned R is
+ * candidate is admissible when R <= max_R (every candidate is a height that
+ * cg_tilecsc_from_csr and cg_create accept) and it leaves at least
+ * min_row_blocks row blocks; the tuned R is
  * the admissible candidate with the smallest coefficient of variation (ties
  * to the smaller R), or 32 when none is admissible.
  *   n, rowptr, colind : square CSR structure as for cg_tilecsc_from_csr
@@ -192,11 +194,21 @@ typedef struct {
  * L2, such as random sparsity. Each slice writes its own partial product
  * (S * 8n more bytes written, and read once more, per product). The sums are
  * formed in a fixed order: the SpMV result equals the unsliced one within
- * rounding. Supported with static maps, the residual schedule, Jacobi and the
- * CG_P1_* options; cg_map_from_magnitude and the tile and max|p| rules return
- * CG_EINVAL on such a handle. The device keeps the tiles in slice order;
- * maps, the map trace and cg_export_layout use the canonical tile order as
- * everywhere else.
+ * rounding. Every schedule, Jacobi and the CG_P1_* options are supported. The
+ * device keeps the tiles in slice order and its map kernels work in that
+ * order; maps, scores, window maps, the map trace and cg_export_layout use the
+ * canonical tile order as everywhere else (the library translates at the call).
+ */
+
+/*
+ * Row blocks taller than 256 rows (R in [257, 16384], Sec. 3.3.3): the device
+ * runs the matrix as slabs of R' rows, R' the largest divisor of R not above
+ * 256, so that a slab's rows fit one wavefront's accumulators. Each canonical
+ * R x C tile is stored as the non-empty R' x C pieces of its slabs; all pieces
+ * of a tile share the tile's precision, so the per-tile map, the rules and
+ * the product are those of the R x C tiles. Maps, scores, traces, window maps
+ * and cg_export_layout are in canonical tiles; the magnitude rule takes the
+ * largest |a_ij| over the whole tile. CG_P1_PAD_COLUMNS needs R <= 255.
  */
 
 /*
@@ -418,13 +430,13 @@ int cg_get_map_trace(const cg_handle* h, int32_t cap, int32_t* k_out, int64_t* c
 
 /* Copy the device-resident layout back to host arrays in canonical form:
  * tile_row_ptr int64[ceil(n/R)+1], tile_col_idx int32[T], tile_nnz_ptr
- * int64[T+1], row_idx uint8[nnz], col_local uint8[nnz], and the three value
+ * int64[T+1], row_idx uint16[nnz], col_local uint8[nnz], and the three value
  * planes val64 double[nnz], val32 float[nnz], bf16 uint16[nnz] (bit
  * patterns). Any output pointer may be NULL to skip it. With
  * CG_P1_PAD_COLUMNS, nnz counts the sentinels (row offset R); with
  * CG_P1_COLUMN_SCALE, val32 and bf16 hold the scaled values fl(a / s_j). */
 int cg_export_layout(const cg_handle* h, int64_t* tile_row_ptr, int32_t* tile_col_idx,
-                     int64_t* tile_nnz_ptr, uint8_t* row_idx, uint8_t* col_local,
+                     int64_t* tile_nnz_ptr, uint16_t* row_idx, uint8_t* col_local,
                      double* val64, float* val32, uint16_t* bf16);
 
 /* Exponents e_j of the per-column scale s_j = 2^e_j (CG_P1_COLUMN_SCALE,

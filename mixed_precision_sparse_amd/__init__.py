@@ -86,7 +86,7 @@ class TileCSC:
 
     @property
     def row_idx(self):
-        return self._arr(self._view.row_idx, self.nnz, np.uint8)
+        return self._arr(self._view.row_idx, self.nnz, np.uint16)
 
     @property
     def col_local(self):
@@ -254,7 +254,7 @@ class Solver:
     def cg_export_layout(self):
         nrb = -(-self.n // self.R)
         out = dict(tile_row_ptr=np.empty(nrb + 1, np.int64), tile_col_idx=np.empty(self.T, np.int32),
-                   tile_nnz_ptr=np.empty(self.T + 1, np.int64), row_idx=np.empty(self.nnz, np.uint8),
+                   tile_nnz_ptr=np.empty(self.T + 1, np.int64), row_idx=np.empty(self.nnz, np.uint16),
                    col_local=np.empty(self.nnz, np.uint8), val64=np.empty(self.nnz, np.float64),
                    val32=np.empty(self.nnz, np.float32), bf16=np.empty(self.nnz, np.uint16))
         check(_lib.load().cg_export_layout(self._h, *[_ptr(out[k]) for k in (
@@ -290,7 +290,7 @@ def cg_spmv(h: Solver, x, y, stream=None):
     h.cg_spmv(x, y, stream)
 
 
-def cg_tune_row_height(n, indptr, indices, C, max_R=256, min_row_blocks=1024):
+def cg_tune_row_height(n, indptr, indices, C, max_R=16384, min_row_blocks=1024):
     """Tuned row-block height and the per-candidate table (see ``cg_tune_row_height`` in mpcg.h).
 
     Returns ``(R, rows)`` with one dict per candidate height: R, row_blocks,

@@ -25,7 +25,7 @@ class cg_tilecsc_view(ct.Structure):
     _fields_ = [
         ("n", i64), ("T", i64), ("nnz", i64), ("R", i32), ("C", i32),
         ("tile_row_ptr", ct.POINTER(i64)), ("tile_col_idx", ct.POINTER(i32)),
-        ("tile_nnz_ptr", ct.POINTER(i64)), ("row_idx", u8p), ("col_local", u8p),
+        ("tile_nnz_ptr", ct.POINTER(i64)), ("row_idx", ct.POINTER(ct.c_uint16)), ("col_local", u8p),
         ("val", ct.POINTER(f64)),
     ]
 

@@ -15,7 +15,7 @@ struct cg_tilecsc {
     std::vector<int64_t> tile_row_ptr;  // [nrb + 1]
     std::vector<int32_t> tile_col_idx;  // [T]
     std::vector<int64_t> tile_nnz_ptr;  // [T + 1]
-    std::vector<uint8_t> row_idx;       // [nnz]
+    std::vector<uint16_t> row_idx;      // [nnz] row offset inside the row block (R <= 16384)
     std::vector<uint8_t> col_local;     // [nnz]
     std::vector<int64_t> perm;          // [nnz] canonical position -> CSR position
     std::vector<double> val;            // [nnz]

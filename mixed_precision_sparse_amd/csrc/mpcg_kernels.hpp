@@ -1598,6 +1598,7 @@ struct MapArgs {
     const int32_t* btab;  // tile rule: batches of the SpMV (a partition of the tiles)
     uint8_t* dirty;       // tile rule: per batch, set when a tile of the batch changed precision
     uint8_t* winmaps;     // tile rule, recording on: [window][T] map of every window (else NULL)
+    const uint8_t* count_w;  // per tile: 1 if it counts in the trace (one piece per tile of R > 256), or NULL: all
     int64_t T;
     int64_t nbatch;
     double rho;          // explicit rho (eval mode)
@@ -1665,9 +1666,10 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
             changed = code != (int)a.map[t];
             a.map[t] = (uint8_t)code;
             if (slot >= 0 && slot < a.winmap_cap) a.winmaps[(size_t)slot * a.T + t] = (uint8_t)code;
-            c0 += code == 0;
-            c1 += code == 1;
-            c2 += code == 2;
+            const bool counted = !a.count_w || a.count_w[t];
+            c0 += counted && code == 0;
+            c1 += counted && code == 1;
+            c2 += counted && code == 2;
         }
         if (__any(changed) && lane == 0) a.dirty[b] = 1;
     }
@@ -1766,13 +1768,14 @@ __global__ __launch_bounds__(kBlock) void pmag_kernel(PMagArgs a) {
     pmag_counts_out(a, cnt, slot, k);
 }
 
-// Precision counts of the active map into trace entry 0 (static maps).
-__global__ __launch_bounds__(kBlock) void map_count_kernel(const uint8_t* map, int64_t T,
+// Precision counts of the active map into trace entry 0 (static maps); with
+// count_w only the tiles it flags count.
+__global__ __launch_bounds__(kBlock) void map_count_kernel(const uint8_t* map, const uint8_t* count_w, int64_t T,
                                                            int32_t* trace_k, int32_t* counts) {
     unsigned c[3] = {0, 0, 0};
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T;
          t += (int64_t)gridDim.x * blockDim.x)
-        c[map[t] < 3 ? map[t] : 0]++;
+        if (!count_w || count_w[t]) c[map[t] < 3 ? map[t] : 0]++;
     block_counts_out(c[0], c[1], c[2], counts + (size_t)blockIdx.x * 3);
     if (blockIdx.x == 0 && threadIdx.x == 0) trace_k[0] = 0;
 }
@@ -1786,18 +1789,14 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
 
 // Magnitude rule, part 1: max |a_ii| over the diagonal entries (atomic max on
 // the bit pattern, which orders non-negative doubles like unsigned integers).
-__global__ __launch_bounds__(kBlock) void diag_absmax_kernel(const int32_t* trp, const int32_t* tcol,
+// trow[t]: the row block of tile t (height R), in any tile order.
+__global__ __launch_bounds__(kBlock) void diag_absmax_kernel(const int32_t* trow, const int32_t* tcol,
                                                              const int32_t* tptr, const void* meta,
                                                              int meta16, const double* v64,
-                                                             int32_t nrb, int32_t T, int32_t R,
+                                                             int32_t T, int32_t R,
                                                              int32_t C, unsigned long long* out) {
     for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
-        int lo = 0, hi = nrb;  // row block of tile t: last I with trp[I] <= t
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) / 2;
-            if (trp[mid] <= t) lo = mid; else hi = mid;
-        }
-        const int64_t row_base = (int64_t)lo * R, col_base = (int64_t)tcol[t] * C;
+        const int64_t row_base = (int64_t)trow[t] * R, col_base = (int64_t)tcol[t] * C;
         double m = 0.0;
         for (int k = tptr[t]; k < tptr[t + 1]; ++k) {
             int r, c;
@@ -1810,17 +1809,26 @@ __global__ __launch_bounds__(kBlock) void diag_absmax_kernel(const int32_t* trp,
 }
 
 // Magnitude rule, part 2: ratio_t = max |a| in tile / max |a_ii|; BF16 below
-// t16, FP32 below t32, else FP64.
+// t16, FP32 below t32, else FP64. One thread per tile t < T. With cptr, tile
+// t is stored as the pieces clist[cptr[t] .. cptr[t+1]) (row blocks taller
+// than the device's slabs): the maximum runs over all of them and every piece
+// gets the tile's code. Without, tile t is device tile t.
 __global__ __launch_bounds__(kBlock) void magnitude_map_kernel(const int32_t* tptr, const double* v64,
-                                                               int32_t T,
+                                                               int32_t T, const int32_t* cptr,
+                                                               const int32_t* clist,
                                                                const unsigned long long* dmax_bits,
                                                                double t16, double t32, uint8_t* map) {
     const double dmax = __longlong_as_double((long long)*dmax_bits);
     for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
+        const int c0 = cptr ? cptr[t] : t, c1 = cptr ? cptr[t + 1] : t + 1;
         double m = 0.0;
-        for (int k = tptr[t]; k < tptr[t + 1]; ++k) m = fmax(m, fabs(v64[k]));
+        for (int c = c0; c < c1; ++c) {
+            const int d = cptr ? clist[c] : c;
+            for (int k = tptr[d]; k < tptr[d + 1]; ++k) m = fmax(m, fabs(v64[k]));
+        }
         const double ratio = m / dmax;
-        map[t] = ratio < t16 ? 2 : (ratio < t32 ? 1 : 0);
+        const uint8_t code = ratio < t16 ? 2 : (ratio < t32 ? 1 : 0);
+        for (int c = c0; c < c1; ++c) map[cptr ? clist[c] : c] = code;
     }
 }
 

@@ -27,7 +27,7 @@ void mpcg::clear_error() { g_last_error.clear(); }
 
 extern "C" const char* cg_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int cg_version(void) { return 10300; }  // 1.3.0
+extern "C" int cg_version(void) { return 10400; }  // 1.4.0
 
 namespace {
 
@@ -76,8 +76,8 @@ extern "C" int cg_tilecsc_from_csr(int64_t n, const int64_t* rowptr, const int32
     mpcg::clear_error();
     if (!out) return mpcg::fail(CG_EINVAL, "cg_tilecsc_from_csr: out is NULL");
     *out = nullptr;
-    if (R < 1 || R > 256 || C < 1 || C > 256)
-        return mpcg::fail(CG_EINVAL, "cg_tilecsc_from_csr: R and C must lie in [1, 256]");
+    if (R < 1 || R > 16384 || C < 1 || C > 256)
+        return mpcg::fail(CG_EINVAL, "cg_tilecsc_from_csr: R must lie in [1, 16384] and C in [1, 256]");
     int rc = validate_csr(n, rowptr, colind, val);
     if (rc != CG_OK) return rc;
 
@@ -153,7 +153,7 @@ extern "C" int cg_tilecsc_from_csr(int64_t n, const int64_t* rowptr, const int32
                         A->tile_col_idx[t] = (int32_t)J;
                         A->tile_nnz_ptr[t] = pos;
                     }
-                    A->row_idx[pos] = (uint8_t)ents[e].row;
+                    A->row_idx[pos] = (uint16_t)ents[e].row;
                     A->col_local[pos] = (uint8_t)(ents[e].col - J * C);
                     A->perm[pos] = ents[e].k;
                     A->val[pos] = val[ents[e].k];

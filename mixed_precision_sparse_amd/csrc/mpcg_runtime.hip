@@ -42,15 +42,23 @@ struct DeviceBuffers {
 struct cg_handle {
     int device = 0;
     hipStream_t stream = nullptr;  // internal stream for the solve loop
-    int64_t n = 0, T = 0, nnz = 0, nrb = 0;
+    int64_t n = 0, T = 0, nnz = 0, nrb = 0;  // canonical sizes (the caller's tiles)
     int32_t R = 0, C = 0, G = 0, rows_per_group = 0, ngroups = 0;
+    // Device tiles: the canonical ones, or with R > 256 the non-empty pieces of
+    // slabs of Rd rows (Rd the largest divisor of R not above 256).
+    int64_t Td = 0, nrbd = 0;
+    int32_t Rd = 0;
     int32_t S = 1;                 // column slices (cg_options.col_slices)
     int32_t single_block = 0;      // cg_options.single_block: 0 auto, 1 when supported, -1 never
     bool stage_x = false;          // cg_options.stage_x: vector segments staged in LDS per batch
     uint8_t* winmaps = nullptr;    // cg_record_window_maps: [winmap_cap][T] tile-rule window maps
     int32_t winmap_cap = 0;
     int64_t nseg = 0;              // SpMV segments: S * ngroups (slice-major)
-    std::vector<int32_t> dperm;    // S > 1: device tile -> canonical tile
+    std::vector<int32_t> dperm;    // device tile -> canonical tile (slices or slabs; empty: identity)
+    uint8_t* dcount = nullptr;     // slabs: [Td] 1 on the first piece of every canonical tile (trace counts)
+    int32_t* cptr = nullptr;       // slabs: [T + 1] pieces of canonical tile t are clist[cptr[t] .. cptr[t+1])
+    int32_t* clist = nullptr;      // slabs: [Td]
+    int32_t* trow = nullptr;       // [Td] device row block of every device tile
     double* qpart = nullptr;       // S > 1: [S][n_pad] partial products of the slices
     bool meta16 = false;
     bool jacobi = false;
@@ -432,7 +440,8 @@ dev::MapArgs map_args(cg_handle* h, double rho, int solve) {
     a.dirty = h->dirty;
     a.winmaps = h->winmaps;
     a.winmap_cap = h->winmap_cap;
-    a.T = h->T;
+    a.count_w = h->dcount;
+    a.T = h->Td;
     a.nbatch = h->nbatch;
     a.rho = rho;
     a.solve = solve;
@@ -712,7 +721,7 @@ void pad_columns(const cg_tilecsc& A, cg_tilecsc& P) {
                 if (k + 1 == A.tile_nnz_ptr[t + 1] || A.col_local[k + 1] != A.col_local[k]) {
                     if (run & 1) {
                         ++o;
-                        P.row_idx[o] = (uint8_t)A.R;
+                        P.row_idx[o] = (uint16_t)A.R;
                         P.col_local[o] = A.col_local[k];
                         P.val[o] = 0.0;
                     }
@@ -745,6 +754,72 @@ void column_scale(const cg_tilecsc& A, std::vector<int16_t>& e, std::vector<doub
             const int64_t c0 = (int64_t)A.tile_col_idx[t] * A.C;
             for (int64_t k = A.tile_nnz_ptr[t]; k < A.tile_nnz_ptr[t + 1]; ++k)
                 scaled[k] = std::ldexp(A.val[k], -(int)e[c0 + A.col_local[k]]);
+        }
+    });
+}
+
+// Slabs of a layout whose row blocks are taller than a wavefront's
+// accumulators: row block I (R rows) becomes slabs I*k .. I*k+k-1 of Rs = R / k
+// rows, and tile t = (I, J) becomes the non-empty Rs x C pieces of its slabs.
+// B lists the pieces slab by slab, column blocks ascending in a slab (the
+// canonical order of an Rs x C layout); a piece keeps its tile's entries in
+// their order (column by column, rows ascending) with row offsets from the
+// slab's first row. parent[d] is the canonical tile of piece d.
+void split_slabs(const cg_tilecsc& A, int Rs, cg_tilecsc& B, std::vector<int32_t>& parent) {
+    const int64_t k = A.R / Rs, nrb = A.nrb, nslab = nrb * k;
+    std::vector<int64_t> pieces(nslab + 1, 0), nz(nslab + 1, 0);
+    mpcg::parallel_for(nrb, [&](int64_t lo, int64_t hi) {
+        std::vector<int64_t> stamp(k, -1);  // last tile with an entry in slab s
+        for (int64_t I = lo; I < hi; ++I)
+            for (int64_t t = A.tile_row_ptr[I]; t < A.tile_row_ptr[I + 1]; ++t)
+                for (int64_t e = A.tile_nnz_ptr[t]; e < A.tile_nnz_ptr[t + 1]; ++e) {
+                    const int64_t sl = A.row_idx[e] / Rs;
+                    ++nz[I * k + sl + 1];
+                    if (stamp[sl] != t) {
+                        stamp[sl] = t;
+                        ++pieces[I * k + sl + 1];
+                    }
+                }
+    });
+    for (int64_t v = 0; v < nslab; ++v) {
+        pieces[v + 1] += pieces[v];
+        nz[v + 1] += nz[v];
+    }
+    const int64_t Td = pieces[nslab], nnz = nz[nslab];
+    B.n = A.n;
+    B.R = Rs;
+    B.C = A.C;
+    B.nrb = (A.n + Rs - 1) / Rs;  // slabs past the last row hold nothing
+    B.tile_row_ptr.assign(pieces.begin(), pieces.begin() + B.nrb + 1);
+    B.tile_col_idx.assign(Td, 0);
+    B.tile_nnz_ptr.assign(Td + 1, nnz);
+    B.row_idx.assign(nnz, 0);
+    B.col_local.assign(nnz, 0);
+    B.val.assign(nnz, 0.0);
+    B.perm.clear();
+    parent.assign(Td, 0);
+    mpcg::parallel_for(nrb, [&](int64_t lo, int64_t hi) {
+        std::vector<int64_t> pnext(k), znext(k), cur(k, -1), stamp(k, -1);
+        for (int64_t I = lo; I < hi; ++I) {
+            for (int64_t sl = 0; sl < k; ++sl) {
+                pnext[sl] = pieces[I * k + sl];
+                znext[sl] = nz[I * k + sl];
+            }
+            for (int64_t t = A.tile_row_ptr[I]; t < A.tile_row_ptr[I + 1]; ++t)
+                for (int64_t e = A.tile_nnz_ptr[t]; e < A.tile_nnz_ptr[t + 1]; ++e) {
+                    const int64_t sl = A.row_idx[e] / Rs;
+                    if (stamp[sl] != t) {  // tile t's piece in slab sl starts here
+                        stamp[sl] = t;
+                        cur[sl] = pnext[sl]++;
+                        B.tile_col_idx[cur[sl]] = A.tile_col_idx[t];
+                        B.tile_nnz_ptr[cur[sl]] = znext[sl];
+                        parent[cur[sl]] = (int32_t)t;
+                    }
+                    const int64_t o = znext[sl]++;
+                    B.row_idx[o] = (uint16_t)(A.row_idx[e] - sl * Rs);
+                    B.col_local[o] = A.col_local[e];
+                    B.val[o] = A.val[e];
+                }
         }
     });
 }
@@ -807,7 +882,7 @@ void build_slices(const cg_tilecsc& A, int S, int G, int64_t ngroups, cg_tilecsc
         for (int64_t d = lo; d < hi; ++d) {
             const int64_t t = dperm[d], k0 = A.tile_nnz_ptr[t], len = A.tile_nnz_ptr[t + 1] - k0;
             const int64_t o = D.tile_nnz_ptr[d];
-            std::memcpy(&D.row_idx[o], &A.row_idx[k0], len);
+            std::memcpy(&D.row_idx[o], &A.row_idx[k0], sizeof(uint16_t) * len);
             std::memcpy(&D.col_local[o], &A.col_local[k0], len);
             std::memcpy(&D.val[o], &A.val[k0], sizeof(double) * len);
         }
@@ -871,8 +946,28 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     h->C = A->C;
     h->nrb = A->nrb;
     h->p1 = p1;
+    // Row blocks taller than one wavefront's row accumulators run as slabs:
+    // B is the layout of the pieces (split_slabs), or the canonical one.
+    cg_tilecsc slabs;
+    std::vector<int32_t> sparent;
+    const cg_tilecsc* B = A;
+    if (A->R > dev::kMaxRows) {
+        int Rs = dev::kMaxRows;
+        while (A->R % Rs) --Rs;
+        try {
+            split_slabs(*A, Rs, slabs, sparent);
+        } catch (const std::bad_alloc&) {
+            return bail(fail(CG_ENOMEM, "cg_create: out of host memory"));
+        }
+        B = &slabs;
+    }
+    h->Td = B->T();
+    h->Rd = B->R;
+    h->nrbd = B->nrb;
+    const int64_t Td = h->Td;
+    if (Td > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: more than 2^31 - 1 device tiles"));
     // Padding stores the sentinel row offset R, which needs the 16-bit form.
-    h->meta16 = !(A->R <= 16 && A->C <= 16) || (p1 & CG_P1_PAD_COLUMNS);
+    h->meta16 = !(B->R <= 16 && B->C <= 16) || (p1 & CG_P1_PAD_COLUMNS);
     if (opt) {
         h->jacobi = opt->jacobi != 0;
         if (opt->window > 0) h->window = std::min(opt->window, 4096);
@@ -891,8 +986,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     // A small matrix would then leave too few groups (wavefronts) to spread its
     // product over the chip: below kMinGroups groups the group shrinks to the
     // largest size that reaches kMinGroups, down to one row block.
-    auto group_rb = [&](int rows) { return std::max(1, std::min(dev::kMaxGroupRB, rows / A->R)); };
-    auto groups_of = [&](int G) { return (h->nrb + G - 1) / G; };
+    auto group_rb = [&](int rows) { return std::max(1, std::min(dev::kMaxGroupRB, rows / B->R)); };
+    auto groups_of = [&](int G) { return (h->nrbd + G - 1) / G; };
     if (dev::kGroupRows > 0) {
         h->G = group_rb(dev::kGroupRows);
     } else if (small_layout(h)) {
@@ -900,12 +995,12 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         // rows per wavefront, so that each wavefront pays the latency of a
         // batch over many windows.
         h->G = std::min<int>(group_rb(256),
-                             (int)std::max<int64_t>(1, (h->nrb + dev::kSmallWaves - 1) / dev::kSmallWaves));
+                             (int)std::max<int64_t>(1, (h->nrbd + dev::kSmallWaves - 1) / dev::kSmallWaves));
     } else {
         h->G = group_rb(32);
         for (int rows : {64, 128, 256}) {
             const int G = group_rb(rows);
-            if (groups_of(G) > 0 && T <= (int64_t)dev::kTileBatch * groups_of(G)) h->G = G;
+            if (groups_of(G) > 0 && Td <= (int64_t)dev::kTileBatch * groups_of(G)) h->G = G;
         }
         constexpr int64_t kMinGroups = 1024;
         if (groups_of(h->G) < kMinGroups) {
@@ -914,36 +1009,58 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
             h->G = G;
         }
     }
-    h->rows_per_group = h->G * A->R;
-    h->ngroups = (int32_t)((h->nrb + h->G - 1) / h->G);
+    h->rows_per_group = h->G * B->R;
+    h->ngroups = (int32_t)((h->nrbd + h->G - 1) / h->G);
 
-    // Device order of the tiles: canonical, or slice by slice (col_slices).
+    // Device order of the tiles: that of B, or slice by slice (col_slices).
     // D is the layout in device order; segment v (slice v / ngroups, row group
-    // v % ngroups) owns device tiles [seg_t0[v], seg_t0[v + 1]).
+    // v % ngroups) owns device tiles [seg_t0[v], seg_t0[v + 1]); trb holds the
+    // row block (of B) of every device tile.
     h->nseg = (int64_t)h->S * h->ngroups;
     cg_tilecsc sliced;
-    const cg_tilecsc* D = A;
+    const cg_tilecsc* D = B;
     std::vector<int32_t> trb;
     std::vector<int64_t> seg_t0;
     if (h->S > 1) {
-        build_slices(*A, h->S, h->G, h->ngroups, sliced, trb, seg_t0, h->dperm);
+        std::vector<int32_t> dslice;  // device tile -> tile of B
+        build_slices(*B, h->S, h->G, h->ngroups, sliced, trb, seg_t0, dslice);
         D = &sliced;
+        h->dperm.resize(Td);
+        for (int64_t d = 0; d < Td; ++d) h->dperm[d] = sparent.empty() ? dslice[d] : sparent[dslice[d]];
     } else {
-        trb.assign(std::max<int64_t>(T, 1), 0);
-        mpcg::parallel_for(h->nrb, [&](int64_t lo, int64_t hi) {
+        trb.assign(std::max<int64_t>(Td, 1), 0);
+        mpcg::parallel_for(h->nrbd, [&](int64_t lo, int64_t hi) {
             for (int64_t I = lo; I < hi; ++I)
-                for (int64_t t = A->tile_row_ptr[I]; t < A->tile_row_ptr[I + 1]; ++t) trb[t] = (int32_t)I;
+                for (int64_t t = B->tile_row_ptr[I]; t < B->tile_row_ptr[I + 1]; ++t) trb[t] = (int32_t)I;
         });
         seg_t0.assign(h->nseg + 1, 0);
         for (int64_t g = 0; g <= h->ngroups; ++g)
-            seg_t0[g] = A->tile_row_ptr[std::min<int64_t>(g * h->G, h->nrb)];
+            seg_t0[g] = B->tile_row_ptr[std::min<int64_t>(g * h->G, h->nrbd)];
+        h->dperm = sparent;
+    }
+    // Slabs: the pieces of every canonical tile (device order), and which
+    // piece counts for its tile in the map trace.
+    std::vector<int32_t> cptr_h, clist_h;
+    std::vector<uint8_t> dcount_h;
+    if (!sparent.empty()) {
+        cptr_h.assign(T + 1, 0);
+        for (int64_t d = 0; d < Td; ++d) ++cptr_h[h->dperm[d] + 1];
+        for (int64_t t = 0; t < T; ++t) cptr_h[t + 1] += cptr_h[t];
+        clist_h.assign(Td, 0);
+        dcount_h.assign(Td, 0);
+        std::vector<int32_t> fill(cptr_h.begin(), cptr_h.end() - 1);
+        for (int64_t d = 0; d < Td; ++d) {
+            const int32_t t = h->dperm[d];
+            dcount_h[d] = fill[t] == cptr_h[t];
+            clist_h[fill[t]++] = (int32_t)d;
+        }
     }
     auto seg_group = [&](int64_t v) { return v % h->ngroups; };
     auto seg_slice = [&](int64_t v) { return v / h->ngroups; };
     // Host-side packing of the device layout: 32-bit offsets and packed (row, col).
-    std::vector<int32_t> trp(h->nrb + 1), tptr(T + 1);
-    for (int64_t i = 0; i <= h->nrb; ++i) trp[i] = (int32_t)A->tile_row_ptr[i];
-    for (int64_t i = 0; i <= T; ++i) tptr[i] = (int32_t)D->tile_nnz_ptr[i];
+    std::vector<int32_t> trp(h->nrb + 1), tptr(Td + 1);
+    for (int64_t i = 0; i <= h->nrb; ++i) trp[i] = (int32_t)A->tile_row_ptr[i];  // canonical
+    for (int64_t i = 0; i <= Td; ++i) tptr[i] = (int32_t)D->tile_nnz_ptr[i];
     std::vector<uint8_t> meta8;
     std::vector<uint16_t> meta16;
     if (h->meta16) {
@@ -1056,7 +1173,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     // that nonzero q+1 of the window starts a tile; the batch's end counts as
     // the start of the sentinel (tile index nt), which is also where padding
     // records point.
-    std::vector<int2> tent(std::max<int64_t>(T, 1), make_int2(0, 0));
+    std::vector<int2> tent(std::max<int64_t>(Td, 1), make_int2(0, 0));
     std::vector<uint64_t> win_mask(std::max<int64_t>(h->nwin, 1), 0);
     std::vector<int32_t> win_tile(std::max<int64_t>(h->nwin, 1), 0);
     mpcg::parallel_for(h->nbatch, [&](int64_t lo, int64_t hi) {
@@ -1076,7 +1193,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
                 int xoff = (int)(D->tile_col_idx[t] * A->C * 8);
                 if (staged)
                     xoff = (int)((std::lower_bound(list, list + bnx[b], D->tile_col_idx[t]) - list) * A->C * 8);
-                tent[t] = make_int2(xoff, (int)((trb[t] % h->G) * A->R * 8));
+                tent[t] = make_int2(xoff, (int)((trb[t] % h->G) * B->R * 8));
             }
             const int64_t kb = D->tile_nnz_ptr[tb], nw = (len + 63) / 64, E = dev::batch_records((int)len, staged);
             int64_t j = 0;
@@ -1130,13 +1247,19 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     TRY(dalloc(h, &h->trp, h->nrb + 1));
     TRY(dalloc(h, &h->win_mask, h->nwin));
     TRY(dalloc(h, &h->win_tile, h->nwin));
-    TRY(dalloc(h, &h->tent, std::max<int64_t>(T, 1)));
+    TRY(dalloc(h, &h->tent, std::max<int64_t>(Td, 1)));
     TRY(dalloc(h, &h->btab, (int64_t)btab.size()));
     TRY(dalloc(h, &h->gbatch, h->nseg + 1));
     TRY(dalloc(h, &h->xcb, (int64_t)xcb.size()));
-    TRY(dalloc(h, &h->tcol, T));
-    TRY(dalloc(h, &h->tptr, T + 1));
-    TRY(dalloc(h, &h->map, T));
+    TRY(dalloc(h, &h->tcol, Td));
+    TRY(dalloc(h, &h->tptr, Td + 1));
+    TRY(dalloc(h, &h->map, Td));
+    TRY(dalloc(h, &h->trow, std::max<int64_t>(Td, 1)));
+    if (!cptr_h.empty()) {
+        TRY(dalloc(h, &h->cptr, T + 1));
+        TRY(dalloc(h, &h->clist, Td));
+        TRY(dalloc(h, &h->dcount, Td));
+    }
     if (h->meta16) {
         uint16_t* m = nullptr;
         TRY(dalloc(h, &m, nnz));
@@ -1166,7 +1289,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     } free_vlow{vlow};
     TRY(dalloc(h, &h->planes, h->planes_bytes));
     TRY(dalloc(h, &h->packed, h->packed_bytes));
-    TRY(dalloc(h, &h->toff, std::max<int64_t>(T, 1)));
+    TRY(dalloc(h, &h->toff, std::max<int64_t>(Td, 1)));
     TRY(dalloc(h, &h->dirty, std::max<int64_t>(h->nbatch, 1)));
     // CG vectors padded with zeros to an even length (the vector kernels work
     // in 16-byte pairs); the padding entry stays zero, as every update of it
@@ -1222,7 +1345,8 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
         (e = hipMemcpyAsync(h->btab, btab.data(), sizeof(int32_t) * btab.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->gbatch, gbatch.data(), sizeof(int32_t) * gbatch.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->xcb, xcb.data(), sizeof(int32_t) * xcb.size(), hipMemcpyHostToDevice, s)) ||
-        (e = hipMemcpyAsync(h->tcol, D->tile_col_idx.data(), sizeof(int32_t) * T, hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->tcol, D->tile_col_idx.data(), sizeof(int32_t) * Td, hipMemcpyHostToDevice, s)) ||
+        (e = hipMemcpyAsync(h->trow, trb.data(), sizeof(int32_t) * Td, hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->tptr, tptr.data(), sizeof(int32_t) * tptr.size(), hipMemcpyHostToDevice, s)) ||
         (e = hipMemcpyAsync(h->meta, h->meta16 ? (const void*)meta16.data() : (const void*)meta8.data(),
                             (h->meta16 ? 2 : 1) * (size_t)nnz, hipMemcpyHostToDevice, s)) ||
@@ -1235,15 +1359,22 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     if (h->jacobi &&
         (e = hipMemcpyAsync(h->dinv, dinv_h.data(), sizeof(double) * n, hipMemcpyHostToDevice, s)))
         return dev_err(e, "upload");
+    if (!cptr_h.empty() &&
+        ((e = hipMemcpyAsync(h->cptr, cptr_h.data(), sizeof(int32_t) * cptr_h.size(), hipMemcpyHostToDevice, s)) ||
+         (e = hipMemcpyAsync(h->clist, clist_h.data(), sizeof(int32_t) * Td, hipMemcpyHostToDevice, s)) ||
+         (e = hipMemcpyAsync(h->dcount, dcount_h.data(), Td, hipMemcpyHostToDevice, s))))
+        return dev_err(e, "upload");
     if (precision_map) {
-        if (h->S > 1) {
-            std::vector<uint8_t> dm(T);
-            for (int64_t d = 0; d < T; ++d) dm[d] = precision_map[h->dperm[d]];
-            if ((e = hipMemcpy(h->map, dm.data(), T, hipMemcpyHostToDevice))) return dev_err(e, "upload");
+        if (!h->dperm.empty()) {
+            std::vector<uint8_t> dm(Td);
+            for (int64_t d = 0; d < Td; ++d) dm[d] = precision_map[h->dperm[d]];
+            if ((e = hipMemcpyAsync(h->map, dm.data(), Td, hipMemcpyHostToDevice, s)) ||
+                (e = hipStreamSynchronize(s)))
+                return dev_err(e, "upload");
         } else if ((e = hipMemcpyAsync(h->map, precision_map, T, hipMemcpyHostToDevice, s))) {
             return dev_err(e, "upload");
         }
-    } else if ((e = hipMemsetAsync(h->map, 0, T, s))) {
+    } else if ((e = hipMemsetAsync(h->map, 0, Td, s))) {
         return dev_err(e, "map");
     }
     if ((e = hipMemsetAsync(h->dirty, 0, (size_t)std::max<int64_t>(h->nbatch, 1), s)) ||
@@ -1309,10 +1440,10 @@ extern "C" int cg_set_precision_map(cg_handle* h, const uint8_t* map, int32_t on
     for (int64_t t = 0; t < h->T; ++t)
         if (map[t] > 2)
             return fail(CG_EINVAL, "cg_set_precision_map: map[" + std::to_string(t) + "] is not 0, 1 or 2");
-    if (h->S > 1) {  // device order of the tiles
-        std::vector<uint8_t> dm(h->T);
-        for (int64_t d = 0; d < h->T; ++d) dm[d] = map[h->dperm[d]];
-        HIP_CHECK(hipMemcpy(h->map, dm.data(), h->T, hipMemcpyHostToDevice));
+    if (!h->dperm.empty()) {  // device order of the tiles
+        std::vector<uint8_t> dm(h->Td);
+        for (int64_t d = 0; d < h->Td; ++d) dm[d] = map[h->dperm[d]];
+        HIP_CHECK(hipMemcpy(h->map, dm.data(), h->Td, hipMemcpyHostToDevice));
     } else {
         HIP_CHECK(hipMemcpy(h->map, map, h->T, hipMemcpyHostToDevice));
     }
@@ -1332,16 +1463,16 @@ extern "C" int cg_get_active_map(const cg_handle* h, uint8_t* out) {
     }
     if (h->sched == kSchedPMag) {  // the column-block codes last computed, per tile
         std::vector<uint8_t> code(std::max<int64_t>(h->ncb, 1));
-        std::vector<int32_t> tcol(std::max<int64_t>(h->T, 1));
+        std::vector<int32_t> tcol(std::max<int64_t>(h->Td, 1));
         HIP_CHECK(hipMemcpy(code.data(), h->cbcode, h->ncb, hipMemcpyDeviceToHost));
-        if (h->T) HIP_CHECK(hipMemcpy(tcol.data(), h->tcol, sizeof(int32_t) * h->T, hipMemcpyDeviceToHost));
-        for (int64_t t = 0; t < h->T; ++t) out[t] = code[tcol[t]];
+        if (h->Td) HIP_CHECK(hipMemcpy(tcol.data(), h->tcol, sizeof(int32_t) * h->Td, hipMemcpyDeviceToHost));
+        for (int64_t d = 0; d < h->Td; ++d) out[h->dperm.empty() ? d : h->dperm[d]] = code[tcol[d]];
         return CG_OK;
     }
-    if (h->S > 1) {  // device order of the tiles
-        std::vector<uint8_t> dm(h->T);
-        HIP_CHECK(hipMemcpy(dm.data(), h->map, h->T, hipMemcpyDeviceToHost));
-        for (int64_t d = 0; d < h->T; ++d) out[h->dperm[d]] = dm[d];
+    if (!h->dperm.empty()) {  // device order of the tiles (the pieces of a tile agree)
+        std::vector<uint8_t> dm(h->Td);
+        HIP_CHECK(hipMemcpy(dm.data(), h->map, h->Td, hipMemcpyDeviceToHost));
+        for (int64_t d = 0; d < h->Td; ++d) out[h->dperm[d]] = dm[d];
         return CG_OK;
     }
     HIP_CHECK(hipMemcpy(out, h->map, h->T, hipMemcpyDeviceToHost));
@@ -1353,14 +1484,15 @@ extern "C" int cg_map_from_magnitude(cg_handle* h, double t_bf16, double t_fp32)
     if (!h) return fail(CG_EINVAL, "cg_map_from_magnitude: h is NULL");
     HIP_CHECK(order_after_user(h));
     if (!(t_bf16 <= t_fp32)) return fail(CG_EINVAL, "cg_map_from_magnitude: need t_bf16 <= t_fp32");
-    if (h->S > 1) return fail(CG_EINVAL, "cg_map_from_magnitude: not available with column slices");
     HIP_CHECK(hipMemset(h->scratch_u64, 0, sizeof(unsigned long long)));
-    const int g = grid_for(h->T, 1, 8192);
-    hipLaunchKernelGGL(dev::diag_absmax_kernel, dim3(g), dim3(dev::kBlock), 0, h->stream, h->trp, h->tcol,
-                       h->tptr, (const void*)h->meta, h->meta16 ? 1 : 0, h->v64, (int32_t)h->nrb,
-                       (int32_t)h->T, h->R, h->C, h->scratch_u64);
-    hipLaunchKernelGGL(dev::magnitude_map_kernel, dim3(g), dim3(dev::kBlock), 0, h->stream, h->tptr, h->v64,
-                       (int32_t)h->T, (const unsigned long long*)h->scratch_u64, t_bf16, t_fp32, h->map);
+    hipLaunchKernelGGL(dev::diag_absmax_kernel, dim3(grid_for(h->Td, 1, 8192)), dim3(dev::kBlock), 0, h->stream,
+                       h->trow, h->tcol, h->tptr, (const void*)h->meta, h->meta16 ? 1 : 0, h->v64,
+                       (int32_t)h->Td, h->Rd, h->C, h->scratch_u64);
+    // Per canonical tile over its pieces (slabs), else per device tile.
+    const int64_t units = h->cptr ? h->T : h->Td;
+    hipLaunchKernelGGL(dev::magnitude_map_kernel, dim3(grid_for(units, 1, 8192)), dim3(dev::kBlock), 0, h->stream,
+                       h->tptr, h->v64, (int32_t)units, (const int32_t*)h->cptr, (const int32_t*)h->clist,
+                       (const unsigned long long*)h->scratch_u64, t_bf16, t_fp32, h->map);
     HIP_CHECK(hipGetLastError());
     HIP_CHECK(repack(h));
     h->sched = kSchedStatic;
@@ -1391,14 +1523,19 @@ extern "C" int cg_set_schedule_tile_rule(cg_handle* h, int32_t period, const dou
     mpcg::clear_error();
     if (!h || !scores) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: NULL argument");
     HIP_CHECK(order_after_user(h));
-    if (h->S > 1) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: not available with column slices");
     if (period < 1) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: period must be >= 1");
     if (!(lo <= hi)) return fail(CG_EINVAL, "cg_set_schedule_tile_rule: need lo <= hi");
     if (!h->scores) {
-        int rc = dalloc(h, &h->scores, h->T);
+        int rc = dalloc(h, &h->scores, std::max<int64_t>(h->Td, 1));
         if (rc != CG_OK) return rc;
     }
-    HIP_CHECK(hipMemcpy(h->scores, scores, sizeof(double) * h->T, hipMemcpyHostToDevice));
+    if (!h->dperm.empty()) {  // every device tile takes its canonical tile's score
+        std::vector<double> ds(h->Td);
+        for (int64_t d = 0; d < h->Td; ++d) ds[d] = scores[h->dperm[d]];
+        HIP_CHECK(hipMemcpy(h->scores, ds.data(), sizeof(double) * h->Td, hipMemcpyHostToDevice));
+    } else {
+        HIP_CHECK(hipMemcpy(h->scores, scores, sizeof(double) * h->T, hipMemcpyHostToDevice));
+    }
     h->period = period;
     h->hi = hi;
     h->lo = lo;
@@ -1410,16 +1547,18 @@ extern "C" int cg_set_schedule_pmag(cg_handle* h, double lo, double hi, int32_t 
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_set_schedule_pmag: h is NULL");
     HIP_CHECK(order_after_user(h));
-    if (h->S > 1) return fail(CG_EINVAL, "cg_set_schedule_pmag: not available with column slices");
     if (std::isnan(lo) || std::isnan(hi) || !(lo <= hi))
         return fail(CG_EINVAL, "cg_set_schedule_pmag: need lo <= hi (no NaN)");
     if (period < 1) return fail(CG_EINVAL, "cg_set_schedule_pmag: period must be >= 1");
     if (!h->cbcode) {
         h->ncb = (h->n + h->C - 1) / h->C;
-        std::vector<int32_t> tcol(std::max<int64_t>(h->T, 1));
-        if (h->T) HIP_CHECK(hipMemcpy(tcol.data(), h->tcol, sizeof(int32_t) * h->T, hipMemcpyDeviceToHost));
-        std::vector<int32_t> tpcb(h->ncb, 0);
-        for (int64_t t = 0; t < h->T; ++t) ++tpcb[tcol[t]];
+        std::vector<int32_t> tcol(std::max<int64_t>(h->Td, 1));
+        if (h->Td) HIP_CHECK(hipMemcpy(tcol.data(), h->tcol, sizeof(int32_t) * h->Td, hipMemcpyDeviceToHost));
+        std::vector<uint8_t> dcount(h->dcount ? h->Td : 0);
+        if (h->dcount) HIP_CHECK(hipMemcpy(dcount.data(), h->dcount, h->Td, hipMemcpyDeviceToHost));
+        std::vector<int32_t> tpcb(h->ncb, 0);  // canonical tiles per column block
+        for (int64_t d = 0; d < h->Td; ++d)
+            if (!h->dcount || dcount[d]) ++tpcb[tcol[d]];
         int rc = dalloc(h, &h->cbcode, h->ncb);
         if (rc == CG_OK) rc = dalloc(h, &h->tpcb, h->ncb);
         if (rc != CG_OK) return rc;
@@ -1466,7 +1605,7 @@ extern "C" int cg_record_window_maps(cg_handle* h, int32_t cap) {
         h->winmap_cap = 0;
     }
     if (cap > 0) {
-        const int rc = dalloc(h, &h->winmaps, (int64_t)cap * h->T);
+        const int rc = dalloc(h, &h->winmaps, (int64_t)cap * h->Td);
         if (rc != CG_OK) return rc;
         h->winmap_cap = cap;
     }
@@ -1482,7 +1621,16 @@ extern "C" int cg_get_window_maps(const cg_handle* h, int32_t cap, uint8_t* out)
     HIP_CHECK(hipMemcpy(&hs, h->st, sizeof(hs), hipMemcpyDeviceToHost));
     const int64_t avail = std::min<int64_t>(hs.ntrace, h->winmap_cap);
     const int64_t m = std::min<int64_t>(avail, std::max(cap, 0));
-    if (m > 0 && out) HIP_CHECK(hipMemcpy(out, h->winmaps, (size_t)(m * h->T), hipMemcpyDeviceToHost));
+    if (m > 0 && out) {
+        if (!h->dperm.empty()) {  // device order of the tiles (the pieces of a tile agree)
+            std::vector<uint8_t> dm((size_t)(m * h->Td));
+            HIP_CHECK(hipMemcpy(dm.data(), h->winmaps, dm.size(), hipMemcpyDeviceToHost));
+            for (int64_t w = 0; w < m; ++w)
+                for (int64_t d = 0; d < h->Td; ++d) out[w * h->T + h->dperm[d]] = dm[w * h->Td + d];
+        } else {
+            HIP_CHECK(hipMemcpy(out, h->winmaps, (size_t)(m * h->T), hipMemcpyDeviceToHost));
+        }
+    }
     return (int)avail;
 }
 
@@ -1639,8 +1787,8 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
     HIP_CHECK(hipGetLastError());
     const bool static_map = h->sched == kSchedStatic;
     if (static_map) {
-        hipLaunchKernelGGL(dev::map_count_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, s, h->map, h->T,
-                           h->trace_k, h->trace_counts);
+        hipLaunchKernelGGL(dev::map_count_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, s, h->map,
+                           (const uint8_t*)h->dcount, h->Td, h->trace_k, h->trace_counts);
     }
 
     // Small systems: every iteration in one launch. Otherwise iterate in
@@ -1738,63 +1886,95 @@ extern "C" int cg_export_column_scale(const cg_handle* h, int32_t* out) {
 }
 
 extern "C" int cg_export_layout(const cg_handle* h, int64_t* tile_row_ptr, int32_t* tile_col_idx,
-                                int64_t* tile_nnz_ptr, uint8_t* row_idx, uint8_t* col_local, double* val64,
+                                int64_t* tile_nnz_ptr, uint16_t* row_idx, uint8_t* col_local, double* val64,
                                 float* val32, uint16_t* bf16) {
     mpcg::clear_error();
     if (!h) return fail(CG_EINVAL, "cg_export_layout: h is NULL");
-    const int64_t T = h->T, nnz = h->nnz;
-    if (tile_row_ptr) {
-        std::vector<int32_t> t(h->nrb + 1);
-        HIP_CHECK(hipMemcpy(t.data(), h->trp, sizeof(int32_t) * t.size(), hipMemcpyDeviceToHost));
-        for (size_t i = 0; i < t.size(); ++i) tile_row_ptr[i] = t[i];
-    }
-    // Device order of tiles and nonzeros; with column slices it is mapped back
-    // to the canonical order (device tile d is canonical tile dperm[d]).
-    std::vector<int32_t> dt(T + 1);
+    const int64_t T = h->T, Td = h->Td, nnz = h->nnz;
+    std::vector<int32_t> trp(h->nrb + 1);  // canonical tile row pointers
+    HIP_CHECK(hipMemcpy(trp.data(), h->trp, sizeof(int32_t) * trp.size(), hipMemcpyDeviceToHost));
+    if (tile_row_ptr)
+        for (size_t i = 0; i < trp.size(); ++i) tile_row_ptr[i] = trp[i];
+    std::vector<int32_t> dt(Td + 1), tcol(std::max<int64_t>(Td, 1)), trow(std::max<int64_t>(Td, 1));
     HIP_CHECK(hipMemcpy(dt.data(), h->tptr, sizeof(int32_t) * dt.size(), hipMemcpyDeviceToHost));
-    const bool sliced = h->S > 1;
-    std::vector<int64_t> ct;  // canonical tile pointers
-    if (sliced) {
+    if (Td) {
+        HIP_CHECK(hipMemcpy(tcol.data(), h->tcol, sizeof(int32_t) * Td, hipMemcpyDeviceToHost));
+        HIP_CHECK(hipMemcpy(trow.data(), h->trow, sizeof(int32_t) * Td, hipMemcpyDeviceToHost));
+    }
+    // Row offsets (from the device tile's row block) and local columns.
+    std::vector<uint16_t> r(std::max<int64_t>(nnz, 1));
+    std::vector<uint8_t> c(std::max<int64_t>(nnz, 1));
+    if (h->meta16) {
+        std::vector<uint16_t> m(std::max<int64_t>(nnz, 1));
+        HIP_CHECK(hipMemcpy(m.data(), h->meta, 2 * (size_t)nnz, hipMemcpyDeviceToHost));
+        for (int64_t k = 0; k < nnz; ++k) {
+            r[k] = (uint16_t)(m[k] >> 8);
+            c[k] = (uint8_t)(m[k] & 255);
+        }
+    } else {
+        std::vector<uint8_t> m(std::max<int64_t>(nnz, 1));
+        HIP_CHECK(hipMemcpy(m.data(), h->meta, (size_t)nnz, hipMemcpyDeviceToHost));
+        for (int64_t k = 0; k < nnz; ++k) {
+            r[k] = (uint16_t)(m[k] >> 4);
+            c[k] = (uint8_t)(m[k] & 15);
+        }
+    }
+    // Device order of tiles and nonzeros; with column slices or slabs it is
+    // mapped back to the canonical order: device tile d is (a piece of)
+    // canonical tile dperm[d]; a piece's rows move by its slab's offset in the
+    // row block, and the pieces of a tile merge column by column.
+    const bool reordered = !h->dperm.empty();
+    std::vector<int64_t> ct;   // canonical tile pointers
+    std::vector<int64_t> pos;  // canonical position of every device nonzero
+    if (reordered) {
         ct.assign(T + 1, 0);
-        for (int64_t d = 0; d < T; ++d) ct[h->dperm[d] + 1] = dt[d + 1] - dt[d];
-        for (int64_t t = 0; t < T; ++t) ct[t + 1] += ct[t];
+        std::vector<int32_t> cp(T + 1, 0), cl(Td), crb(std::max<int64_t>(T, 1), 0);
+        for (int64_t d = 0; d < Td; ++d) {
+            ct[h->dperm[d] + 1] += dt[d + 1] - dt[d];
+            ++cp[h->dperm[d] + 1];
+        }
+        for (int64_t t = 0; t < T; ++t) {
+            ct[t + 1] += ct[t];
+            cp[t + 1] += cp[t];
+        }
+        {
+            std::vector<int32_t> fill(cp.begin(), cp.end() - 1);
+            for (int64_t d = 0; d < Td; ++d) cl[fill[h->dperm[d]]++] = (int32_t)d;
+        }
+        for (int64_t I = 0; I < h->nrb; ++I)
+            for (int64_t t = trp[I]; t < trp[I + 1]; ++t) crb[t] = (int32_t)I;
+        pos.assign(std::max<int64_t>(nnz, 1), 0);
+        mpcg::parallel_for(T, [&](int64_t lo, int64_t hi) {
+            std::vector<std::pair<int64_t, int64_t>> ent;  // (local column, canonical row offset) key, device index
+            for (int64_t t = lo; t < hi; ++t) {
+                ent.clear();
+                for (int32_t q = cp[t]; q < cp[t + 1]; ++q) {
+                    const int64_t d = cl[q];
+                    const int64_t off = (int64_t)trow[d] * h->Rd - (int64_t)crb[t] * h->R;
+                    for (int64_t k = dt[d]; k < dt[d + 1]; ++k) {
+                        r[k] = (uint16_t)(r[k] + off);
+                        ent.emplace_back(((int64_t)c[k] << 20) | r[k], k);
+                    }
+                }
+                std::sort(ent.begin(), ent.end());
+                for (size_t i = 0; i < ent.size(); ++i) pos[ent[i].second] = ct[t] + (int64_t)i;
+            }
+        });
     }
     // Copies a per-nonzero array from device order into canonical order.
     auto to_canonical = [&](const char* src, char* dst, size_t w) {
-        if (!sliced) {
+        if (!reordered) {
             std::memcpy(dst, src, w * (size_t)nnz);
             return;
         }
-        for (int64_t d = 0; d < T; ++d)
-            std::memcpy(dst + w * (size_t)ct[h->dperm[d]], src + w * (size_t)dt[d], w * (size_t)(dt[d + 1] - dt[d]));
+        for (int64_t k = 0; k < nnz; ++k) std::memcpy(dst + w * (size_t)pos[k], src + w * (size_t)k, w);
     };
-    if (tile_col_idx) {
-        std::vector<int32_t> c(std::max<int64_t>(T, 1));
-        if (T) HIP_CHECK(hipMemcpy(c.data(), h->tcol, sizeof(int32_t) * T, hipMemcpyDeviceToHost));
-        for (int64_t d = 0; d < T; ++d) tile_col_idx[sliced ? h->dperm[d] : d] = c[d];
-    }
+    if (tile_col_idx)
+        for (int64_t d = 0; d < Td; ++d) tile_col_idx[reordered ? h->dperm[d] : d] = tcol[d];
     if (tile_nnz_ptr)
-        for (int64_t t = 0; t <= T; ++t) tile_nnz_ptr[t] = sliced ? ct[t] : dt[t];
-    if (row_idx || col_local) {
-        std::vector<uint8_t> r(std::max<int64_t>(nnz, 1)), c(std::max<int64_t>(nnz, 1));
-        if (h->meta16) {
-            std::vector<uint16_t> m(std::max<int64_t>(nnz, 1));
-            HIP_CHECK(hipMemcpy(m.data(), h->meta, 2 * (size_t)nnz, hipMemcpyDeviceToHost));
-            for (int64_t k = 0; k < nnz; ++k) {
-                r[k] = (uint8_t)(m[k] >> 8);
-                c[k] = (uint8_t)(m[k] & 255);
-            }
-        } else {
-            std::vector<uint8_t> m(std::max<int64_t>(nnz, 1));
-            HIP_CHECK(hipMemcpy(m.data(), h->meta, (size_t)nnz, hipMemcpyDeviceToHost));
-            for (int64_t k = 0; k < nnz; ++k) {
-                r[k] = (uint8_t)(m[k] >> 4);
-                c[k] = (uint8_t)(m[k] & 15);
-            }
-        }
-        if (row_idx) to_canonical((const char*)r.data(), (char*)row_idx, 1);
-        if (col_local) to_canonical((const char*)c.data(), (char*)col_local, 1);
-    }
+        for (int64_t t = 0; t <= T; ++t) tile_nnz_ptr[t] = reordered ? ct[t] : dt[t];
+    if (row_idx) to_canonical((const char*)r.data(), (char*)row_idx, 2);
+    if (col_local) to_canonical((const char*)c.data(), (char*)col_local, 1);
     if (val64) {
         std::vector<double> v(std::max<int64_t>(nnz, 1));
         HIP_CHECK(hipMemcpy(v.data(), h->v64, sizeof(double) * nnz, hipMemcpyDeviceToHost));

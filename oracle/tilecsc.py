@@ -39,7 +39,7 @@ class TileCSC:
     tile_row_ptr: np.ndarray  # int64[nRB+1]
     tile_col_idx: np.ndarray  # int32[T]
     tile_nnz_ptr: np.ndarray  # int64[T+1]
-    row_idx: np.ndarray       # uint8[nnz]   (R <= 256)
+    row_idx: np.ndarray       # uint16[nnz]  (R <= 16384)
     col_local: np.ndarray     # uint8[nnz]   local column of every nonzero (C <= 256)
     perm: np.ndarray          # int64[nnz]   canonical position -> CSR position
     val: np.ndarray           # float64[nnz] canonical order
@@ -80,8 +80,8 @@ class TileCSC:
 def build(n: int, indptr: np.ndarray, indices: np.ndarray, data: np.ndarray,
           R: int, C: int) -> TileCSC:
     """Canonical Tile-CSC of a square CSR matrix (sorted, unique column indices)."""
-    if not (1 <= R <= 256 and 1 <= C <= 256):
-        raise ValueError("tile sides must lie in [1, 256]")
+    if not (1 <= R <= 16384 and 1 <= C <= 256):
+        raise ValueError("tile height must lie in [1, 16384] and width in [1, 256]")
     indptr = np.asarray(indptr, dtype=np.int64)
     indices = np.asarray(indices, dtype=np.int64)
     nnz = int(indptr[-1])
@@ -107,7 +107,7 @@ def build(n: int, indptr: np.ndarray, indices: np.ndarray, data: np.ndarray,
     tile_row_ptr = np.zeros(nrb + 1, dtype=np.int64)
     np.cumsum(tiles_per_rb, out=tile_row_ptr[1:])
     return TileCSC(n=n, R=R, C=C, tile_row_ptr=tile_row_ptr, tile_col_idx=tile_col_idx,
-                   tile_nnz_ptr=tile_nnz_ptr, row_idx=r_s.astype(np.uint8),
+                   tile_nnz_ptr=tile_nnz_ptr, row_idx=r_s.astype(np.uint16),
                    col_local=c_s.astype(np.uint8), perm=perm.astype(np.int64),
                    val=np.asarray(data, dtype=np.float64)[perm])
 

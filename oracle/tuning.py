@@ -12,7 +12,8 @@ perfectly even and leaves the device idle). The reading taken here:
   :func:`cv_squared`), so that two candidates a floating-point evaluation
   cannot tell apart are still ordered correctly;
 * a candidate must leave at least ``min_row_blocks`` row blocks, and it must
-  not exceed ``max_R`` (the largest height the kernel supports);
+  not exceed ``max_R`` (by default the largest candidate, so every candidate
+  height the paper lists is admissible);
 * the tuned R is the admissible candidate with the smallest coefficient of
   variation, ties going to the smaller R; with no admissible candidate it is
   the smallest candidate.
@@ -71,7 +72,7 @@ def balance(counts: np.ndarray):
     return math.sqrt(float(cv_squared(c))), float(Fraction(len(c) * int(c.max()), total))
 
 
-def select_height(candidates, max_R: int = 256, min_row_blocks: int = 1024) -> int:
+def select_height(candidates, max_R: int = 16384, min_row_blocks: int = 1024) -> int:
     """The tuned R from (R, counts) pairs in candidate order (Sec. 3.3.3 reading above).
 
     Admissible: R <= max_R and at least ``min_row_blocks`` row blocks. The
@@ -87,7 +88,7 @@ def select_height(candidates, max_R: int = 256, min_row_blocks: int = 1024) -> i
     return best[0] if best is not None else candidates[0][0]
 
 
-def tune_row_height(n: int, indptr, indices, C: int, max_R: int = 256, min_row_blocks: int = 1024,
+def tune_row_height(n: int, indptr, indices, C: int, max_R: int = 16384, min_row_blocks: int = 1024,
                     candidates=CANDIDATES):
     """Tuned R and one table row per candidate: (R, row blocks, tiles, cv, max/mean, admissible)."""
     table, pairs = [], []

@@ -23,6 +23,12 @@ static void print_i32(const char* key, const int32_t* v, int64_t n) {
     printf("\n");
 }
 
+static void print_u16(const char* key, const uint16_t* v, int64_t n) {
+    printf("%s", key);
+    for (int64_t i = 0; i < n; ++i) printf(" %u", (unsigned)v[i]);
+    printf("\n");
+}
+
 static void print_u8(const char* key, const uint8_t* v, int64_t n) {
     printf("%s", key);
     for (int64_t i = 0; i < n; ++i) printf(" %u", (unsigned)v[i]);
@@ -45,7 +51,7 @@ int main(void) {
     print_i64("tile_row_ptr", v.tile_row_ptr, (v.n + v.R - 1) / v.R + 1);
     print_i32("tile_col_idx", v.tile_col_idx, v.T);
     print_i64("tile_nnz_ptr", v.tile_nnz_ptr, v.T + 1);
-    print_u8("row_idx", v.row_idx, v.nnz);
+    print_u16("row_idx", v.row_idx, v.nnz);
     print_u8("col_local", v.col_local, v.nnz);
     printf("val");
     for (int64_t i = 0; i < v.nnz; ++i) printf(" %.17g", v.val[i]);

@@ -15,7 +15,7 @@ import pytest
 import scipy.sparse as sp
 
 from gen import make_workload, static_map, tile_scores
-from oracle import cg as ocg, rounding as ord_, spmv as ospmv, tilecsc as otc
+from oracle import cg as ocg, maps as omaps, rounding as ord_, spmv as ospmv, tilecsc as otc
 
 pytestmark = pytest.mark.gpu
 
@@ -205,17 +205,33 @@ def test_sliced_cg_with_initial_guess(dev):
     S.close()
 
 
-def test_sliced_handle_rejects_unsupported_rules(dev):
+@pytest.mark.parametrize("slices", [2, 5])
+def test_sliced_handle_runs_every_rule(slices, dev):
+    """The magnitude, tile and max|p| rules on a sliced handle: the device works in
+    slice order, the maps come back in canonical order equal to the oracle's."""
     w = make_workload(3, "small")
     A = w.A
-    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
-    S = mpcg.Solver(L, col_slices=2)
-    with pytest.raises(mpcg.CGError):
-        S.cg_map_from_magnitude(1e-4, 1e-2)
-    with pytest.raises(mpcg.CGError):
-        S.cg_set_schedule_tile_rule(10, tile_scores(L.T, 2), 1e-3, 1e-6)
-    with pytest.raises(mpcg.CGError):
-        S.cg_set_schedule_pmag(1e-9, 1e-8)
+    L, Lo = _both(A, w.R, w.C)
+    S = mpcg.Solver(L, col_slices=slices)
+    x = np.random.default_rng(slices).uniform(-1, 1, A.n)
+    S.cg_map_from_magnitude(1e-4, 1e-2)
+    m = omaps.magnitude_rule(Lo, 1e-4, 1e-2)
+    assert np.array_equal(S.cg_get_active_map(), m) and len(set(m.tolist())) >= 2
+    y = _spmv(S, x, dev)
+    assert np.all(np.abs(y - ospmv.spmv(Lo, A.indptr, A.indices, m, x))
+                  <= 1e-13 * ospmv.abs_bound(A.indptr, A.indices, A.data, x))
+    s = tile_scores(L.T, 2)
+    S.cg_set_schedule_tile_rule(10, s, 1e-3, 1e-6)
+    for rho in (1.0, 3e-3, 2e-5, 1e-12):
+        S.cg_eval_tile_rule(rho)
+        assert np.array_equal(S.cg_get_active_map(), omaps.tile_rule(s, rho, 1e-3, 1e-6)), rho
+    S.cg_set_schedule_pmag(1e-3, 1e-1)
+    xp = x * 10.0 ** np.random.default_rng(1).integers(-5, 1, -(-A.n // w.C))[np.arange(A.n) // w.C]
+    y = _spmv(S, xp, dev)
+    m = omaps.pmag_rule(xp, Lo.C, Lo.tile_col_idx, 1e-3, 1e-1)
+    assert np.array_equal(S.cg_get_active_map(), m) and len(set(m.tolist())) >= 2
+    assert np.all(np.abs(y - ospmv.spmv(Lo, A.indptr, A.indices, m, xp))
+                  <= 1e-13 * ospmv.abs_bound(A.indptr, A.indices, A.data, xp))
     S.close()
     with pytest.raises(mpcg.CGError):
         mpcg.Solver(L, col_slices=65)

@@ -70,7 +70,8 @@ def test_host_layout_matches_oracle_on_workloads(cfg):
     _compare_layout(L_lib, L_or)
 
 
-@pytest.mark.parametrize("R,C", [(1, 1), (3, 5), (16, 16), (32, 32), (64, 16), (256, 256), (100, 7)])
+@pytest.mark.parametrize("R,C", [(1, 1), (3, 5), (16, 16), (32, 32), (64, 16), (256, 256), (100, 7),
+                                 (257, 8), (300, 16), (512, 64), (4096, 32), (16384, 256)])
 def test_host_layout_matches_oracle_random(R, C):
     n = 517
     M = sp.random(n, n, density=0.01, random_state=np.random.RandomState(R * 1000 + C), format="csr")
@@ -99,8 +100,8 @@ def test_host_layout_empty_matrix():
     assert b"no nonzeros" in lib.cg_last_error() and not out.value
 
 
-@pytest.mark.parametrize("case", ["unsorted", "duplicate", "out_of_range", "nan", "bad_R", "bad_C",
-                                  "n0", "rowptr"])
+@pytest.mark.parametrize("case", ["unsorted", "duplicate", "out_of_range", "nan", "bad_R", "bad_R_tall",
+                                  "bad_C", "n0", "rowptr"])
 def test_host_layout_rejects_bad_input(case):
     n = 4
     indptr = np.array([0, 2, 3, 4, 5], np.int64)
@@ -117,6 +118,8 @@ def test_host_layout_rejects_bad_input(case):
         data[2] = np.nan
     elif case == "bad_R":
         R = 0
+    elif case == "bad_R_tall":
+        R = 16385
     elif case == "bad_C":
         C = 257
     elif case == "n0":

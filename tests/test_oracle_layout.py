@@ -72,6 +72,12 @@ CASES = [
     (33, 0.2, 3, 8, 16, (0,)),                 # non-square tiles
     (20, 0.3, 4, 1, 1, ()),                    # 1x1 tiles
     (70, 0.02, 5, 32, 8, (60, 61, 62, 63, 64, 65, 66, 67, 68, 69)),  # empty last row block
+    # Row blocks taller than 256 rows (Sec. 3.3.3 tunes R up to 16384): row
+    # offsets past one byte, a height that is not a power of two, one row
+    # block taller than the matrix.
+    (611, 0.01, 6, 300, 16, tuple(range(250, 290))),
+    (700, 0.006, 7, 512, 64, ()),
+    (530, 0.008, 8, 16384, 32, ()),
 ]
 
 
