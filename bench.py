@@ -402,21 +402,15 @@ def all_workloads(torch, dev, mpcg, cfgs, reps, slices=()):
         vec_bytes = (64 if w.jacobi else 56) * A.n
         rec = {"workload": w.description, "n": A.n, "nnz": A.nnz, "tiles": L.T, "tol": w.tol, "maxit": w.maxit}
         own = w.map_spec["kind"]
+        # default handles (automatic column slices), then one per forced slice count
         runs = [("fp64", None, 0)] + ([("own", own, 0)] if own != "fp64" else [])
-        for ns in slices:  # column-sliced handles (the tile rule needs canonical order)
-            runs += [(f"fp64_slices{ns}", None, ns)] + \
-                ([(f"own_slices{ns}", own, ns)] if own not in ("fp64", "tile_rule") else [])
-        static_own = None  # the magnitude rule's map, set as a fixed map on sliced handles
+        for ns in slices:
+            runs += [(f"fp64_slices{ns}", None, ns)] + ([(f"own_slices{ns}", own, ns)] if own != "fp64" else [])
         for label, kind, ns in runs:
             S = mpcg.Solver(L, np.zeros(L.T, np.uint8), jacobi=w.jacobi, col_slices=ns)
-            if kind == "magnitude" and ns > 0:
-                S.cg_set_precision_map(static_own)
-                m = static_own
-            else:
-                m = np.zeros(L.T, np.uint8) if kind is None else configure_map(S, w, L, mpcg)
-                if kind == "magnitude":
-                    static_own = m
-            r = {"map": "all FP64" if kind is None else kind, "col_slices": ns}
+            m = np.zeros(L.T, np.uint8) if kind is None else configure_map(S, w, L, mpcg)
+            r = {"map": "all FP64" if kind is None else kind, "col_slices_option": ns,
+                 "col_slices": S.cg_get_options()["col_slices"]}
             if m is not None:
                 for _ in range(5):
                     S.cg_spmv(xin, y)
@@ -472,8 +466,11 @@ def tile_shapes(torch, dev, mpcg, cfgs, reps):
     """cg_spmv under the all-FP64 map at the workload's tile shape and at the tuned heights.
 
     The tuned height comes from cg_tune_row_height (paper Sec. 3.3.3) with its
-    defaults (R <= 256, at least 1024 row blocks). Maps are per tile and differ
-    between tilings, so every shape is timed with the FP64 map.
+    defaults (every candidate 32 .. 16384, at least 1024 row blocks). Maps are
+    per tile and differ between tilings, so every shape is timed with the FP64
+    map. A height above 256 runs on the device as slabs of R' rows (R' the
+    largest divisor of R not above 256) whose pieces are the tiles of the
+    R' x C layout: its algorithmic bytes count those pieces.
     """
     from gen import make_workload
 
@@ -505,10 +502,18 @@ def tile_shapes(torch, dev, mpcg, cfgs, reps):
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
-            nbytes = spmv_algorithmic_bytes(L, np.zeros(L.T, np.uint8))
+            Rs, Ld = R, L
+            if R > 256:
+                Rs = max(d for d in range(1, 257) if R % d == 0)
+                Ld = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, Rs, C)
+            nbytes = spmv_algorithmic_bytes(Ld, np.zeros(Ld.T, np.uint8))
+            pieces = Ld.T
+            if Ld is not L:
+                Ld.close()
             gbs = nbytes / (ms * 1e-3) / 1e9
             counts = np.diff(L.tile_row_ptr)
-            rec = {"R": R, "C": C, "shape": label, "tiles": L.T, "spmv_us": round(ms * 1e3, 2),
+            rec = {"R": R, "C": C, "shape": label, "tiles": L.T, "device_rows": Rs, "device_tiles": pieces,
+                   "spmv_us": round(ms * 1e3, 2),
                    "algorithmic_bytes": nbytes, "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                    "row_block_tile_cv": round(float(counts.std() / max(counts.mean(), 1e-300)), 4)}
             res.append(rec)
@@ -657,7 +662,7 @@ def spmv_probe(torch, dev, mpcg, cfgs, slices):
         m = np.zeros(L.T, np.uint8)
         xin = torch.from_numpy(np.random.default_rng(7).uniform(-1, 1, A.n)).to(dev)
         y = torch.empty_like(xin)
-        for ns in [0] + list(slices):
+        for ns in [1] + list(slices):
             S = mpcg.Solver(L, m, col_slices=ns)
             for _ in range(5):
                 S.cg_spmv(xin, y)

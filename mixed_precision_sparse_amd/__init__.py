@@ -270,6 +270,13 @@ class Solver:
     def device_bytes(self) -> int:
         return int(_lib.load().cg_device_bytes(self._h))
 
+    def cg_get_options(self) -> dict:
+        """The options the handle runs with, after its automatic choices (cg_get_options)."""
+        o = _lib.cg_options()
+        check(_lib.load().cg_get_options(self._h, ct.byref(o)))
+        return {k: int(getattr(o, k)) for k in ("jacobi", "window", "use_graph", "p1", "col_slices",
+                                                 "single_block", "stage_x")}
+
     def close(self):
         if self._h:
             _lib.load().cg_destroy(self._h)

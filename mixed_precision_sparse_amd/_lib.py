@@ -67,6 +67,7 @@ SIGNATURES = {
     "cg_export_layout": (ct.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp]),
     "cg_export_column_scale": (ct.c_int, [vp, vp]),
     "cg_tune_row_height": (ct.c_int, [i64, vp, vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp]),
+    "cg_get_options": (ct.c_int, [vp, ct.POINTER(cg_options)]),
     "cg_get_sizes": (ct.c_int, [vp, ct.POINTER(i64), ct.POINTER(i64), ct.POINTER(i64),
                                 ct.POINTER(i32), ct.POINTER(i32)]),
     "cg_device_bytes": (i64, [vp]),

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -824,6 +825,34 @@ void split_slabs(const cg_tilecsc& A, int Rs, cg_tilecsc& B, std::vector<int32_t
     });
 }
 
+// Automatic column slices: S = ceil(8n / L2) (at most 64) when x is larger
+// than one XCD's L2 and at least half of the nonzeros lie more than L2 / 16
+// entries from the diagonal (their gathers leave an L2-sized window around
+// the rows being swept); else 1.
+int auto_slices(const cg_tilecsc& A, int device) {
+    int64_t l2 = 4 << 20;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.l2CacheSize > 0) l2 = prop.l2CacheSize;
+    else (void)hipGetLastError();
+    if (8 * A.n <= l2 || A.nnz() == 0) return 1;
+    const int64_t near = l2 / 16;
+    std::atomic<int64_t> far{0};
+    mpcg::parallel_for(A.nrb, [&](int64_t lo, int64_t hi) {
+        int64_t f = 0;
+        for (int64_t I = lo; I < hi; ++I)
+            for (int64_t t = A.tile_row_ptr[I]; t < A.tile_row_ptr[I + 1]; ++t) {
+                const int64_t c0 = (int64_t)A.tile_col_idx[t] * A.C;
+                for (int64_t k = A.tile_nnz_ptr[t]; k < A.tile_nnz_ptr[t + 1]; ++k) {
+                    const int64_t i = I * A.R + A.row_idx[k], j = c0 + A.col_local[k];
+                    f += (i > j ? i - j : j - i) > near;
+                }
+            }
+        far += f;
+    });
+    if (2 * far.load() < A.nnz()) return 1;
+    return (int)std::min<int64_t>(64, (8 * A.n + l2 - 1) / l2);
+}
+
 // Device order of the tiles with S column slices: slice s holds the column
 // blocks [ceil(s ncb / S), ceil((s+1) ncb / S)); the tiles are listed slice by
 // slice, then row group by row group (segment s * ngroups + g), then in
@@ -968,19 +997,21 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     if (Td > INT32_MAX) return bail(fail(CG_EINVAL, "cg_create: more than 2^31 - 1 device tiles"));
     // Padding stores the sentinel row offset R, which needs the 16-bit form.
     h->meta16 = !(B->R <= 16 && B->C <= 16) || (p1 & CG_P1_PAD_COLUMNS);
+    h->S = 0;  // automatic unless opt says otherwise
     if (opt) {
         h->jacobi = opt->jacobi != 0;
         if (opt->window > 0) h->window = std::min(opt->window, 4096);
         if (opt->use_graph >= 0) h->use_graph = opt->use_graph != 0;
         if (opt->col_slices < 0 || opt->col_slices > 64)
             return bail(fail(CG_EINVAL, "cg_create: col_slices must lie in [0, 64]"));
-        h->S = std::max(1, opt->col_slices);
+        h->S = opt->col_slices;
         if (opt->single_block < -1 || opt->single_block > 1)
             return bail(fail(CG_EINVAL, "cg_create: single_block must be -1, 0 or 1"));
         h->single_block = opt->single_block;
         if (opt->stage_x < 0 || opt->stage_x > 1) return bail(fail(CG_EINVAL, "cg_create: stage_x must be 0 or 1"));
         h->stage_x = opt->stage_x != 0;
     }
+    if (h->S == 0) h->S = auto_slices(*A, h->device);
     // Row blocks per wavefront: the largest of 32, 64, 128, 256 rows whose row
     // groups hold at most one batch of tiles on average (at least one row block).
     // A small matrix would then leave too few groups (wavefronts) to spread its
@@ -1409,6 +1440,20 @@ extern "C" int cg_destroy(cg_handle* h) {
     if (h->ev_user) (void)hipEventDestroy(h->ev_user);
     if (h->stream) (void)hipStreamDestroy(h->stream);
     delete h;  // frees device buffers
+    return CG_OK;
+}
+
+extern "C" int cg_get_options(const cg_handle* h, cg_options* out) {
+    mpcg::clear_error();
+    if (!h || !out) return fail(CG_EINVAL, "cg_get_options: NULL argument");
+    *out = cg_options{};
+    out->jacobi = h->jacobi ? 1 : 0;
+    out->window = h->window;
+    out->use_graph = h->use_graph ? 1 : 0;
+    out->p1 = h->p1;
+    out->col_slices = h->S;
+    out->single_block = small_layout(h) ? 1 : -1;
+    out->stage_x = h->stage_doubles > 0 ? 1 : 0;
     return CG_OK;
 }
 

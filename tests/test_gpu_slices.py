@@ -235,3 +235,35 @@ def test_sliced_handle_runs_every_rule(slices, dev):
     S.close()
     with pytest.raises(mpcg.CGError):
         mpcg.Solver(L, col_slices=65)
+
+
+def test_automatic_slices(dev):
+    """col_slices = 0 picks S = ceil(8n / L2 of one XCD) for a matrix whose gathers scatter
+    far from the diagonal, and no slices for a banded one; the sliced handle's product
+    still matches the oracle's."""
+    props = torch.cuda.get_device_properties(0)
+    l2 = getattr(props, "L2_cache_size", 0) or (4 << 20)
+    n = l2 // 2  # x is 4 L2; near = n / 8 entries
+    log(f"L2 of one XCD as reported: {l2} bytes; n = {n}")
+    rng = np.random.default_rng(5)
+    # six random columns per row: 6/7 (7/8)^2 of the entries lie farther than n / 8 from the diagonal
+    rows = np.repeat(np.arange(n), 6)
+    cols = rng.integers(0, n, rows.size)
+    M = sp.csr_matrix((rng.standard_normal(rows.size), (rows, cols)), shape=(n, n)) + sp.eye(n)
+    A = _M(M)
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, 16, 16)
+    S = mpcg.Solver(L)
+    want = min(64, -(-8 * n // l2))
+    assert S.cg_get_options()["col_slices"] == want == 4
+    x = rng.uniform(-1, 1, n)
+    y = _spmv(S, x, dev)
+    Lo = otc.build(A.n, A.indptr, A.indices, A.data, 16, 16)
+    m = np.zeros(Lo.T, np.uint8)
+    assert np.all(np.abs(y - ospmv.spmv(Lo, A.indptr, A.indices, m, x))
+                  <= 1e-13 * ospmv.abs_bound(A.indptr, A.indices, A.data, x))
+    S.close()
+    assert mpcg.Solver(L, col_slices=1).cg_get_options()["col_slices"] == 1
+    # banded: every entry within 8 of the diagonal
+    B = _M(sp.diags([np.full(n - abs(k), 1.0 + abs(k)) for k in range(-8, 9)], list(range(-8, 9)), format="csr"))
+    LB = mpcg.cg_tilecsc_from_csr(B.n, B.indptr, B.indices, B.data, 16, 16)
+    assert mpcg.Solver(LB).cg_get_options()["col_slices"] == 1
