@@ -258,6 +258,7 @@ def main():
 
     def run_solves(solver, steps):
         its, ks = 0, []
+        status, K, hist = None, 0, None
         torch.cuda.synchronize()
         t = time.perf_counter()
         for _ in range(steps):
