@@ -1662,7 +1662,8 @@ __device__ inline void block_counts_out(unsigned c0, unsigned c1, unsigned c2, i
 // from its score and rho_k, and the window's precision counts are recorded.
 // One wavefront per SpMV batch (lane l: the batch's tile l); a batch with a
 // tile whose code changed is marked dirty, so that the repack that follows
-// rebuilds only those batches' packed values.
+// rebuilds only those batches' packed values. The grid is sized to the
+// batches; block b adds its counts to slot b % kTraceBlocks of the entry.
 __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
     State* st = a.st;
     double rho = a.rho;
@@ -1696,7 +1697,10 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
         if (__any(changed) && lane == 0) a.dirty[b] = 1;
     }
     if (slot >= 0) {
-        block_counts_out(c0, c1, c2, a.trace_counts + ((size_t)slot * kTraceBlocks + blockIdx.x) * 3);
+        const unsigned t = block_count3(c0, c1, c2);
+        if (threadIdx.x < 3)
+            atomicAdd(a.trace_counts + ((size_t)slot * kTraceBlocks + blockIdx.x % kTraceBlocks) * 3 + threadIdx.x,
+                      (int32_t)t);
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             a.trace_k[slot] = st->k;
             st->ntrace = slot + 1;

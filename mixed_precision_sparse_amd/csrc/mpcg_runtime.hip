@@ -438,6 +438,11 @@ dev::VecArgs vec_args(cg_handle* h, const double* b, const double* x0) {
     return a;
 }
 
+// Tile-rule grid: one wavefront per SpMV batch, at most 8192 blocks.
+int tile_rule_grid(const cg_handle* h) {
+    return (int)std::max<int64_t>(1, std::min<int64_t>((h->nbatch + dev::kWavesPerBlock - 1) / dev::kWavesPerBlock, 8192));
+}
+
 dev::MapArgs map_args(cg_handle* h, double rho, int solve) {
     dev::MapArgs a{};
     a.map = h->map;
@@ -514,7 +519,7 @@ int solve_window(const cg_handle* h) {
 void enqueue_iteration(cg_handle* h, int i, hipStream_t s, bool rule_at_end = false) {
     if (h->sched == kSchedTileRule && i % h->period == 0) {
         dev::MapArgs ma = map_args(h, 0.0, 1);
-        hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, s, ma);
+        hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(tile_rule_grid(h)), dim3(dev::kBlock), 0, s, ma);
         launch_repack(h, 1, s);
     }
     dev::SpmvArgs sa = spmv_args(h, h->p, h->S > 1 ? h->qpart : h->q, &h->st->uprec);
@@ -1695,7 +1700,7 @@ extern "C" int cg_eval_tile_rule(cg_handle* h, double rho) {
     HIP_CHECK(order_after_user(h));
     if (h->sched != kSchedTileRule) return fail(CG_EINVAL, "cg_eval_tile_rule: no tile rule is set");
     dev::MapArgs ma = map_args(h, rho, 0);
-    hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(dev::kTraceBlocks), dim3(dev::kBlock), 0, h->stream, ma);
+    hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(tile_rule_grid(h)), dim3(dev::kBlock), 0, h->stream, ma);
     HIP_CHECK(hipGetLastError());
     HIP_CHECK(repack(h));
     return CG_OK;
