@@ -179,13 +179,21 @@ def main():
                     help="no GPU: read rocprofv3 counter CSVs of --pmc-probe runs (directories holding "
                          "FETCH_SIZE, WRITE_SIZE and optionally TCC_HIT_sum/TCC_MISS_sum), scale them by the "
                          "copy reference, and write " + os.path.relpath(TRAFFIC_FILE, ROOT))
+    ap.add_argument("--traffic-groups", default="",
+                    help="with --traffic-from: comma-separated names of the groups of 5 SpMV dispatches, in "
+                         "order (default: the three maps of --pmc-probe)")
+    ap.add_argument("--traffic-out", default=None,
+                    help="with --traffic-from: JSON file to write (default: the file the benchmark reads)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.traffic_from:
-        traffic_from(args.traffic_from)
+        if args.traffic_groups:
+            traffic_from(args.traffic_from, args.traffic_groups.split(","), args.traffic_out)
+        else:
+            traffic_from(args.traffic_from, out_path=args.traffic_out)
         return
 
     import torch
@@ -559,14 +567,17 @@ def _counter_rows(d):
     return rows
 
 
-def traffic_from(dirs):
-    """Bytes per SpMV launch from rocprofv3 --pmc runs of --pmc-probe.
+def traffic_from(dirs, names=("fp64", "mixed_50_30_20", "bf16"), out_path=None):
+    """Bytes per SpMV launch from rocprofv3 --pmc runs of --pmc-probe (or --spmv-probe).
 
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for the
     stream copy of 256 MiB that opens the probe (its bytes are known: 256 MiB each way).
-    The SpMV dispatches come in three groups of five (FP64, mixed, BF16 maps, in that
-    order). With TCC_HIT_sum/TCC_MISS_sum, the L2 hit rate of each group is reported too.
-    Writes the JSON file the benchmark reads, stamped with the kernel source hash."""
+    The SpMV dispatches come in groups of five, one group per name in `names` (for
+    --pmc-probe: FP64, mixed, BF16 maps, in that order). With TCC_HIT_sum/TCC_MISS_sum,
+    the L2 hit rate of each group is reported too. Writes a JSON file (by default the one
+    the benchmark reads, bytes_per_launch from the first group), stamped with the kernel
+    source hash."""
+    names = list(names)
     per = {}  # counter -> list of (dispatch, kernel, value)
     for d in dirs:
         for kname, cname, val, disp in _counter_rows(d):
@@ -583,24 +594,23 @@ def traffic_from(dirs):
     res = {}
     for cname in ("FETCH_SIZE", "WRITE_SIZE"):
         copy, g = groups(cname)
-        if not copy or len(g) < 3:
-            raise SystemExit(f"{cname}: expected the stream copy and three groups of 5 SpMV dispatches")
+        if not copy or len(g) < len(names):
+            raise SystemExit(f"{cname}: expected the stream copy and {len(names)} groups of 5 SpMV dispatches")
         scale = ref / copy[0]
         res[cname] = {"reference_kib": copy[0], "scale": round(scale, 4),
-                      "per_map_bytes": [float(np.mean(x)) * scale * 1024.0 for x in g[:3]]}
-    names = ["fp64", "mixed_50_30_20", "bf16"]
+                      "per_map_bytes": [float(np.mean(x)) * scale * 1024.0 for x in g[:len(names)]]}
     out["scale"] = {c: res[c]["scale"] for c in res}
     out["bytes_per_launch_by_map"] = {n: {"read": res["FETCH_SIZE"]["per_map_bytes"][i],
                                           "written": res["WRITE_SIZE"]["per_map_bytes"][i],
                                           "total": res["FETCH_SIZE"]["per_map_bytes"][i]
                                           + res["WRITE_SIZE"]["per_map_bytes"][i]} for i, n in enumerate(names)}
-    out["bytes_per_launch"] = round(out["bytes_per_launch_by_map"]["fp64"]["total"])
+    out["bytes_per_launch"] = round(out["bytes_per_launch_by_map"][names[0]]["total"])
     if "TCC_HIT_sum" in per and "TCC_MISS_sum" in per:
         _, gh = groups("TCC_HIT_sum")
         _, gm = groups("TCC_MISS_sum")
         out["l2"] = {f"spmv_hit_rate_{n}_map": round(float(np.sum(gh[i]) / (np.sum(gh[i]) + np.sum(gm[i]))), 4)
                      for i, n in enumerate(names)}
-    with open(TRAFFIC_FILE, "w") as fh:
+    with open(out_path or TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out), flush=True)
 
@@ -646,16 +656,19 @@ def small_systems(torch, dev, mpcg):
 
 
 def spmv_probe(torch, dev, mpcg, cfgs, slices):
-    """Launch sequence for counter runs of the SpMV on any workload: the copy of known
-    size, then per workload and column-slice count (0 = unsliced) five cg_spmv launches
-    under the all-FP64 map. With slices the combine kernel follows every SpMV."""
+    """Launch sequence for counter runs of the SpMV on any workload: the library's stream
+    copy of 256 MiB (the scale reference of --traffic-from), then per workload and
+    column-slice count (1 = unsliced, then each of `slices`) five cg_spmv launches under
+    the all-FP64 map, one group of five per handle. With slices the combine kernel follows
+    every SpMV."""
     from gen import make_workload
 
     src = torch.empty(COPY_BYTES // 8, dtype=torch.float64, device=dev).uniform_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    dst.copy_(src)
+    mpcg.cg_stream_copy(src, dst, 8192)
     torch.cuda.synchronize()
+    del src, dst
     for cfg in cfgs:
         w = make_workload(cfg, "full")
         A = w.A

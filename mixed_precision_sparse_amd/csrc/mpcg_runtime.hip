@@ -130,7 +130,8 @@ struct cg_handle {
     // The last cg_spmv / cg_true_residual launch on a caller's stream: calls
     // that rewrite the map, the packed values or the scalar state wait for it.
     hipEvent_t ev_user = nullptr;
-    bool user_pending = false;
+    bool user_pending = false;  // a caller's stream: ev_user follows its last launch
+    bool null_pending = false;  // the default stream: a launch since the last wait (no event needed)
     // cg_true_residual: (||r||^2, ||b||^2) partials per block and the result.
     double* part_res = nullptr;
     int64_t part_res_cap = 0;
@@ -670,11 +671,30 @@ int scratch_address(int d, double** out) {
 // cg_true_residual) has finished, before a call rewrites what it reads (the
 // map, the packed values, the column codes, the scalar state). Those calls
 // use the handle's own stream or blocking copies, which are not ordered after
-// a caller's non-blocking stream.
+// a caller's non-blocking stream. Launches on the default stream are waited
+// for by synchronising that stream, so they need no event of their own (an
+// event recorded after every cg_spmv costs a few microseconds per call).
 hipError_t order_after_user(cg_handle* h) {
-    if (!h->user_pending) return hipSuccess;
-    h->user_pending = false;
-    return hipEventSynchronize(h->ev_user);
+    hipError_t e = hipSuccess;
+    if (h->null_pending) {
+        h->null_pending = false;
+        e = hipStreamSynchronize(nullptr);
+    }
+    if (e == hipSuccess && h->user_pending) {
+        h->user_pending = false;
+        e = hipEventSynchronize(h->ev_user);
+    }
+    return e;
+}
+
+// Notes a launch on a caller's stream for order_after_user.
+hipError_t note_user_launch(cg_handle* h, hipStream_t s) {
+    if (!s) {
+        h->null_pending = true;
+        return hipSuccess;
+    }
+    h->user_pending = true;
+    return hipEventRecord(h->ev_user, s);
 }
 
 bool ranges_overlap(const void* a, const void* b, size_t bytes) {
@@ -1728,8 +1748,7 @@ extern "C" int cg_spmv(cg_handle* h, const double* x, double* y, void* stream) {
         launch_spmv<dev::kSpmvPlain>(h, a, static_cast<hipStream_t>(stream));
     }
     HIP_CHECK(hipGetLastError());
-    HIP_CHECK(hipEventRecord(h->ev_user, static_cast<hipStream_t>(stream)));
-    h->user_pending = true;
+    HIP_CHECK(note_user_launch(h, static_cast<hipStream_t>(stream)));
     return CG_OK;
 }
 

@@ -94,10 +94,11 @@ def test_true_residual_after_solve_matches_oracle_solve(dev):
     S.close()
 
 
-def test_map_change_waits_for_spmv_in_flight(dev):
-    """cg_spmv on a non-blocking stream, then the tile rule rewrites the map with no host
-    synchronisation in between: y must be the product under the map the SpMV was launched
-    with (the map change waits for it)."""
+@pytest.mark.parametrize("stream_kind", ["side", "default"])
+def test_map_change_waits_for_spmv_in_flight(stream_kind, dev):
+    """cg_spmv on a non-blocking stream (or the default stream), then the tile rule rewrites
+    the map with no host synchronisation in between: y must be the product under the map the
+    SpMV was launched with (the map change waits for it)."""
     w = make_workload(5, "small")
     A = w.A
     L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
@@ -107,7 +108,7 @@ def test_map_change_waits_for_spmv_in_flight(dev):
     S.cg_set_schedule_tile_rule(10, scores, 1e-3, 1e-6)
     S.cg_eval_tile_rule(1.0)  # mostly BF16
     m_old = S.cg_get_active_map()
-    s = torch.cuda.Stream()
+    s = torch.cuda.Stream() if stream_kind == "side" else torch.cuda.default_stream()
     x = np.random.default_rng(4).uniform(-1, 1, A.n)
     xd = torch.from_numpy(x).to(dev)
     ys = [torch.full_like(xd, float("nan")) for _ in range(8)]
