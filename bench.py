@@ -159,6 +159,12 @@ def main():
     ap.add_argument("--col-slices", default="",
                     help="with --workloads or --spmv-probe: comma-separated column-slice counts (e.g. 8,16) whose handles "
                          "are timed beside the unsliced ones")
+    ap.add_argument("--pmag", default="",
+                    help="comma-separated workloads (e.g. 2,5): instead of the CG bench, time CG under the "
+                         "max|p| rule (paper Sec. 4.7) evaluated every iteration, select the reuse interval "
+                         "K* from a recorded run (Sec. 3.4) and time the rule reused over K* iterations, "
+                         "at the paper's setting (lo = tol/10, hi = tol) and at lo = 1e-4, hi = 1e-2, beside "
+                         "the all-FP64 map; prints one JSON line")
     ap.add_argument("--small-systems", action="store_true",
                     help="instead of the CG bench, time CG (FP64 map, tol 1e-10) on 2D 5-point and 3D "
                          "7-point Laplacians of a few hundred to a few thousand rows, on one workgroup "
@@ -208,6 +214,9 @@ def main():
         return
     if args.small_systems:
         small_systems(torch, dev, mpcg)
+        return
+    if args.pmag:
+        pmag_bench(torch, dev, mpcg, [int(c) for c in args.pmag.split(",")])
         return
     if args.spmv_probe:
         spmv_probe(torch, dev, mpcg, [int(c) for c in args.spmv_probe.split(",")],
@@ -612,6 +621,65 @@ def traffic_from(dirs, names=("fp64", "mixed_50_30_20", "bf16"), out_path=None):
                      for i, n in enumerate(names)}
     with open(out_path or TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
+    print(json.dumps(out), flush=True)
+
+
+def pmag_bench(torch, dev, mpcg, cfgs):
+    """Time to solution under the max|p| rule (Sec. 4.7), per iteration and reused over K*.
+
+    Per workload: one untimed solve, then the median of three timed ones, for the all-FP64
+    map and for the rule at two settings; the per-iteration run is recorded once more to
+    select K* (cg_select_reuse_interval, 10 % of upward transitions delayed at most), and the
+    rule is then timed with period K*. Precision fractions are tile-iterations summed over
+    the map trace; true residuals from cg_true_residual.
+    """
+    from gen import make_workload
+
+    out = {"metric": "cg_time_to_solution_pmag_rule", "workloads": []}
+    for cfg in cfgs:
+        w = make_workload(cfg, "full")
+        A = w.A
+        L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+        b = torch.from_numpy(w.b).to(dev)
+        x = torch.zeros_like(b)
+
+        def timed(S):
+            S.cg_solve(b, x, w.tol, w.maxit)
+            best = []
+            for _ in range(3):
+                torch.cuda.synchronize()
+                t = time.perf_counter()
+                st, K, _ = S.cg_solve(b, x, w.tol, w.maxit)
+                torch.cuda.synchronize()
+                best.append(time.perf_counter() - t)
+            return {"status": st, "iterations": K, "time_to_solution_ms": round(float(np.median(best)) * 1e3, 3),
+                    "true_residual": S.cg_true_residual(b, x)}
+
+        rec = {"workload": w.description, "n": A.n, "nnz": A.nnz, "tol": w.tol, "maxit": w.maxit}
+        S = mpcg.Solver(L, np.zeros(L.T, np.uint8), jacobi=w.jacobi)
+        rec["fp64"] = timed(S)
+        for name, lo, hi in (("paper_setting", w.tol / 10, w.tol), ("lo_1e-4_hi_1e-2", 1e-4, 1e-2)):
+            S.cg_set_schedule_pmag(lo, hi, 1)
+            r = {"lo": lo, "hi": hi, "per_iteration": timed(S)}
+            ks, cnt = S.cg_get_map_trace(cap=w.maxit + 2)
+            r["per_iteration"]["tile_iterations_fp64_fp32_bf16"] = \
+                (cnt.sum(axis=0) / max(cnt.sum(), 1)).round(4).tolist()
+            S.cg_record_column_codes(True)
+            S.cg_solve(b, x, w.tol, w.maxit)
+            kstar, table = mpcg.cg_select_reuse_interval(S.cg_get_column_codes(), 0.1)
+            S.cg_record_column_codes(False)
+            r["kstar"] = kstar
+            r["delayed_upward_fraction_by_interval"] = table
+            S.cg_set_schedule_pmag(lo, hi, kstar)
+            r["reused"] = timed(S)
+            rec[name] = r
+            print(f"# cfg{cfg} max|p| {name}: per iteration {r['per_iteration']['time_to_solution_ms']} ms "
+                  f"(K={r['per_iteration']['iterations']}, fractions {r['per_iteration']['tile_iterations_fp64_fp32_bf16']}), "
+                  f"K*={kstar}: {r['reused']['time_to_solution_ms']} ms; FP64 map {rec['fp64']['time_to_solution_ms']} ms",
+                  file=sys.stderr, flush=True)
+        S.close()
+        L.close()
+        out["workloads"].append(rec)
     print(json.dumps(out), flush=True)
 
 
