@@ -165,6 +165,10 @@ def main():
                          "K* from a recorded run (Sec. 3.4) and time the rule reused over K* iterations, "
                          "at the paper's setting (lo = tol/10, hi = tol) and at lo = 1e-4, hi = 1e-2, beside "
                          "the all-FP64 map; prints one JSON line")
+    ap.add_argument("--stage-x", action="store_true",
+                    help="with --workloads: also time each workload on a handle with cg_options.stage_x = 1 (x "
+                         "segments staged in LDS per batch); with --spmv-probe: one more group of five launches "
+                         "per workload on such a handle")
     ap.add_argument("--small-systems", action="store_true",
                     help="instead of the CG bench, time CG (FP64 map, tol 1e-10) on 2D 5-point and 3D "
                          "7-point Laplacians of a few hundred to a few thousand rows, on one workgroup "
@@ -220,10 +224,10 @@ def main():
         return
     if args.spmv_probe:
         spmv_probe(torch, dev, mpcg, [int(c) for c in args.spmv_probe.split(",")],
-                   [int(c) for c in args.col_slices.split(",") if c])
+                   [int(c) for c in args.col_slices.split(",") if c], args.stage_x)
         return
     if args.workloads:
-        all_workloads(torch, dev, mpcg, [int(c) for c in args.workloads.split(",")], args.spmv_reps,
+        all_workloads(torch, dev, mpcg, [int(c) for c in args.workloads.split(",")], args.spmv_reps, args.stage_x,
                       [int(c) for c in args.col_slices.split(",") if c])
         return
 
@@ -393,7 +397,7 @@ def configure_map(S, w, L, mpcg_mod):
     return None
 
 
-def all_workloads(torch, dev, mpcg, cfgs, reps, slices=()):
+def all_workloads(torch, dev, mpcg, cfgs, reps, stage_x=False, slices=()):
     """Warm time to solution, iterations/s and SpMV bandwidth per workload, both maps.
 
     Every solve starts from x0 = 0 on the device with b resident; one untimed
@@ -424,11 +428,14 @@ def all_workloads(torch, dev, mpcg, cfgs, reps, slices=()):
         runs = [("fp64", None, 0)] + ([("own", own, 0)] if own != "fp64" else [])
         for ns in slices:
             runs += [(f"fp64_slices{ns}", None, ns)] + ([(f"own_slices{ns}", own, ns)] if own != "fp64" else [])
+        if stage_x:  # x segments staged in LDS per batch (cg_options.stage_x)
+            runs += [("fp64_stage_x", None, 0)]
         for label, kind, ns in runs:
-            S = mpcg.Solver(L, np.zeros(L.T, np.uint8), jacobi=w.jacobi, col_slices=ns)
+            S = mpcg.Solver(L, np.zeros(L.T, np.uint8), jacobi=w.jacobi, col_slices=ns,
+                            stage_x=1 if label.endswith("stage_x") else 0)
             m = np.zeros(L.T, np.uint8) if kind is None else configure_map(S, w, L, mpcg)
             r = {"map": "all FP64" if kind is None else kind, "col_slices_option": ns,
-                 "col_slices": S.cg_get_options()["col_slices"]}
+                 "col_slices": S.cg_get_options()["col_slices"], "stage_x": S.cg_get_options()["stage_x"]}
             if m is not None:
                 for _ in range(5):
                     S.cg_spmv(xin, y)
@@ -723,12 +730,13 @@ def small_systems(torch, dev, mpcg):
     print(json.dumps(out), flush=True)
 
 
-def spmv_probe(torch, dev, mpcg, cfgs, slices):
+def spmv_probe(torch, dev, mpcg, cfgs, slices, stage_x=False):
     """Launch sequence for counter runs of the SpMV on any workload: the library's stream
     copy of 256 MiB (the scale reference of --traffic-from), then per workload and
     column-slice count (1 = unsliced, then each of `slices`) five cg_spmv launches under
-    the all-FP64 map, one group of five per handle. With slices the combine kernel follows
-    every SpMV."""
+    the all-FP64 map, one group of five per handle; with stage_x, one more handle per
+    workload that stages x segments in LDS. With slices the combine kernel follows every
+    SpMV."""
     from gen import make_workload
 
     src = torch.empty(COPY_BYTES // 8, dtype=torch.float64, device=dev).uniform_()
@@ -744,13 +752,14 @@ def spmv_probe(torch, dev, mpcg, cfgs, slices):
         m = np.zeros(L.T, np.uint8)
         xin = torch.from_numpy(np.random.default_rng(7).uniform(-1, 1, A.n)).to(dev)
         y = torch.empty_like(xin)
-        for ns in [1] + list(slices):
-            S = mpcg.Solver(L, m, col_slices=ns)
+        for ns in [1] + list(slices) + ([-1] if stage_x else []):
+            S = mpcg.Solver(L, m, col_slices=max(ns, 1), stage_x=1 if ns < 0 else 0)
             for _ in range(5):
                 S.cg_spmv(xin, y)
             torch.cuda.synchronize()
             S.close()
-            print(f"# spmv probe: cfg{cfg}, {ns} column slices, 5 cg_spmv launches, all-FP64 map, "
+            what = "x staged in LDS" if ns < 0 else f"{ns} column slices"
+            print(f"# spmv probe: cfg{cfg}, {what}, 5 cg_spmv launches, all-FP64 map, "
                   f"algorithmic bytes {spmv_algorithmic_bytes(L, m)}", file=sys.stderr, flush=True)
         L.close()
 
