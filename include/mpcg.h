@@ -252,7 +252,7 @@ typedef struct {
  *   stream        : stream for the set-up copies and kernels.
  * Errors: CG_EINVAL (map code > 2, bad layout, n >= 2^28 or T or nnz >= 2^31,
  * no nonzeros, Jacobi with a zero or missing diagonal entry, unknown p1 bits, padding with
- * R = 256, col_slices outside [0, 64], single_block outside [-1, 1]),
+ * R > 255, col_slices outside [0, 64], single_block outside [-1, 1], stage_x outside [0, 1]),
  * CG_ENOMEM, CG_EDEVICE.
  */
 int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, const cg_options* opt,

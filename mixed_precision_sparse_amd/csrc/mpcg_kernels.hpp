@@ -20,7 +20,7 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kTileBatch = 64;   // tile descriptors staged in LDS per pass
-constexpr int kMaxRows = 256;    // rows owned by one wavefront (R <= 256)
+constexpr int kMaxRows = 256;    // rows owned by one wavefront (taller row blocks run as slabs of at most this)
 constexpr int kMaxGroupRB = 63;  // row blocks per wavefront at most (boundaries fit one wave)
 
 // Solver scalars, resident on the device for the whole solve. Each field has
