@@ -177,11 +177,23 @@ __device__ inline void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Vector stores of the CG loop. nt: streaming (non-temporal) stores, for
-// solves whose working set exceeds the last-level cache, where they cut a
-// cfg5-sized iteration by about 2 %; a solve that fits the cache keeps plain
-// stores (streaming ones made it 6 % slower).
+// Vector accesses of the CG loop. nt: streaming (non-temporal) loads and
+// stores, for solves whose working set exceeds the last-level cache. There
+// they keep the cache for p, which the next product gathers: every vector
+// access but p's streams, and p is stored plainly. Per iteration, a 4096^2
+// Q1 solve takes 582 us (597 with plain accesses, 590 with streaming stores
+// only), a 100^3 27-point one 71.4 us (78.7, 77.1). A solve that fits the
+// cache keeps plain accesses (streaming ones made the 128^3 Laplacian 5-6 %
+// slower).
 typedef double f64x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ double2 load_vec(const double2* p, bool nt) {
+    if (!nt) return *p;
+    const f64x2 w = __builtin_nontemporal_load(reinterpret_cast<const f64x2*>(p));
+    double2 v;
+    v.x = w.x;
+    v.y = w.y;
+    return v;
+}
 __device__ __forceinline__ void store_vec(double2* p, double2 v, bool nt) {
     if (nt) {
         f64x2 w;
@@ -1200,7 +1212,6 @@ struct VecArgs {
     int32_t r_ready;         // init: r already holds b - A x0
     int32_t nq;              // partial products summed into q (column slices), >= 1
     int64_t qstride;         // distance between two partial products
-    int32_t nt;              // update and direction kernels: streaming stores (see store_vec)
 };
 
 // st->ntrace and st->stage are read with atomic loads: the single-workgroup
@@ -1309,7 +1320,7 @@ constexpr int kVecPairs = MPCG_VEC_PAIRS;
 // direction kernel. `done` does not change during this launch, so every block
 // takes the same decision, and block 0 records it in `live` for the direction
 // kernel.
-template <bool JAC>
+template <bool JAC, bool NT>
 __global__ __launch_bounds__(kVecBlock) void cg_update_kernel(VecArgs a) {
     __shared__ double s_tmp[kVecWaves];
     State* st = a.st;
@@ -1329,8 +1340,8 @@ __global__ __launch_bounds__(kVecBlock) void cg_update_kernel(VecArgs a) {
         for (int j = 0; j < kVecPairs; ++j) {
             const int64_t i = base + j * stride + tid;
             if (i < npairs) {
-                rv[j] = r2[i];
-                qv[j] = q2[i];
+                rv[j] = load_vec(&r2[i], NT);
+                qv[j] = load_vec(&q2[i], NT);
                 for (int s = 1; s < a.nq; ++s) {  // column slices: q is the sum of the partials
                     const double2 qs = q2[s * (a.qstride / 2) + i];
                     qv[j].x += qs.x;
@@ -1357,13 +1368,13 @@ __global__ __launch_bounds__(kVecBlock) void cg_update_kernel(VecArgs a) {
                     double2 rn;
                     rn.x = rv[j].x - alpha * qv[j].x;
                     rn.y = rv[j].y - alpha * qv[j].y;
-                    store_vec(&r2[i], rn, a.nt != 0);
+                    store_vec(&r2[i], rn, NT);
                     rr += rn.x * rn.x + rn.y * rn.y;
                     if (JAC) {
                         double2 zn;
                         zn.x = dv[j].x * rn.x;
                         zn.y = dv[j].y * rn.y;
-                        store_vec(&z2[i], zn, a.nt != 0);
+                        store_vec(&z2[i], zn, NT);
                         rz += rn.x * zn.x + rn.y * zn.y;
                     }
                 }
@@ -1390,7 +1401,7 @@ __global__ __launch_bounds__(kVecBlock) void cg_update_kernel(VecArgs a) {
 // The launch runs when the update kernel of this iteration ran (`live`, which
 // no block of this launch writes); `done` may be set by block 0 while other
 // blocks still run, and they must still apply this iteration's x update.
-template <bool JAC>
+template <bool JAC, bool NT>
 __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
     __shared__ double s_tmp[kVecWaves];
     State* st = a.st;
@@ -1412,8 +1423,8 @@ __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
             const int64_t i = base + j * stride + tid;
             if (i < npairs) {
                 pv[j] = p2[i];
-                zv[j] = z2[i];
-                xv[j] = x2[i];
+                zv[j] = load_vec(&z2[i], NT);
+                xv[j] = load_vec(&x2[i], NT);
             }
         }
     };
@@ -1435,8 +1446,8 @@ __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(VecArgs a) {
                 xn.y = xv[j].y + alpha * pv[j].y;
                 pn.x = zv[j].x + beta * pv[j].x;
                 pn.y = zv[j].y + beta * pv[j].y;
-                store_vec(&x2[i], xn, a.nt != 0);
-                store_vec(&p2[i], pn, a.nt != 0);
+                store_vec(&x2[i], xn, NT);
+                p2[i] = pn;  // p stays cached for the next product's gathers
             }
         }
     }

@@ -204,9 +204,9 @@ constexpr int kSpmvGridCap = MPCG_SPMV_GRID_CAP;
 constexpr int kResGridCap = 4096;
 // MI355X's last-level (Infinity) cache. A CG iteration whose working set (the
 // matrix stream at 10 bytes per nonzero and 12 per tile, and five vectors)
-// exceeds it stores its vectors with streaming stores: measured 2-4 % faster
-// per iteration on the 100^3 27-point and 4096^2 Q1 workloads, 6 % slower on
-// the 128^3 Laplacian, whose 240 MB fit the cache.
+// exceeds it streams its vector accesses past the cache, except p's (see
+// store_vec): 3-9 % faster per iteration on the 100^3 27-point and 4096^2 Q1
+// workloads, and 5-6 % slower on the 128^3 Laplacian, whose 240 MB fit.
 constexpr int64_t kLastLevelCache = int64_t(256) << 20;  // blocks of the column-slice residual-norm kernel
 // SpMV grid: at most kSpmvPersist times the blocks the chip holds at once
 // (0: one wavefront per segment up to the cap).
@@ -434,7 +434,6 @@ dev::VecArgs vec_args(cg_handle* h, const double* b, const double* x0) {
     a.T = h->T;
     a.n = (int32_t)h->n;
     a.jacobi = h->jacobi ? 1 : 0;
-    a.nt = h->nt_stores ? 1 : 0;
     a.r_ready = 0;
     return a;
 }
@@ -512,6 +511,24 @@ int solve_window(const cg_handle* h) {
     return std::max(1, h->window / period) * period;
 }
 
+// The update (UPDATE = true) or direction kernel in the handle's instantiation:
+// Jacobi or not, streaming vector accesses or not.
+template <bool UPDATE>
+void launch_vec_kernel(cg_handle* h, const dev::VecArgs& va, hipStream_t s) {
+    const dim3 g(h->upd_blocks), b(dev::kVecBlock);
+    if (UPDATE) {
+        if (h->jacobi && h->nt_stores) hipLaunchKernelGGL((dev::cg_update_kernel<true, true>), g, b, 0, s, va);
+        else if (h->jacobi) hipLaunchKernelGGL((dev::cg_update_kernel<true, false>), g, b, 0, s, va);
+        else if (h->nt_stores) hipLaunchKernelGGL((dev::cg_update_kernel<false, true>), g, b, 0, s, va);
+        else hipLaunchKernelGGL((dev::cg_update_kernel<false, false>), g, b, 0, s, va);
+    } else {
+        if (h->jacobi && h->nt_stores) hipLaunchKernelGGL((dev::cg_direction_kernel<true, true>), g, b, 0, s, va);
+        else if (h->jacobi) hipLaunchKernelGGL((dev::cg_direction_kernel<true, false>), g, b, 0, s, va);
+        else if (h->nt_stores) hipLaunchKernelGGL((dev::cg_direction_kernel<false, true>), g, b, 0, s, va);
+        else hipLaunchKernelGGL((dev::cg_direction_kernel<false, false>), g, b, 0, s, va);
+    }
+}
+
 // One CG iteration: [map window step] -> SpMV with fused p.q and alpha ->
 // x/r update with fused r.r (r.z), beta, rho and stop flag -> new direction.
 // i is the iteration's index in its window (the solve's k modulo the window
@@ -529,16 +546,10 @@ void enqueue_iteration(cg_handle* h, int i, hipStream_t s, bool rule_at_end = fa
     va.part_in = h->part_spmv;
     va.nparts_in = spmv_grid(h);
     va.part_out = h->part_vec;
-    if (h->jacobi)
-        hipLaunchKernelGGL(dev::cg_update_kernel<true>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
-    else
-        hipLaunchKernelGGL(dev::cg_update_kernel<false>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
+    launch_vec_kernel<true>(h, va, s);  // update
     va.part_in = h->part_vec;
     va.nparts_in = h->upd_blocks;
-    if (h->jacobi)
-        hipLaunchKernelGGL(dev::cg_direction_kernel<true>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
-    else
-        hipLaunchKernelGGL(dev::cg_direction_kernel<false>, dim3(h->upd_blocks), dim3(dev::kVecBlock), 0, s, va);
+    launch_vec_kernel<false>(h, va, s);  // direction
     if (h->sched == kSchedPMag) {  // the map of the next window (iteration i + 1 starts it)
         if (pmag_split(h) ? (rule_at_end && i == h->window - 1) : (i + 1) % h->pm_period == 0)
             launch_pmag(h, h->p, 1, s);
