@@ -354,10 +354,10 @@ __global__ __launch_bounds__(kBlock) void build_segments_kernel(const int32_t* _
 // minus (its position in the batch << log2 of its value width). One
 // wavefront per batch: lane l sizes tile l and a wave prefix sum places it,
 // then the lanes copy the batch's values 64 at a time, each finding its tile
-// from the window records. Rerun at every map change; in a solve (solve = 1)
-// only at the start of a tile-rule window, and then only for the batches the
-// tile rule marked dirty (each batch's part is self-contained). Every
-// batch it rebuilds is marked clean.
+// from the window records. Rerun at every map change: repack_kernel rebuilds
+// every batch; in a solve the tile-rule kernel rebuilds, at the start of each
+// window, only the batches in which a tile changed precision (each batch's part
+// is self-contained).
 struct RepackArgs {
     const int32_t* btab;
     const int32_t* tptr;
@@ -367,72 +367,72 @@ struct RepackArgs {
     int32_t* toff;
     const uint64_t* win_mask;
     const int32_t* win_tile;
-    const State* st;
-    uint8_t* dirty;      // per batch: packed values out of date (cleared here)
     int64_t nbatch;
-    int32_t solve;
-    int32_t only_dirty;  // 1: rebuild only the batches marked dirty; 0: every batch
 };
+
+// One batch by one wavefront: lane l holds p, the precision code of the
+// batch's tile l (lanes past the batch's nt tiles hold nothing). s_toff and
+// s_prec are the wavefront's LDS slots (kTileBatch each).
+__device__ inline void repack_batch(const RepackArgs& a, const int32_t* e, int lane, int p, int* s_toff,
+                                    int* s_prec) {
+    const int tb = e[kBtTile], nt = e[kBtTiles], first = e[kBtFirstNnz], len = e[kBtLen];
+    const bool valid = lane < nt;
+    const int sh = 3 - p;
+    const int start = valid ? a.tptr[tb + lane] - first : 0;
+    const int bytes = valid ? ((a.tptr[tb + lane + 1] - a.tptr[tb + lane]) << sh) : 0;
+    int incl = (bytes + 7) & ~7;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += t;
+    }
+    const int base = incl - ((bytes + 7) & ~7);
+    if (valid) {
+        const int to = base - (start << sh);
+        a.toff[tb + lane] = to;
+        s_toff[lane] = to;
+        s_prec[lane] = p;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const char* src = a.planes + (int64_t)e[kBtSegment] * 16;
+    char* dst = a.packed + (int64_t)e[kBtPacked] * 16;
+    for (int o = 0, v = e[kBtRecords]; o < len; o += kWave, ++v) {
+        const uint64_t m = a.win_mask[v];
+        const int j = a.win_tile[v] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const int i = o + lane;
+        if (i < len) {
+            const int pj = s_prec[j];
+            const int shj = 3 - pj;
+            const int64_t from = (int64_t)pj * (10 - 2 * pj) * len + ((int64_t)i << shj);
+            const int64_t to = (int64_t)s_toff[j] + ((int64_t)i << shj);
+            if (pj == 0)
+                *reinterpret_cast<uint64_t*>(dst + to) = *reinterpret_cast<const uint64_t*>(src + from);
+            else if (pj == 1)
+                *reinterpret_cast<uint32_t*>(dst + to) = *reinterpret_cast<const uint32_t*>(src + from);
+            else
+                *reinterpret_cast<uint16_t*>(dst + to) = *reinterpret_cast<const uint16_t*>(src + from);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __global__ __launch_bounds__(kBlock) void repack_kernel(RepackArgs a) {
     __shared__ int s_toff[kWavesPerBlock][kTileBatch];
     __shared__ int s_prec[kWavesPerBlock][kTileBatch];
-    if (a.solve) {
-        if (load_done(a.st)) return;
-        if (a.st->k % a.st->period != 0) return;
-    }
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
     const int64_t waves = (int64_t)gridDim.x * kWavesPerBlock;
     for (int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + w; b < a.nbatch; b += waves) {
         const int32_t* e = a.btab + b * kBtFields;
-        const int tb = e[kBtTile], nt = e[kBtTiles], first = e[kBtFirstNnz], len = e[kBtLen];
-        if (nt == 0 || (a.only_dirty && !a.dirty[b])) continue;
-        const bool valid = lane < nt;
-        const int p = valid ? min((int)a.map[tb + lane], 2) : 0;
-        const int sh = 3 - p;
-        const int start = valid ? a.tptr[tb + lane] - first : 0;
-        const int bytes = valid ? ((a.tptr[tb + lane + 1] - a.tptr[tb + lane]) << sh) : 0;
-        int incl = (bytes + 7) & ~7;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int t = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += t;
-        }
-        const int base = incl - ((bytes + 7) & ~7);
-        if (valid) {
-            const int to = base - (start << sh);
-            a.toff[tb + lane] = to;
-            s_toff[w][lane] = to;
-            s_prec[w][lane] = p;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const char* src = a.planes + (int64_t)e[kBtSegment] * 16;
-        char* dst = a.packed + (int64_t)e[kBtPacked] * 16;
-        for (int o = 0, v = e[kBtRecords]; o < len; o += kWave, ++v) {
-            const uint64_t m = a.win_mask[v];
-            const int j = a.win_tile[v] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            const int i = o + lane;
-            if (i < len) {
-                const int pj = s_prec[w][j];
-                const int shj = 3 - pj;
-                const int64_t from = (int64_t)pj * (10 - 2 * pj) * len + ((int64_t)i << shj);
-                const int64_t to = (int64_t)s_toff[w][j] + ((int64_t)i << shj);
-                if (pj == 0)
-                    *reinterpret_cast<uint64_t*>(dst + to) = *reinterpret_cast<const uint64_t*>(src + from);
-                else if (pj == 1)
-                    *reinterpret_cast<uint32_t*>(dst + to) = *reinterpret_cast<const uint32_t*>(src + from);
-                else
-                    *reinterpret_cast<uint16_t*>(dst + to) = *reinterpret_cast<const uint16_t*>(src + from);
-            }
-        }
-        if (lane == 0) a.dirty[b] = 0;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int tb = e[kBtTile], nt = e[kBtTiles];
+        if (nt == 0) continue;
+        const int p = lane < nt ? min((int)a.map[tb + lane], 2) : 0;
+        repack_batch(a, e, lane, p, s_toff[w], s_prec[w]);
     }
 }
 
@@ -1629,7 +1629,7 @@ struct MapArgs {
     int32_t* trace_k;
     int32_t* trace_counts;
     const int32_t* btab;  // tile rule: batches of the SpMV (a partition of the tiles)
-    uint8_t* dirty;       // tile rule: per batch, set when a tile of the batch changed precision
+    RepackArgs rp;        // tile rule with repack = 1: the packed values to rebuild
     uint8_t* winmaps;     // tile rule, recording on: [window][T] map of every window (else NULL)
     const uint8_t* count_w;  // per tile: 1 if it counts in the trace (one piece per tile of R > 256), or NULL: all
     int64_t T;
@@ -1637,6 +1637,7 @@ struct MapArgs {
     double rho;          // explicit rho (eval mode)
     int32_t solve;       // 1: in-solve window step (reads k and rho_k from the state)
     int32_t winmap_cap;  // windows winmaps holds
+    int32_t repack;      // tile rule: rebuild the packed values of every batch with a changed tile
 };
 
 // The block's totals of three per-thread counts, returned in thread c for
@@ -1671,10 +1672,11 @@ __device__ inline void block_counts_out(unsigned c0, unsigned c1, unsigned c2, i
 
 // Windowed tile rule: at k % period == 0 every tile's precision is re-selected
 // from its score and rho_k, and the window's precision counts are recorded.
-// One wavefront per SpMV batch (lane l: the batch's tile l); a batch with a
-// tile whose code changed is marked dirty, so that the repack that follows
-// rebuilds only those batches' packed values. The grid is sized to the
-// batches; block b adds its counts to slot b % kTraceBlocks of the entry.
+// One wavefront per SpMV batch (lane l: the batch's tile l); with repack = 1
+// the wavefront rebuilds the packed values of a batch in which a tile changed
+// precision, right away (the other batches' packed values stay valid). The
+// grid is sized to the batches; block b adds its counts to slot
+// b % kTraceBlocks of the entry.
 __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
     State* st = a.st;
     double rho = a.rho;
@@ -1687,16 +1689,20 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
         slot = k / st->period;
         if (slot >= st->trace_cap) slot = -1;
     }
+    __shared__ int s_toff[kWavesPerBlock][kTileBatch];
+    __shared__ int s_prec[kWavesPerBlock][kTileBatch];
     unsigned c0 = 0, c1 = 0, c2 = 0;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
-    for (int64_t b = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; b < a.nbatch; b += waves) {
+    const int w = threadIdx.x / kWave;
+    const int64_t waves = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + w; b < a.nbatch; b += waves) {
         const int32_t* e = a.btab + b * kBtFields;
         const int tb = e[kBtTile], nt = e[kBtTiles];
         bool changed = false;
+        int code = 0;
         if (lane < nt) {
             const int64_t t = (int64_t)tb + lane;
-            const int code = tile_rule_code(a.scores[t], rho, st->hi, st->lo);
+            code = tile_rule_code(a.scores[t], rho, st->hi, st->lo);
             changed = code != (int)a.map[t];
             a.map[t] = (uint8_t)code;
             if (slot >= 0 && slot < a.winmap_cap) a.winmaps[(size_t)slot * a.T + t] = (uint8_t)code;
@@ -1705,7 +1711,7 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
             c1 += counted && code == 1;
             c2 += counted && code == 2;
         }
-        if (__any(changed) && lane == 0) a.dirty[b] = 1;
+        if (a.repack && __any(changed)) repack_batch(a.rp, e, lane, code, s_toff[w], s_prec[w]);
     }
     if (slot >= 0) {
         const unsigned t = block_count3(c0, c1, c2);

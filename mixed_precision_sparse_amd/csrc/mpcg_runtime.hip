@@ -90,7 +90,6 @@ struct cg_handle {
     char* planes = nullptr;        // per-batch value segments (FP64, FP32, BF16)
     char* packed = nullptr;        // per-batch packed values of the active map (same offsets)
     int32_t* toff = nullptr;       // [T] packed start of every tile (see repack_kernel)
-    uint8_t* dirty = nullptr;      // [nbatch] packed segment out of date (tile rule -> repack)
     int64_t planes_bytes = 0, packed_bytes = 0;
     std::vector<int32_t> btab_host;  // host copy of the batch table
     double* dinv = nullptr;
@@ -382,9 +381,7 @@ void launch_pmag(cg_handle* h, const double* v, int solve, hipStream_t s) {
     hipLaunchKernelGGL(dev::pmag_kernel, dim3((unsigned)blocks), dim3(dev::kBlock), 0, s, a);
 }
 
-// Packs the active map's values (every map change). solve = 1: only at the
-// start of a tile-rule window of a running solve (the kernel checks).
-void launch_repack(cg_handle* h, int solve, hipStream_t s) {
+dev::RepackArgs repack_args(const cg_handle* h) {
     dev::RepackArgs a{};
     a.btab = h->btab;
     a.tptr = h->tptr;
@@ -394,19 +391,20 @@ void launch_repack(cg_handle* h, int solve, hipStream_t s) {
     a.toff = h->toff;
     a.win_mask = h->win_mask;
     a.win_tile = h->win_tile;
-    a.st = h->st;
-    a.dirty = h->dirty;
     a.nbatch = h->nbatch;
-    a.solve = solve;
-    a.only_dirty = solve;  // in a solve the tile rule has just marked the batches it changed
+    return a;
+}
+
+// Packs the active map's values of every batch (every map change outside a solve).
+void launch_repack(cg_handle* h, hipStream_t s) {
     const int64_t blocks = (h->nbatch + dev::kWavesPerBlock - 1) / dev::kWavesPerBlock;
     hipLaunchKernelGGL(dev::repack_kernel, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 16384))),
-                       dim3(dev::kBlock), 0, s, a);
+                       dim3(dev::kBlock), 0, s, repack_args(h));
 }
 
 // Repacks after a map written on the handle's stream; synchronous.
 hipError_t repack(cg_handle* h) {
-    launch_repack(h, 0, h->stream);
+    launch_repack(h, h->stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return hipStreamSynchronize(h->stream);
@@ -452,7 +450,7 @@ dev::MapArgs map_args(cg_handle* h, double rho, int solve) {
     a.trace_k = h->trace_k;
     a.trace_counts = h->trace_counts;
     a.btab = h->btab;
-    a.dirty = h->dirty;
+    a.rp = repack_args(h);
     a.winmaps = h->winmaps;
     a.winmap_cap = h->winmap_cap;
     a.count_w = h->dcount;
@@ -537,8 +535,8 @@ void launch_vec_kernel(cg_handle* h, const dev::VecArgs& va, hipStream_t s) {
 void enqueue_iteration(cg_handle* h, int i, hipStream_t s, bool rule_at_end = false) {
     if (h->sched == kSchedTileRule && i % h->period == 0) {
         dev::MapArgs ma = map_args(h, 0.0, 1);
+        ma.repack = 1;  // the batches whose tiles change precision are repacked in the same launch
         hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(tile_rule_grid(h)), dim3(dev::kBlock), 0, s, ma);
-        launch_repack(h, 1, s);
     }
     dev::SpmvArgs sa = spmv_args(h, h->p, h->S > 1 ? h->qpart : h->q, &h->st->uprec);
     launch_spmv<dev::kSpmvCg>(h, sa, s);
@@ -1366,7 +1364,6 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     TRY(dalloc(h, &h->planes, h->planes_bytes));
     TRY(dalloc(h, &h->packed, h->packed_bytes));
     TRY(dalloc(h, &h->toff, std::max<int64_t>(Td, 1)));
-    TRY(dalloc(h, &h->dirty, std::max<int64_t>(h->nbatch, 1)));
     // CG vectors padded with zeros to an even length (the vector kernels work
     // in 16-byte pairs); the padding entry stays zero, as every update of it
     // combines zeros (q's padding is never written by the SpMV).
@@ -1454,8 +1451,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     } else if ((e = hipMemsetAsync(h->map, 0, Td, s))) {
         return dev_err(e, "map");
     }
-    if ((e = hipMemsetAsync(h->dirty, 0, (size_t)std::max<int64_t>(h->nbatch, 1), s)) ||
-        (e = hipMemsetAsync(h->planes, 0, h->planes_bytes, s)) ||
+    if ((e = hipMemsetAsync(h->planes, 0, h->planes_bytes, s)) ||
         (e = hipMemsetAsync(h->packed, 0, h->packed_bytes, s)))
         return dev_err(e, "planes");
     hipLaunchKernelGGL(dev::build_segments_kernel,
@@ -1467,7 +1463,7 @@ extern "C" int cg_create(const cg_tilecsc* A, const uint8_t* precision_map, cons
     hs.spmv_uprec = -1;
     hs.trace_cap = (int32_t)h->trace_cap;
     if ((e = hipMemcpyAsync(h->st, &hs, sizeof(hs), hipMemcpyHostToDevice, s))) return dev_err(e, "state");
-    launch_repack(h, 0, s);
+    launch_repack(h, s);
     if ((e = hipGetLastError()) != hipSuccess) return dev_err(e, "repack kernel");
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return dev_err(e, "set-up");
     *out = h;
