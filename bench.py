@@ -108,20 +108,28 @@ def time_events(torch, fn, reps, warm=5):
     return e0.elapsed_time(e1) / reps
 
 
-def bandwidth_references(torch, dev, mpcg):
-    """Read-only and copy bandwidth of the library's stream kernels on 2 GiB buffers (best grid)."""
+def bandwidth_references(torch, dev, mpcg, write_share=None):
+    """Read-only and copy bandwidth of the library's stream kernels on 2 GiB buffers (best grid);
+    with write_share (bytes written per byte read), also a 2 GiB read stream that writes that
+    share alongside (None otherwise). Bytes per second count reads and writes."""
     src = torch.empty(STREAM_BYTES // 8, dtype=torch.float64, device=dev).uniform_()
     dst = torch.empty_like(src)
     sink = torch.empty(65536, dtype=torch.float64, device=dev)
-    best_r, best_c = 0.0, 0.0
+    wdst = None
+    if write_share is not None:
+        wdst = dst[: int(STREAM_BYTES * write_share) // 16 * 2]
+    best_r, best_c, best_m = 0.0, 0.0, None
     for blocks in (4096, 8192, 16384, 32768):
         ms = time_events(torch, lambda: mpcg.cg_stream_read(src, sink, blocks), 10, 3)
         best_r = max(best_r, STREAM_BYTES / (ms * 1e-3) / 1e9)
         ms = time_events(torch, lambda: mpcg.cg_stream_copy(src, dst, blocks), 10, 3)
         best_c = max(best_c, 2 * STREAM_BYTES / (ms * 1e-3) / 1e9)
-    del src, dst, sink
+        if wdst is not None:
+            ms = time_events(torch, lambda: mpcg.cg_stream_mix(src, wdst, sink, blocks), 10, 3)
+            best_m = max(best_m or 0.0, (STREAM_BYTES + wdst.numel() * 8) / (ms * 1e-3) / 1e9)
+    del src, dst, sink, wdst
     torch.cuda.empty_cache()
-    return round(best_r, 1), round(best_c, 1)
+    return round(best_r, 1), round(best_c, 1), (round(best_m, 1) if best_m is not None else None)
 
 
 def load_counters():
@@ -317,11 +325,13 @@ def main():
     S64.close()
     S.close()
 
-    read_gbs, copy_gbs = bandwidth_references(torch, dev, mpcg)
+    # The FP64-map SpMV writes y (8n bytes) and reads the rest of its algorithmic bytes.
+    sp64 = spmv["fp64"]
+    share = 8 * A.n / (sp64["algorithmic_bytes"] - 8 * A.n)
+    read_gbs, copy_gbs, mix_gbs = bandwidth_references(torch, dev, mpcg, share)
     traffic, l2 = load_counters()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, L.T, args.cpu_seconds)
 
-    sp64 = spmv["fp64"]
     out = {
         "metric": METRIC,
         "value": round(iters_per_s, 2),
@@ -359,6 +369,8 @@ def main():
         "tile_csc_spmv": spmv,
         "read_ceiling_gbs": read_gbs,
         "copy_ceiling_gbs": copy_gbs,
+        "spmv_mix_ceiling_gbs": mix_gbs,
+        "spmv_mix_write_share": round(share, 4),
         "roofline": {
             "bound": "hbm",
             "kernel": "spmv_tilecsc_kernel (cg_spmv, all-FP64 map)",
@@ -370,6 +382,7 @@ def main():
             "algorithmic_bytes_per_launch": sp64["algorithmic_bytes"],
             "launch_us": sp64["us"],
             "frac_of_read_ceiling": round(sp64["gbs"] / read_gbs, 4),
+            "frac_of_mix_ceiling": round(sp64["gbs"] / mix_gbs, 4),
         },
         "l2": l2,
         "cpu_baseline": cpu,

@@ -421,13 +421,20 @@ int cg_true_residual_noalloc(cg_handle* h, const double* b, const double* x, dou
  * Bandwidth references (measurement aids for benchmarks; no part of the
  * method): cg_stream_read reads `bytes` from src once with 16-byte
  * non-temporal loads and writes one sum per block to sink[blocks];
- * cg_stream_copy copies `bytes` from src to dst. Both are asynchronous on
- * stream, with a grid of `blocks` 256-thread blocks. bytes must be a positive
- * multiple of 16 and the pointers 16-byte aligned device memory.
+ * cg_stream_copy copies `bytes` from src to dst; cg_stream_mix reads
+ * read_bytes from src as cg_stream_read does (same sink) and, interleaved
+ * with the reads in proportion, writes write_bytes of running sums to dst
+ * with 16-byte stores (a read stream with the share of writes of a kernel
+ * under study). All are asynchronous on stream, with a grid of `blocks`
+ * 256-thread blocks; sink must hold `blocks` doubles. Byte counts must be
+ * multiples of 16 (read and copy sizes positive; write_bytes may be 0, and
+ * dst NULL then) and the pointers 16-byte aligned device memory.
  * Errors: CG_EINVAL, CG_EDEVICE.
  */
 int cg_stream_read(const void* src, int64_t bytes, double* sink, int32_t blocks, void* stream);
 int cg_stream_copy(const void* src, void* dst, int64_t bytes, int32_t blocks, void* stream);
+int cg_stream_mix(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, double* sink, int32_t blocks,
+                  void* stream);
 
 /* Map trace of the last cg_solve: one entry per map change (the first at
  * k = 0). Writes up to cap entries: k_out[i] (iteration the map took effect)

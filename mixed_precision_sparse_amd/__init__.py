@@ -21,7 +21,7 @@ from ._lib import (CG_BF16, CG_BREAKDOWN, CG_EDEVICE, CG_EINVAL, CG_ENOMEM, CG_F
 
 __all__ = [
     "TileCSC", "Solver", "cg_tilecsc_from_csr", "cg_create", "cg_spmv", "cg_solve", "cg_tune_row_height",
-    "cg_version", "library_path", "CGError", "cg_stream_read", "cg_stream_copy",
+    "cg_version", "library_path", "CGError", "cg_stream_read", "cg_stream_copy", "cg_stream_mix",
 ]
 
 STATUS = {CG_OK: "converged", CG_NOT_CONVERGED: "maxit", CG_BREAKDOWN: "breakdown"}
@@ -346,11 +346,29 @@ def _bytes_ptr(t):
     return t.data_ptr(), t.numel() * t.element_size()
 
 
+def _check_sink(sink, blocks):
+    import torch
+
+    if not isinstance(sink, torch.Tensor) or sink.dtype != torch.float64 or sink.numel() < int(blocks):
+        raise ValueError("sink must be a float64 tensor of at least `blocks` entries")
+
+
 def cg_stream_read(src, sink, blocks, stream=None):
     """Bandwidth reference: read all of src once (sink: float64 tensor of at least `blocks` entries)."""
     p, nbytes = _bytes_ptr(src)
+    _check_sink(sink, blocks)
     check(_lib.load().cg_stream_read(ct.c_void_p(p), nbytes, ct.c_void_p(_dev_ptr(sink)), int(blocks),
                                      ct.c_void_p(_stream(stream))))
+
+
+def cg_stream_mix(src, dst, sink, blocks, stream=None):
+    """Bandwidth reference: read all of src once and, interleaved in proportion, write all of dst
+    (sink: float64 tensor of at least `blocks` entries; it receives the block sums of src)."""
+    p, rbytes = _bytes_ptr(src)
+    q, wbytes = _bytes_ptr(dst)
+    _check_sink(sink, blocks)
+    check(_lib.load().cg_stream_mix(ct.c_void_p(p), rbytes, ct.c_void_p(q), wbytes, ct.c_void_p(_dev_ptr(sink)),
+                                    int(blocks), ct.c_void_p(_stream(stream))))
 
 
 def cg_stream_copy(src, dst, blocks, stream=None):

@@ -63,6 +63,7 @@ SIGNATURES = {
     "cg_true_residual_noalloc": (ct.c_int, [vp, vp, vp, vp, vp]),
     "cg_stream_read": (ct.c_int, [vp, i64, vp, i32, vp]),
     "cg_stream_copy": (ct.c_int, [vp, vp, i64, i32, vp]),
+    "cg_stream_mix": (ct.c_int, [vp, i64, vp, i64, vp, i32, vp]),
     "cg_get_map_trace": (ct.c_int, [vp, i32, vp, vp]),
     "cg_export_layout": (ct.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp]),
     "cg_export_column_scale": (ct.c_int, [vp, vp]),
