@@ -88,5 +88,11 @@ int main(void) {
     for (int i = 0; i < nk && i < 4; ++i) printf(" %d:%.17g", (int)intervals[i], fractions[i]);
     printf("\n");
     printf("version %d\n", cg_version());
+
+    /* Bandwidth references: argument errors come back before any device call. */
+    double sink[1];
+    printf("stream_rc %d %d %d %d %d\n", cg_stream_read(NULL, 16, sink, 1, NULL),
+           cg_stream_copy(val, NULL, 16, 1, NULL), cg_stream_mix(val, 15, NULL, 0, sink, 1, NULL),
+           cg_stream_mix(val, 16, NULL, 16, sink, 1, NULL), cg_stream_mix(NULL, 16, NULL, 0, sink, 0, NULL));
     return 0;
 }

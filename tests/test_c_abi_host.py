@@ -95,3 +95,5 @@ def test_c_error_path_and_host_helpers(output):
     assert nk == len(ref) and got == {int(K): float(f) for K, f in ref}
     assert got == {1: 0.0, 2: 1.0}
     assert int(output["version"]) >= 10300
+    # every stream reference rejects its bad arguments with CG_EINVAL (-1), no device call made
+    assert _ints(output["stream_rc"]) == [-1] * 5
