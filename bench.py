@@ -108,6 +108,20 @@ def time_events(torch, fn, reps, warm=5):
     return e0.elapsed_time(e1) / reps
 
 
+def median_launch_ms(torch, fn, reps=20, warm=5):
+    """Median over reps launches of fn(), each between its own pair of HIP events on the
+    current stream, after warm untimed launches."""
+    for _ in range(warm):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
 def bandwidth_references(torch, dev, mpcg, write_share=None):
     """Read-only and copy bandwidth of the library's stream kernels on 2 GiB buffers (best grid);
     with write_share (bytes written per byte read), also a 2 GiB read stream that writes that
@@ -274,8 +288,9 @@ def main():
                     ("tile_rule_first_window", m_first)):
         S.cg_set_precision_map(m)
         t_ms = time_events(torch, lambda: S.cg_spmv(xin, y), args.spmv_reps, 10)
+        med_ms = median_launch_ms(torch, lambda: S.cg_spmv(xin, y))
         nb = spmv_algorithmic_bytes(L, m)
-        spmv[name] = {"us": round(t_ms * 1e3, 2), "algorithmic_bytes": nb,
+        spmv[name] = {"us": round(t_ms * 1e3, 2), "us_median_of_20": round(med_ms * 1e3, 2), "algorithmic_bytes": nb,
                       "gbs": round(nb / (t_ms * 1e-3) / 1e9, 1),
                       "frac_hbm": round(nb / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "map_nnz_fp64_fp32_bf16": [int(v) for v in
