@@ -465,6 +465,7 @@ struct SpmvArgs {
     int32_t stage_shift;   // staged batches: log2 of the 16-byte chunks per column block (C / 2)
     int32_t stage_doubles; // LDS doubles of one wavefront's vector stage (0: no staged batch)
     int32_t nt;            // CG mode: streaming stores of q (see store_vec)
+    int32_t planes_map;    // per-tile map: values from the precision planes, not the packed segments
 };
 
 template <typename MetaT>
@@ -882,7 +883,7 @@ __device__ __forceinline__ double spmv_wave(const SpmvArgs& a, double* __restric
     // Values come from the precision planes under a uniform precision or the
     // max|p| rule (which changes the map every iteration), else from the map's
     // packed segment.
-    const bool from_planes = CB || uprec >= 0;
+    const bool from_planes = CB || uprec >= 0 || a.planes_map != 0;
     c.desc = desc;
     c.acc = reinterpret_cast<char*>(acc);
     c.spare = (MAXROWS + lane) * 8;
@@ -986,7 +987,7 @@ __device__ __forceinline__ double spmv_wave_multi(const SpmvArgs& a, double* __r
     c.tcol = a.tcol;
     c.cbcode = a.cbcode;
     c.xcb = a.xcb;
-    const bool from_planes = CB || uprec >= 0;
+    const bool from_planes = CB || uprec >= 0 || a.planes_map != 0;
     c.desc = desc;
     c.acc = reinterpret_cast<char*>(acc);
     c.spare = (MAXROWS + lane) * 8;
@@ -1629,7 +1630,6 @@ struct MapArgs {
     int32_t* trace_k;
     int32_t* trace_counts;
     const int32_t* btab;  // tile rule: batches of the SpMV (a partition of the tiles)
-    RepackArgs rp;        // tile rule with repack = 1: the packed values to rebuild
     uint8_t* winmaps;     // tile rule, recording on: [window][T] map of every window (else NULL)
     const uint8_t* count_w;  // per tile: 1 if it counts in the trace (one piece per tile of R > 256), or NULL: all
     int64_t T;
@@ -1637,7 +1637,6 @@ struct MapArgs {
     double rho;          // explicit rho (eval mode)
     int32_t solve;       // 1: in-solve window step (reads k and rho_k from the state)
     int32_t winmap_cap;  // windows winmaps holds
-    int32_t repack;      // tile rule: rebuild the packed values of every batch with a changed tile
 };
 
 // The block's totals of three per-thread counts, returned in thread c for
@@ -1672,11 +1671,10 @@ __device__ inline void block_counts_out(unsigned c0, unsigned c1, unsigned c2, i
 
 // Windowed tile rule: at k % period == 0 every tile's precision is re-selected
 // from its score and rho_k, and the window's precision counts are recorded.
-// One wavefront per SpMV batch (lane l: the batch's tile l); with repack = 1
-// the wavefront rebuilds the packed values of a batch in which a tile changed
-// precision, right away (the other batches' packed values stay valid). The
-// grid is sized to the batches; block b adds its counts to slot
-// b % kTraceBlocks of the entry.
+// One wavefront per SpMV batch (lane l: the batch's tile l). The grid is sized
+// to the batches; block b adds its counts to slot b % kTraceBlocks of the
+// entry. Nothing is repacked: while the tile rule owns the map, the SpMV reads
+// each tile's values from its precision's plane.
 __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
     State* st = a.st;
     double rho = a.rho;
@@ -1689,8 +1687,6 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
         slot = k / st->period;
         if (slot >= st->trace_cap) slot = -1;
     }
-    __shared__ int s_toff[kWavesPerBlock][kTileBatch];
-    __shared__ int s_prec[kWavesPerBlock][kTileBatch];
     unsigned c0 = 0, c1 = 0, c2 = 0;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
@@ -1698,12 +1694,9 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
     for (int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + w; b < a.nbatch; b += waves) {
         const int32_t* e = a.btab + b * kBtFields;
         const int tb = e[kBtTile], nt = e[kBtTiles];
-        bool changed = false;
-        int code = 0;
         if (lane < nt) {
             const int64_t t = (int64_t)tb + lane;
-            code = tile_rule_code(a.scores[t], rho, st->hi, st->lo);
-            changed = code != (int)a.map[t];
+            const int code = tile_rule_code(a.scores[t], rho, st->hi, st->lo);
             a.map[t] = (uint8_t)code;
             if (slot >= 0 && slot < a.winmap_cap) a.winmaps[(size_t)slot * a.T + t] = (uint8_t)code;
             const bool counted = !a.count_w || a.count_w[t];
@@ -1711,7 +1704,6 @@ __global__ __launch_bounds__(kBlock) void tile_rule_kernel(MapArgs a) {
             c1 += counted && code == 1;
             c2 += counted && code == 2;
         }
-        if (a.repack && __any(changed)) repack_batch(a.rp, e, lane, code, s_toff[w], s_prec[w]);
     }
     if (slot >= 0) {
         const unsigned t = block_count3(c0, c1, c2);

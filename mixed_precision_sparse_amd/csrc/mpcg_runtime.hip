@@ -53,6 +53,7 @@ struct cg_handle {
     int32_t single_block = 0;      // cg_options.single_block: 0 auto, 1 when supported, -1 never
     bool stage_x = false;          // cg_options.stage_x: vector segments staged in LDS per batch
     uint8_t* winmaps = nullptr;    // cg_record_window_maps: [winmap_cap][T] tile-rule window maps
+    bool planes_map = false;       // a solve's tile rule changed the map: packed values stale until a repack
     int32_t winmap_cap = 0;
     int64_t nseg = 0;              // SpMV segments: S * ngroups (slice-major)
     std::vector<int32_t> dperm;    // device tile -> canonical tile (slices or slabs; empty: identity)
@@ -304,6 +305,11 @@ dev::SpmvArgs spmv_args(cg_handle* h, const double* x, double* y, const int32_t*
     a.stage_shift = h->stage_shift;
     a.stage_doubles = (int32_t)h->stage_doubles;
     a.nt = h->nt_stores ? 1 : 0;
+    // Under the windowed tile rule (and until the next repack after one of its
+    // solves) each tile's values come from its precision's plane: the rule
+    // changes the map every window, and reading the planes measured no slower
+    // on its maps than a repack per window plus reading packed segments.
+    a.planes_map = (h->sched == kSchedTileRule || h->planes_map) ? 1 : 0;
     return a;
 }
 
@@ -407,7 +413,9 @@ hipError_t repack(cg_handle* h) {
     launch_repack(h, h->stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return hipStreamSynchronize(h->stream);
+    e = hipStreamSynchronize(h->stream);
+    if (e == hipSuccess) h->planes_map = false;
+    return e;
 }
 
 dev::VecArgs vec_args(cg_handle* h, const double* b, const double* x0) {
@@ -450,7 +458,6 @@ dev::MapArgs map_args(cg_handle* h, double rho, int solve) {
     a.trace_k = h->trace_k;
     a.trace_counts = h->trace_counts;
     a.btab = h->btab;
-    a.rp = repack_args(h);
     a.winmaps = h->winmaps;
     a.winmap_cap = h->winmap_cap;
     a.count_w = h->dcount;
@@ -535,7 +542,6 @@ void launch_vec_kernel(cg_handle* h, const dev::VecArgs& va, hipStream_t s) {
 void enqueue_iteration(cg_handle* h, int i, hipStream_t s, bool rule_at_end = false) {
     if (h->sched == kSchedTileRule && i % h->period == 0) {
         dev::MapArgs ma = map_args(h, 0.0, 1);
-        ma.repack = 1;  // the batches whose tiles change precision are repacked in the same launch
         hipLaunchKernelGGL(dev::tile_rule_kernel, dim3(tile_rule_grid(h)), dim3(dev::kBlock), 0, s, ma);
     }
     dev::SpmvArgs sa = spmv_args(h, h->p, h->S > 1 ? h->qpart : h->q, &h->st->uprec);
@@ -1808,7 +1814,10 @@ extern "C" int cg_solve(cg_handle* h, const double* b, const double* x0, double 
         drop_graph(h);
     }
     int64_t need_trace = 16;
-    if (h->sched == kSchedTileRule) need_trace = maxit / h->period + 2;
+    if (h->sched == kSchedTileRule) {
+        need_trace = maxit / h->period + 2;
+        h->planes_map = true;  // the windows change the map without repacking it
+    }
     if (h->sched == kSchedResidual) need_trace = (int64_t)h->stage_prec.size() + 1;
     if (h->sched == kSchedPMag) need_trace = (int64_t)maxit / h->pm_period + 2;
     if (need_trace > h->trace_cap) {

@@ -422,17 +422,20 @@ def test_tile_rule_window_maps_bit_exact(dev):
     S.close()
 
 
-def test_tile_rule_packed_values_follow_the_map_after_a_solve(dev):
-    """In a solve the tile rule repacks only the batches whose tiles changed
-    precision; afterwards cg_spmv under the final map matches the oracle."""
+def test_tile_rule_products_follow_the_map_after_a_solve(dev):
+    """In a solve the tile rule changes the map every window and the SpMV reads each
+    tile's values from its precision's plane (no repack). Afterwards cg_spmv under the
+    final map matches the oracle: with the rule still set, after the schedule is
+    cleared (the packed values are stale then, so the product must keep reading the
+    planes), and after a new map is uploaded (and repacked)."""
     w = make_workload(5, "small")
     A = w.A
     L, Lo = build_both(w)
     s = tile_scores(L.T, 2)
     S = mpcg.Solver(L)
-    S.cg_set_schedule_tile_rule(10, s, w.map_spec["hi"], w.map_spec["lo"])
     bd = torch.from_numpy(w.b).to(dev)
     for maxit in (35, 120, 400):
+        S.cg_set_schedule_tile_rule(10, s, w.map_spec["hi"], w.map_spec["lo"])
         xd = torch.zeros_like(bd)
         S.cg_solve(bd, xd, w.tol, maxit)
         ks, counts = S.cg_get_map_trace()
@@ -441,4 +444,10 @@ def test_tile_rule_packed_values_follow_the_map_after_a_solve(dev):
         assert len(ks) >= 2 and len({tuple(c) for c in counts.tolist()}) >= 2  # the map really changed
         x = np.random.default_rng(maxit).uniform(-1, 1, A.n)
         spmv_check(S, Lo, A, m, x, dev)
+        S.cg_clear_schedule()
+        assert np.array_equal(S.cg_get_active_map(), m)
+        spmv_check(S, Lo, A, m, x, dev)
+        m2 = np.random.default_rng(maxit + 1).integers(0, 3, L.T).astype(np.uint8)
+        S.cg_set_precision_map(m2)
+        spmv_check(S, Lo, A, m2, x, dev)
     S.close()
