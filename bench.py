@@ -204,6 +204,10 @@ def main():
                     help="counter run on the headline workload: the 256 MiB copy of cg_stream_copy (the "
                          "scale reference), then 5 cg_spmv launches per map (all FP64, 50/30/20 mixed, "
                          "all BF16); no timing")
+    ap.add_argument("--map-switch-probe", action="store_true",
+                    help="copy-trace run on the headline workload: after the handle is built, three map "
+                         "switches (cg_set_precision_map), each followed by one cg_spmv; prints the bytes a "
+                         "switch should move (the map) beside the matrix's value and index bytes")
     ap.add_argument("--spmv-only", action="store_true",
                     help="kernel-trace run on the headline workload: --spmv-reps timed cg_spmv launches under "
                          "the all-FP64 map and nothing else on the GPU; prints one JSON line")
@@ -268,6 +272,9 @@ def main():
 
     if args.pmc_probe:
         pmc_probe(torch, dev, S, L, A, xin, y, scores, mpcg)
+        return
+    if args.map_switch_probe:
+        map_switch_probe(torch, S, L, xin, y, scores)
         return
     if args.spmv_only:
         spmv_ms = time_events(torch, lambda: S.cg_spmv(xin, y), args.spmv_reps, 10)
@@ -599,6 +606,26 @@ def pmc_probe(torch, dev, S, L, A, xin, y, scores, mpcg):
         torch.cuda.synchronize()
         print(f"# pmc probe: 5 cg_spmv launches, {name} map, algorithmic bytes "
               f"{spmv_algorithmic_bytes(L, m)}", file=sys.stderr, flush=True)
+
+
+def map_switch_probe(torch, S, L, xin, y, scores):
+    """Launch sequence for a memory-copy trace: one cg_spmv, then three map switches on the live
+    handle, each followed by one cg_spmv. A switch must move the map (one byte per tile) and
+    nothing of the matrix: the packed copy of the selected values is rebuilt on the device from
+    the resident planes. The copies after the first product's dispatch are the switches'."""
+    from gen import static_map
+
+    S.cg_spmv(xin, y)  # everything before this product is set-up; the switches come after it
+    torch.cuda.synchronize()
+    print(f"# map switch probe: T = {L.T} tiles (map bytes), nnz = {L.nnz}: values "
+          f"{14 * L.nnz} bytes in three planes, indices {L.nnz * (2 if max(L.R, L.C) > 16 else 1)} bytes",
+          file=sys.stderr, flush=True)
+    for name, m in (("mixed_50_30_20", static_map(scores, 0.2, 0.3)), ("bf16", np.full(L.T, 2, np.uint8)),
+                    ("fp64", np.zeros(L.T, np.uint8))):
+        S.cg_set_precision_map(m)
+        S.cg_spmv(xin, y)
+        torch.cuda.synchronize()
+        print(f"# map switch probe: switched to {name}, one cg_spmv", file=sys.stderr, flush=True)
 
 
 def _counter_rows(d):
