@@ -110,3 +110,31 @@ def test_handles_return_their_device_memory(dev):
     log(f"device bytes per handle {held}, free memory change {free0 - free1} bytes")
     assert held > 0
     assert free0 - free1 <= 4 << 20  # allocator granularity, not leaked handles
+
+
+def test_device_allocation_failure_is_reported_and_harmless(dev):
+    """A device allocation that cannot succeed (window maps for 2^31 - 1 windows: terabytes)
+    comes back as CG_ENOMEM with a message, records nothing, and leaves the handle solving
+    exactly as before, window recording included."""
+    w = make_workload(5, "small")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    S = mpcg.Solver(L)
+    scores = np.random.default_rng(2).uniform(0, 1, L.T)
+    S.cg_set_schedule_tile_rule(10, scores, w.map_spec["hi"], w.map_spec["lo"])
+    b = torch.from_numpy(w.b).to(dev)
+    x = torch.zeros_like(b)
+    ref = S.cg_solve(b, x, w.tol, 200)
+    with pytest.raises(mpcg.CGError) as e:
+        S.cg_record_window_maps(2**31 - 1)
+    assert e.value.code == mpcg.CG_ENOMEM and "allocation" in str(e.value), str(e.value)
+    log(f"  {e.value}")
+    x2 = torch.zeros_like(b)
+    got = S.cg_solve(b, x2, w.tol, 200)
+    torch.cuda.synchronize()
+    assert got[:2] == ref[:2] and np.array_equal(got[2], ref[2]) and torch.equal(x, x2)
+    assert S.cg_get_window_maps().shape[0] == 0  # nothing was being recorded
+    S.cg_record_window_maps(4)  # a possible request still works afterwards
+    S.cg_solve(b, x2, w.tol, 200)
+    assert S.cg_get_window_maps().shape[0] == 4
+    S.close()
