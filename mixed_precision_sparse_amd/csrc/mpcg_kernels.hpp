@@ -1289,12 +1289,17 @@ __global__ __launch_bounds__(kBlock) void cg_init_finish_kernel(VecArgs a) {
         st->stage = 0;
         st->alpha = 0.0;
         st->beta = 0.0;
-        const double rho0 = st->norm0 > 0.0 ? 1.0 : 0.0;
+        // A non-finite r0 (b or x0 holds a NaN or an infinity) starts at rho_0 = 1
+        // and, past the tolerance and iteration-cap tests, stops as a breakdown
+        // before the first update: its p.q would not be finite.
+        const bool finite = isfinite(st->norm0);
+        const double rho0 = (st->norm0 > 0.0 || !finite) ? 1.0 : 0.0;
         a.hist[0] = rho0;
         if (st->nstage > 0) advance_stage(st, a.trace_k, a.trace_counts, 0, rho0, a.T, true);
         int done = 0;
         if (st->norm0 == 0.0 || rho0 <= st->tol) done = 1;
         else if (st->maxit <= 0) done = 2;
+        else if (!finite) done = 3;
         store_done(st, done);
     }
 }

@@ -40,6 +40,9 @@ CASES = {
     "alpha_overflow": _diag_case([1e-310, 1.0, 1.0, 1.0], [1.0, 0.0, 0.0, 0.0]),
     # alpha = 1e200 finite, r_new.r_new overflows -> beta = inf after the update
     "beta_overflow": _diag_case([1e-250, 1.0], [1e100, 1.0]),
+    # a NaN or an infinity in b: r0 is not finite -> rho_0 = 1, breakdown before the first update
+    "b_nan": _diag_case([2.0, 3.0, 4.0, 5.0], [1.0, np.nan, 0.0, 0.0]),
+    "b_inf": _diag_case([2.0, 3.0, 4.0, 5.0], [1.0, -np.inf, 0.0, 0.0]),
 }
 
 
@@ -64,3 +67,24 @@ def test_breakdown_matches_oracle(case, single_block, dev):
     xs = x.cpu().numpy()
     np.testing.assert_allclose(xs, ref.x, rtol=1e-14, atol=0.0)
     S.close()
+
+
+@pytest.mark.parametrize("tol, maxit", [(1.0, 10), (1e-30, 0), (0.5, 0)])
+@pytest.mark.parametrize("single_block", [1, -1])
+def test_non_finite_rhs_follows_the_stopping_order(tol, maxit, single_block, dev):
+    """With a non-finite b the tolerance test (rho_0 = 1 <= tol) and the iteration cap come
+    first, as in the oracle; only past them does the solve stop as a breakdown."""
+    M, b = CASES["b_nan"]
+    n = M.shape[0]
+    L = mpcg.cg_tilecsc_from_csr(n, M.indptr.astype(np.int64), M.indices.astype(np.int32), M.data, 4, 4)
+    Lo = otc.build(n, M.indptr, M.indices, M.data, 4, 4)
+    ref = ocg.solve(Lo, M.indptr, M.indices, M.data, b, ocg.StaticSchedule(np.zeros(Lo.T, np.uint8)), tol, maxit)
+    S = mpcg.Solver(L, single_block=single_block)
+    bd = torch.from_numpy(b).to(dev)
+    x = torch.full_like(bd, float("nan"))
+    status, K, hist = S.cg_solve(bd, x, tol, maxit)
+    assert (status, K) == (ref.status, ref.K) and ref.status in ("converged", "maxit")
+    np.testing.assert_array_equal(hist, ref.hist)
+    np.testing.assert_array_equal(x.cpu().numpy(), ref.x)
+    S.close()
+

@@ -176,6 +176,15 @@ def test_degenerate_inputs():
     xs = np.array([1.0, 2.0, 3.0])
     ex = _solve(M, M @ xs, 1e-10, 10, x0=xs)  # exact initial guess
     assert ex.K == 0 and np.array_equal(ex.x, xs)
+    # A NaN or an infinity in b (reading R8 with R6): r0 is not finite, rho_0 = 1; the
+    # tolerance test and the cap come first, then the first p.q is not finite: breakdown
+    # before any update.
+    for bad in (np.nan, np.inf, -np.inf):
+        b = np.array([1.0, bad, 0.0])
+        nf = _solve(M, b, 1e-10, 10)
+        assert nf.status == "breakdown" and nf.K == 0 and nf.hist == [1.0] and not nf.x.any()
+        assert _solve(M, b, 1.0, 10).status == "converged"
+        assert _solve(M, b, 1e-10, 0).status == "maxit"
 
 
 def test_integer_stencil_mixed_map_reproduces_fp64_history():
