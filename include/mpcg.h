@@ -381,7 +381,9 @@ int cg_spmv(cg_handle* h, const double* x, double* y, void* stream);
  *   stream     : the solve is ordered after prior work on stream; the call
  *                returns when the solve has finished.
  * Returns CG_OK (converged), CG_NOT_CONVERGED (K = maxit), CG_BREAKDOWN
- * (p.q <= 0 or non-finite alpha/beta; x holds the last iterate), or an error:
+ * (p.q <= 0 or non-finite alpha/beta; x holds the last iterate; a NaN or an
+ * infinity in b or x0 gives rho_0 = 1 and, past the tolerance and cap tests,
+ * a breakdown with K = 0), or an error:
  * CG_EINVAL (NULL h, b, x or iterations, tol < 0, maxit < 0), CG_ENOMEM,
  * CG_EDEVICE.
  */
