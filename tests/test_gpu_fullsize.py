@@ -5,8 +5,9 @@ CG results in tests/golden/cg_cfg*_full.json (written by
 tests/golden/make_golden.py, which calls only gen and oracle), and the SpMV
 compared on every row with the oracle's product of the rounded matrix
 (oracle.spmv.spmv_full), under the FP64 map, a random mixed map and the
-workload's own map (for the windowed tile rule: the map and packed values
-left by a short solve whose later windows rebuild only changed batches).
+workload's own map (for the windowed tile rule: the map left by a short
+solve whose later windows change it without a repack; the product reads
+every tile from its precision's plane).
 """
 
 import hashlib
@@ -134,15 +135,15 @@ def test_fullsize_layout_and_spmv(cfg, dev):
             S.cg_eval_tile_rule(rho)
             assert np.array_equal(S.cg_get_active_map(), omaps.tile_rule(sc, rho, w.map_spec["hi"], w.map_spec["lo"]))
         log(f"cfg{cfg}: tile-rule maps equal the oracle's")
-        # A short solve: its windows at k = 10 and 20 rebuild only the batches whose tiles
-        # changed precision; the product afterwards reads that packed state.
+        # A short solve: its windows at k = 10 and 20 change the map without any repack;
+        # the product afterwards reads every tile from its precision's plane.
         bd = torch.from_numpy(w.b).to(dev)
         xs = torch.zeros_like(bd)
         st, K, hist = S.cg_solve(bd, xs, w.tol, 25)
         assert K == 25
         m = S.cg_get_active_map()
         assert np.array_equal(m, omaps.tile_rule(sc, hist[20], w.map_spec["hi"], w.map_spec["lo"]))
-        check_all_rows("tile rule window k=20 (after partial repacks)", m)
+        check_all_rows("tile rule window k=20 (after in-solve map changes)", m)
     S.close()
 
 
