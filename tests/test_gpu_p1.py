@@ -277,6 +277,45 @@ def test_p1_cg_matches_oracle(cfg, flags, dev):
     S.close()
 
 
+@pytest.mark.parametrize("flags", [RV | CS, CS | PAD])
+def test_p1_tile_rule_matches_oracle(flags, dev):
+    """The paper's numerics under the windowed per-tile rule, whose maps the product reads
+    from the value planes: the run agrees with the oracle's (same windows, rounding, scale
+    and padding), and its window maps equal the oracle's while the trajectories agree."""
+    w = make_workload(5, "small")
+    A = w.A
+    L, Lo = _both(A, w.R, w.C)
+    ms = w.map_spec
+    tol = 1e-2 if flags & RV else w.tol
+    sched = ocg.TileRuleSchedule(tile_scores(Lo.T, 2), ms["period"], ms["hi"], ms["lo"])
+    log(f"p1 tile rule flags={flags} n={w.n} tol={tol}")
+    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, w.b, sched, tol, w.maxit,
+                    round_vector=bool(flags & RV), column_scale=bool(flags & CS))
+    S = mpcg.Solver(L, p1=flags)
+    S.cg_set_schedule_tile_rule(ms["period"], tile_scores(L.T, 2), ms["hi"], ms["lo"])
+    S.cg_record_window_maps(w.maxit // ms["period"] + 2)
+    bd = torch.from_numpy(w.b).to(dev)
+    xd = torch.zeros_like(bd)
+    status, K, hist = S.cg_solve(bd, xd, tol, w.maxit)
+    x = xd.cpu().numpy()
+    tr = float(np.linalg.norm(w.b - A.to_scipy() @ x) / np.linalg.norm(w.b))
+    log(f"  gpu {status} K={K} true={tr:.3e}; oracle {ref.status} K={ref.K} true={ref.true_residual:.3e}")
+    assert status == ref.status and _k_close(K, ref.K), (status, K, ref.status, ref.K)
+    assert _agree(tr, ref.true_residual, tol), (tr, ref.true_residual)
+    m = min(K, ref.K, 20)
+    assert np.allclose(hist[: m + 1], ref.hist[: m + 1], rtol=1e-6, atol=0)
+    maps = S.cg_get_window_maps()
+    checked = 0
+    for i, (wk, _c, mref) in enumerate(ref.windows):
+        if i >= len(maps) or wk > min(K, ref.K) or abs(hist[wk] - ref.hist[wk]) > 1e-9 * ref.hist[wk]:
+            break
+        assert np.array_equal(maps[i], mref), (i, wk)
+        checked += 1
+    log(f"  {checked} window maps equal the oracle's")
+    assert checked >= 2
+    S.close()
+
+
 def test_p1_jacobi_ratchet_with_padding(dev):
     """Padding changes storage only: the padded Jacobi-PCG ratchet run matches the plain oracle."""
     w = make_workload(4, "small")
