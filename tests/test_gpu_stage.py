@@ -96,3 +96,27 @@ def test_staged_cg_matches_oracle(cfg, mapkind, dev):
     assert abs(max(tr, w.tol) - max(ref.true_residual, w.tol)) <= 1e-2 * max(ref.true_residual, w.tol)
     np.testing.assert_allclose(hist[:20], ref.hist[:20], rtol=1e-6)
     S.close()
+
+
+def test_staged_tile_rule_solve_equals_unstaged(dev):
+    """Under the windowed tile rule the product reads every tile from its precision's plane;
+    the staged sweep must still form the same products in the same order, so a staged and an
+    unstaged handle run the same solve bit for bit."""
+    w = make_workload(5, "small")
+    A = w.A
+    ms = w.map_spec
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    runs = []
+    for stage in (1, 0):
+        S = mpcg.Solver(L, stage_x=stage, single_block=-1)
+        S.cg_set_schedule_tile_rule(ms["period"], tile_scores(L.T, 2), ms["hi"], ms["lo"])
+        bd = torch.from_numpy(w.b).to(dev)
+        x = torch.zeros_like(bd)
+        status, K, hist = S.cg_solve(bd, x, w.tol, 300)
+        torch.cuda.synchronize()
+        runs.append((status, K, np.asarray(hist).copy(), x.cpu().numpy(), S.cg_get_map_trace()[1].copy()))
+        S.close()
+    (s1, k1, h1, x1, c1), (s0, k0, h0, x0, c0) = runs
+    log(f"staged tile rule: K={k1} {s1}, unstaged K={k0} {s0}, {len(c1)} windows")
+    assert (s1, k1) == (s0, k0) and np.array_equal(h1, h0) and np.array_equal(x1, x0)
+    assert np.array_equal(c1, c0) and len(c1) >= 3
