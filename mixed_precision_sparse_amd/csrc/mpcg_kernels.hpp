@@ -1033,9 +1033,12 @@ __device__ __forceinline__ double spmv_wave_multi(const SpmvArgs& a, double* __r
             if (MODE == kSpmvCg && MAXROWS > kWave) {
                 // The group's own p entries (for p.q at the group's end) go to LDS
                 // now, 16 bytes per lane by LDS-direct loads; the sweeps' waits
-                // cover them. Entries past n read as zero.
-                for (int j = 0; j < a.rows_per_group / 2; j += kWave)
-                    if (j + lane < a.rows_per_group / 2)
+                // cover them. An odd group (R odd) takes one pair more, whose
+                // second entry is the next group's and is not used; entries past
+                // n read as zero.
+                const int npairs = (a.rows_per_group + 1) / 2;
+                for (int j = 0; j < npairs; j += kWave)
+                    if (j + lane < npairs)
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (__attribute__((address_space(3))) void*)(pown + 2 * j),
                                                                  16, row0 * 8 + (j + lane) * 16, 0, 0, 0);
             }

@@ -451,3 +451,41 @@ def test_tile_rule_products_follow_the_map_after_a_solve(dev):
         S.cg_set_precision_map(m2)
         spmv_check(S, Lo, A, m2, x, dev)
     S.close()
+
+
+@pytest.mark.parametrize("R", [3, 5, 13])
+@pytest.mark.parametrize("rule", ["tile_rule", "pmag"])
+def test_cg_odd_row_groups(R, rule, dev):
+    """Row groups of an odd number of rows above 64 (odd R; here the small-system sizing,
+    about 16 groups): the CG-mode product's p.q must use every row's own p entry. Runs the
+    multi-launch path under the tile rule and the max|p| rule against the oracle."""
+    import scipy.sparse as sp
+
+    m = 36  # 1296 rows: groups of 27, 17 and 7 row blocks, 81, 85 and 91 rows
+    T1 = sp.diags([-1.0, 2.0, -1.0], [-1, 0, 1], shape=(m, m))
+    M = (sp.kron(sp.eye(m), T1) + sp.kron(T1, sp.eye(m))).tocsr()
+    M.sort_indices()
+    n = M.shape[0]
+    indptr, indices, data = M.indptr.astype(np.int64), M.indices.astype(np.int32), M.data.astype(np.float64)
+    b = M @ np.random.default_rng(R).uniform(-1, 1, n)
+    C = 2
+    L = mpcg.cg_tilecsc_from_csr(n, indptr, indices, data, R, C)
+    Lo = otc.build(n, indptr, indices, data, R, C)
+    S = mpcg.Solver(L)  # automatic sizing: one workgroup's row groups
+    assert S.cg_get_options()["single_block"] == 1
+    if rule == "tile_rule":
+        scores = np.random.default_rng(7).uniform(0, 1, L.T) * 10.0 ** np.random.default_rng(8).integers(-2, 3, L.T)
+        S.cg_set_schedule_tile_rule(3, scores, 1e-1, 1e-4)
+        sched = ocg.TileRuleSchedule(scores, 3, 1e-1, 1e-4)
+    else:
+        S.cg_set_schedule_pmag(1e-6, 1e-3)
+        sched = ocg.PMagSchedule(Lo.C, Lo.tile_col_idx, 1e-6, 1e-3)
+    ref = ocg.solve(Lo, indptr, indices, data, b, sched, 1e-10, 500, keep_maps=False)
+    bd = torch.from_numpy(b).to(dev)
+    xd = torch.zeros_like(bd)
+    status, K, hist = S.cg_solve(bd, xd, 1e-10, 500)
+    log(f"odd groups R={R} {rule}: gpu {status} K={K}; oracle {ref.status} K={ref.K}")
+    assert status == ref.status and _k_close(K, ref.K), (status, K, ref.status, ref.K)
+    k = min(K, ref.K, 20)
+    assert np.allclose(hist[: k + 1], ref.hist[: k + 1], rtol=1e-6, atol=0)
+    S.close()
