@@ -1,13 +1,17 @@
 """Seeded random configurations against the oracle: random SPD matrices and tile shapes (row
-blocks from 1 to 1024 rows, tiles from 1 to 256 columns, odd sizes included), maps and schedules (static map,
-magnitude rule, windowed tile rule, max|p| rule, residual ratchet), and handle options
-(Jacobi, column slices, vector staging, the single-workgroup solve, the paper's SpMV numerics).
-Every case checks the SpMV on every row (1e-13 (|A||x|)_i, or the oracle's own bound with the
-paper's numerics) and a CG solve against the oracle: the first 20 residuals to 1e-6 always; for
-runs the oracle finishes within 150 iterations also the status, K within 2 % and the true
-residual within 1e-2; slower or capped runs, whose end depends on the summation order, must not
-end more than ten times behind the oracle's true residual. The cases are drawn once from a
-fixed seed."""
+blocks from 1 to 1024 rows, tiles from 1 to 256 columns, odd sizes included), maps and
+schedules (static map, magnitude rule, windowed tile rule, max|p| rule, residual ratchet), and
+handle options (Jacobi, column slices, vector staging, the single-workgroup solve, the paper's
+SpMV numerics). Every case checks:
+- the exported layout and value planes, bit for bit;
+- the SpMV on every row (1e-13 (|A||x|)_i, or the oracle's own bound with the paper's numerics);
+- a CG solve: the first 20 residuals to 1e-6 always; for runs the oracle finishes within 150
+  iterations also the status, K within 2 % and the true residual within 1e-2; slower or capped
+  runs, whose end depends on the summation order, must not end more than ten times behind the
+  oracle's true residual;
+- the library's true residual and its allocation-free twin (the same bits) against the host's,
+  up to the rounding of b - A x.
+The cases are drawn once from a fixed seed."""
 
 import sys
 
@@ -15,7 +19,7 @@ import numpy as np
 import pytest
 import scipy.sparse as sp
 
-from oracle import cg as ocg, maps as omaps, spmv as ospmv, tilecsc as otc
+from oracle import cg as ocg, maps as omaps, rounding as ord_, spmv as ospmv, tilecsc as otc
 
 pytestmark = pytest.mark.gpu
 
@@ -109,6 +113,28 @@ def test_random_configuration_matches_oracle(i, dev):
     Lo = otc.build(A.n, A.indptr, A.indices, A.data, R, C)
     S = mpcg.Solver(L, **opts)
 
+    # The exported canonical layout and value planes, bit for bit (device tiles of slabs and
+    # slices mapped back; with the column scale the low planes hold the scaled values).
+    ex = S.cg_export_layout()
+    if opts["p1"] & PAD:  # the padded layout of Fig. 4(b): sentinel entries close odd columns
+        ptr, ridx, cloc, val = otc.padded_layout(Lo)
+        ref = dict(tile_row_ptr=Lo.tile_row_ptr, tile_col_idx=Lo.tile_col_idx, tile_nnz_ptr=ptr, row_idx=ridx,
+                   col_local=cloc)
+        tile = np.repeat(np.arange(Lo.T, dtype=np.int64), np.diff(ptr))
+    else:
+        ref = {k: getattr(Lo, k) for k in ("tile_row_ptr", "tile_col_idx", "tile_nnz_ptr", "row_idx", "col_local")}
+        val, cloc, tile = Lo.val, Lo.local_col(), Lo.tile_of_nnz()
+    for name, arr in ref.items():
+        assert np.array_equal(ex[name].astype(arr.dtype), arr), name
+    assert np.array_equal(ex["val64"].view(np.uint64), val.view(np.uint64))
+    low = val
+    if opts["p1"] & CS:
+        e = ospmv.column_scale_exponents(A.n, A.indptr, A.indices, A.data)
+        col = np.minimum(Lo.tile_col_idx.astype(np.int64)[tile] * C + cloc, A.n - 1)
+        low = np.ldexp(val, -e[col])
+    assert np.array_equal(ex["val32"].view(np.uint32), ord_.to_fp32(low).view(np.uint32))
+    assert np.array_equal(ex["bf16"], ord_.bf16_bits(low))
+
     # SpMV under a random static map, every row.
     m = rng.integers(0, 3, L.T).astype(np.uint8)
     S.cg_set_precision_map(m)
@@ -150,6 +176,16 @@ def test_random_configuration_matches_oracle(i, dev):
     xs = torch.zeros_like(bd)
     status, K, hist = S.cg_solve(bd, xs, tol, maxit)
     tr = float(np.linalg.norm(b - A.S @ xs.cpu().numpy()) / np.linalg.norm(b))
+    # The library's true residual (exact FP64 values) and its allocation-free twin: the same
+    # bits, and the host's value up to the rounding of b - A x.
+    tr_dev = S.cg_true_residual(bd, xs)
+    out = torch.full((1,), float("nan"), dtype=torch.float64, device=dev)
+    S.cg_true_residual_noalloc(bd, xs, out)
+    torch.cuda.synchronize()
+    assert out.item() == tr_dev
+    xh = xs.cpu().numpy()
+    slack = 1e-13 * np.linalg.norm(abs(A.S) @ np.abs(xh) + np.abs(b)) / np.linalg.norm(b)
+    assert abs(tr_dev - tr) <= 1e-10 * tr + slack, (tr_dev, tr)
     log(f"  gpu {status} K={K} true={tr:.3e}; oracle {ref.status} K={ref.K} true={ref.true_residual:.3e}")
     k = min(K, ref.K, 20)
     assert np.allclose(hist[: k + 1], ref.hist[: k + 1], rtol=1e-6, atol=0)
