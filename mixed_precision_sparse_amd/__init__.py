@@ -41,6 +41,17 @@ def _dev_ptr(t) -> int:
     return t.data_ptr()
 
 
+def _vec_ptr(t, n: int, device: int, name: str) -> int:
+    """Device pointer of a float64 vector the library reads or writes n entries of: it must be
+    on the handle's GPU and hold at least n entries (the library cannot check either)."""
+    p = _dev_ptr(t)
+    if t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} entries; the handle needs {n}")
+    if t.device.index != device:
+        raise ValueError(f"{name} is on cuda:{t.device.index}; the handle lives on cuda:{device}")
+    return p
+
+
 def _stream(stream) -> int:
     import torch
 
@@ -155,6 +166,9 @@ class Solver:
         check(lib.cg_get_sizes(self._h, ct.byref(n), ct.byref(T), ct.byref(nnz), None, None))
         # nnz counts the padding sentinels when CG_P1_PAD_COLUMNS is set
         self.n, self.T, self.nnz, self.R, self.C = n.value, T.value, nnz.value, A.R, A.C
+        import torch
+
+        self.device = torch.cuda.current_device()
         self.jacobi = bool(jacobi)
         self.p1 = int(p1)
 
@@ -217,32 +231,37 @@ class Solver:
         check(_lib.load().cg_clear_schedule(self._h))
 
     # -- compute -------------------------------------------------------------
+    def _vec(self, t, name):
+        return _vec_ptr(t, self.n, self.device, name)
+
     def cg_spmv(self, x, y, stream=None):
-        check(_lib.load().cg_spmv(self._h, ct.c_void_p(_dev_ptr(x)), ct.c_void_p(_dev_ptr(y)),
+        check(_lib.load().cg_spmv(self._h, ct.c_void_p(self._vec(x, "x")), ct.c_void_p(self._vec(y, "y")),
                                   ct.c_void_p(_stream(stream))))
 
     def cg_solve(self, b, x, tol, maxit, x0=None, stream=None):
         """Returns (status string, iterations, residual history as a numpy array)."""
         hist = np.empty(int(maxit) + 1, dtype=np.float64)
         it = ct.c_int32()
-        rc = check(_lib.load().cg_solve(self._h, ct.c_void_p(_dev_ptr(b)),
-                                        ct.c_void_p(_dev_ptr(x0)) if x0 is not None else None,
-                                        float(tol), int(maxit), ct.c_void_p(_dev_ptr(x)),
+        rc = check(_lib.load().cg_solve(self._h, ct.c_void_p(self._vec(b, "b")),
+                                        ct.c_void_p(self._vec(x0, "x0")) if x0 is not None else None,
+                                        float(tol), int(maxit), ct.c_void_p(self._vec(x, "x")),
                                         ct.byref(it), _ptr(hist), ct.c_void_p(_stream(stream))))
         return STATUS[rc], int(it.value), hist[: it.value + 1].copy()
 
     def cg_true_residual(self, b, x, stream=None) -> float:
         """||b - A x|| / ||b|| with the exact FP64 values (device vectors in, host float out)."""
         out = ct.c_double()
-        check(_lib.load().cg_true_residual(self._h, ct.c_void_p(_dev_ptr(b)), ct.c_void_p(_dev_ptr(x)),
+        check(_lib.load().cg_true_residual(self._h, ct.c_void_p(self._vec(b, "b")), ct.c_void_p(self._vec(x, "x")),
                                            ct.byref(out), ct.c_void_p(_stream(stream))))
         return float(out.value)
 
     def cg_true_residual_noalloc(self, b, x, out, stream=None):
         """The same value as cg_true_residual, written into the device float64 tensor `out`
         (first entry) on the stream, with no allocation and no synchronisation."""
-        check(_lib.load().cg_true_residual_noalloc(self._h, ct.c_void_p(_dev_ptr(b)), ct.c_void_p(_dev_ptr(x)),
-                                                   ct.c_void_p(_dev_ptr(out)), ct.c_void_p(_stream(stream))))
+        check(_lib.load().cg_true_residual_noalloc(self._h, ct.c_void_p(self._vec(b, "b")),
+                                                   ct.c_void_p(self._vec(x, "x")),
+                                                   ct.c_void_p(_vec_ptr(out, 1, self.device, "out")),
+                                                   ct.c_void_p(_stream(stream))))
 
     def cg_get_map_trace(self, cap=100000):
         ks = np.empty(cap, dtype=np.int32)

@@ -138,3 +138,29 @@ def test_device_allocation_failure_is_reported_and_harmless(dev):
     S.cg_solve(b, x2, w.tol, 200)
     assert S.cg_get_window_maps().shape[0] == 4
     S.close()
+
+
+def test_binding_rejects_vectors_shorter_than_the_matrix(dev):
+    """The C ABI takes device vectors of n doubles on trust; the binding knows n and refuses a
+    shorter tensor before any device call, so no kernel reads or writes past it."""
+    w = make_workload(2, "small")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    S = mpcg.Solver(L)
+    n = A.n
+    full = torch.zeros(n, dtype=torch.float64, device=dev)
+    short = torch.zeros(n - 1, dtype=torch.float64, device=dev)
+    y = torch.empty_like(full)
+    for fn in (lambda: S.cg_spmv(short, y), lambda: S.cg_spmv(full, short),
+               lambda: S.cg_solve(short, y, 1e-8, 10), lambda: S.cg_solve(full, short, 1e-8, 10),
+               lambda: S.cg_solve(full, y, 1e-8, 10, x0=short),
+               lambda: S.cg_true_residual(short, y), lambda: S.cg_true_residual(full, short),
+               lambda: S.cg_true_residual_noalloc(full, y, torch.empty(0, dtype=torch.float64, device=dev))):
+        with pytest.raises(ValueError):
+            fn()
+    with pytest.raises(TypeError):
+        S.cg_spmv(full.float(), y)
+    b = torch.from_numpy(w.b).to(dev)
+    status, K, _ = S.cg_solve(b, y, w.tol, w.maxit)  # the handle is untouched
+    assert status == "converged" and K > 0
+    S.close()
