@@ -190,6 +190,8 @@ class Solver:
     def cg_set_schedule_residual(self, thresholds, prec):
         th = np.ascontiguousarray(thresholds, dtype=np.float64)
         pr = np.ascontiguousarray(prec, dtype=np.uint8)
+        if pr.size < 1 or th.size != pr.size - 1:
+            raise ValueError("need one precision per stage and one threshold fewer than precisions")
         check(_lib.load().cg_set_schedule_residual(self._h, int(pr.size), _ptr(th), _ptr(pr)))
 
     def cg_set_schedule_tile_rule(self, period, scores, hi, lo):

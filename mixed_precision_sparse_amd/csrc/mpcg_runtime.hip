@@ -1599,14 +1599,14 @@ extern "C" int cg_set_schedule_residual(cg_handle* h, int32_t nstage, const doub
     HIP_CHECK(order_after_user(h));
     if (nstage < 1 || nstage > 8) return fail(CG_EINVAL, "cg_set_schedule_residual: nstage must lie in [1, 8]");
     if (nstage > 1 && !thresholds) return fail(CG_EINVAL, "cg_set_schedule_residual: thresholds is NULL");
-    h->thresholds.assign(thresholds, thresholds + (nstage - 1));
-    h->stage_prec.clear();
-    for (int i = 0; i < nstage; ++i) {
+    // Checked in full before the handle changes: a rejected call leaves the schedule as it was.
+    for (int i = 0; i < nstage; ++i)
         if (prec[i] > 2) return fail(CG_EINVAL, "cg_set_schedule_residual: prec values must be 0, 1 or 2");
-        h->stage_prec.push_back(prec[i]);
-    }
-    for (double t : h->thresholds)
-        if (!std::isfinite(t)) return fail(CG_EINVAL, "cg_set_schedule_residual: thresholds must be finite");
+    for (int i = 0; i + 1 < nstage; ++i)
+        if (!std::isfinite(thresholds[i]))
+            return fail(CG_EINVAL, "cg_set_schedule_residual: thresholds must be finite");
+    h->thresholds.assign(thresholds, thresholds + (nstage - 1));
+    h->stage_prec.assign(prec, prec + nstage);
     h->sched = kSchedResidual;
     return upload_schedule(h);
 }

@@ -59,7 +59,11 @@ def test_invalid_arguments_leave_the_handle_usable(dev):
     with pytest.raises(ValueError):
         S.cg_set_precision_map(np.zeros(L.T + 1, np.uint8))
     _rejects(lambda: S.cg_map_from_magnitude(1e-2, 1e-4), "cg_map_from_magnitude")
-    _rejects(lambda: S.cg_set_schedule_residual((1e-3,), (2, 1, 0, 0, 0, 0, 0, 0, 0)), "cg_set_schedule_residual")
+    _rejects(lambda: S.cg_set_schedule_residual((1e-3,) * 8, (2, 1, 0, 0, 0, 0, 0, 0, 0)), "cg_set_schedule_residual")
+    with pytest.raises(ValueError):  # one threshold fewer than precisions, checked by the binding
+        S.cg_set_schedule_residual((1e-3,), (2, 1, 0))
+    with pytest.raises(ValueError):
+        S.cg_set_schedule_residual((), ())
     _rejects(lambda: S.cg_set_schedule_residual((1e-3, 1e-6), (2, 5, 0)), "cg_set_schedule_residual")
     _rejects(lambda: S.cg_set_schedule_residual((np.nan, 1e-6), (2, 1, 0)), "cg_set_schedule_residual")
     scores = np.random.default_rng(2).uniform(0, 1, L.T)
@@ -163,4 +167,32 @@ def test_binding_rejects_vectors_shorter_than_the_matrix(dev):
     b = torch.from_numpy(w.b).to(dev)
     status, K, _ = S.cg_solve(b, y, w.tol, w.maxit)  # the handle is untouched
     assert status == "converged" and K > 0
+    S.close()
+
+
+def test_rejected_residual_schedule_keeps_the_previous_one(dev):
+    """A residual schedule is checked in full before the handle changes: after rejected calls
+    (a bad precision in a later stage, a NaN threshold) the schedule set before them is still
+    the one in force, on the device and on the host side that sizes the stage trace."""
+    w = make_workload(2, "small")
+    A = w.A
+    L = mpcg.cg_tilecsc_from_csr(A.n, A.indptr, A.indices, A.data, w.R, w.C)
+    S = mpcg.Solver(L, single_block=-1)
+    b = torch.from_numpy(w.b).to(dev)
+    S.cg_set_schedule_residual((1e-2, 1e-5), (2, 1, 0))
+    x = torch.zeros_like(b)
+    ref = S.cg_solve(b, x, w.tol, w.maxit)
+    ref_map = S.cg_get_active_map()
+    ref_trace = S.cg_get_map_trace()
+    _rejects(lambda: S.cg_set_schedule_residual((1e-3, 1e-6), (1, 0, 7)), "cg_set_schedule_residual")
+    _rejects(lambda: S.cg_set_schedule_residual((1e-3, np.inf), (0, 0, 0)), "cg_set_schedule_residual")
+    x2 = torch.zeros_like(b)
+    got = S.cg_solve(b, x2, w.tol, w.maxit)
+    torch.cuda.synchronize()
+    log(f"ratchet: {ref[0]} K={ref[1]}; after the rejected calls {got[0]} K={got[1]}")
+    assert got[:2] == ref[:2] and np.array_equal(got[2], ref[2]) and torch.equal(x, x2)
+    assert np.array_equal(S.cg_get_active_map(), ref_map)
+    trace = S.cg_get_map_trace()
+    assert len(ref_trace[0]) >= 2  # the run passed at least one stage threshold
+    assert all(np.array_equal(a, c) for a, c in zip(trace, ref_trace))
     S.close()
