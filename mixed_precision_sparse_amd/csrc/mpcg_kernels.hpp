@@ -184,7 +184,10 @@ __device__ inline void wave_lds_sync() {
 // Q1 solve takes 582 us (597 with plain accesses, 590 with streaming stores
 // only), a 100^3 27-point one 71.4 us (78.7, 77.1). A solve that fits the
 // cache keeps plain accesses (streaming ones made the 128^3 Laplacian 5-6 %
-// slower).
+// slower). One more exception: the update stores plainly the vector that the
+// direction kernel reads right after it (r, or z with Jacobi), which then
+// comes from the cache: 581 -> 576 us on the Q1 solve, no change on the
+// 27-point and power-law ones.
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ double2 load_vec(const double2* p, bool nt) {
     if (!nt) return *p;
@@ -1377,13 +1380,13 @@ __global__ __launch_bounds__(kVecBlock) void cg_update_kernel(VecArgs a) {
                     double2 rn;
                     rn.x = rv[j].x - alpha * qv[j].x;
                     rn.y = rv[j].y - alpha * qv[j].y;
-                    store_vec(&r2[i], rn, NT);
+                    store_vec(&r2[i], rn, NT && JAC);  // r is read next unless z is
                     rr += rn.x * rn.x + rn.y * rn.y;
                     if (JAC) {
                         double2 zn;
                         zn.x = dv[j].x * rn.x;
                         zn.y = dv[j].y * rn.y;
-                        store_vec(&z2[i], zn, NT);
+                        z2[i] = zn;  // read next by the direction kernel
                         rz += rn.x * zn.x + rn.y * zn.y;
                     }
                 }
