@@ -11,8 +11,11 @@ SpMV numerics). Every case checks:
   oracle's true residual;
 - the library's true residual and its allocation-free twin (the same bits) against the host's,
   up to the rounding of b - A x.
-The cases are drawn once from a fixed seed."""
+The cases are drawn once from a fixed seed. Environment overrides for longer sweeps:
+MPCG_RANDOM_SEEDS="a:b" runs the cases of seeds a .. b-1 instead of the first 60, and
+MPCG_RANDOM_LARGE=1 draws n from 100,000 .. 399,999 instead of 40 .. 5,999."""
 
+import os
 import sys
 
 import numpy as np
@@ -28,7 +31,9 @@ mpcg = pytest.importorskip("mixed_precision_sparse_amd")
 
 RV, CS, PAD = mpcg.CG_P1_ROUND_VECTOR, mpcg.CG_P1_COLUMN_SCALE, mpcg.CG_P1_PAD_COLUMNS
 SCHEDULES = ("static", "magnitude", "tile_rule", "pmag", "ratchet")
-NCASES = 60
+_seeds = os.environ.get("MPCG_RANDOM_SEEDS", "0:60").split(":")
+CASES = range(int(_seeds[0]), int(_seeds[1]))
+N_RANGE = (100000, 400000) if os.environ.get("MPCG_RANDOM_LARGE") == "1" else (40, 6000)
 
 
 @pytest.fixture(scope="module")
@@ -57,7 +62,7 @@ class _M:
 def _case(i):
     """One configuration, drawn from its own seed."""
     rng = np.random.default_rng(1000 + i)
-    n = int(rng.integers(40, 6000))
+    n = int(rng.integers(*N_RANGE))
     band = int(rng.integers(1, 9))
     rows, cols = [], []
     for d in range(1, band + 1):
@@ -105,7 +110,7 @@ def _spmv_ref(Lo, A, prec, x, p1):
     return ospmv.spmv(Lo, A.indptr, A.indices, prec, x), 1e-13 * ospmv.abs_bound(A.indptr, A.indices, A.data, x)
 
 
-@pytest.mark.parametrize("i", range(NCASES))
+@pytest.mark.parametrize("i", CASES)
 def test_random_configuration_matches_oracle(i, dev):
     A, R, C, sched, opts, b, rng = _case(i)
     log(f"case {i}: n={A.n} nnz={A.S.nnz} R={R} C={C} schedule={sched} options={opts}")
