@@ -105,18 +105,35 @@ class Result:
     true_residual: float = float("nan")
 
 
-class PerturbedOperator:
-    """Holds the three value streams in CSR order and forms (A + E(map)) on demand."""
+def _row_order(indptr, reverse):
+    """Storage positions of the CSR entries in the order each row is summed: as stored, or
+    every row reversed. Both are plain sums of the same terms; only the rounding differs."""
+    indptr = np.asarray(indptr, dtype=np.int64)
+    nnz = int(indptr[-1])
+    if not reverse:
+        return np.arange(nnz, dtype=np.int64)
+    row = np.repeat(np.arange(indptr.size - 1, dtype=np.int64), np.diff(indptr))
+    pos = np.arange(nnz, dtype=np.int64)
+    return (indptr[row] + indptr[row + 1] - 1 - pos).astype(np.int64)
 
-    def __init__(self, L: TileCSC, indptr, indices, data):
+
+class PerturbedOperator:
+    """Holds the three value streams in CSR order and forms (A + E(map)) on demand.
+
+    reverse_rows sums every row of the product in reverse storage order (the same terms in
+    another order), for telling rounding-order effects from errors."""
+
+    def __init__(self, L: TileCSC, indptr, indices, data, reverse_rows=False):
         self.n = L.n
         self.T = L.T
         tile_canon = L.tile_of_nnz()
-        self.tile_of_csr = np.empty_like(tile_canon)
-        self.tile_of_csr[L.perm] = tile_canon
-        a = np.asarray(data, dtype=np.float64)
+        tile_of_csr = np.empty_like(tile_canon)
+        tile_of_csr[L.perm] = tile_canon
+        order = _row_order(indptr, reverse_rows)
+        self.tile_of_csr = tile_of_csr[order]
+        a = np.asarray(data, dtype=np.float64)[order]
         self.streams = (a, to_fp32(a).astype(np.float64), to_bf16_value(a))
-        self.M = sp.csr_matrix((a.copy(), np.asarray(indices), np.asarray(indptr)),
+        self.M = sp.csr_matrix((a.copy(), np.asarray(indices)[order], np.asarray(indptr)),
                                shape=(L.n, L.n))
 
     def set_map(self, prec_map):
@@ -137,16 +154,20 @@ class P1Operator:
     at precision m.
     """
 
-    def __init__(self, L: TileCSC, indptr, indices, data, round_vector=True, column_scale=False):
+    def __init__(self, L: TileCSC, indptr, indices, data, round_vector=True, column_scale=False,
+                 reverse_rows=False):
         self.n = L.n
         tile_canon = L.tile_of_nnz()
-        self.tile_of_csr = np.empty_like(tile_canon)
-        self.tile_of_csr[L.perm] = tile_canon
+        tile_of_csr = np.empty_like(tile_canon)
+        tile_of_csr[L.perm] = tile_canon
+        order = _row_order(indptr, reverse_rows)
+        self.tile_of_csr = tile_of_csr[order]
         self.indptr = np.asarray(indptr)
-        self.indices = np.asarray(indices)
+        self.indices = np.asarray(indices)[order]
         a = np.asarray(data, dtype=np.float64)
         e = (column_scale_exponents(L.n, indptr, indices, a)[self.indices] if column_scale
              else np.zeros(a.size, dtype=np.int64))
+        a = a[order]
         self.streams = tuple(p1_stored_values(a, np.full(a.size, m, np.uint8), e) for m in (0, 1, 2))
         self.round_vector = round_vector
         self.parts = []
@@ -171,19 +192,21 @@ class P1Operator:
 
 def solve(L: TileCSC, indptr, indices, data, b, schedule, tol, maxit, x0=None,
           jacobi=False, trace=None, keep_maps=True, round_vector=False,
-          column_scale=False) -> Result:
+          column_scale=False, reverse_rows=False) -> Result:
     """CG (or Jacobi-PCG) with the mixed-precision product.
 
     round_vector / column_scale select the paper's own product (P1Operator);
-    r0 = b - A x0 always uses the exact FP64 matrix.
+    r0 = b - A x0 always uses the exact FP64 matrix. reverse_rows sums the product's rows in
+    reverse storage order: a second correct rounding of the same iteration, whose distance
+    from the first shows how far rounding order alone moves a run.
     """
     n = L.n
     A = sp.csr_matrix((np.asarray(data, dtype=np.float64), np.asarray(indices),
                        np.asarray(indptr)), shape=(n, n))
     if round_vector or column_scale:
-        op = P1Operator(L, indptr, indices, data, round_vector, column_scale)
+        op = P1Operator(L, indptr, indices, data, round_vector, column_scale, reverse_rows)
     else:
-        op = PerturbedOperator(L, indptr, indices, data)
+        op = PerturbedOperator(L, indptr, indices, data, reverse_rows)
     b = np.asarray(b, dtype=np.float64)
     x = np.zeros(n) if x0 is None else np.array(x0, dtype=np.float64)
     r = b - A @ x

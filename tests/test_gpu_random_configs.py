@@ -5,10 +5,12 @@ handle options (Jacobi, column slices, vector staging, the single-workgroup solv
 SpMV numerics). Every case checks:
 - the exported layout and value planes, bit for bit;
 - the SpMV on every row (1e-13 (|A||x|)_i, or the oracle's own bound with the paper's numerics);
-- a CG solve: the first 20 residuals to 1e-6 always; for runs the oracle finishes within 150
-  iterations also the status, K within 2 % and the true residual within 1e-2; slower or capped
-  runs, whose end depends on the summation order, must not end more than ten times behind the
-  oracle's true residual;
+- a CG solve against the oracle run twice, with each row of its product summed in storage order
+  and in reverse order (two correct roundings; where they part, rounding order alone decides):
+  the first 20 residuals to 1e-6, up to where the two oracle runs part by more than 1e-10; for
+  runs the oracle finishes within 150 iterations also the status, K within 2 % of the range
+  the two oracle runs span and the true residual within 1e-2 of theirs; slower or capped runs
+  must not end more than ten times behind the oracle's true residual;
 - the library's true residual and its allocation-free twin (the same bits) against the host's,
   up to the rounding of b - A x.
 The cases are drawn once from a fixed seed. Environment overrides for longer sweeps:
@@ -100,6 +102,12 @@ def _case(i):
     return A, R, C, sched, opts, b, rng
 
 
+def _fresh(sched):
+    """A schedule object in its initial state (the schedules keep their stage or window)."""
+    import copy
+    return copy.deepcopy(sched)
+
+
 def _spmv_ref(Lo, A, prec, x, p1):
     if p1 & (RV | CS):
         e = ospmv.column_scale_exponents(A.n, A.indptr, A.indices, A.data) if p1 & CS else None
@@ -175,8 +183,10 @@ def test_random_configuration_matches_oracle(i, dev):
     # With the vector rounded the true residual floors near 1e-3; stop above it.
     tol = 1e-2 if opts["p1"] & RV else 1e-10
     maxit = 400
-    ref = ocg.solve(Lo, A.indptr, A.indices, A.data, b, ref_sched, tol, maxit, jacobi=opts["jacobi"],
-                    keep_maps=False, round_vector=bool(opts["p1"] & RV), column_scale=bool(opts["p1"] & CS))
+    refs = [ocg.solve(Lo, A.indptr, A.indices, A.data, b, sch, tol, maxit, jacobi=opts["jacobi"], keep_maps=False,
+                      round_vector=bool(opts["p1"] & RV), column_scale=bool(opts["p1"] & CS), reverse_rows=rev)
+            for sch, rev in ((ref_sched, False), (_fresh(ref_sched), True))]
+    ref = refs[0]
     bd = torch.from_numpy(b).to(dev)
     xs = torch.zeros_like(bd)
     status, K, hist = S.cg_solve(bd, xs, tol, maxit)
@@ -191,23 +201,32 @@ def test_random_configuration_matches_oracle(i, dev):
     xh = xs.cpu().numpy()
     slack = 1e-13 * np.linalg.norm(abs(A.S) @ np.abs(xh) + np.abs(b)) / np.linalg.norm(b)
     assert abs(tr_dev - tr) <= 1e-10 * tr + slack, (tr_dev, tr)
-    log(f"  gpu {status} K={K} true={tr:.3e}; oracle {ref.status} K={ref.K} true={ref.true_residual:.3e}")
-    k = min(K, ref.K, 20)
+    Ks = [r.K for r in refs]
+    ts = [r.true_residual for r in refs]
+    log(f"  gpu {status} K={K} true={tr:.3e}; oracle {ref.status} K={Ks} true={ts}")
+    # Where the two oracle roundings part by more than 1e-10, rounding order alone decides.
+    h0, h1 = np.asarray(refs[0].hist), np.asarray(refs[1].hist)
+    kk = min(h0.size, h1.size)
+    apart = np.abs(h0[:kk] - h1[:kk]) > 1e-10 * h0[:kk]
+    onset = int(np.argmax(apart)) if apart.any() else kk
+    k = min(K, ref.K, 20, onset - 1)
     assert np.allclose(hist[: k + 1], ref.hist[: k + 1], rtol=1e-6, atol=0)
     if ref.status == "breakdown":
-        assert status == "breakdown"
+        assert status == "breakdown" or status == refs[1].status
     elif ref.status == "converged" and ref.K <= 150:
-        # A clean run: the bars of the workload tests. Near the tolerance the true residual
-        # differs from the recurrence's by a rounding gap that depends on the summation
-        # order, so both are clamped at twice the tolerance.
-        assert status == ref.status, (status, ref.status)
-        assert abs(K - ref.K) <= max(1, int(0.02 * ref.K)), (K, ref.K)
-        a, r = max(tr, 2 * tol), max(ref.true_residual, 2 * tol)
-        assert abs(a - r) <= 1e-2 * r, (tr, ref.true_residual)
+        # A clean run: the bars of the workload tests, against the range of the two roundings.
+        # Near the tolerance the true residual differs from the recurrence's by a rounding gap
+        # that depends on the summation order, so both are clamped at twice the tolerance.
+        assert status in (ref.status, refs[1].status), (status, ref.status)
+        dK = max(1, int(0.02 * max(Ks)))
+        assert min(Ks) - dK <= K <= max(Ks) + dK, (K, Ks)
+        a = max(tr, 2 * tol)
+        lo, hi = max(min(ts), 2 * tol), max(max(ts), 2 * tol)
+        assert lo * (1 - 1e-2) <= a <= hi * (1 + 1e-2), (tr, ts)
     else:
         # Slow or capped runs under a perturbed operator: K, the final iterate and its true
         # residual depend on the summation order (the design notes' reading R27); the
         # solve must still not end far behind the oracle's.
         assert status in ("converged", "maxit"), status
-        assert tr <= 10 * max(ref.true_residual, tol), (tr, ref.true_residual)
+        assert tr <= 10 * max(max(ts), tol), (tr, ts)
     S.close()

@@ -209,3 +209,49 @@ def test_low_precision_values_raise_true_residual_floor():
                    cg.StaticSchedule(np.zeros(L.T, np.uint8)), 1e-10, 10_000)
     assert r64.status == "converged" and r64.true_residual < 1e-9
     assert r16.true_residual > 100 * r16.hist[-1]
+
+
+def test_reversed_row_order_is_the_same_product_rounded_differently():
+    """reverse_rows sums each row of the product in the opposite order: the exact sum of the
+    same terms (integer values: bit for bit), the same value within rounding on real data,
+    and a different rounding on rows whose terms cancel."""
+    rng = np.random.default_rng(5)
+    n = 300
+    M = sp.random(n, n, density=0.05, random_state=np.random.RandomState(5), format="csr")
+    M = _csr(M + M.T + sp.diags(np.full(n, 40.0)))
+    L = tc.build(n, M.indptr, M.indices, M.data, 16, 16)
+    m = rng.integers(0, 3, L.T).astype(np.uint8)
+    for p1 in (False, True):
+        ops = [cg.P1Operator(L, M.indptr, M.indices, M.data, True, True, rev) if p1 else
+               cg.PerturbedOperator(L, M.indptr, M.indices, M.data, rev) for rev in (False, True)]
+        for op in ops:
+            op.set_map(m)
+        # Integer-valued data and vector: every partial sum is exact in either order.
+        Mi = _csr(sp.csr_matrix((np.round(M.data * 4), M.indices, M.indptr), shape=(n, n)))
+        Li = tc.build(n, Mi.indptr, Mi.indices, Mi.data, 16, 16)
+        xi = rng.integers(-8, 9, n).astype(np.float64)
+        ints = [cg.PerturbedOperator(Li, Mi.indptr, Mi.indices, Mi.data, rev) for rev in (False, True)]
+        for op in ints:
+            op.set_map(np.zeros(Li.T, np.uint8))
+        assert np.array_equal(ints[0] @ xi, ints[1] @ xi)
+        x = rng.uniform(-1, 1, n)
+        y0, y1 = ops[0] @ x, ops[1] @ x
+        bound = 1e-13 * (abs(M) @ np.abs(x))
+        assert np.all(np.abs(y0 - y1) <= bound)
+        assert np.any(y0 != y1)  # the order did change
+
+
+def test_reversed_row_order_solve_agrees_on_a_well_conditioned_system():
+    rng = np.random.default_rng(6)
+    n = 200
+    M = sp.random(n, n, density=0.03, random_state=np.random.RandomState(6), format="csr")
+    M = _csr(M + M.T + sp.diags(np.full(n, 10.0)))
+    L = tc.build(n, M.indptr, M.indices, M.data, 8, 8)
+    b = rng.standard_normal(n)
+    sched = cg.StaticSchedule(np.zeros(L.T, np.uint8))
+    r0 = cg.solve(L, M.indptr, M.indices, M.data, b, sched, 1e-12, 500)
+    r1 = cg.solve(L, M.indptr, M.indices, M.data, b, sched, 1e-12, 500, reverse_rows=True)
+    assert r0.status == r1.status == "converged" and abs(r0.K - r1.K) <= 1
+    k = min(r0.K, r1.K)
+    assert np.allclose(r0.hist[:k], r1.hist[:k], rtol=1e-9, atol=0)
+    assert np.linalg.norm(r0.x - r1.x) <= 1e-10 * np.linalg.norm(r0.x)
