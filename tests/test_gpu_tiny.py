@@ -104,3 +104,46 @@ def test_tiny_system_matches_oracle(n, kind, R, C, single_block, jacobi, dev):
     tr = np.linalg.norm(b - M @ xh) / np.linalg.norm(b)
     assert tr <= 10 * max(ref.true_residual, 1e-12), (tr, ref.true_residual)
     S.close()
+
+
+SCHED_CASES = [(n, R, C) for n in (1, 2, 5, 17) for (R, C) in ((1, 1), (16, 16), (256, 256))]
+
+
+@pytest.mark.parametrize("n,R,C", SCHED_CASES)
+@pytest.mark.parametrize("sched", ["tile_rule", "pmag", "ratchet"])
+@pytest.mark.parametrize("p1", [0, 3])
+def test_tiny_system_schedules_match_oracle(n, R, C, sched, p1, dev):
+    """The rules that change the map during a solve (the windowed tile rule, the max|p| rule,
+    the residual stages), with and without the paper's SpMV numerics (vector rounding and
+    column scale), on the smallest systems: status, K within one and the true residual."""
+    indptr, indices, data, M = _matrix(n, "dense" if n > 1 else "tri")
+    L = mpcg.cg_tilecsc_from_csr(n, indptr, indices, data, R, C)
+    Lo = otc.build(n, indptr, indices, data, R, C)
+    rng = np.random.default_rng(7 * n + R + C)
+    S = mpcg.Solver(L, p1=p1)
+    if sched == "tile_rule":
+        scores = rng.uniform(0, 1, L.T) * 10.0 ** rng.integers(-2, 3, L.T)
+        S.cg_set_schedule_tile_rule(2, scores, 1e-1, 1e-4)
+        rs = ocg.TileRuleSchedule(scores, 2, 1e-1, 1e-4)
+    elif sched == "pmag":
+        S.cg_set_schedule_pmag(1e-6, 1e-3, period=1)
+        rs = ocg.PMagSchedule(Lo.C, Lo.tile_col_idx, 1e-6, 1e-3, 1)
+    else:
+        S.cg_set_schedule_residual((1e-2, 1e-5), (2, 1, 0))
+        rs = ocg.RatchetSchedule((1e-2, 1e-5), (2, 1, 0))
+    b = M @ rng.uniform(-1, 1, n)
+    tol, maxit = (1e-2 if p1 else 1e-12), 100
+    ref = ocg.solve(Lo, indptr, indices, data, b, rs, tol, maxit, keep_maps=False,
+                    round_vector=bool(p1 & mpcg.CG_P1_ROUND_VECTOR),
+                    column_scale=bool(p1 & mpcg.CG_P1_COLUMN_SCALE))
+    bd = torch.from_numpy(b).to(dev)
+    xs = torch.full_like(bd, float("nan"))
+    status, K, hist = S.cg_solve(bd, xs, tol, maxit)
+    log(f"tiny n={n} R={R} C={C} {sched} p1={p1}: gpu {status} K={K}; oracle {ref.status} K={ref.K}")
+    assert status == ref.status
+    assert abs(K - ref.K) <= 1
+    xh = xs.cpu().numpy()
+    assert np.all(np.isfinite(xh))
+    tr = np.linalg.norm(b - M @ xh) / np.linalg.norm(b)
+    assert tr <= 10 * max(ref.true_residual, tol), (tr, ref.true_residual)
+    S.close()
