@@ -8,9 +8,10 @@ SpMV numerics). Every case checks:
 - a CG solve against the oracle run twice, with each row of its product summed in storage order
   and in reverse order (two correct roundings; where they part, rounding order alone decides):
   the first 20 residuals to 1e-6, up to where the two oracle runs part by more than 1e-10; for
-  runs the oracle finishes within 150 iterations also the status, K within 2 % of the range
-  the two oracle runs span and the true residual within 1e-2 of theirs; slower or capped runs
-  must not end more than ten times behind the oracle's true residual;
+  runs the oracle finishes within 150 iterations with both roundings together to the end also
+  the status, K within 2 % of the range the two oracle runs span and the true residual within
+  1e-2 of theirs; slower, capped or order-sensitive runs must not end more than ten times
+  behind the oracle's true residual;
 - the library's true residual and its allocation-free twin (the same bits) against the host's,
   up to the rounding of b - A x.
 The cases are drawn once from a fixed seed. Environment overrides for longer sweeps:
@@ -213,8 +214,9 @@ def test_random_configuration_matches_oracle(i, dev):
     assert np.allclose(hist[: k + 1], ref.hist[: k + 1], rtol=1e-6, atol=0)
     if ref.status == "breakdown":
         assert status == "breakdown" or status == refs[1].status
-    elif ref.status == "converged" and ref.K <= 150:
-        # A clean run: the bars of the workload tests, against the range of the two roundings.
+    elif ref.status == "converged" and ref.K <= 150 and onset > min(Ks):
+        # A clean run (the two roundings stay together to the end): the bars of the workload
+        # tests, against the range of the two roundings.
         # Near the tolerance the true residual differs from the recurrence's by a rounding gap
         # that depends on the summation order, so both are clamped at twice the tolerance.
         assert status in (ref.status, refs[1].status), (status, ref.status)
@@ -224,9 +226,11 @@ def test_random_configuration_matches_oracle(i, dev):
         lo, hi = max(min(ts), 2 * tol), max(max(ts), 2 * tol)
         assert lo * (1 - 1e-2) <= a <= hi * (1 + 1e-2), (tr, ts)
     else:
-        # Slow or capped runs under a perturbed operator: K, the final iterate and its true
-        # residual depend on the summation order (the design notes' reading R27); the
-        # solve must still not end far behind the oracle's.
+        # Slow or capped runs under a perturbed operator, and runs whose two oracle roundings
+        # part before the end (where the max|p| and tile rules then see different vectors and
+        # choose different maps): K, the final iterate and its true residual depend on the
+        # summation order (the design notes' reading R27); the solve must still not end far
+        # behind the oracle's.
         assert status in ("converged", "maxit"), status
         assert tr <= 10 * max(max(ts), tol), (tr, ts)
     S.close()
