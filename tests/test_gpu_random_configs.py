@@ -229,8 +229,7 @@ def test_random_configuration_matches_oracle(i, dev):
         # Slow or capped runs under a perturbed operator, and runs whose two oracle roundings
         # part before the end (where the max|p| and tile rules then see different vectors and
         # choose different maps): K, the final iterate and its true residual depend on the
-        # summation order (the design notes' reading R27); the solve must still not end far
-        # behind the oracle's.
+        # summation order; the solve must still not end far behind the oracle's.
         assert status in ("converged", "maxit"), status
         assert tr <= 10 * max(max(ts), tol), (tr, ts)
     S.close()
