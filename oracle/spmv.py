@@ -4,7 +4,7 @@ EvoCG models a reduced-precision SpMV as y = (A + E(a)) p (Eq. 2 and Eq. 5):
 tile t's entries are read from the value stream its precision code selects
 (Sec. 3.3.2), widened exactly, multiplied by the FP64 vector entry and summed
 in FP64. The vector is not rounded (a reading: the paper's action names "the
-vector tile and its column block", this build rounds only the matrix).
+vector tile and its column block", this definition rounds only the matrix).
 
 Two forms are given:
 
